@@ -1,0 +1,214 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path over an FP4 global KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on DeepSeek V4.1 Flash; cited by host, title and section):
+ *   [JU]  jokeuncle.pages.dev, "两张架构图里藏着 890 字节", sections 二, 三, 四
+ *   [WG]  weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本", sections 3.1, 3.2, 4
+ *   [SY]  syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B",
+ *         sections "CSA2" (Figure 4), "Hierarchical Sparse Indexer" (Figure 5),
+ *         "FP4 主 KV 缓存" (Figure 1(b))
+ *   [GP]  ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", sections 3.2, 3.3, 7
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on `stream`; none of them synchronises.
+ *  - The caller owns every buffer, including the workspace; the library holds
+ *    no state and allocates nothing, so calls are re-entrant.  Two calls that
+ *    share a workspace must be ordered on one stream.
+ *  - Return value: CSA2_OK or an error code.  Host-side validation runs before
+ *    any launch; on a validation error nothing is launched and no output is
+ *    written.  CSA2_ERR_HIP reports a launch failure; faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - Device-side lengths (`len`, `swa_len`, `pool_len`) are clamped to their
+ *    buffer capacities; device-side indices outside [0, len_b) or equal to -1
+ *    are masked (never dereferenced, never selected, never attended).
+ *
+ * FP4 cache planes (structure-of-arrays, one plane per field)
+ * ----------------------------------------------------------
+ *  An FP4 row of `dim` values is stored as
+ *     codes  : dim/2 bytes; value 2i in bits 0-3, value 2i+1 in bits 4-7;
+ *              each nibble is E2M1 (sign, 2 exponent bits, 1 mantissa bit,
+ *              magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6})          [JU 三 事实一]
+ *     scales : dim/group bytes, one per consecutive `group` values.
+ *  value = e2m1(code) * scale(byte).
+ *  Main KV    : dim 512, group 16 -> 256 + 32 = 288 B per entry; the scale byte is
+ *               E4M3 on the pages [JU 三 事实一; SY FP4 主 KV 缓存; GP 7] or E8M0
+ *               ("MXFP4") -- both are supported, chosen by `main_fmt`.
+ *  Indexer K  : dim 128, group 32, E8M0 -> 64 + 4 = 68 B per entry [JU 三 事实二].
+ *  A cache for B sequences of capacity `cap` entries is laid out
+ *     main_codes [B][cap][256], main_scales [B][cap][32],
+ *     idx_codes  [B][cap][64],  idx_scales  [B][cap][4].
+ *  Planes must be 16-byte aligned.
+ *
+ * Quantisation rule (the pages fix the format, not the rounding; readings):
+ *  scale = the smallest representable scale s with 6*s >= max|x| over the
+ *  group (E8M0: s = 2^(b-127), b in [0,254]; E4M3: OCP E4M3FN finite codes
+ *  0x00..0x7E); the maximum code when none qualifies; code 0 when max|x| = 0.
+ *  Each |x|/s is rounded to the nearest E2M1 magnitude, ties to the even code;
+ *  a zero magnitude always encodes as +0 (code 0).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- constants of the published configuration [JU 二 config map; JU 三] ---- */
+#define CSA2_MAIN_DIM 512          /* head_dim of the compressed main KV          */
+#define CSA2_MAIN_GROUP 16         /* values per main-KV scale byte               */
+#define CSA2_MAIN_CODE_BYTES 256   /* 512 values x 4 bit                          */
+#define CSA2_MAIN_SCALE_BYTES 32   /* 512 / 16                                    */
+#define CSA2_IDX_DIM 128           /* index_head_dim                              */
+#define CSA2_IDX_GROUP 32          /* values per indexer-K scale byte (E8M0)      */
+#define CSA2_IDX_CODE_BYTES 64
+#define CSA2_IDX_SCALE_BYTES 4
+#define CSA2_INDEX_TOPK 512        /* index_topk                                  */
+#define CSA2_BLOCK 8               /* candidate_block_size                        */
+#define CSA2_POOL_BLOCKS 2048      /* candidate_topk_blocks                       */
+#define CSA2_SWA 128               /* sliding_window                              */
+#define CSA2_ATTN_HEADS 64         /* query heads of the core attention           */
+
+#define CSA2_MAX_TOPK 2048
+#define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
+#define CSA2_MAX_CACHE_ROWS 1048576 /* entries per sequence accepted by index_full */
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  CSA2_ERR_SHAPE = 2,       /* a size argument is out of range or inconsistent   */
+  CSA2_ERR_ALIGN = 3,       /* a plane pointer is not 16-byte aligned            */
+  CSA2_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head count)       */
+  CSA2_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  CSA2_ERR_HIP = 6          /* a HIP launch failed                               */
+} csa2_status;
+
+typedef enum { CSA2_SCALE_E8M0 = 0, CSA2_SCALE_E4M3 = 1 } csa2_scale_fmt;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* csa2_status_string(int status);
+
+/* Library version, as "csa2 <major>.<minor> gfx950". */
+const char* csa2_version(void);
+
+/*
+ * csa2_quantize_fp4 -- FP4 (E2M1) quantisation of fp32 rows with one scale
+ * byte per `group` values.  It is the quantiser the cache write applies to the
+ * main KV and to the indexer K [JU 三 事实一, 事实二; GP 7].
+ *   x      : fp32 [rows][dim], row-major.
+ *   dim    : multiple of `group`; group is 16 or 32; dim <= 4096.
+ *   fmt    : CSA2_SCALE_E8M0 or CSA2_SCALE_E4M3.
+ *   codes  : out, u8 [rows][dim/2].   scales : out, u8 [rows][dim/group].
+ * Errors: NULL pointer, rows < 0, bad dim/group/fmt, misaligned x/codes.
+ */
+int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group,
+                      int32_t fmt, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * csa2_cache_write -- the compressor of a KV-source (Full) layer writing T
+ * tokens as T/m compressed entries [JU 四 item 1; GP 3.2 (Z); SY CSA2]:
+ *   for group j (tokens m*j .. m*j+m-1) and channel c:
+ *     pooled[c] = sum_t softmax_t(gate[t][c]) * latent[t][c]   (fp32; m == 1: latent)
+ *     y = pooled * rsqrt(mean_c(pooled^2) + eps) * gamma        (RMSNorm)
+ *     main entry = FP4(y), group 16, scale format `main_fmt`
+ *     k = y @ w_idx (512 -> 128, fp32)  -> FP4(k), group 32, E8M0 (indexer K)
+ *   latent, gate : bf16 bits [T][512]; gate is not read when m == 1 (may be NULL).
+ *   m            : tokens per entry, 1..8; T must be a multiple of m.
+ *   gamma        : fp32 [512] RMSNorm weight, NULL = all ones.
+ *   w_idx        : fp32 [512][128] indexer-K projection (row c, column d).
+ *   main_codes/main_scales/idx_codes/idx_scales : out, rows [T/m] of the
+ *                  planes above, i.e. pointers to the destination entry.
+ * Errors: NULL pointer, T < 0, T % m != 0, m outside 1..8, bad main_fmt,
+ *         misaligned planes.
+ */
+int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int32_t m,
+                     const float* gamma, float eps, const float* w_idx, int32_t main_fmt,
+                     uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
+                     uint8_t* idx_scales, void* stream);
+
+/*
+ * csa2_index_full -- Full-mode hierarchical sparse indexer: one scoring pass
+ * over every visible entry, feeding two selections [GP 3.3; SY Figure 5; WG 3.2]:
+ *   score[b][p] = sum_h w[b][h] * max(0, q[b][h] . deq(idx K[b][p]))  for p < len[b]
+ *   topk[b]  : the k positions of highest score (ties: lower position first),
+ *              written in ascending position order, -1 padded when len[b] < k.
+ *   blocks   : block i covers positions [block*i, block*i+block) ∩ [0, len[b]);
+ *              its score is the maximum member score (an upper bound of each).
+ *              The n_blocks highest-scoring blocks (ties: lower block first) are
+ *              expanded into pool[b] (ascending positions, -1 padded to
+ *              n_blocks*block); pool_len[b] = number of positions written.
+ *   idx_codes/idx_scales : indexer-K planes [B][cap][64] / [B][cap][4].
+ *   len      : int32 [B] visible entries per sequence (device).
+ *   q        : bf16 bits [B][H][128] indexer queries; w : fp32 [B][H] head weights.
+ *   H        : 8, 16, 32 or 64.   k : 1..2048.   block : 8.
+ *   n_blocks : 0..2048 with n_blocks*block <= 16384; 0 = no pool.
+ *   topk     : out int32 [B][k].
+ *   pool, pool_len : out int32 [B][n_blocks*block], [B] (may be NULL iff n_blocks == 0).
+ *   scores_opt : optional out fp32 [B][cap]; entries p >= len[b] are unspecified.
+ *   ws, ws_bytes : workspace of at least csa2_index_full_workspace(...) bytes.
+ */
+size_t csa2_index_full_workspace(int32_t B, int64_t cap, int32_t k, int32_t block,
+                                 int32_t n_blocks);
+int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                    const int32_t* len, int32_t B, const uint16_t* q, const float* w,
+                    int32_t H, int32_t k, int32_t block, int32_t n_blocks, int32_t* topk,
+                    int32_t* pool, int32_t* pool_len, float* scores_opt, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_pool -- Reindex mode: a layer's own indexer query rescored over
+ * the shared candidate pool only, then its own top-k [SY Figure 5 (right);
+ * GP 3.3; SY CSA2 Figure 4 (Reindex)].  Same score formula as index_full.
+ *   pool     : int32 [B][pool_cap] positions (from csa2_index_full); entries
+ *              i < pool_len[b] are candidates; -1 or out-of-range are masked.
+ *   topk     : out int32 [B][k] ascending positions, -1 padded; ties prefer
+ *              the lower position.
+ *   pool_scores_opt : optional out fp32 [B][pool_cap] (score of pool[b][i]).
+ *   H, k as for csa2_index_full; pool_cap <= 16384.
+ */
+size_t csa2_index_pool_workspace(int32_t B, int32_t pool_cap, int32_t k);
+int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                    const int32_t* len, int32_t B, const int32_t* pool,
+                    const int32_t* pool_len, int32_t pool_cap, const uint16_t* q,
+                    const float* w, int32_t H, int32_t k, int32_t* topk,
+                    float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_sparse_attn_decode -- core attention of one CSA2 layer for one decode
+ * query per sequence: the selected main-KV entries concatenated with the
+ * sliding-window entries, attended by the layer's own query; FP4 is storage
+ * only, rows are dequantised before the products [SY CSA2 Figure 4; SY FP4 主 KV
+ * 缓存; JU 顺便算清另外三笔账 (512 + 128 positions)].
+ *   rows_b = [deq(main[b][topk[b][j]]) for valid j] ++ [deq(swa[b][r]) for r < swa_len[b]]
+ *   out[b][h] = softmax_j(sm_scale * q[b][h] . rows_b[j]) @ rows_b   (K = V = row)
+ *   q        : bf16 bits [B][H][512].  H : 16, 32 or 64 (multiple of 16).
+ *   main_codes/main_scales : main planes [B][cap][256] / [B][cap][32], format main_fmt.
+ *   len      : int32 [B] valid main entries per sequence.
+ *   topk     : int32 [B][k], k <= 2048 (any order; duplicates are attended twice).
+ *   swa_codes/swa_scales : window planes, sequence b at row offset b*swa_stride,
+ *              same format as main; swa_len : int32 [B] rows used (<= swa_cap).
+ *   swa_cap  : 0..128; may be 0 (then swa pointers may be NULL).
+ *   out      : out bf16 bits [B][H][512].
+ *   lse_opt  : optional out fp32 [B][H], natural-log sum of exp(sm_scale*logits);
+ *              -inf (and a zero output row) when a sequence attends no row.
+ *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes.
+ */
+size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap);
+int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                            const uint8_t* main_scales, int64_t cap, int32_t main_fmt,
+                            const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
+                            const uint8_t* swa_codes, const uint8_t* swa_scales,
+                            int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
+                            float sm_scale, uint16_t* out, float* lse_opt, void* ws,
+                            size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */
