@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of one CSA2 decoder step over an FP4 global KV cache on MI355X.
+
+A step is one pass of the whole hot path over one batch of decode queries:
+  cache write of the step's new entries (one token per sequence, ratio 1),
+  1 Full indexer call (scores every visible entry -> top-512 + 2048-block pool),
+  4 Reindex calls (pool rescoring -> own top-512),
+  20 sparse-attention calls (1 per decoder layer: top-512 rows + 128 window rows).
+Default workload: 16 sequences x 131072 FP4 entries (128K context), 64 indexer
+heads, 64 attention heads x 512 dims.  Inputs are seeded synthetic tensors,
+resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout.  `value` is indexer positions scored per
+second over whole steps; attention queries/s, per-call times and roofline
+fractions are reported alongside.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer positions scored/s + sparse-attn decode queries/s at 128K; % HBM roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step128",
+                    choices=["tiny", "full128", "step128", "write1m", "stress"])
+    ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
+                    help="main-KV scale byte format")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, choices=["write", "index_full", "index_pool", "attn"],
+                    help="run only one call type in the timed loop (for profiling)")
+    ap.add_argument("--copy-calib-mb", type=float, default=0.0,
+                    help="instead of the benchmark, run a plain device copy of this many MB "
+                         "(to calibrate HBM byte counters) and exit")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa):
+    """Bytes each call must move at minimum (inputs read once, outputs written once)."""
+    sum_len = int(sum(lengths))
+    sum_pool = int(sum(pool_len))
+    full = sum_len * 68 + B * (H_idx * 128 * 2 + H_idx * 4 + 4) + B * (k * 4 + n_blocks * 8 * 4 + 4)
+    pool = sum_pool * 68 + B * (n_blocks * 8 * 4 + 4) + B * (H_idx * 128 * 2 + H_idx * 4 + 4) + B * k * 4
+    rows = B * (k + swa)
+    attn = rows * 288 + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8
+    write = B * 512 * 2 + 512 * 128 * 4 + B * 356
+    return dict(write=write, index_full=full, index_pool=pool, attn=attn)
+
+
+def copy_calibration(mb: float):
+    import torch
+
+    n = int(mb * 1e6) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[copy] {n * 4} bytes read + {n * 4} bytes written per copy, 5 copies")
+
+
+def cpu_baseline(wl, fmt, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import csa2_synth as syn
+    import oracle
+
+    dev = torch.device("cuda:0")
+    n_idx = 1 + wl.n_reindex
+    positions = 0
+    spent = 0.0
+    seqs = 0
+    for b in range(wl.B):
+        xi = syn.idx_values(wl, b, dev).cpu().numpy()
+        xm = syn.main_values(wl, b, dev).cpu().numpy()
+        ic, isc = oracle.quantize(xi, 32, oracle.E8M0)
+        mc, ms = oracle.quantize(xm, 16, fmt)
+        del xi, xm
+        qw = [(syn.index_query(wl, i, dev)[b].cpu().numpy(), syn.index_weights(wl, i, dev)[b].cpu().numpy())
+              for i in range(n_idx)]
+        aq = [syn.attn_query(wl, j, dev)[b].cpu().numpy() for j in range(wl.n_attn_calls)]
+        L = wl.cap
+        t0 = time.perf_counter()
+        topk, pool, pl, _ = oracle.index_full(ic, isc, L, qw[0][0], qw[0][1], wl.k, 8, wl.n_blocks)
+        tks = [topk]
+        for i in range(1, n_idx):
+            t, _ = oracle.index_pool(ic, isc, L, pool, pl, qw[i][0], qw[i][1], wl.k)
+            tks.append(t)
+        j = 0
+        for i in range(n_idx):
+            for _ in range(1 + wl.reuse_per_index):
+                oracle.attention(aq[j], mc, ms, L, fmt, tks[i], mc[L - 128:], ms[L - 128:], 128,
+                                 1 / np.sqrt(512))
+                j += 1
+        spent += time.perf_counter() - t0
+        positions += L + (n_idx - 1) * pl
+        seqs += 1
+        log(f"[cpu] oracle sequence {b}: {spent:.1f}s so far")
+        if spent >= budget_s:
+            break
+    return dict(value=positions / spent, unit="positions/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{seqs} of {wl.B} sequences of one decoder step (full scoring, "
+                       f"{n_idx - 1} pool rescorings, {wl.n_attn_calls} attention calls), "
+                       f"{spent:.1f} s of oracle time")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the batch shards "
+              "trivially across GPUs, but no multi-GPU path is built here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_calib_mb > 0:
+        copy_calibration(args.copy_calib_mb)
+        return
+
+    import csa2_synth as syn
+    import compressed_kv_cache_mxfp4_amd as K
+    from compressed_kv_cache_mxfp4_amd.decode_step import DecodeStep
+
+    dev = torch.device("cuda:0")
+    wl = syn.WORKLOADS[args.workload]
+    fmt = K.E8M0 if args.fmt == "e8m0" else K.E4M3
+    B, cap = wl.B, wl.cap
+    log(f"[bench] {torch.cuda.get_device_name(dev)}; workload {wl.name}: B={B} M={cap} "
+        f"H_idx={wl.H_idx} k={wl.k} blocks={wl.n_blocks} layers={wl.n_attn_calls}")
+
+    # ---- resident inputs
+    cache = dict(
+        main_codes=torch.empty(B, cap, 256, dtype=torch.uint8, device=dev),
+        main_scales=torch.empty(B, cap, 32, dtype=torch.uint8, device=dev),
+        idx_codes=torch.empty(B, cap, 64, dtype=torch.uint8, device=dev),
+        idx_scales=torch.empty(B, cap, 4, dtype=torch.uint8, device=dev),
+    )
+    for b in range(B):
+        K.quantize_fp4(syn.main_values(wl, b, dev), 16, fmt, cache["main_codes"][b], cache["main_scales"][b])
+        K.quantize_fp4(syn.idx_values(wl, b, dev), 32, K.E8M0, cache["idx_codes"][b], cache["idx_scales"][b])
+    lengths = torch.full((B,), cap, dtype=torch.int32, device=dev)
+    step = DecodeStep(cache, lengths, k=wl.k, n_blocks=wl.n_blocks, n_reindex=wl.n_reindex,
+                      reuse_per_index=wl.reuse_per_index, main_fmt=fmt)
+    n_idx = 1 + wl.n_reindex
+    idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
+    attn_q = [syn.attn_query(wl, j, dev) for j in range(step.n_attn)]
+    # the step's new tokens: one per sequence, written as ratio-1 entries into a staging area
+    wl_w = syn.Workload("append", wl.seed + 100, B=B, cap=1, H_idx=8, k=1, block=8, n_blocks=0,
+                        write_tokens=B, write_m=1)
+    new_lat, _, w_proj = syn.write_inputs(wl_w, dev)
+    staged = dict(main_codes=torch.empty(B, 256, dtype=torch.uint8, device=dev),
+                  main_scales=torch.empty(B, 32, dtype=torch.uint8, device=dev),
+                  idx_codes=torch.empty(B, 64, dtype=torch.uint8, device=dev),
+                  idx_scales=torch.empty(B, 4, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+
+    only = args.only
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if only in (None, "write"):
+            K.cache_write(new_lat, None, 1, w_proj, fmt, out=staged)
+        if ev is not None:
+            ev[1].record()
+        if only in (None, "index_full", "index_pool"):
+            c = step.cache
+            if only != "index_pool":
+                q, w = idx_qw[0]
+                K.index_full(c["idx_codes"], c["idx_scales"], lengths, q, w, k=wl.k, n_blocks=wl.n_blocks,
+                             out=dict(topk=step.topk[0], pool=step.pool, pool_len=step.pool_len),
+                             _ws=step.ws_full)
+            if ev is not None:
+                ev[2].record()
+            if only != "index_full":
+                for i in range(1, n_idx):
+                    q, w = idx_qw[i]
+                    K.index_pool(c["idx_codes"], c["idx_scales"], lengths, step.pool, step.pool_len, q, w,
+                                 k=wl.k, out=dict(topk=step.topk[i]), _ws=step.ws_pool)
+        elif ev is not None:
+            ev[2].record()
+        if ev is not None:
+            ev[3].record()
+        if only in (None, "attn"):
+            step.run_attention(attn_q)
+        if ev is not None:
+            ev[4].record()
+
+    if only in ("index_pool", "attn"):
+        one_step_full = only
+        only = None
+        one_step()          # produce pool/top-k once
+        only = one_step_full
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    pool_len = step.pool_len.cpu().tolist()
+    log(f"[bench] warmup done; pool_len={pool_len[0]}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    seg = [[evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i in range(4)]
+    avg = [sum(x) / len(x) for x in seg]  # ms per step for each phase
+    n_pool = n_idx - 1
+    per_call_us = dict(write=avg[0] * 1e3, index_full=avg[1] * 1e3,
+                       index_pool=(avg[2] * 1e3 / n_pool) if n_pool else 0.0,
+                       attn=avg[3] * 1e3 / step.n_attn)
+    calls = dict(write=1, index_full=1, index_pool=n_pool, attn=step.n_attn)
+    nbytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128)
+    kernels = {}
+    for name in per_call_us:
+        us = per_call_us[name]
+        if calls[name] == 0 or us <= 0:
+            continue
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        kernels[name] = dict(calls_per_step=calls[name], us_per_call=round(us, 3),
+                             bytes_per_call=nbytes[name], achieved_GBs=round(gbs, 1),
+                             frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    dominant = max(kernels, key=lambda n: kernels[n]["us_per_call"] * kernels[n]["calls_per_step"])
+
+    positions = B * cap + n_pool * sum(pool_len)
+    value = positions / (ms_per_step * 1e-3)
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                tj = json.load(f)
+            traffic = tj.get(dominant, {}).get("bytes_per_call")
+        except (OSError, ValueError):
+            traffic = None
+    d = kernels[dominant]
+    roofline = dict(bound="hbm", kernel=f"csa2_{dominant}", achieved=d["achieved_GBs"], peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=d["frac_hbm"], traffic=traffic)
+    res = dict(
+        metric=METRIC, value=value, unit="positions/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic",
+        config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
+                    topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,
+                    layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
+                    main_scale=args.fmt.upper(), only=args.only),
+        attn_queries_per_s=B * step.n_attn / (ms_per_step * 1e-3),
+        kernels=kernels, roofline=roofline,
+    )
+    if not args.no_cpu_baseline and args.only is None:
+        del step, cache
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(wl, fmt, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

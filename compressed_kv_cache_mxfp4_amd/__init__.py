@@ -1,0 +1,25 @@
+"""MI355X (gfx950) implementation of the CSA2 decode hot path over an FP4
+global KV cache: cache write, hierarchical sparse indexer (Full and Reindex
+modes) and sparse attention, as hand-written HIP kernels behind the C ABI in
+include/csa2.h.  This package is the thin Python binding (ctypes + torch for
+device memory and streams)."""
+from ._lib import (  # noqa: F401
+    E4M3,
+    E8M0,
+    Csa2Error,
+    cache_write,
+    index_full,
+    index_pool,
+    lib,
+    quantize_fp4,
+    sparse_attn_decode,
+    workspace,
+)
+
+MAIN_DIM = 512
+IDX_DIM = 128
+TOPK = 512
+BLOCK = 8
+POOL_BLOCKS = 2048
+SWA = 128
+ATTN_HEADS = 64

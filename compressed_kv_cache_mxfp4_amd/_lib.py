@@ -1,0 +1,293 @@
+"""ctypes binding of libcsa2.so: argument marshalling only.
+
+Every function below checks tensor dtypes/shapes/devices, passes raw device
+pointers and the current HIP stream to the C ABI (include/csa2.h) and raises
+on a non-zero status.  All computation happens in the HIP kernels; there is no
+fallback path: if the library is missing, importing a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libcsa2.so")
+
+E8M0 = 0
+E4M3 = 1
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Csa2Error(
+            f"{LIB_PATH} is missing: build it with `python -m compressed_kv_cache_mxfp4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.csa2_status_string.restype = ctypes.c_char_p
+    L.csa2_status_string.argtypes = [ctypes.c_int]
+    L.csa2_version.restype = ctypes.c_char_p
+    L.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
+    L.csa2_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P]
+    L.csa2_index_full_workspace.restype = sz
+    L.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
+    L.csa2_index_full.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.csa2_index_pool_workspace.restype = sz
+    L.csa2_index_pool_workspace.argtypes = [i32, i32, i32]
+    L.csa2_index_pool.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, i32, P, P, P, sz, P]
+    L.csa2_attn_workspace.restype = sz
+    L.csa2_attn_workspace.argtypes = [i32, i32, i32, i32]
+    L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
+                                          P, f32, P, P, P, sz, P]
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = lib().csa2_status_string(rc).decode()
+        raise Csa2Error(f"{what}: {msg} (status {rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype, dev=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, dev: torch.device, kind: str = "index") -> torch.Tensor:
+    """A cached, zero-initialised uint8 device buffer of at least nbytes, one
+    per (device, stream, kind).  The attention workspace holds split counters
+    that must start at zero and that every call returns to zero, so it is
+    never shared with the indexer's scratch."""
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream, kind)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS[key] = buf
+    return buf
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors are passed as their 16-bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    return t
+
+
+# ------------------------------------------------------------------ quantiser
+def quantize_fp4(x: torch.Tensor, group: int, fmt: int, codes=None, scales=None):
+    """fp32 [..., dim] -> (codes u8 [..., dim/2], scales u8 [..., dim/group])."""
+    _req(x, "x", torch.float32)
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (dim // 2,), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (dim // group,), dtype=torch.uint8, device=dev)
+    _req(codes, "codes", torch.uint8, dev)
+    _req(scales, "scales", torch.uint8, dev)
+    _check(lib().csa2_quantize_fp4(_ptr(x), rows, dim, group, fmt, _ptr(codes), _ptr(scales),
+                                   _stream(dev)), "csa2_quantize_fp4")
+    return codes, scales
+
+
+# ---------------------------------------------------------------- cache write
+def cache_write(latent, gate, m: int, w_idx, main_fmt: int, gamma=None, eps: float = 1e-6,
+                out=None):
+    """latent/gate bf16 (or int16 bits) [T][512]; w_idx fp32 [512][128].
+
+    Returns dict(main_codes [T/m][256], main_scales [T/m][32], idx_codes [T/m][64],
+    idx_scales [T/m][4]); `out` may supply these tensors (e.g. views into a cache).
+    """
+    latent = _bits16(latent)
+    _req(latent, "latent", torch.int16)
+    dev = latent.device
+    T = latent.shape[0]
+    if m > 1:
+        gate = _bits16(gate)
+        _req(gate, "gate", torch.int16, dev, latent.shape)
+    else:
+        gate = None
+    _req(w_idx, "w_idx", torch.float32, dev, (512, 128))
+    if gamma is not None:
+        _req(gamma, "gamma", torch.float32, dev, (512,))
+    n = T // m
+    if out is None:
+        out = dict(
+            main_codes=torch.empty(n, 256, dtype=torch.uint8, device=dev),
+            main_scales=torch.empty(n, 32, dtype=torch.uint8, device=dev),
+            idx_codes=torch.empty(n, 64, dtype=torch.uint8, device=dev),
+            idx_scales=torch.empty(n, 4, dtype=torch.uint8, device=dev),
+        )
+    for key, width in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4)):
+        _req(out[key], key, torch.uint8, dev, (n, width))
+    _check(lib().csa2_cache_write(_ptr(latent), _ptr(gate), T, m, _ptr(gamma), float(eps),
+                                  _ptr(w_idx), main_fmt, _ptr(out["main_codes"]),
+                                  _ptr(out["main_scales"]), _ptr(out["idx_codes"]),
+                                  _ptr(out["idx_scales"]), _stream(dev)), "csa2_cache_write")
+    return out
+
+
+# -------------------------------------------------------------------- indexer
+def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int = 2048,
+               block: int = 8, return_scores: bool = False, out=None, _ws=None):
+    """Full-mode indexer over B sequences.
+
+    idx_codes u8 [B][cap][64], idx_scales u8 [B][cap][4], lengths int32 [B],
+    q bf16/int16 [B][H][128], w fp32 [B][H].
+    Returns (topk int32 [B][k], pool int32 [B][n_blocks*block], pool_len int32 [B]
+    [, scores fp32 [B][cap]]).
+    """
+    q = _bits16(q)
+    _req(idx_codes, "idx_codes", torch.uint8)
+    dev = idx_codes.device
+    B, cap = idx_codes.shape[0], idx_codes.shape[1]
+    _req(idx_codes, "idx_codes", torch.uint8, dev, (B, cap, 64))
+    _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    H = q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    out = out or {}
+    topk = out.get("topk")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=dev)
+    pool = out.get("pool")
+    if pool is None:
+        pool = torch.empty(B, max(n_blocks * block, 1), dtype=torch.int32, device=dev)
+    pool_len = out.get("pool_len")
+    if pool_len is None:
+        pool_len = torch.empty(B, dtype=torch.int32, device=dev)
+    scores = out.get("scores")
+    if return_scores and scores is None:
+        scores = torch.empty(B, cap, dtype=torch.float32, device=dev)
+    wsb = lib().csa2_index_full_workspace(B, cap, k, block, n_blocks)
+    ws = _ws if _ws is not None else workspace(wsb, dev)
+    _check(lib().csa2_index_full(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, _ptr(q),
+                                 _ptr(w), H, k, block, n_blocks, _ptr(topk), _ptr(pool),
+                                 _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
+           "csa2_index_full")
+    pool = pool[:, : n_blocks * block]
+    if return_scores:
+        return topk, pool, pool_len, scores
+    return topk, pool, pool_len
+
+
+def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 512,
+               return_scores: bool = False, out=None, _ws=None):
+    """Reindex mode: rescore pool [B][pool_cap] with (q, w), top-k per sequence."""
+    q = _bits16(q)
+    _req(idx_codes, "idx_codes", torch.uint8)
+    dev = idx_codes.device
+    B, cap = idx_codes.shape[0], idx_codes.shape[1]
+    _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    pool_cap = pool.shape[1]
+    _req(pool, "pool", torch.int32, dev, (B, pool_cap))
+    _req(pool_len, "pool_len", torch.int32, dev, (B,))
+    H = q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    out = out or {}
+    topk = out.get("topk")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=dev)
+    ps = out.get("pool_scores")
+    if return_scores and ps is None:
+        ps = torch.empty(B, pool_cap, dtype=torch.float32, device=dev)
+    wsb = lib().csa2_index_pool_workspace(B, pool_cap, k)
+    ws = _ws if _ws is not None else workspace(wsb, dev, "pool")
+    _check(lib().csa2_index_pool(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B,
+                                 _ptr(pool), _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, k,
+                                 _ptr(topk), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)),
+           "csa2_index_pool")
+    return (topk, ps) if return_scores else topk
+
+
+# ------------------------------------------------------------------ attention
+def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
+                       swa_codes=None, swa_scales=None, swa_len=None, swa_stride: int = 0,
+                       swa_cap: int = 0, swa_row0: int = 0, sm_scale: Optional[float] = None,
+                       return_lse: bool = False, out=None, _ws=None):
+    """Sparse attention over topk rows ++ window rows.
+
+    q bf16/int16 [B][H][512]; main planes [B][cap][256] / [B][cap][32];
+    topk int32 [B][k]; window row r of sequence b is row swa_row0 + b*swa_stride + r
+    of the contiguous tensors swa_codes (rows of 256 B) / swa_scales (rows of 32 B),
+    so the window may be a separate buffer or the tail of the main cache
+    (swa_codes=main_codes, swa_row0=cap-128, swa_stride=cap); swa_len int32 [B].
+    Returns out bf16 bits (int16) [B][H][512] (and lse fp32 [B][H]).
+    """
+    q = _bits16(q)
+    _req(q, "q", torch.int16)
+    dev = q.device
+    B, H = q.shape[0], q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 512))
+    cap = main_codes.shape[1]
+    _req(main_codes, "main_codes", torch.uint8, dev, (B, cap, 256))
+    _req(main_scales, "main_scales", torch.uint8, dev, (B, cap, 32))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    k = topk.shape[1]
+    _req(topk, "topk", torch.int32, dev, (B, k))
+    if swa_cap > 0:
+        if swa_codes.dtype != torch.uint8 or swa_scales.dtype != torch.uint8:
+            raise TypeError("window planes must be uint8")
+        if swa_codes.device != dev or swa_scales.device != dev:
+            raise ValueError("window planes on another device")
+        if not (swa_codes.is_contiguous() and swa_scales.is_contiguous()):
+            raise ValueError("window planes must be contiguous")
+        need = swa_row0 + (B - 1) * swa_stride + swa_cap
+        if swa_row0 < 0 or swa_codes.numel() < need * 256 or swa_scales.numel() < need * 32:
+            raise ValueError("window planes smaller than swa_row0 + B rows of swa_stride")
+        _req(swa_len, "swa_len", torch.int32, dev, (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / (512 ** 0.5)
+    o = None if out is None else out.get("out")
+    if o is None:
+        o = torch.empty(B, H, 512, dtype=torch.int16, device=dev)
+    lse = None
+    if return_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    wsb = lib().csa2_attn_workspace(B, H, k, swa_cap)
+    ws = _ws if _ws is not None else workspace(wsb, dev, "attn")
+    _check(lib().csa2_sparse_attn_decode(
+        _ptr(q), H, _ptr(main_codes), _ptr(main_scales), cap, main_fmt, _ptr(lengths), _ptr(topk), k,
+        B, ctypes.c_void_p(swa_codes.data_ptr() + 256 * swa_row0) if swa_cap else None,
+        ctypes.c_void_p(swa_scales.data_ptr() + 32 * swa_row0) if swa_cap else None,
+        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, float(sm_scale), _ptr(o),
+        _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode")
+    return (o, lse) if return_lse else o

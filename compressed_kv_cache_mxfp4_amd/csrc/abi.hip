@@ -1,0 +1,154 @@
+// abi.hip -- the extern "C" boundary of libcsa2 (declared in include/csa2.h).
+// Host-side validation happens here, before any launch; kernels live in
+// quant.hip, index.hip and attn.hip.
+#include <hip/hip_runtime.h>
+
+#include "csa2.h"
+#include "csa2_internal.hpp"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int launched(int rc) { return rc == 0 ? CSA2_OK : CSA2_ERR_HIP; }
+inline bool valid_fmt(int f) { return f == CSA2_SCALE_E8M0 || f == CSA2_SCALE_E4M3; }
+inline bool valid_index_heads(int H) { return H == 8 || H == 16 || H == 32 || H == 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "null pointer argument";
+    case CSA2_ERR_SHAPE: return "size argument out of range or inconsistent";
+    case CSA2_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* csa2_version(void) { return "csa2 0.1 gfx950"; }
+
+int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group, int32_t fmt,
+                      uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || dim <= 0 || dim > 4096) return CSA2_ERR_SHAPE;
+  if (group != 16 && group != 32) return CSA2_ERR_SHAPE;
+  if (dim % group != 0) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 1u)) return CSA2_ERR_ALIGN;
+  return launched(csa2::launch_quantize(x, rows, dim, group, fmt, codes, scales, as_stream(stream)));
+}
+
+int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int32_t m,
+                     const float* gamma, float eps, const float* w_idx, int32_t main_fmt,
+                     uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
+                     uint8_t* idx_scales, void* stream) {
+  if (T < 0 || m < 1 || m > 8 || T % m != 0) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return CSA2_ERR_SHAPE;
+  if (T == 0) return CSA2_OK;
+  if (!latent || (m > 1 && !gate) || !w_idx || !main_codes || !main_scales || !idx_codes || !idx_scales)
+    return CSA2_ERR_NULL;
+  if (!aligned16(latent) || (m > 1 && !aligned16(gate)) || !aligned16(main_codes) ||
+      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u))
+    return CSA2_ERR_ALIGN;
+  return launched(csa2::launch_cache_write(latent, gate, T, m, gamma, eps, w_idx, main_fmt,
+                                           main_codes, main_scales, idx_codes, idx_scales,
+                                           as_stream(stream)));
+}
+
+size_t csa2_index_full_workspace(int32_t B, int64_t cap, int32_t k, int32_t block,
+                                 int32_t n_blocks) {
+  (void)k;
+  (void)n_blocks;
+  if (B <= 0 || cap <= 0 || block != CSA2_BLOCK) return 0;
+  return csa2::index_full_ws_layout(B, cap, block).total;
+}
+
+int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                    const int32_t* len, int32_t B, const uint16_t* q, const float* w, int32_t H,
+                    int32_t k, int32_t block, int32_t n_blocks, int32_t* topk, int32_t* pool,
+                    int32_t* pool_len, float* scores_opt, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+  if (n_blocks < 0 || n_blocks > CSA2_POOL_BLOCKS || (int64_t)n_blocks * block > CSA2_MAX_POOL)
+    return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !len || !q || !w || !topk) return CSA2_ERR_NULL;
+  if (n_blocks > 0 && (!pool || !pool_len)) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  if (cap == 0) return CSA2_ERR_SHAPE;
+  if (!ws || ws_bytes < csa2_index_full_workspace(B, cap, k, block, n_blocks)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_full(idx_codes, idx_scales, cap, len, B, q, w, H, k, block,
+                                          n_blocks, topk, pool, pool_len, scores_opt, ws,
+                                          as_stream(stream)));
+}
+
+size_t csa2_index_pool_workspace(int32_t B, int32_t pool_cap, int32_t k) {
+  (void)k;
+  if (B <= 0 || pool_cap <= 0) return 0;
+  return csa2::index_pool_ws_bytes(B, pool_cap);
+}
+
+int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                    const int32_t* len, int32_t B, const int32_t* pool, const int32_t* pool_len,
+                    int32_t pool_cap, const uint16_t* q, const float* w, int32_t H, int32_t k,
+                    int32_t* topk, float* pool_scores_opt, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (B < 0 || cap <= 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (pool_cap < 0 || pool_cap > CSA2_MAX_POOL) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !len || !pool || !pool_len || !q || !w || !topk)
+    return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  if (!pool_scores_opt && (!ws || ws_bytes < csa2_index_pool_workspace(B, pool_cap, k)))
+    return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_pool(idx_codes, idx_scales, cap, len, B, pool, pool_len,
+                                          pool_cap, q, w, H, k, topk, pool_scores_opt, ws,
+                                          as_stream(stream)));
+}
+
+size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap) {
+  if (B <= 0 || H <= 0 || k < 0 || swa_cap < 0) return 0;
+  return csa2::attn_ws_bytes(B, H, k, swa_cap);
+}
+
+int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                            const uint8_t* main_scales, int64_t cap, int32_t main_fmt,
+                            const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
+                            const uint8_t* swa_codes, const uint8_t* swa_scales,
+                            int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
+                            float sm_scale, uint16_t* out, float* lse_opt, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
+  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!q || !out) return CSA2_ERR_NULL;
+  if (k > 0 && (!main_codes || !main_scales || !len || !topk)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)))
+    return CSA2_ERR_ALIGN;
+  if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
+                                           k, B, swa_codes, swa_scales, swa_stride, swa_cap,
+                                           swa_len, sm_scale, out, lse_opt, ws,
+                                           as_stream(stream)));
+}
+
+}  // extern "C"

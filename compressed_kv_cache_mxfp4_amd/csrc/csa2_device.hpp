@@ -1,0 +1,103 @@
+// csa2_device.hpp -- device-side helpers shared by the CSA2 kernels (gfx950).
+//
+// FP4 cache rows are E2M1 nibbles (value 2i in the low nibble of byte i) with
+// one scale byte per group [jokeuncle.pages.dev, "两张架构图里藏着 890 字节",
+// section 三].  Decoding uses the gfx950 scaled-convert instructions; their
+// scale operand is a power of two carried in the exponent field of an fp32,
+// which is exactly an E8M0 byte shifted into place.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// E8M0 byte as the fp32 power of two the scaled converts expect (b << 23;
+// b = 0 encodes 2^-127 the same way the hardware reads exponent field 0).
+__device__ __forceinline__ float e8m0_operand(uint32_t b) { return __uint_as_float(b << 23); }
+
+// Exact value of an E8M0 byte as an fp32 (0 -> 2^-127, a subnormal).
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return b == 0 ? __uint_as_float(0x00400000u) : (b == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(b << 23));
+}
+
+// Exact value of an OCP E4M3FN byte (positive codes; sign honoured).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (e == 0)
+    v = (float)m * 0x1p-9f;
+  else if (e == 15 && m == 7)
+    v = __uint_as_float(0x7FC00000u);
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+// Two E2M1 values of byte `sel` of `codes` -> bf16 pair, times 2^(b-127).
+template <int SEL>
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16(uint32_t codes, float e8m0_op) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, e8m0_op, SEL);
+}
+
+// Eight E2M1 values (one dword) -> bf16x8 with an E8M0 scale.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float e8m0_op) {
+  bf16x2 a = fp4x2_to_bf16<0>(codes, e8m0_op);
+  bf16x2 b = fp4x2_to_bf16<1>(codes, e8m0_op);
+  bf16x2 c = fp4x2_to_bf16<2>(codes, e8m0_op);
+  bf16x2 d = fp4x2_to_bf16<3>(codes, e8m0_op);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Eight E2M1 values -> fp32 with unit scale (for E4M3-scaled rows).
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t codes, float out[8]) {
+  const float one = 1.0f;
+  auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0);
+  auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1);
+  auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2);
+  auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3);
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
+// ------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return r >> 16;
+}
+
+}  // namespace csa2

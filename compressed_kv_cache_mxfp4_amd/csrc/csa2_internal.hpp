@@ -1,0 +1,47 @@
+// csa2_internal.hpp -- host-side launchers shared between the translation
+// units of libcsa2 (not part of the public C ABI).  Each returns 0 on success
+// and -1 when a launch failed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, uint8_t* codes,
+                    uint8_t* scales, hipStream_t st);
+
+int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int m,
+                       const float* gamma, float eps, const float* w_idx, int main_fmt,
+                       uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
+                       uint8_t* idx_scales, hipStream_t st);
+
+// Workspace layout of the indexer calls (bytes, 256-aligned pieces).
+struct IndexFullWs {
+  size_t scores_off, bmax_off, total;
+};
+IndexFullWs index_full_ws_layout(int B, int64_t cap, int block);
+
+int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const uint16_t* q, const float* w, int H, int k,
+                      int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
+                      float* scores_opt, void* ws, hipStream_t st);
+
+size_t index_pool_ws_bytes(int B, int pool_cap);
+
+int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
+                      int pool_cap, const uint16_t* q, const float* w, int H, int k,
+                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st);
+
+size_t attn_ws_bytes(int B, int H, int k, int swa_cap);
+
+int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
+                       const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,
+                       const int32_t* topk, int k, int B, const uint8_t* swa_codes,
+                       const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
+                       const int32_t* swa_len, float sm_scale, uint16_t* out, float* lse_opt,
+                       void* ws, hipStream_t st);
+
+}  // namespace csa2

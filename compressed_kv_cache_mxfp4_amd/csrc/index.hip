@@ -1,0 +1,571 @@
+// index.hip -- hierarchical sparse indexer for CSA2 decode on gfx950.
+//
+// Full mode [ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", section 3.3;
+// syt-nju.github.io, "为什么读输入只激活 8B", Figure 5; weigao.cc, section 3.2]:
+// one scoring pass over every visible indexer-K entry feeds two selections --
+// the position top-k (the layer's own attention set) and the block top-n
+// (block score = max of its 8 positions, an upper bound) whose expansion is the
+// shared candidate pool.  Reindex mode rescores only the pool with the layer's
+// own query and takes its own top-k.
+//
+// score(p) = sum_h w_h * max(0, q_h . K_p), K_p = FP4(E2M1) x E8M0 per 32 dims.
+//
+// Scoring kernel: streaming, HBM-bound.  Each wave keeps its query's heads in
+// registers as bf16 MFMA A-operands and walks 64-entry super-tiles; a lane
+// loads 16 B of FP4 codes (32 dims of one entry) plus that group's E8M0 byte,
+// which is exactly one B-operand fragment of v_mfma_f32_16x16x32_bf16 after a
+// register-level dequantisation (v_cvt_scalef32_pk_bf16_fp4).  The dims of a
+// 32-wide K step are permuted identically in A and B, so every load is one
+// contiguous 16-byte piece.  ReLU, head weights and the head sum run on the
+// accumulators; the 8-entry block maximum is a 3-step lane reduction.
+//
+// Selection kernel: one 1024-thread workgroup per sequence; keys held in
+// registers; an MSB radix search with adaptive bin ranges (2048 LDS bins per
+// pass, at most 3 passes) finds the k-th key, then a block scan emits the
+// winners in ascending index order with ties resolved to the lower index.
+#include "csa2_device.hpp"
+#include "csa2.h"
+#include "csa2_internal.hpp"
+
+namespace csa2 {
+
+// ======================================================================
+// Scoring
+// ======================================================================
+constexpr int kScoreThreads = 256;
+constexpr int kSuperTile = 64;
+
+struct StageRegs {
+  int32_t row;     // row this lane's item maps to (valid or a safe 0)
+  uint32_t valid;  // item exists and is visible
+  uint32_t sc;     // 4 scale bytes of this lane's item
+  uint4 cw[4];     // 16 code bytes for (tile t, this lane's group g)
+};
+
+template <bool GATHER>
+__device__ __forceinline__ void score_stage_load(StageRegs& s, int64_t base, int64_t N, int64_t L,
+                                                 const int32_t* __restrict__ pool_b,
+                                                 const uint8_t* __restrict__ codes_b,
+                                                 const uint8_t* __restrict__ scales_b, int lane) {
+  const int64_t it = base + lane;
+  int32_t row = 0;
+  uint32_t valid = 0;
+  if (it < N) {
+    if (GATHER) {
+      const int32_t p = pool_b[it];
+      if (p >= 0 && (int64_t)p < L) {
+        row = p;
+        valid = 1;
+      }
+    } else {
+      row = (int32_t)it;
+      valid = 1;
+    }
+  }
+  s.row = row;
+  s.valid = valid;
+  s.sc = *reinterpret_cast<const uint32_t*>(scales_b + (int64_t)row * 4);
+  const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int32_t r = GATHER ? __shfl(row, 16 * t + n, 64) : (int32_t)(((base + 16 * t + n) < N) ? (base + 16 * t + n) : 0);
+    s.cw[t] = *reinterpret_cast<const uint4*>(codes_b + (int64_t)r * 64 + 16 * g);
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ float score_stage_compute(const StageRegs& s, const bf16x8 (&A)[MT][4],
+                                                     const float (&wr)[MT][4], int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  float mine = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t s4 = (uint32_t)__shfl((int)s.sc, 16 * t + n, 64);
+    const float sop = e8m0_operand((s4 >> (8 * g)) & 0xFFu);
+    const uint32_t cw[4] = {s.cw[t].x, s.cw[t].y, s.cw[t].z, s.cw[t].w};
+    floatx4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bv = fp4x8_to_bf16(cw[ks], sop);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], bv, acc[mt], 0, 0, 0);
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += wr[mt][i] * __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+    part += shfl_xor_f(part, 16);
+    part += shfl_xor_f(part, 32);
+    if (g == t) mine = part;
+  }
+  return mine;
+}
+
+// Grid: (chunks, B).  Each workgroup scores `4 * stpw` super-tiles of one
+// sequence; with GATHER the items are pool[b][i], otherwise positions i.
+template <int MT, bool GATHER>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+    const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int64_t cap,
+    const int32_t* __restrict__ len, const int32_t* __restrict__ pool,
+    const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
+    const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
+    float* __restrict__ bmax, int64_t bmax_stride, int stpw) {
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, n = lane & 15;
+  int64_t L = len[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int64_t N = L;
+  if (GATHER) {
+    int64_t pl = pool_len[b];
+    N = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
+  }
+  const int64_t chunk0 = (int64_t)blockIdx.x * 4 * stpw * kSuperTile;
+  if (chunk0 >= N) return;
+
+  // Query heads as A operands: lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
+  bf16x8 A[MT][4];
+  float wr[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 16 * mt + n;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (h < H) {
+        const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * H + h) * 128 + 32 * g + 8 * ks);
+        A[mt][ks] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        A[mt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * mt + 4 * g + i;
+      wr[mt][i] = hh < H ? w[(int64_t)b * H + hh] : 0.0f;
+    }
+  }
+
+  const uint8_t* codes_b = idx_codes + (int64_t)b * cap * 64;
+  const uint8_t* scales_b = idx_scales + (int64_t)b * cap * 4;
+  const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
+  float* scores_b = scores + (int64_t)b * score_stride;
+
+  StageRegs cur, nxt;
+  int64_t base = chunk0 + (int64_t)wave * kSuperTile;
+  if (base >= N) return;
+  score_stage_load<GATHER>(cur, base, N, L, pool_b, codes_b, scales_b, lane);
+  for (int j = 0; j < stpw; ++j) {
+    const int64_t nbase = base + 4 * kSuperTile;
+    const bool more = (j + 1 < stpw) && (nbase < N);
+    if (more) score_stage_load<GATHER>(nxt, nbase, N, L, pool_b, codes_b, scales_b, lane);
+    const float sc = score_stage_compute<MT>(cur, A, wr, lane);
+    const int64_t it = base + lane;
+    if (it < N) scores_b[it] = cur.valid ? sc : __uint_as_float(0x7FC00000u);
+    if (!GATHER) {
+      float bm = (it < N) ? sc : -INFINITY;
+      bm = fmaxf(bm, shfl_xor_f(bm, 1));
+      bm = fmaxf(bm, shfl_xor_f(bm, 2));
+      bm = fmaxf(bm, shfl_xor_f(bm, 4));
+      if ((lane & 7) == 0 && it < N) bmax[(int64_t)b * bmax_stride + (it >> 3)] = bm;
+    }
+    if (!more) break;
+    cur = nxt;
+    base = nbase;
+  }
+}
+
+// ======================================================================
+// Selection
+// ======================================================================
+// One workgroup per sequence.  Keys (monotone uint32 images of the scores)
+// sit in registers with wave-contiguous ownership: candidate i lives in wave
+// i / (64*E), slot (i / 64) % E, lane i % 64, so loads are coalesced 64-wide
+// runs.  The k-th key is found by an MSB radix search whose bin range adapts
+// to the keys present (2048 LDS bins per pass, at most 3 passes); the winners
+// are emitted in ascending candidate order through wave ballots.  Ordering:
+// larger key first, equal keys to the lower candidate index.  Wave-level
+// reductions and scans use DPP (row shifts, mirrors, row broadcasts).
+
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// Reduce within each 16-lane row (every lane of the row gets the row's value).
+template <class Op>
+__device__ __forceinline__ uint32_t row_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_mov<0xB1>(v, 0u));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4E>(v, 0u));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141>(v, 0u));  // row_half_mirror
+  v = op(v, dpp_mov<0x140>(v, 0u));  // row_mirror
+  return v;
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = row_reduce(v, op);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_mov<0x111>(x, 0u);       // row_shr:1
+  x += dpp_mov<0x112>(x, 0u);       // row_shr:2
+  x += dpp_mov<0x114>(x, 0u);       // row_shr:4
+  x += dpp_mov<0x118>(x, 0u);       // row_shr:8
+  x += dpp_mov<0x142, 0xa>(x, 0u);  // row_bcast:15 into rows 1 and 3
+  x += dpp_mov<0x143, 0xc>(x, 0u);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+struct SelScratch {
+  uint32_t hist[2048];
+  uint32_t wred[3][16];
+  uint32_t bc[4];
+};
+
+// float -> uint32 key with the same order; NaN (absent) -> 0; -0 -> +0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.0f) return 0x80000000u;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int EPT>
+struct KeyRegs {
+  uint32_t r[EPT > 0 ? EPT : 1];
+};
+
+// Candidate of slot j for this thread.
+template <int NT, int EPT>
+__device__ __forceinline__ int sel_index(int n, int j) {
+  const int E = EPT > 0 ? EPT : (n + NT - 1) / NT;
+  return (threadIdx.x >> 6) * 64 * E + 64 * j + (threadIdx.x & 63);
+}
+
+template <int NT, int EPT, class Src>
+__device__ __forceinline__ void load_keys(KeyRegs<EPT>& K, const Src& src, int n) {
+  if constexpr (EPT > 0) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int i = sel_index<NT, EPT>(n, j);
+      K.r[j] = i < n ? src.key(i) : 0u;
+    }
+  }
+}
+
+// Top-k of the n candidates (key 0 = absent): calls emit(i, rank) for the
+// winners in ascending i, rank = 0, 1, ...; returns min(k, #present).
+template <int NT, int EPT, class Src, class Emit>
+__device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
+                           Emit emit) {
+  constexpr int NW = NT / 64;
+  constexpr int TB = 2048 / NT;  // histogram bins per thread in the search
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int E = EPT > 0 ? EPT : (n + NT - 1) / NT;
+  auto KEY = [&](int j) -> uint32_t {
+    if constexpr (EPT > 0) {
+      return K.r[j];
+    } else {
+      const int i = sel_index<NT, EPT>(n, j);
+      return i < n ? src.key(i) : 0u;
+    }
+  };
+  constexpr int UNR = EPT > 0 ? EPT : 1;
+
+  uint32_t cnt = 0u, mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll UNR
+  for (int j = 0; j < E; ++j) {
+    const uint32_t kk = KEY(j);
+    cnt += kk ? 1u : 0u;
+    mn = kk ? min(mn, kk) : mn;
+    mx = max(mx, kk);
+  }
+  cnt = wave_reduce(cnt, [](uint32_t a, uint32_t b) { return a + b; });
+  mn = wave_reduce(mn, [](uint32_t a, uint32_t b) { return min(a, b); });
+  mx = wave_reduce(mx, [](uint32_t a, uint32_t b) { return max(a, b); });
+  if (lane == 0) {
+    sh.wred[0][wave] = cnt;
+    sh.wred[1][wave] = mn;
+    sh.wred[2][wave] = mx;
+  }
+  __syncthreads();
+  cnt = sh.wred[0][0];
+  mn = sh.wred[1][0];
+  mx = sh.wred[2][0];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) {
+    cnt += sh.wred[0][v];
+    mn = min(mn, sh.wred[1][v]);
+    mx = max(mx, sh.wred[2][v]);
+  }
+  __syncthreads();  // every wave has read the partials before they are reused
+  const uint32_t target = min((uint32_t)k, cnt);
+  if (target == 0u) return 0;
+
+  uint32_t lo = mn, hi = mx, above = 0u, T;
+  for (;;) {
+    if (lo == hi) {
+      T = lo;
+      break;
+    }
+    const uint32_t span = hi - lo;
+    const int nbits = 32 - __clz((int)span);
+    const int shift = nbits > 11 ? nbits - 11 : 0;
+    const int nb = (int)(span >> shift) + 1;
+    for (int i = t; i < nb; i += NT) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll UNR
+    for (int j = 0; j < E; ++j) {
+      const uint32_t kk = KEY(j);
+      if (kk >= lo && kk <= hi) atomicAdd(&sh.hist[(kk - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins top, top-1, ..., top-TB+1 (descending score order)
+    const int top = nb - 1 - TB * t;
+    uint32_t hb[TB];
+    uint32_t s = 0u;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      hb[j] = (top - j) >= 0 ? sh.hist[top - j] : 0u;
+      s += hb[j];
+    }
+    const uint32_t incl = wave_incl_scan(s);
+    if (lane == 63) sh.wred[0][wave] = incl;
+    __syncthreads();
+    uint32_t excl = incl - s;
+    for (int v = 0; v < wave; ++v) excl += sh.wred[0][v];
+    const uint32_t need = target - above;
+    if (excl < need && need <= excl + s) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        if (acc < need && need <= acc + hb[j]) {
+          sh.bc[0] = (uint32_t)(top - j);
+          sh.bc[1] = acc;
+        }
+        acc += hb[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t tb = sh.bc[0], gt = sh.bc[1];
+    above += gt;
+    const uint32_t nlo = lo + (tb << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    hi = (hi - nlo < width) ? hi : nlo + width;
+    lo = nlo;
+    if (shift == 0) {
+      T = lo;
+      break;
+    }
+  }
+  const uint32_t need_eq = target - above;
+
+  // per-wave counts above / equal to the threshold, then ordered emission
+  uint32_t wgt = 0u, weq = 0u;
+#pragma unroll UNR
+  for (int j = 0; j < E; ++j) {
+    const uint32_t kk = KEY(j);
+    wgt += (uint32_t)__popcll(__ballot(kk > T));
+    weq += (uint32_t)__popcll(__ballot(kk == T));
+  }
+  if (lane == 0) {
+    sh.wred[1][wave] = wgt;
+    sh.wred[2][wave] = weq;
+  }
+  __syncthreads();
+  uint32_t eq_pref = 0u, out_pref = 0u;
+  for (int v = 0; v < wave; ++v) {
+    const uint32_t g_v = sh.wred[1][v], e_v = sh.wred[2][v];
+    const uint32_t take_v = eq_pref >= need_eq ? 0u : min(e_v, need_eq - eq_pref);
+    out_pref += g_v + take_v;
+    eq_pref += e_v;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t r_sel = out_pref, r_eq = eq_pref;
+#pragma unroll UNR
+  for (int j = 0; j < E; ++j) {
+    const uint32_t kk = KEY(j);
+    const bool eq = kk == T;
+    const uint64_t eqb = __ballot(eq);
+    const uint32_t eq_rank = r_eq + (uint32_t)__popcll(eqb & below);
+    const bool sel = kk > T || (eq && eq_rank < need_eq);
+    const uint64_t selb = __ballot(sel);
+    if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)));
+    r_eq += (uint32_t)__popcll(eqb);
+    r_sel += (uint32_t)__popcll(selb);
+  }
+  __syncthreads();
+  return (int)target;
+}
+
+struct KeysFromArray {
+  const float* p;
+  __device__ uint32_t key(int i) const { return float_key(p[i]); }
+};
+
+constexpr int kBlock = 8;
+
+// Positions of candidate blocks: candidate i is position blk[i/8]*8 + i%8.
+struct KeysFromBlocks {
+  const float* scores;
+  const int32_t* blk;
+  __device__ uint32_t key(int i) const { return float_key(scores[blk[i >> 3] * kBlock + (i & 7)]); }
+};
+
+// Full-mode selection for one sequence (grid = B):
+//  1. block top-n_blocks -> pool (ascending positions);
+//  2. block top-k -> candidate positions: every position of rank <= k lies in a
+//     block of rank <= k (each block ranked ahead of it holds a distinct
+//     position ranked ahead of it), so the position top-k is exact over the
+//     positions of the top-k blocks;
+//  3. position top-k over those candidates.
+template <int NT, int EPT_B, int EPT_P>
+__global__ __launch_bounds__(NT) void select_full_kernel(
+    const float* __restrict__ scores, int64_t sstride, const float* __restrict__ bmax,
+    int64_t bstride, const int32_t* __restrict__ len, int64_t cap, int k, int n_blocks,
+    int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len) {
+  __shared__ SelScratch sh;
+  __shared__ int32_t blk[CSA2_POOL_BLOCKS];
+  __shared__ int32_t cblk[CSA2_MAX_TOPK];
+  const int b = blockIdx.x;
+  int64_t L = len[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int nb = (int)((L + kBlock - 1) / kBlock);
+  const float* sc = scores + (int64_t)b * sstride;
+  int32_t* tk = topk + (int64_t)b * k;
+  KeysFromArray bsrc{bmax + (int64_t)b * bstride};
+  KeyRegs<EPT_B> kb;
+  load_keys<NT, EPT_B>(kb, bsrc, nb);
+  if (n_blocks > 0) {
+    const int nsel = select_core<NT, EPT_B>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r) { blk[r] = i; });
+    int pl = nsel * kBlock;
+    if (nsel > 0 && blk[nsel - 1] == nb - 1) pl -= nb * kBlock - (int)L;
+    int32_t* pb = pool + (int64_t)b * n_blocks * kBlock;
+    for (int i = threadIdx.x; i < n_blocks * kBlock; i += NT)
+      pb[i] = i < pl ? blk[i >> 3] * kBlock + (i & 7) : -1;
+    if (threadIdx.x == 0) pool_len[b] = pl;
+  }
+  const int ncb = select_core<NT, EPT_B>(kb, bsrc, nb, k, sh, [&](int i, int r) { cblk[r] = i; });
+  int nc = ncb * kBlock;
+  if (ncb > 0 && cblk[ncb - 1] == nb - 1) nc -= nb * kBlock - (int)L;
+  KeysFromBlocks psrc{sc, cblk};
+  KeyRegs<EPT_P> kp;
+  load_keys<NT, EPT_P>(kp, psrc, nc);
+  const int cnt = select_core<NT, EPT_P>(kp, psrc, nc, k, sh,
+                                         [&](int i, int r) { tk[r] = cblk[i >> 3] * kBlock + (i & 7); });
+  for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
+}
+
+// Reindex selection: top-k of the pool scores (NaN = masked entry).
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void select_pool_kernel(
+    const float* __restrict__ pool_scores, const int32_t* __restrict__ pool,
+    const int32_t* __restrict__ pool_len, int pool_cap, int k, int32_t* __restrict__ topk) {
+  __shared__ SelScratch sh;
+  const int b = blockIdx.x;
+  int n = pool_len[b];
+  n = n < 0 ? 0 : (n > pool_cap ? pool_cap : n);
+  const int32_t* pb = pool + (int64_t)b * pool_cap;
+  int32_t* tk = topk + (int64_t)b * k;
+  KeysFromArray src{pool_scores + (int64_t)b * pool_cap};
+  KeyRegs<EPT> kr;
+  load_keys<NT, EPT>(kr, src, n);
+  const int cnt = select_core<NT, EPT>(kr, src, n, k, sh, [&](int i, int r) { tk[r] = pb[i]; });
+  for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
+}
+
+// ======================================================================
+// Host launchers
+// ======================================================================
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+IndexFullWs index_full_ws_layout(int B, int64_t cap, int block) {
+  IndexFullWs l;
+  l.scores_off = 0;
+  l.bmax_off = align256((size_t)B * (size_t)cap * 4);
+  const int64_t nb = (cap + block - 1) / block;
+  l.total = l.bmax_off + align256((size_t)B * (size_t)nb * 4);
+  return l;
+}
+
+template <bool GATHER>
+static void launch_score(int MT, dim3 grid, hipStream_t st, const uint8_t* ic, const uint8_t* is,
+                         int64_t cap, const int32_t* len, const int32_t* pool,
+                         const int32_t* pool_len, int pool_cap, const uint16_t* q, const float* w,
+                         int H, float* scores, int64_t sstride, float* bmax, int64_t bstride,
+                         int stpw) {
+  if (MT == 1)
+    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+  else if (MT == 2)
+    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+  else
+    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+}
+
+int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const uint16_t* q, const float* w, int H, int k,
+                      int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
+                      float* scores_opt, void* ws, hipStream_t st) {
+  if (B == 0) return 0;
+  const IndexFullWs l = index_full_ws_layout(B, cap, block);
+  float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
+  float* bmax = reinterpret_cast<float*>((char*)ws + l.bmax_off);
+  const int64_t nbk = (cap + block - 1) / block;
+  const int MT = (H + 15) / 16;
+  const int stpw = 2;
+  const int64_t chunk = 4LL * stpw * kSuperTile;
+  dim3 grid((unsigned)((cap + chunk - 1) / chunk), (unsigned)B);
+  if (cap > 0)
+    launch_score<false>(MT, grid, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
+                        H, scores, cap, bmax, nbk, stpw);
+  if (hipGetLastError() != hipSuccess) return -1;
+  const bool kbig = k > 512;
+#define CSA2_SELFULL(NT, EB, EP) \
+  select_full_kernel<NT, EB, EP><<<B, NT, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, pool_len)
+  if (nbk <= 4 * 1024) {
+    if (kbig) CSA2_SELFULL(1024, 4, 16); else CSA2_SELFULL(1024, 4, 4);
+  } else if (nbk <= 16 * 1024) {
+    if (kbig) CSA2_SELFULL(1024, 16, 16); else CSA2_SELFULL(1024, 16, 4);
+  } else if (nbk <= 32 * 1024) {
+    if (kbig) CSA2_SELFULL(1024, 32, 16); else CSA2_SELFULL(1024, 32, 4);
+  } else {
+    if (kbig) CSA2_SELFULL(1024, 0, 16); else CSA2_SELFULL(1024, 0, 4);
+  }
+#undef CSA2_SELFULL
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+size_t index_pool_ws_bytes(int B, int pool_cap) { return align256((size_t)B * (size_t)pool_cap * 4); }
+
+int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
+                      int pool_cap, const uint16_t* q, const float* w, int H, int k,
+                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st) {
+  if (B == 0) return 0;
+  float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>(ws);
+  const int MT = (H + 15) / 16;
+  const int stpw = 2;
+  const int64_t chunk = 4LL * stpw * kSuperTile;
+  dim3 grid((unsigned)((pool_cap + chunk - 1) / chunk), (unsigned)B);
+  if (pool_cap > 0)
+    launch_score<true>(MT, grid, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
+                       w, H, ps, pool_cap, nullptr, 0, stpw);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (pool_cap <= 4 * 1024)
+    select_pool_kernel<1024, 4><<<B, 1024, 0, st>>>(ps, pool, pool_len, pool_cap, k, topk);
+  else
+    select_pool_kernel<1024, 16><<<B, 1024, 0, st>>>(ps, pool, pool_len, pool_cap, k, topk);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa2

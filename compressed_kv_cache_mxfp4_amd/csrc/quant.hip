@@ -1,0 +1,251 @@
+// quant.hip -- FP4 quantiser and the KV-source cache write (gfx950).
+//
+// Format [jokeuncle.pages.dev, "两张架构图里藏着 890 字节", section 三 (事实一, 事实二);
+// ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", section 7]:
+// E2M1 values, one scale byte per group (16 for the main KV with an E4M3 or
+// E8M0 scale, 32 for the indexer K with E8M0).  Rounding (a reading; the
+// pages do not print it): the smallest scale s with 6*s >= group max, then
+// round-to-nearest E2M1, ties to the even code, zero magnitude -> +0.
+//
+// The cache write follows [jokeuncle.pages.dev, section 四 item 1] (per-channel
+// softmax pooling over the m tokens of a group, fp32 when m > 1),
+// [ggaaooppeenngg.github.io, section 3.2 "Z"] (pooled -> RMSNorm -> FP4) and
+// [syt-nju.github.io, "为什么读输入只激活 8B", section CSA2] (indexer K projected
+// from the main-KV entry).
+#include "csa2_device.hpp"
+#include "csa2_internal.hpp"
+
+namespace csa2 {
+
+// ---------------------------------------------------------------- scale rule
+__device__ __forceinline__ uint32_t scale_code_e8m0(float amax) {
+  if (!(amax > 0.0f)) return 0u;
+  uint32_t u = __float_as_uint(amax);
+  int eb = (int)(u >> 23);
+  if (eb == 0) return 0u;      // subnormal max: 6 * 2^-127 already covers it
+  if (eb >= 255) return 254u;  // inf: saturate
+  // amax = f * 2^(eb-127), f in [1,2): need 2^(b-127) >= f/6 * 2^(eb-127)
+  int b = eb - 2 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  b = b < 0 ? 0 : (b > 254 ? 254 : b);
+  return (uint32_t)b;
+}
+
+__device__ __forceinline__ uint32_t scale_code_e4m3(float amax) {
+  if (!(amax > 0.0f)) return 0u;
+  if (6.0f * e4m3_value(0x7Eu) < amax) return 0x7Eu;  // saturate
+  int lo = 0, hi = 0x7E;                               // smallest b with 6*val(b) >= amax
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (6.0f * e4m3_value((uint32_t)mid) >= amax)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return (uint32_t)lo;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_code(float amax) {
+  return FMT == 0 ? scale_code_e8m0(amax) : scale_code_e4m3(amax);
+}
+
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t b) {
+  return FMT == 0 ? e8m0_value(b) : e4m3_value(b);
+}
+
+// Nearest E2M1 code of x / s, ties to the even code; all products are exact.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
+  float a = fabsf(x);
+  if (!(a > 0.0f)) return 0u;
+  uint32_t c = (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
+               (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
+               (uint32_t)(a > 5.0f * s);
+  if (c != 0u && (__float_as_uint(x) >> 31)) c |= 8u;
+  return c;
+}
+
+// ------------------------------------------------------- generic quantiser
+// One lane per 4 consecutive values; GROUP/4 lanes share a scale.
+template <int GROUP, int FMT>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ x, int64_t n4,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  constexpr int LPG = GROUP / 4;
+  const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = i4 < n4;
+  float4 v = active ? reinterpret_cast<const float4*>(x)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+  for (int m = 1; m < LPG; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
+  const uint32_t b = scale_code<FMT>(amax);
+  const float s = scale_value<FMT>(b);
+  if (!active) return;
+  uint32_t c = e2m1_code(v.x, s) | (e2m1_code(v.y, s) << 4) | (e2m1_code(v.z, s) << 8) |
+               (e2m1_code(v.w, s) << 12);
+  reinterpret_cast<uint16_t*>(codes)[i4] = (uint16_t)c;
+  if ((i4 % LPG) == 0) scales[i4 / LPG] = (uint8_t)b;
+}
+
+int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, uint8_t* codes,
+                    uint8_t* scales, hipStream_t st) {
+  const int64_t n4 = rows * (int64_t)dim / 4;
+  if (n4 == 0) return 0;
+  const int threads = 256;
+  const int64_t blocks = (n4 + threads - 1) / threads;
+  if (group == 16 && fmt == 0)
+    quantize_kernel<16, 0><<<dim3((unsigned)blocks), threads, 0, st>>>(x, n4, codes, scales);
+  else if (group == 16 && fmt == 1)
+    quantize_kernel<16, 1><<<dim3((unsigned)blocks), threads, 0, st>>>(x, n4, codes, scales);
+  else if (group == 32 && fmt == 0)
+    quantize_kernel<32, 0><<<dim3((unsigned)blocks), threads, 0, st>>>(x, n4, codes, scales);
+  else
+    quantize_kernel<32, 1><<<dim3((unsigned)blocks), threads, 0, st>>>(x, n4, codes, scales);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------- cache write
+// Grid (entry tiles of 16, 4 column tiles of 32).  Every workgroup pools and
+// normalises its 16 entries (one wave per entry at a time); the column-tile-0
+// workgroup writes the main-KV FP4.  Each workgroup then projects onto its 32
+// indexer-K columns -- exactly one E8M0 group -- and quantises them.
+constexpr int kWriteEntries = 16;
+constexpr int kWriteColTiles = 4;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ gate, int64_t n_entries,
+    int m, const float* __restrict__ gamma, float eps, const float* __restrict__ w_idx,
+    uint8_t* __restrict__ main_codes, uint8_t* __restrict__ main_scales,
+    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales) {
+  __shared__ float yT[512][kWriteEntries];  // latent after RMSNorm, channel-major
+  __shared__ float kb[kWriteEntries][33];   // projected keys of this column tile
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ct = blockIdx.y;
+  const int64_t e0 = (int64_t)blockIdx.x * kWriteEntries;
+
+  for (int ei = wave; ei < kWriteEntries; ei += 4) {
+    const int64_t e = e0 + ei;
+    if (e >= n_entries) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = 0.0f;
+      continue;
+    }
+    float pooled[8];
+    if (m == 1) {
+      uint4 xv = *reinterpret_cast<const uint4*>(latent + e * 512 + 8 * lane);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) pooled[c] = bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+    } else {
+      float gmax[8], num[8], den[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { gmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
+      for (int t = 0; t < m; ++t) {
+        uint4 gv = *reinterpret_cast<const uint4*>(gate + (e * m + t) * 512 + 8 * lane);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) gmax[c] = fmaxf(gmax[c], bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu));
+      }
+      for (int t = 0; t < m; ++t) {
+        uint4 gv = *reinterpret_cast<const uint4*>(gate + (e * m + t) * 512 + 8 * lane);
+        uint4 xv = *reinterpret_cast<const uint4*>(latent + (e * m + t) * 512 + 8 * lane);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float ex = expf(bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu) - gmax[c]);
+          num[c] += ex * bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+          den[c] += ex;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) pooled[c] = num[c] / den[c];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss += pooled[c] * pooled[c];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / 512.0f + eps);
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) y[c] = pooled[c] * r * (gamma ? gamma[8 * lane + c] : 1.0f);
+    if (ct == 0) {
+      // main-KV FP4: a group of 16 channels spans two lanes
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(y[c]));
+      amax = fmaxf(amax, shfl_xor_f(amax, 1));
+      const uint32_t b = scale_code<FMT>(amax);
+      const float s = scale_value<FMT>(b);
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) word |= e2m1_code(y[c], s) << (4 * c);
+      *reinterpret_cast<uint32_t*>(main_codes + e * 256 + 4 * lane) = word;
+      if ((lane & 1) == 0) main_scales[e * 32 + lane / 2] = (uint8_t)b;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = y[c];
+  }
+  __syncthreads();
+
+  // projection k[e][d] = sum_c y[e][c] * W[c][d] for d in this column tile;
+  // thread: one column, two entries
+  {
+    const int d = 32 * ct + (threadIdx.x & 31);
+    const int e2 = 2 * (threadIdx.x >> 5);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 16
+    for (int c = 0; c < 512; ++c) {
+      const float wv = w_idx[c * 128 + d];
+      const float2 yv = *reinterpret_cast<const float2*>(&yT[c][e2]);
+      a0 += yv.x * wv;
+      a1 += yv.y * wv;
+    }
+    kb[e2][threadIdx.x & 31] = a0;
+    kb[e2 + 1][threadIdx.x & 31] = a1;
+  }
+  __syncthreads();
+
+  // indexer-K FP4 of this column tile: thread = (entry, 8 consecutive dims)
+  if (threadIdx.x < 64) {
+    const int ei = threadIdx.x >> 2, ch = threadIdx.x & 3;
+    const int64_t e = e0 + ei;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = kb[ei][8 * ch + j];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, shfl_xor_f(amax, 1));
+    amax = fmaxf(amax, shfl_xor_f(amax, 2));
+    const uint32_t b = scale_code_e8m0(amax);
+    const float s = e8m0_value(b);
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], s) << (4 * j);
+    if (e < n_entries) {
+      *reinterpret_cast<uint32_t*>(idx_codes + e * 64 + 16 * ct + 4 * ch) = word;
+      if (ch == 0) idx_scales[e * 4 + ct] = (uint8_t)b;
+    }
+  }
+}
+
+int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int m,
+                       const float* gamma, float eps, const float* w_idx, int main_fmt,
+                       uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
+                       uint8_t* idx_scales, hipStream_t st) {
+  const int64_t n = T / m;
+  if (n == 0) return 0;
+  const int64_t blocks = (n + kWriteEntries - 1) / kWriteEntries;
+  const dim3 grid((unsigned)blocks, kWriteColTiles);
+  if (main_fmt == 0)
+    cache_write_kernel<0><<<grid, 256, 0, st>>>(
+        latent, gate, n, m, gamma, eps, w_idx, main_codes, main_scales, idx_codes, idx_scales);
+  else
+    cache_write_kernel<1><<<grid, 256, 0, st>>>(
+        latent, gate, n, m, gamma, eps, w_idx, main_codes, main_scales, idx_codes, idx_scales);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa2

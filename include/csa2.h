@@ -167,6 +167,9 @@ int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
  * GP 3.3; SY CSA2 Figure 4 (Reindex)].  Same score formula as index_full.
  *   pool     : int32 [B][pool_cap] positions (from csa2_index_full); entries
  *              i < pool_len[b] are candidates; -1 or out-of-range are masked.
+ *              Precondition: the valid entries of a row appear in strictly
+ *              ascending order (csa2_index_full writes them so); masked entries
+ *              may appear anywhere.  Ties and output order rely on it.
  *   topk     : out int32 [B][k] ascending positions, -1 padded; ties prefer
  *              the lower position.
  *   pool_scores_opt : optional out fp32 [B][pool_cap] (score of pool[b][i]).
@@ -197,7 +200,9 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
  *   out      : out bf16 bits [B][H][512].
  *   lse_opt  : optional out fp32 [B][H], natural-log sum of exp(sm_scale*logits);
  *              -inf (and a zero output row) when a sequence attends no row.
- *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes.
+ *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes
+ *              (reserved; the current kernels keep no scratch in it).
+ * The result is deterministic (no atomics; fixed reduction order).
  */
 size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap);
 int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_codes,

@@ -1,0 +1,140 @@
+"""Host-only checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function declared in include/csa2.h, and the
+host-side argument validation rejects bad calls with the documented status
+before anything is launched (so these calls never touch a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+LIB = os.path.join(ROOT, "compressed_kv_cache_mxfp4_amd", "lib", "libcsa2.so")
+
+CSA2_OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP = range(7)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from compressed_kv_cache_mxfp4_amd import build
+
+        build.build()
+    L = ctypes.CDLL(LIB)
+    L.csa2_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"csa2_cache_write", "csa2_index_full", "csa2_index_pool", "csa2_sparse_attn_decode",
+            "csa2_quantize_fp4"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.csa2_status_string(code)
+    assert lib.csa2_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)       # never dereferenced: validation fails first
+FAKE_ODD = P(0x1001)
+
+
+def test_quantize_validation(lib):
+    f = lib.csa2_quantize_fp4
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    assert f(FAKE, 4, 48, 32, 0, FAKE, FAKE, None) == ERR_SHAPE       # dim % group
+    assert f(FAKE, 4, 64, 8, 0, FAKE, FAKE, None) == ERR_SHAPE        # group
+    assert f(FAKE, 4, 64, 32, 7, FAKE, FAKE, None) == ERR_UNSUP       # format
+    assert f(None, 4, 64, 32, 0, FAKE, FAKE, None) == ERR_NULL
+    assert f(FAKE_ODD, 4, 64, 32, 0, FAKE, FAKE, None) == ERR_ALIGN
+    assert f(None, 0, 64, 32, 0, None, None, None) == CSA2_OK         # empty: nothing to do
+
+
+def test_cache_write_validation(lib):
+    f = lib.csa2_cache_write
+    f.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_int32, P, P, P, P, P]
+    assert f(FAKE, FAKE, 7, 2, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # T % m
+    assert f(FAKE, FAKE, 8, 9, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # m
+    assert f(FAKE, None, 8, 2, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_NULL  # gate
+    assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 5, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUP
+    assert f(FAKE_ODD, None, 8, 1, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN
+
+
+def _index_full(lib):
+    f = lib.csa2_index_full
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.csa2_index_full_workspace.restype = ctypes.c_size_t
+    lib.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
+    return f
+
+
+def test_index_full_validation(lib):
+    f = _index_full(lib)
+    ok = dict(ic=FAKE, isc=FAKE, cap=4096, len=FAKE, B=2, q=FAKE, w=FAKE, H=64, k=512, block=8, nb=2048,
+              topk=FAKE, pool=FAKE, pl=FAKE, sc=None, ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ic"], a["isc"], a["cap"], a["len"], a["B"], a["q"], a["w"], a["H"], a["k"], a["block"],
+                 a["nb"], a["topk"], a["pool"], a["pl"], a["sc"], a["ws"], a["wsb"], None)
+
+    assert call(H=48) == ERR_UNSUP
+    assert call(block=16) == ERR_UNSUP
+    assert call(k=0) == ERR_SHAPE
+    assert call(k=4096) == ERR_SHAPE
+    assert call(nb=4096) == ERR_SHAPE
+    assert call(cap=(1 << 20) + 1) == ERR_SHAPE
+    assert call(q=None) == ERR_NULL
+    assert call(pool=None) == ERR_NULL
+    assert call(pool=None, pl=None, nb=0, ws=None) == ERR_WS
+    assert call(ic=FAKE_ODD) == ERR_ALIGN
+    need = lib.csa2_index_full_workspace(2, 4096, 512, 8, 2048)
+    assert need >= 2 * 4096 * 4
+    assert call(wsb=need - 1) == ERR_WS
+    assert call(B=0) == CSA2_OK
+
+
+def test_index_pool_and_attention_validation(lib):
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f = lib.csa2_index_pool
+    f.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, i32, P, P, P, ctypes.c_size_t, P]
+    assert f(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 20000, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 1 << 30, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 12, 512, FAKE, None, FAKE, 1 << 30, None) == ERR_UNSUP
+    assert f(FAKE, FAKE, 4096, FAKE, 2, None, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 1 << 30, None) == ERR_NULL
+    assert f(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 16, None) == ERR_WS
+    a = lib.csa2_sparse_attn_decode
+    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, ctypes.c_float, P, P, P,
+                  ctypes.c_size_t, P]
+    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0.04, FAKE, None,
+            FAKE, 1 << 40, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return a(*args)
+
+    assert call(1, 40) == ERR_UNSUP      # heads (multiple of 16 required)
+    assert call(5, 3) == ERR_UNSUP       # scale format
+    assert call(13, 129) == ERR_SHAPE    # window > 128
+    assert call(12, 100) == ERR_SHAPE    # stride < window
+    assert call(8, 5000) == ERR_SHAPE    # k
+    assert call(15, float("nan")) == ERR_SHAPE
+    assert call(0, None) == ERR_NULL
+    assert call(10, None) == ERR_NULL    # window planes missing
+    assert call(19, 8) == ERR_WS
+    assert call(0, FAKE_ODD) == ERR_ALIGN

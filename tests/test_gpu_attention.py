@@ -1,0 +1,183 @@
+"""GPU parity of the sparse attention and of the cache write.
+
+Attention: per (sequence, head) max|o - r| / max|r| <= 1e-2 against the fp64
+oracle (output in bf16); the log-sum-exp within 1e-4 absolute.  Edge cases:
+masked and out-of-range top-k slots, duplicate slots (attended twice), window
+shorter than its capacity, no window, an empty sequence, both scale formats,
+16/32/64 heads, k not a multiple of the 64-row chunk.
+
+Cache write: FP4 bytes equal the oracle's except where a certificate holds:
+the oracle's pre-quantisation value lies within 1e-5 relative of an E2M1
+midpoint of its group's scale, or the group maximum lies within 1e-5 of a
+scale boundary (then the whole group may differ).
+"""
+import numpy as np
+import pytest
+import torch
+
+import csa2_synth as syn
+import compressed_kv_cache_mxfp4_amd as K
+import oracle
+from gpu_common import DEV, attn_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _make_cache(B, cap, fmt, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = torch.randn(B, cap, 512, generator=g, device=DEV)
+    c, s = K.quantize_fp4(x, 16, fmt)
+    xc = x.cpu().numpy()
+    rc, rs = oracle.quantize(xc, 16, fmt)
+    assert np.array_equal(rc, c.cpu().numpy()) and np.array_equal(rs, s.cpu().numpy())
+    return c, s, rc, rs
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_parity_with_window(fmt, H):
+    say(f"attention parity fmt={fmt} H={H}")
+    B, cap, k, W = 3, 3000, 512, 128
+    c, s, rc, rs = _make_cache(B, cap, fmt, 1 + fmt + H)
+    g = np.random.default_rng(5)
+    topk = np.stack([np.sort(g.choice(cap, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    topk[0, 10] = -1
+    topk[0, 11] = cap + 7           # out of range: masked
+    topk[1, 20] = topk[1, 21]       # duplicate: attended twice
+    topk[2, 300:] = -1              # short selection
+    lens = np.array([cap, cap - 100, cap], np.int32)
+    topk[1, 30] = cap - 50          # beyond len[1]: masked
+    swa_len = np.array([128, 100, 0], np.int32)
+    q = syn.as_bf16_bits(torch.randn(B, H, 512, generator=torch.Generator().manual_seed(9)) * 0.5)
+    qd = q.to(DEV)
+    out, lse = K.sparse_attn_decode(qd, c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV),
+                                    fmt, swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV),
+                                    swa_stride=cap, swa_cap=W, swa_row0=cap - W, return_lse=True)
+    torch.cuda.synchronize()
+    ref = np.zeros((B, H, 512), np.float32)
+    rl = np.zeros((B, H), np.float32)
+    for b in range(B):
+        ref[b], rl[b] = oracle.attention(q[b].numpy(), rc[b], rs[b], lens[b], fmt, topk[b],
+                                         rc[b, cap - W:], rs[b, cap - W:], swa_len[b], 1 / np.sqrt(512))
+    worst = attn_close(out.cpu(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=1e-4, rtol=0)
+    say(f"  worst relative error {worst:.2e}")
+
+
+def test_attention_odd_sizes_and_empty():
+    fmt = 0
+    B, cap, k = 2, 700, 77
+    c, s, rc, rs = _make_cache(B, cap, fmt, 3)
+    g = np.random.default_rng(6)
+    topk = g.integers(0, cap, (B, k)).astype(np.int32)
+    lens = np.array([cap, 0], np.int32)   # second sequence attends nothing
+    q = syn.as_bf16_bits(torch.randn(B, 32, 512, generator=torch.Generator().manual_seed(2)))
+    out, lse = K.sparse_attn_decode(q.to(DEV), c, s, torch.from_numpy(lens).to(DEV),
+                                    torch.from_numpy(topk).to(DEV), fmt, return_lse=True)
+    ref0, l0 = oracle.attention(q[0].numpy(), rc[0], rs[0], cap, fmt, topk[0], None, None, 0, 1 / np.sqrt(512))
+    o = out.cpu()
+    attn_close(o[:1], ref0[None])
+    assert (o[1].view(torch.bfloat16).float() == 0).all()
+    lse = lse.cpu().numpy()
+    assert np.isneginf(lse[1]).all()
+    np.testing.assert_allclose(lse[0], l0, atol=1e-4)
+
+
+@pytest.mark.parametrize("k,W", [(600, 128), (2048, 128), (1100, 0)])
+def test_attention_long_selection(k, W):
+    """Selections longer than one 640-row register batch (several batches joined)."""
+    say(f"attention long selection k={k} W={W}")
+    fmt = 1
+    B, cap = 2, 5000
+    c, s, rc, rs = _make_cache(B, cap, fmt, 11 + k)
+    g = np.random.default_rng(k)
+    topk = np.stack([g.choice(cap, k, replace=False) for _ in range(B)]).astype(np.int32)
+    topk[1, k // 2:] = -1
+    lens = np.array([cap, cap], np.int32)
+    swa_len = np.array([W, W // 2], np.int32)
+    q = syn.as_bf16_bits(torch.randn(B, 16, 512, generator=torch.Generator().manual_seed(k)) * 0.7)
+    kw = dict(swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV), swa_stride=cap,
+              swa_cap=W, swa_row0=cap - W) if W else {}
+    out, lse = K.sparse_attn_decode(q.to(DEV), c, s, torch.from_numpy(lens).to(DEV),
+                                    torch.from_numpy(topk).to(DEV), fmt, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    ref = np.zeros((B, 16, 512), np.float32)
+    rl = np.zeros((B, 16), np.float32)
+    for b in range(B):
+        ref[b], rl[b] = oracle.attention(q[b].numpy(), rc[b], rs[b], lens[b], fmt, topk[b],
+                                         rc[b, cap - W:] if W else None, rs[b, cap - W:] if W else None,
+                                         swa_len[b], 1 / np.sqrt(512))
+    worst = attn_close(out.cpu(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=1e-4, rtol=0)
+    say(f"  worst relative error {worst:.2e}")
+
+
+def test_attention_window_only_separate_buffer():
+    fmt = 1
+    B, cap, W = 2, 64, 128
+    c, s, rc, rs = _make_cache(B, cap, fmt, 4)
+    wc, ws_, rwc, rws = _make_cache(B, W, fmt, 5)
+    q = syn.as_bf16_bits(torch.randn(B, 64, 512, generator=torch.Generator().manual_seed(3)))
+    topk = torch.full((B, 1), -1, dtype=torch.int32)
+    swa_len = np.array([128, 1], np.int32)
+    out = K.sparse_attn_decode(q.to(DEV), c, s, torch.full((B,), cap, dtype=torch.int32, device=DEV),
+                               topk.to(DEV), fmt, swa_codes=wc, swa_scales=ws_,
+                               swa_len=torch.from_numpy(swa_len).to(DEV), swa_stride=W, swa_cap=W)
+    ref = np.stack([oracle.attention(q[b].numpy(), rc[b], rs[b], cap, fmt, topk[b].numpy(), rwc[b], rws[b],
+                                     swa_len[b], 1 / np.sqrt(512))[0] for b in range(B)])
+    attn_close(out.cpu(), ref)
+
+
+# ---------------------------------------------------------------- cache write
+def _certified_code_mismatch(vals, ref_codes, ref_scales, got_codes, got_scales, group, fmt):
+    """Count byte mismatches; assert each is covered by a certificate."""
+    n_bad = 0
+    rows, dim = vals.shape
+    deq_s = np.vectorize(lambda b: oracle.scale_value(int(b), fmt))
+    for r in np.where((ref_codes != got_codes).any(1) | (ref_scales != got_scales).any(1))[0]:
+        for gi in range(dim // group):
+            sl = slice(gi * group, (gi + 1) * group)
+            cs = slice(gi * group // 2, (gi + 1) * group // 2)
+            if ref_scales[r, gi] == got_scales[r, gi] and np.array_equal(ref_codes[r, cs], got_codes[r, cs]):
+                continue
+            v = vals[r, sl].astype(np.float64)
+            amax = np.abs(v).max()
+            if ref_scales[r, gi] != got_scales[r, gi]:
+                # the group max must sit at a scale boundary: 6*s(b) for the oracle's b or b-1
+                b = int(ref_scales[r, gi])
+                edges = [6 * oracle.scale_value(bb, fmt) for bb in (b - 1, b) if bb >= 0]
+                assert min(abs(amax - e) / e for e in edges if e > 0) <= 1e-5, (r, gi, amax, edges)
+                n_bad += 1
+                continue
+            s = float(deq_s(ref_scales[r, gi]))
+            for i in range(group):
+                byte = (gi * group + i) // 2
+                sh = 4 * (i % 2)
+                if ((ref_codes[r, byte] >> sh) & 15) == ((got_codes[r, byte] >> sh) & 15):
+                    continue
+                mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * s
+                a = abs(v[i])
+                assert np.min(np.abs(a - mids) / np.maximum(mids, 1e-300)) <= 1e-5, (r, gi, i, a / s)
+                n_bad += 1
+    return n_bad
+
+
+@pytest.mark.parametrize("m,fmt,gamma", [(1, 0, False), (2, 1, False), (2, 0, True), (4, 1, True)])
+def test_cache_write_parity(m, fmt, gamma):
+    say(f"cache write m={m} fmt={fmt} gamma={gamma}")
+    wl = syn.small("w", 31 + m, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=1024 * m, write_m=m)
+    lat, gate, w = syn.write_inputs(wl, DEV)
+    gm = (torch.linspace(0.5, 1.5, 512, device=DEV) if gamma else None)
+    got = K.cache_write(lat, gate, m, w, fmt, gamma=gm, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.cache_write(lat.cpu().numpy(), gate.cpu().numpy(), m, w.cpu().numpy(), fmt,
+                             gamma=None if gm is None else gm.cpu().numpy(), eps=1e-6)
+    g = {k_: v.cpu().numpy() for k_, v in got.items()}
+    nm = _certified_code_mismatch(ref["y"], ref["main_codes"], ref["main_scales"], g["main_codes"],
+                                  g["main_scales"], 16, fmt)
+    nk = _certified_code_mismatch(ref["k"], ref["idx_codes"], ref["idx_scales"], g["idx_codes"],
+                                  g["idx_scales"], 32, 0)
+    say(f"  certified mismatches: main {nm}, indexer {nk}")
+    # nearly all bytes are identical
+    assert (g["main_codes"] == ref["main_codes"]).mean() > 0.999
+    assert (g["idx_codes"] == ref["idx_codes"]).mean() > 0.999

@@ -1,0 +1,190 @@
+"""GPU parity of the hierarchical sparse indexer (Full and Reindex modes).
+
+Policy:
+  * scores: within 1e-5 relative of the oracle (floor 1e-7 x the largest score);
+  * selection exactness: the GPU's top-k and pool equal a numpy brute-force
+    selection (lexsort by score desc, index asc) applied to the GPU's own
+    scores -- bit for bit, no exceptions;
+  * end to end: GPU indices vs the oracle's; any difference must be a
+    certified near-tie of the oracle's k-th (block) score.
+Edge cases: ragged lengths (not multiples of 8, below k, zero), every head
+count, n_blocks = 0 / < k / >= k, masked pool entries, duplicate rows (exact
+ties), determinism across runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import csa2_synth as syn
+import compressed_kv_cache_mxfp4_amd as K
+import oracle
+from gpu_common import (DEV, brute_pool, brute_topk, build_gpu_cache, certify_topk,
+                        oracle_cache_seq, say, score_close)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(wl, cache, lens, layer=0, k=None, n_blocks=None):
+    q = syn.index_query(wl, layer, DEV)
+    w = syn.index_weights(wl, layer, DEV)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    topk, pool, pool_len, scores = K.index_full(
+        cache["idx_codes"], cache["idx_scales"], lt, q, w, k=k or wl.k,
+        n_blocks=wl.n_blocks if n_blocks is None else n_blocks, return_scores=True)
+    torch.cuda.synchronize()
+    return q, w, topk.cpu().numpy(), pool.cpu().numpy(), pool_len.cpu().numpy(), scores.cpu().numpy()
+
+
+def _check_full(wl, cache, lens, k, n_blocks, layer=0):
+    q, w, topk, pool, pool_len, scores = _run_full(wl, cache, lens, layer, k, n_blocks)
+    qn, wn = q.cpu().numpy(), w.cpu().numpy()
+    certified = 0
+    for b, L in enumerate(lens):
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        rt, rp, rpl, rs = oracle.index_full(ref["idx_codes"][:L], ref["idx_scales"][:L], L, qn[b], wn[b],
+                                            k, 8, n_blocks)
+        gs = scores[b, :L]
+        score_close(gs, rs)
+        # selection exactness on the GPU's own scores
+        assert np.array_equal(topk[b], brute_topk(gs, k)), f"seq {b}: top-k is not the exact top-k of the GPU scores"
+        if n_blocks > 0:
+            bp, bpl, _ = brute_pool(gs, n_blocks)
+            assert pool_len[b] == bpl
+            assert np.array_equal(pool[b], bp), f"seq {b}: pool is not exact on the GPU scores"
+            assert pool_len[b] == rpl
+            # pool blocks vs the oracle's, certified near-ties only
+            gblk = np.unique(pool[b][pool[b] >= 0] // 8)
+            rblk = np.unique(rp[rp >= 0] // 8)
+            _, _, rbs = brute_pool(rs, n_blocks)
+            certified += certify_topk(gblk, rblk, rbs, n_blocks)
+        certified += certify_topk(topk[b], rt, rs, k)
+    return certified
+
+
+@pytest.mark.parametrize("H", [8, 16, 32, 64])
+def test_index_full_tiny_workload_shapes(H):
+    wl = syn.small("t", 10 + H, B=2, cap=4096, H_idx=H, k=512, n_blocks=64)
+    say(f"index_full tiny H={H}")
+    cache = build_gpu_cache(wl, 0)
+    n = _check_full(wl, cache, [4096, 4096], 512, 64)
+    say(f"  certified near-ties: {n}")
+
+
+@pytest.mark.parametrize("lens,k,nb", [
+    ([3000, 2989, 5, 0], 512, 64),      # ragged, below k, empty
+    ([5000, 4093, 777, 8], 100, 2048),  # pool covers everything
+    ([6000, 6000, 17, 1], 256, 0),       # no pool
+    ([6000, 5999, 600, 64], 16, 4),      # n_blocks < k
+])
+def test_index_full_ragged(lens, k, nb):
+    wl = syn.small("r", 7, B=len(lens), cap=6016, H_idx=32, k=k, n_blocks=nb)
+    say(f"index_full ragged lens={lens} k={k} nb={nb}")
+    cache = build_gpu_cache(wl, 0)
+    _check_full(wl, cache, lens, k, nb)
+
+
+def test_index_full_several_tiles_mid_size():
+    wl = syn.small("m", 3, B=3, cap=40000, H_idx=64, k=512, n_blocks=2048, boost_rows=64, boost_factor=4.0)
+    say("index_full 3 x 40000, pool 16384")
+    cache = build_gpu_cache(wl, 0)
+    _check_full(wl, cache, [40000, 39997, 20001], 512, 2048)
+
+
+def test_duplicate_rows_tie_exactly_and_prefer_lower_index():
+    wl = syn.small("d", 5, B=1, cap=4096, H_idx=64, k=64, n_blocks=16)
+    cache = build_gpu_cache(wl, 0)
+    # copy one row's bytes to many places on the device
+    src = 100
+    dst = torch.tensor([7, 300, 301, 1999, 2500, 4095], device=DEV)
+    for key in ("idx_codes", "idx_scales"):
+        cache[key][0, dst] = cache[key][0, src].clone()
+    q, w, topk, pool, pool_len, scores = _run_full(wl, cache, [4096])
+    s = scores[0]
+    assert len(set(s[[src, 7, 300, 301, 1999, 2500, 4095]].view(np.uint32).tolist())) == 1
+    assert np.array_equal(topk[0], brute_topk(s, 64))
+    # zero every other row, so the seven copies tie for the top and straddle k = 4
+    qbits = q
+    ic = cache["idx_codes"].clone()
+    isc = cache["idx_scales"].clone()
+    ic[0] = 0
+    ic[0, dst] = cache["idx_codes"][0, src]
+    ic[0, src] = cache["idx_codes"][0, src]
+    topk2, pool2, pl2 = K.index_full(ic, isc, torch.tensor([4096], dtype=torch.int32, device=DEV), qbits,
+                                     w, k=4, n_blocks=2)
+    t2 = topk2.cpu().numpy()[0]
+    assert list(t2) == [7, src, 300, 301], t2
+    p2 = pool2.cpu().numpy()[0]
+    assert list(p2[:16]) == list(range(0, 8)) + list(range(96, 104))
+
+
+def test_determinism_two_runs_bitwise():
+    wl = syn.small("det", 9, B=2, cap=20000, H_idx=64, k=512, n_blocks=2048)
+    cache = build_gpu_cache(wl, 0)
+    a = _run_full(wl, cache, [20000, 15000])
+    b = _run_full(wl, cache, [20000, 15000])
+    for x, y in zip(a[2:], b[2:]):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_index_pool_matches_oracle_and_reproduces_full_topk():
+    wl = syn.small("p", 21, B=3, cap=30000, H_idx=64, k=512, n_blocks=1024, n_reindex=2)
+    say("index_pool 3 x 30000")
+    cache = build_gpu_cache(wl, 0)
+    lens = [30000, 29999, 9000]
+    q0, w0, topk, pool, pool_len, scores = _run_full(wl, cache, lens)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    pool_t = torch.from_numpy(pool).to(DEV)
+    pl_t = torch.from_numpy(pool_len).to(DEV)
+    # same query as the Full layer -> same top-k, same scores at pool positions
+    t_same, ps_same = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool_t, pl_t, q0, w0,
+                                   k=512, return_scores=True)
+    t_same = t_same.cpu().numpy()
+    ps_same = ps_same.cpu().numpy()
+    for b in range(3):
+        n = pool_len[b]
+        assert np.array_equal(t_same[b], topk[b])
+        assert np.array_equal(ps_same[b, :n].view(np.uint32), scores[b, pool[b, :n]].view(np.uint32))
+    # a Reindex layer's own query vs the oracle (pool from the oracle's own Full layer)
+    q1 = syn.index_query(wl, 1, DEV)
+    w1 = syn.index_weights(wl, 1, DEV)
+    q0n, w0n, q1n, w1n = (t.cpu().numpy() for t in (q0, w0, q1, w1))
+    for b, L in enumerate(lens):
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        _, rpool, rpl, _ = oracle.index_full(ref["idx_codes"][:L], ref["idx_scales"][:L], L, q0n[b], w0n[b],
+                                            512, 8, 1024)
+        rt, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], L, rpool, rpl, q1n[b], w1n[b], 512)
+        pt = torch.zeros(1, 1024 * 8, dtype=torch.int32, device=DEV) - 1
+        pt[0, :] = torch.from_numpy(rpool).to(DEV)
+        gt, gps = K.index_pool(cache["idx_codes"][b:b + 1], cache["idx_scales"][b:b + 1],
+                               lt[b:b + 1], pt, torch.tensor([rpl], dtype=torch.int32, device=DEV),
+                               q1[b:b + 1], w1[b:b + 1], k=512, return_scores=True)
+        gt = gt.cpu().numpy()[0]
+        gps = gps.cpu().numpy()[0, :rpl]
+        score_close(gps, rps)
+        assert np.array_equal(gt, brute_topk(gps, 512, rpool[:rpl]))
+        diff = set(gt.tolist()) ^ set(rt.tolist())
+        if diff:
+            pos_to_score = {int(p): float(s) for p, s in zip(rpool[:rpl], rps)}
+            kth = np.sort(rps)[::-1][511]
+            for p in diff:
+                if p >= 0:
+                    assert abs(pos_to_score[p] - kth) <= 2e-5 * abs(kth) + 1e-7 * np.abs(rps).max()
+
+
+def test_index_pool_masks_invalid_entries():
+    wl = syn.small("pm", 23, B=1, cap=2048, H_idx=16, k=8, n_blocks=0)
+    cache = build_gpu_cache(wl, 0)
+    q = syn.index_query(wl, 0, DEV)
+    w = syn.index_weights(wl, 0, DEV)
+    # valid entries ascending (the documented precondition); masked entries anywhere
+    pool = torch.tensor([[3, 5, -1, 7, 4000, 9, 11, 2047, -5, 12, 13, 1500]], dtype=torch.int32, device=DEV)
+    L = 2000
+    t, ps = K.index_pool(cache["idx_codes"], cache["idx_scales"], torch.tensor([L], dtype=torch.int32, device=DEV),
+                         pool, torch.tensor([12], dtype=torch.int32, device=DEV), q, w, k=8, return_scores=True)
+    ps = ps.cpu().numpy()[0]
+    assert np.isnan(ps[[2, 4, 7, 8]]).all()
+    ref = oracle_cache_seq(wl, 0, 0, cache, need_main=False)
+    rt, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], L, pool.cpu().numpy()[0], 12,
+                                q.cpu().numpy()[0], w.cpu().numpy()[0], 8)
+    score_close(ps, rps)
+    assert np.array_equal(t.cpu().numpy()[0], rt)
