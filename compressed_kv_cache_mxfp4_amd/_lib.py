@@ -88,14 +88,13 @@ _WS = {}
 
 
 def workspace(nbytes: int, dev: torch.device, kind: str = "index") -> torch.Tensor:
-    """A cached, zero-initialised uint8 device buffer of at least nbytes, one
-    per (device, stream, kind).  The attention workspace holds split counters
-    that must start at zero and that every call returns to zero, so it is
-    never shared with the indexer's scratch."""
+    """A cached uint8 device buffer of at least nbytes, one per (device,
+    stream, kind).  Calls on one stream are ordered, so they may share it;
+    the kernels need no particular initial contents."""
     key = (dev, torch.cuda.current_stream(dev).cuda_stream, kind)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _WS[key] = buf
     return buf
 

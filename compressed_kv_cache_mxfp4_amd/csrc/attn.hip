@@ -9,42 +9,43 @@
 // the query heads).  [jokeuncle.pages.dev, "两张架构图里藏着 890 字节", 顺便算清
 // 另外三笔账]: 512 selected + 128 window rows per query.
 //
-// One workgroup (8 waves) per (sequence, group of 16 heads).  A decode call is
-// bound by memory latency (two dependent round trips: the index list, then
-// the rows), so every row load of the workgroup is issued before any math:
-// up to 640 rows (a super-chunk) sit in registers as raw FP4 (72 bytes per
-// lane).  Two passes per super-chunk: pass 1 computes every logit from the
-// registers (independent MFMA chains per 128-row chunk) and reduces the exact
-// max and sum once; pass 2 re-dequantises each chunk into LDS for P.R.  Longer
-// selections run several super-chunks joined by an online-softmax rescale.
-//  * Q.R^T: wave w takes rows 16w..16w+15 of each 128-row chunk.  Lane (g, m) holds 64
-//    code bytes of row m (dims 128g..128g+127) and their 8 scale bytes and
-//    dequantises them straight into the A operand of v_mfma_f32_16x16x32_bf16:
-//    K step ks covers dims 128g+8ks..+7 in lane group g, and the query
-//    fragments (B operand, from an LDS copy of the 16 queries) use the same
-//    permutation.  The bf16 rows are also stored row-major in LDS.
-//  * P.R: wave w takes dims 64w..64w+63 for the 16 heads.  P comes from LDS;
-//    the row-major R tile is read column-wise with the gfx950 transpose read
-//    (ds_read_b64_tr_b16): within a 16-lane group, source lane a+4j points at
-//    R[r0+j][d0+4a] and lane n receives R[r0..r0+3][d0+n], i.e. four K slots
-//    of the MFMA B operand.
+// Split-rows design (flash decoding).  The row slots of a sequence (top-k
+// entries, then window entries) are cut into 128-slot chunks; one workgroup
+// (8 waves) takes one (sequence, 16 heads, chunk), so a decode call with 16
+// sequences, 64 heads and 512 + 128 rows runs 320 workgroups rather than 64.
+// Each workgroup leaves an unnormalised partial output with its own max and
+// sum; a combine kernel merges the chunks of each (sequence, head) exactly.
+//  * Q.R^T: wave w takes rows 16w..16w+15 of the chunk.  Lane (g, m) holds the
+//    code bytes of row m for dims 64g..64g+63 and 256+64g..256+64g+63 and
+//    their 8 scale bytes, and dequantises them straight into the A operand of
+//    v_mfma_f32_16x16x32_bf16: K step ks covers dims 64g+8ks (ks < 8) or
+//    256+64g+8(ks-8) in lane group g.  The query fragments (B operand) come
+//    from one LDS copy of the 16 queries with the same permutation (loading
+//    them per wave from global memory would move 8x the bytes through the
+//    CU's vector-memory path).  Every row is dequantised exactly once; the
+//    bf16 values stay in registers until their half of R is staged.
+//  * P.R: each 256-dim half of R lives in LDS in turn (67 KB, so two
+//    workgroups share a CU); wave w takes dims 32w..32w+31 of the half for the
+//    16 heads.  P comes from LDS; the row-major R tile is read column-wise
+//    with the gfx950 transpose read (ds_read_b64_tr_b16): within a 16-lane
+//    group, source lane a+4j points at R[r0+j][d0+4a] and lane n receives
+//    R[r0..r0+3][d0+n], i.e. four K slots of the MFMA B operand.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-constexpr int kChunk = 128;            // rows per chunk (8 waves x 16)
+constexpr int kChunk = 128;            // row slots per workgroup (8 waves x 16)
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kPrefetch = 5;           // chunks whose rows are loaded up front
-constexpr int kRLd = 520;              // R row stride in bf16 (padded)
-constexpr int kPLd = 136;              // P row stride in bf16 (padded)
+constexpr int kHLd = 264;              // R half-row stride in bf16 (256 + pad)
+constexpr int kPLd = 136;              // P row stride in bf16 (128 + pad)
+constexpr int kQLd = 520;              // query row stride in bf16 (512 + pad)
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 struct AttnSmem {
-  uint16_t R[kChunk * kRLd];
-  uint16_t Q[16 * kRLd];
+  uint16_t R[kChunk * kHLd];  // also holds the 16 x kQLd query tile before the first barrier
   uint16_t P[16 * kPLd];
   float red_m[kAttnWaves][16];
   float red_l[kAttnWaves][16];
@@ -69,8 +70,8 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, uint32_t sbyte) {
 }
 
 struct RowFetch {
-  uint4 c[4];   // 64 code bytes: dims 128g .. 128g+127 of the lane's row
-  uint2 s;      // 8 scale bytes: groups 8g .. 8g+7
+  uint4 c[4];   // code bytes: c[0..1] dims 64g..64g+63, c[2..3] dims 256+64g..256+64g+63
+  uint32_t s[2];  // scale bytes: s[0] groups 4g..4g+3, s[1] groups 16+4g..16+4g+3
   uint32_t ok;  // row exists and is visible
 };
 
@@ -108,203 +109,235 @@ __device__ __forceinline__ RowSrc locate_row(int slot, int32_t p, int nslots, in
 
 __device__ __forceinline__ void fetch_row(RowFetch& f, const RowSrc& r, int g) {
   if (r.ok) {
-    const uint4* c4 = reinterpret_cast<const uint4*>(r.codes + 64 * g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.c[j] = c4[j];
-    f.s = *reinterpret_cast<const uint2*>(r.scales + 8 * g);
+    const uint4* lo = reinterpret_cast<const uint4*>(r.codes + 32 * g);
+    const uint4* hi = reinterpret_cast<const uint4*>(r.codes + 128 + 32 * g);
+    f.c[0] = lo[0];
+    f.c[1] = lo[1];
+    f.c[2] = hi[0];
+    f.c[3] = hi[1];
+    f.s[0] = *reinterpret_cast<const uint32_t*>(r.scales + 4 * g);
+    f.s[1] = *reinterpret_cast<const uint32_t*>(r.scales + 16 + 4 * g);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.c[j] = make_uint4(0u, 0u, 0u, 0u);
-    f.s = make_uint2(0u, 0u);
+    f.s[0] = f.s[1] = 0u;
   }
   f.ok = r.ok;
 }
 
-// Dequantise the 16 K steps of one lane's row slice (dims 128g..128g+127).
+// Dims of K step ks in lane group g: 64g+8ks (ks < 8), 256+64g+8(ks-8).
+__device__ __forceinline__ int step_dim(int ks, int g) {
+  return (ks < 8 ? 0 : 256) + 64 * g + 8 * (ks & 7);
+}
+
+// Dequantise K step ks of one lane's row slice.
 template <int FMT>
 __device__ __forceinline__ bf16x8 row_step(const RowFetch& f, int ks) {
   const uint4 c4 = f.c[ks >> 2];
   const uint32_t cwd = (ks & 3) == 0 ? c4.x : ((ks & 3) == 1 ? c4.y : ((ks & 3) == 2 ? c4.z : c4.w));
-  const uint32_t sbyte = (((ks >> 1) < 4 ? f.s.x : f.s.y) >> (8 * ((ks >> 1) & 3))) & 0xFFu;
+  const uint32_t sbyte = (f.s[ks >> 3] >> (8 * ((ks >> 1) & 3))) & 0xFFu;
   return dequant8<FMT>(cwd, sbyte);
 }
 
+// O(16 heads x 32 dims of half h, wave w) += P . R_half  (4 K steps of 32 rows)
+__device__ __forceinline__ void pv_half(const AttnSmem& sm, int w, int g, int n, floatx4 (&O)[2]) {
+  const int ta = n & 3, tj = n >> 2;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sm.P[n * kPLd + 32 * ks + 8 * g]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = 32 * w + 16 * nt + 4 * ta;
+      const int r0 = 32 * ks + 8 * g + tj;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kHLd + col]));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) shortx4*)(&sm.R[(r0 + 4) * kHLd + col]));
+      shortx8 bv;
+      bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
+      bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
+      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bv), O[nt], 0, 0, 0);
+    }
+  }
+}
+
+// One (sequence, 16 heads, 128-slot chunk).  Grid: XCD-aware linear order in
+// which the head groups of one (sequence, chunk) share an XCD (and its L2
+// copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512] (fp32, relative
+// to the chunk max) and ml[(b*H+h)*S + s] = (max, sum).
 template <int FMT>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
     const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
-    const int32_t* __restrict__ swa_len, float sm_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
+    float* __restrict__ part, float2* __restrict__ ml) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
-  const int hg = blockIdx.x, b = blockIdx.y;
+  const int HG = H >> 4;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, j = id >> 3;
+  const int hg = j % HG;
+  const int t = (j / HG) * 8 + xcd;
+  if (t >= B * S) return;  // workgroup-uniform
+  const int b = t / S, sidx = t - b * S;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int nslots = k + swa_cap;
   int64_t L = len ? len[b] : 0;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int SL = swa_len ? swa_len[b] : 0;
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
-  const int ta = n & 3, tj = n >> 2;
 
-  // running statistics of heads 4g+i (O side) across super-chunks
-  float Mrun[4], Lrun[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { Mrun[i] = -INFINITY; Lrun[i] = 0.f; }
-  float MrunP = -INFINITY;  // the same running max for head n (P side)
-  floatx4 O[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Super-chunks of kPrefetch*kChunk row slots (one for k + window <= 640).
-  for (int s0 = 0; s0 < nslots; s0 += kPrefetch * kChunk) {
-    const int nch = min(kPrefetch, (nslots - s0 + kChunk - 1) / kChunk);
-    // ---- prologue: two round trips (index-list entries, then every row load)
-    int32_t pidx[kPrefetch];
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc) {
-      const int slot = s0 + cc * kChunk + 16 * w + n;
-      const int32_t v = k > 0 ? topk[(int64_t)b * k + min(slot, k - 1)] : -1;
-      pidx[cc] = slot < k ? v : -1;
-    }
-    uint4 qv[2];
-    if (s0 == 0) {
-      const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) qv[j] = qp[tid + kAttnThreads * j];  // 16 heads x 64 pieces
-    }
-    RowFetch rows[kPrefetch];
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc) {
-      const RowSrc src = locate_row(s0 + cc * kChunk + 16 * w + n, pidx[cc], nslots, b, k, L, SL,
-                                    cap, swa_stride, main_codes, main_scales, swa_codes, swa_scales);
-      fetch_row(rows[cc], src, g);
-    }
-    if (s0 == 0) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int e = tid + kAttnThreads * j;
-        *reinterpret_cast<uint4*>(&sm.Q[(e >> 6) * kRLd + 8 * (e & 63)]) = qv[j];
-      }
-    }
-    __syncthreads();
-
-    // ---- pass 1: logits of the wave's 16 rows of every chunk (independent MFMA chains)
-    floatx4 sacc[kPrefetch];
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc) sacc[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&sm.Q[n * kRLd + 128 * g + 8 * ks]);
-#pragma unroll
-      for (int cc = 0; cc < kPrefetch; ++cc) {
-        if (cc < nch)
-          sacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_step<FMT>(rows[cc], ks), qf, sacc[cc], 0, 0, 0);
-      }
-    }
-    float x[kPrefetch][4];
-    float mw = -INFINITY;
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc) {
-      const uint64_t vmask = __ballot(rows[cc].ok != 0u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = cc < nch && ((vmask >> (4 * g + i)) & 1ull);
-        x[cc][i] = ok ? sacc[cc][i] * sm_scale : -INFINITY;
-        mw = fmaxf(mw, x[cc][i]);
-      }
-    }
-    mw = fmaxf(mw, shfl_xor_f(mw, 16));
-    mw = fmaxf(mw, shfl_xor_f(mw, 32));
-    if (g == 0) sm.red_m[w][n] = mw;
-    __syncthreads();
-    float Msc = sm.red_m[0][n];
-#pragma unroll
-    for (int v = 1; v < kAttnWaves; ++v) Msc = fmaxf(Msc, sm.red_m[v][n]);
-    const float MnewP = fmaxf(MrunP, Msc);
-    MrunP = MnewP;
-    float lw = 0.f;
-    uint32_t pb[kPrefetch][4];
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = (MnewP == -INFINITY) ? 0.0f : __expf(x[cc][i] - MnewP);
-        pb[cc][i] = f32_to_bf16_bits(p);
-        lw += p;
-      }
-    lw += shfl_xor_f(lw, 16);
-    lw += shfl_xor_f(lw, 32);
-    if (g == 0) sm.red_l[w][n] = lw;
-
-    // ---- pass 2: per chunk, R (re-dequantised) and P to LDS, then O += P.R
-#pragma unroll
-    for (int cc = 0; cc < kPrefetch; ++cc) {
-      if (cc >= nch) break;  // workgroup-uniform
-      uint16_t* rrow = &sm.R[(16 * w + n) * kRLd + 128 * g];
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = row_step<FMT>(rows[cc], ks);
-      *reinterpret_cast<uint2*>(&sm.P[n * kPLd + 16 * w + 4 * g]) =
-          make_uint2(pb[cc][0] | (pb[cc][1] << 16), pb[cc][2] | (pb[cc][3] << 16));
-      __syncthreads();
-      if (cc == 0) {
-        // rescale the running output of heads 4g+i to this super-chunk's max
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hh = 4 * g + i;
-          float m2 = sm.red_m[0][hh];
-          float l2 = sm.red_l[0][hh];
-#pragma unroll
-          for (int v = 1; v < kAttnWaves; ++v) {
-            m2 = fmaxf(m2, sm.red_m[v][hh]);
-            l2 += sm.red_l[v][hh];
-          }
-          const float mn = fmaxf(Mrun[i], m2);
-          const float alpha = (Mrun[i] == -INFINITY) ? 0.0f : __expf(Mrun[i] - mn);
-          Lrun[i] = Lrun[i] * alpha + l2;
-          Mrun[i] = mn;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) O[nt][i] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sm.P[n * kPLd + 32 * ks + 8 * g]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int col = 64 * w + 16 * nt + 4 * ta;
-          const int r0 = 32 * ks + 8 * g + tj;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kRLd + col]));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)(&sm.R[(r0 + 4) * kRLd + col]));
-          shortx8 bv;
-          bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-          bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-          O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bv), O[nt], 0, 0, 0);
-        }
-      }
-      __syncthreads();
-    }
+  // ---- loads: index entry and the 16 queries (to LDS, 32 B per thread), then the row
+  const int slot = kChunk * sidx + 16 * w + n;
+  int32_t pidx = -1;
+  if (slot < k) pidx = topk[(int64_t)b * k + slot];
+  const uint4* qg = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
+  const uint4 qv0 = qg[tid], qv1 = qg[tid + kAttnThreads];
+  RowFetch row;
+  {
+    const RowSrc src = locate_row(slot, pidx, nslots, b, k, L, SL, cap, swa_stride, main_codes,
+                                  main_scales, swa_codes, swa_scales);
+    fetch_row(row, src, g);
   }
+  // the query tile borrows the R buffer, which is not written before the max barrier
+  uint16_t* Q = sm.R;
+  *reinterpret_cast<uint4*>(&Q[(tid >> 6) * kQLd + 8 * (tid & 63)]) = qv0;
+  *reinterpret_cast<uint4*>(&Q[((tid >> 6) + 8) * kQLd + 8 * (tid & 63)]) = qv1;
+  __syncthreads();
 
-  const int h0 = 16 * hg;
+  // ---- logits of the wave's 16 rows (every row dequantised once, kept for P.R)
+  floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ra[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    ra[ks] = row_step<FMT>(row, ks);
+    const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + step_dim(ks, g)]);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[ks], qf, sacc, 0, 0, 0);
+  }
+  // lane (g, n): rows 4g+i of the wave's tile, head n
+  const uint64_t vmask = __ballot(row.ok != 0u);
+  float x[4];
+  float mw = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * g + i;
-    const float inv = Lrun[i] > 0.f ? 1.0f / Lrun[i] : 0.0f;
-    uint16_t* orow = out + ((int64_t)b * H + h0 + hh) * 512 + 64 * w + n;
+    x[i] = ((vmask >> (4 * g + i)) & 1ull) ? sacc[i] * sm_scale : -INFINITY;
+    mw = fmaxf(mw, x[i]);
+  }
+  mw = fmaxf(mw, shfl_xor_f(mw, 16));
+  mw = fmaxf(mw, shfl_xor_f(mw, 32));
+  if (g == 0) sm.red_m[w][n] = mw;
+  __syncthreads();  // also: every wave is done reading the query tile
+  float M = sm.red_m[0][n];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) orow[16 * nt] = (uint16_t)f32_to_bf16_bits(O[nt][i] * inv);
-    if (lse && w == 0 && n == 0)
-      lse[(int64_t)b * H + h0 + hh] = Lrun[i] > 0.f ? Mrun[i] + logf(Lrun[i]) : -INFINITY;
+  for (int v = 1; v < kAttnWaves; ++v) M = fmaxf(M, sm.red_m[v][n]);
+  float lw = 0.f;
+  uint32_t pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = (M == -INFINITY) ? 0.0f : __expf(x[i] - M);
+    pb[i] = f32_to_bf16_bits(p);
+    lw += p;
+  }
+  lw += shfl_xor_f(lw, 16);
+  lw += shfl_xor_f(lw, 32);
+  if (g == 0) sm.red_l[w][n] = lw;
+  *reinterpret_cast<uint2*>(&sm.P[n * kPLd + 16 * w + 4 * g]) =
+      make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+  uint16_t* rrow = &sm.R[(16 * w + n) * kHLd + 64 * g];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
+  __syncthreads();
+
+  float* prow = part + ((int64_t)b * H + 16 * hg) * S * 512;
+  if (w == 0 && g == 0) {
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < kAttnWaves; ++v) l += sm.red_l[v][n];
+    ml[((int64_t)b * H + 16 * hg + n) * S + sidx] = make_float2(M, l);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1) {
+      __syncthreads();  // every wave is done reading the first half
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[8 + ks];
+      __syncthreads();
+    }
+    floatx4 O[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    pv_half(sm, w, g, n, O);
+    // lane (g, n): heads 4g+i, dims 256h + 32w + 16nt + n
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 32 * w + n;
+      dst[0] = O[0][i];
+      dst[16] = O[1][i];
+    }
   }
 }
 
+static_assert(16 * kQLd <= kChunk * kHLd, "query tile must fit in the R buffer");
+
+// Merge the S chunk partials of each (sequence, head): one wave per head,
+// 8 dims per lane; chunk loads are issued four at a time.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
+                                                           const float2* __restrict__ ml, int BH,
+                                                           int S, uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;
+  const int lane = threadIdx.x & 63;
+  const float2* m = ml + (int64_t)bh * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, m[s].x);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float Lsum = 0.f;
+  if (M != -INFINITY) {
+    const float4* src = reinterpret_cast<const float4*>(part + (int64_t)bh * S * 512) + 2 * lane;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float wgt[4];
+      float4 v[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        wgt[j] = 0.f;
+        v[j][0] = v[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (s < S) {
+          const float2 e = m[s];
+          if (e.x != -INFINITY) {
+            wgt[j] = __expf(e.x - M);
+            Lsum += wgt[j] * e.y;
+            v[j][0] = src[s * 128];
+            v[j][1] = src[s * 128 + 1];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[0] += wgt[j] * v[j][0].x; acc[1] += wgt[j] * v[j][0].y;
+        acc[2] += wgt[j] * v[j][0].z; acc[3] += wgt[j] * v[j][0].w;
+        acc[4] += wgt[j] * v[j][1].x; acc[5] += wgt[j] * v[j][1].y;
+        acc[6] += wgt[j] * v[j][1].z; acc[7] += wgt[j] * v[j][1].w;
+      }
+    }
+  }
+  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
+  uint4 o;
+  o.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+  o.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
+  o.z = f32_to_bf16_bits(acc[4] * inv) | (f32_to_bf16_bits(acc[5] * inv) << 16);
+  o.w = f32_to_bf16_bits(acc[6] * inv) | (f32_to_bf16_bits(acc[7] * inv) << 16);
+  *reinterpret_cast<uint4*>(out + (int64_t)bh * 512 + 8 * lane) = o;
+  if (lse && lane == 0) lse[bh] = Lsum > 0.f ? M + logf(Lsum) : -INFINITY;
+}
+
+static int attn_splits(int k, int swa_cap) { return (k + swa_cap + kChunk - 1) / kChunk; }
+
 size_t attn_ws_bytes(int B, int H, int k, int swa_cap) {
-  (void)B; (void)H; (void)k; (void)swa_cap;
-  return 256;  // no scratch is used; a token buffer keeps the interface stable
+  const size_t n = (size_t)B * H * attn_splits(k, swa_cap);
+  const size_t part = (n * 512 * sizeof(float) + 255) & ~(size_t)255;
+  return part + ((n * sizeof(float2) + 255) & ~(size_t)255) + 256;
 }
 
 int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
@@ -313,24 +346,31 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
                        const int32_t* swa_len, float sm_scale, uint16_t* out, float* lse_opt,
                        void* ws, hipStream_t st) {
-  (void)ws;
   if (B == 0) return 0;
+  const int S = attn_splits(k, swa_cap);
+  const size_t n = (size_t)B * H * S;
+  float* part = reinterpret_cast<float*>(ws);
+  float2* ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
+                                         ((n * 512 * sizeof(float) + 255) & ~(size_t)255));
   const size_t smem = sizeof(AttnSmem);
   static bool attr_done[2] = {false, false};
-  dim3 grid((unsigned)(H / 16), (unsigned)B);
+  const int pairs8 = (B * S + 7) / 8;
+  const unsigned grid = (unsigned)(pairs8 * 8 * (H / 16));
   if (main_fmt == 0) {
     if (!attr_done[0]) {
-      hipFuncSetAttribute((const void*)attn_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      hipFuncSetAttribute((const void*)attn_split_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
       attr_done[0] = true;
     }
-    attn_kernel<0><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, out, lse_opt);
+    attn_split_kernel<0><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S, part, ml);
   } else {
     if (!attr_done[1]) {
-      hipFuncSetAttribute((const void*)attn_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      hipFuncSetAttribute((const void*)attn_split_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
       attr_done[1] = true;
     }
-    attn_kernel<1><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, out, lse_opt);
+    attn_split_kernel<1><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S, part, ml);
   }
+  const int BH = B * H;
+  attn_combine_kernel<<<(unsigned)((BH + 3) / 4), 256, 0, st>>>(part, ml, BH, S, out, lse_opt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -201,8 +201,12 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
  *   lse_opt  : optional out fp32 [B][H], natural-log sum of exp(sm_scale*logits);
  *              -inf (and a zero output row) when a sequence attends no row.
  *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes
- *              (reserved; the current kernels keep no scratch in it).
- * The result is deterministic (no atomics; fixed reduction order).
+ *              (B*H*ceil((k+swa_cap)/128) partial outputs of 512 fp32 plus a
+ *              (max, sum) pair each); no initial contents needed, contents
+ *              undefined afterwards.
+ * Two kernels on `stream`: per 128-row chunk partial attention, then an exact
+ * merge of the chunks of each (sequence, head).  The result is deterministic
+ * (no atomics; fixed reduction order).
  */
 size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap);
 int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_codes,
