@@ -22,6 +22,8 @@ HIPCC_FLAGS = [
     "-fno-gpu-rdc", "-Wall", "-Wno-unused-function",
     # no packed fp32 arithmetic anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the epilogues read them with VALU ops anyway
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(_ROOT, "include"), "-I", CSRC,
 ]
 

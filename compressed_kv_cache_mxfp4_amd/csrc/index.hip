@@ -34,55 +34,72 @@ namespace csa2 {
 // ======================================================================
 constexpr int kScoreThreads = 256;
 constexpr int kSuperTile = 64;
+constexpr int kScoreWaves = 2048;  // resident waves targeted per launch (2 per SIMD)
 
-struct StageRegs {
-  int32_t row;     // row this lane's item maps to (valid or a safe 0)
-  uint32_t valid;  // item exists and is visible
-  uint32_t sc;     // 4 scale bytes of this lane's item
-  uint4 cw[4];     // 16 code bytes for (tile t, this lane's group g)
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// Rows of the four 16-entry tiles of one super-tile as seen by lane (g, n):
+// entry base + 16t + n of tile t.  Entries past the end map to row 0 (always
+// present: the cache holds at least one row), so loads need no branch.
+struct ScoreRows {
+  int32_t r[4];
+  uint32_t ok;  // bit t: entry of tile t exists and is visible
+};
+
+// Loaded operands of one super-tile: tile t's codes (entry 16t+n, dims
+// 32g..32g+31) and the E8M0 byte of that (entry, group).
+struct ScoreStage {
+  uint4 cw[4];
+  uint32_t sb[4];
 };
 
 template <bool GATHER>
-__device__ __forceinline__ void score_stage_load(StageRegs& s, int64_t base, int64_t N, int64_t L,
-                                                 const int32_t* __restrict__ pool_b,
-                                                 const uint8_t* __restrict__ codes_b,
-                                                 const uint8_t* __restrict__ scales_b, int lane) {
-  const int64_t it = base + lane;
-  int32_t row = 0;
-  uint32_t valid = 0;
-  if (it < N) {
-    if (GATHER) {
-      const int32_t p = pool_b[it];
-      if (p >= 0 && (int64_t)p < L) {
-        row = p;
-        valid = 1;
-      }
-    } else {
-      row = (int32_t)it;
-      valid = 1;
-    }
-  }
-  s.row = row;
-  s.valid = valid;
-  s.sc = *reinterpret_cast<const uint32_t*>(scales_b + (int64_t)row * 4);
-  const int g = lane >> 4, n = lane & 15;
+__device__ __forceinline__ void score_rows(ScoreRows& R, int64_t base, int64_t N, int64_t L,
+                                           const int32_t* __restrict__ pool_b, int n) {
+  R.ok = 0u;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int32_t r = GATHER ? __shfl(row, 16 * t + n, 64) : (int32_t)(((base + 16 * t + n) < N) ? (base + 16 * t + n) : 0);
-    s.cw[t] = *reinterpret_cast<const uint4*>(codes_b + (int64_t)r * 64 + 16 * g);
+    const int64_t it = base + 16 * t + n;
+    const bool in = it < N;
+    int32_t row;
+    if (GATHER) {
+      const int32_t p = pool_b[in ? it : 0];
+      const bool vis = in && p >= 0 && (int64_t)p < L;
+      row = vis ? p : 0;
+      R.ok |= (vis ? 1u : 0u) << t;
+    } else {
+      row = in ? (int32_t)it : 0;
+      R.ok |= (in ? 1u : 0u) << t;
+    }
+    R.r[t] = row;
   }
 }
 
-template <int MT>
-__device__ __forceinline__ float score_stage_compute(const StageRegs& s, const bf16x8 (&A)[MT][4],
-                                                     const float (&wr)[MT][4], int lane) {
-  const int g = lane >> 4, n = lane & 15;
-  float mine = 0.0f;
+// Byte offsets fit 32 bits (at most CSA2_MAX_CACHE_ROWS rows of 64 B per
+// sequence), so loads take a uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ void score_load(ScoreStage& S, const ScoreRows& R,
+                                           const uint8_t* __restrict__ codes_b,
+                                           const uint8_t* __restrict__ scales_b, int g) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint32_t s4 = (uint32_t)__shfl((int)s.sc, 16 * t + n, 64);
-    const float sop = e8m0_operand((s4 >> (8 * g)) & 0xFFu);
-    const uint32_t cw[4] = {s.cw[t].x, s.cw[t].y, s.cw[t].z, s.cw[t].w};
+    const uint32_t r = (uint32_t)R.r[t];
+    S.cw[t] = *reinterpret_cast<const uint4*>(codes_b + (r * 64u + 16u * (uint32_t)g));
+    S.sb[t] = scales_b[r * 4u + (uint32_t)g];
+  }
+}
+
+// Score of entry 16g+n of the super-tile (lane order), before masking.
+template <int MT>
+__device__ __forceinline__ float score_compute(const ScoreStage& S, const bf16x8 (&A)[MT][4],
+                                               const float (&wr)[MT][4]) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float sop = e8m0_operand(S.sb[t]);
+    const uint32_t cw[4] = {S.cw[t].x, S.cw[t].y, S.cw[t].z, S.cw[t].w};
     floatx4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -93,27 +110,47 @@ __device__ __forceinline__ float score_stage_compute(const StageRegs& s, const b
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], bv, acc[mt], 0, 0, 0);
     }
-    float part = 0.0f;
+    // lane (g, n) holds heads 16mt+4g+i of entry 16t+n
+    float p = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wr[mt][i] * __int_as_float(max(__float_as_int(acc[mt][i]), 0));
-    part += shfl_xor_f(part, 16);
-    part += shfl_xor_f(part, 32);
-    if (g == t) mine = part;
+      for (int i = 0; i < 4; ++i) p += wr[mt][i] * __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+    part[t] = p;
   }
-  return mine;
+  // Reduce-scatter over the four 16-lane rows: row g ends with tile g's sum.
+  const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+  const float s02 = __uint_as_float(a02[0]) + __uint_as_float(a02[1]);
+  const float s13 = __uint_as_float(a13[0]) + __uint_as_float(a13[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Grid: (chunks, B).  Each workgroup scores `4 * stpw` super-tiles of one
-// sequence; with GATHER the items are pool[b][i], otherwise positions i.
-template <int MT, bool GATHER>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+__device__ __forceinline__ float max8_lanes(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v), 0u)));   // xor 1
+  v = fmaxf(v, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(v), 0u)));   // xor 2
+  v = fmaxf(v, __uint_as_float(dpp_mov<0x141>(__float_as_uint(v), 0u)));  // half-row mirror
+  return v;
+}
+
+// Grid: (workgroups per sequence, B).  Persistent waves: wave j of a
+// sequence scores super-tiles j, j + W, j + 2W, ... (W waves per sequence)
+// through a ring of kScoreStages operand stages, so kScoreStages - 1
+// super-tiles are in flight while one is computed.  With GATHER the items
+// are pool[b][i], otherwise positions i; the pool entries of a super-tile
+// are read one ring step before its codes.
+constexpr int kScoreStages = 3;
+
+template <int MT, bool GATHER, int NS = kScoreStages, int OCC = 2, bool WLDS = false>
+__global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int64_t cap,
     const int32_t* __restrict__ len, const int32_t* __restrict__ pool,
     const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
     const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
-    float* __restrict__ bmax, int64_t bmax_stride, int stpw) {
+    float* __restrict__ bmax, int64_t bmax_stride) {
+  __shared__ __align__(16) uint16_t qs[64 * 128];
+  __shared__ float ws[64];
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
@@ -124,57 +161,82 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     int64_t pl = pool_len[b];
     N = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
   }
-  const int64_t chunk0 = (int64_t)blockIdx.x * 4 * stpw * kSuperTile;
-  if (chunk0 >= N) return;
+  const int64_t W = (int64_t)gridDim.x * 4;
+  const int64_t st0 = (int64_t)blockIdx.x * 4 + wave;
+  if ((int64_t)blockIdx.x * 4 * kSuperTile >= N) return;  // workgroup-uniform
 
-  // Query heads as A operands: lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
+  // Query heads (zero beyond H) and head weights, staged once per workgroup.
+  {
+    const int h = threadIdx.x >> 2, part = threadIdx.x & 3;  // 64 heads x 4 pieces of 64 B
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = h < H ? *reinterpret_cast<const uint4*>(q + ((int64_t)b * H + h) * 128 + 32 * part + 8 * j)
+                   : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&qs[h * 128 + 32 * part + 8 * j]) = v[j];
+    if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
+  }
+  __syncthreads();
+  if (st0 * kSuperTile >= N) return;  // wave-uniform; no barrier follows
+  // A operand: lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
   bf16x8 A[MT][4];
   float wr[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int h = 16 * mt + n;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (h < H) {
-        const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * H + h) * 128 + 32 * g + 8 * ks);
-        A[mt][ks] = __builtin_bit_cast(bf16x8, v);
-      } else {
-        A[mt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      A[mt][ks] = *reinterpret_cast<const bf16x8*>(&qs[(16 * mt + n) * 128 + 32 * g + 8 * ks]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * mt + 4 * g + i;
-      wr[mt][i] = hh < H ? w[(int64_t)b * H + hh] : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) wr[mt][i] = ws[16 * mt + 4 * g + i];
   }
+  const float4* wq = reinterpret_cast<const float4*>(ws) + g;  // heads 16mt+4g .. +3 at wq[4mt]
 
   const uint8_t* codes_b = idx_codes + (int64_t)b * cap * 64;
   const uint8_t* scales_b = idx_scales + (int64_t)b * cap * 4;
   const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
   float* scores_b = scores + (int64_t)b * score_stride;
 
-  StageRegs cur, nxt;
-  int64_t base = chunk0 + (int64_t)wave * kSuperTile;
-  if (base >= N) return;
-  score_stage_load<GATHER>(cur, base, N, L, pool_b, codes_b, scales_b, lane);
-  for (int j = 0; j < stpw; ++j) {
-    const int64_t nbase = base + 4 * kSuperTile;
-    const bool more = (j + 1 < stpw) && (nbase < N);
-    if (more) score_stage_load<GATHER>(nxt, nbase, N, L, pool_b, codes_b, scales_b, lane);
-    const float sc = score_stage_compute<MT>(cur, A, wr, lane);
-    const int64_t it = base + lane;
-    if (it < N) scores_b[it] = cur.valid ? sc : __uint_as_float(0x7FC00000u);
-    if (!GATHER) {
-      float bm = (it < N) ? sc : -INFINITY;
-      bm = fmaxf(bm, shfl_xor_f(bm, 1));
-      bm = fmaxf(bm, shfl_xor_f(bm, 2));
-      bm = fmaxf(bm, shfl_xor_f(bm, 4));
-      if ((lane & 7) == 0 && it < N) bmax[(int64_t)b * bmax_stride + (it >> 3)] = bm;
+  const int64_t step = W * kSuperTile;
+  const int64_t base0 = st0 * kSuperTile;
+  const int64_t iters = (N - base0 + step - 1) / step;  // >= 1
+  ScoreRows rows[NS];
+  ScoreStage stg[NS];
+  // ring invariant at the top of round r (iteration i = r*NS + u handled by
+  // slot u): stages hold iterations i .. i+NS-2, rows[(u+NS-1)%NS] iteration i+NS-1
+#pragma unroll
+  for (int u = 0; u < NS; ++u) score_rows<GATHER>(rows[u], base0 + u * step, N, L, pool_b, n);
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) score_load(stg[u], rows[u], codes_b, scales_b, g);
+  for (int64_t i0 = 0; i0 < iters; i0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int64_t i = i0 + u;
+      const int64_t bs = base0 + i * step;
+      const uint32_t ok = rows[u].ok;
+      // refill: stage of iteration i+NS-1 (its rows are ready), rows of i+NS
+      score_load(stg[(u + NS - 1) % NS], rows[(u + NS - 1) % NS], codes_b, scales_b, g);
+      score_rows<GATHER>(rows[u], bs + NS * step, N, L, pool_b, n);
+      if (i < iters) {
+        if (WLDS) {
+          // head weights re-read from LDS each super-tile (keeps 16 VGPRs free)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const float4 v = wq[4 * mt];
+            wr[mt][0] = v.x; wr[mt][1] = v.y; wr[mt][2] = v.z; wr[mt][3] = v.w;
+          }
+        }
+        const float sc = score_compute<MT>(stg[u], A, wr);
+        const int64_t it = bs + lane;
+        const bool mine_ok = (ok >> g) & 1u;
+        if (it < N) scores_b[it] = mine_ok ? sc : __uint_as_float(0x7FC00000u);
+        if (!GATHER) {
+          const float bm = max8_lanes(it < N ? sc : -INFINITY);
+          if ((lane & 7) == 0 && it < N) bmax[(int64_t)b * bmax_stride + (it >> 3)] = bm;
+        }
+      }
     }
-    if (!more) break;
-    cur = nxt;
-    base = nbase;
   }
 }
 
@@ -189,11 +251,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 // are emitted in ascending candidate order through wave ballots.  Ordering:
 // larger key first, equal keys to the lower candidate index.  Wave-level
 // reductions and scans use DPP (row shifts, mirrors, row broadcasts).
-
-template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, true);
-}
 
 // Reduce within each 16-lane row (every lane of the row gets the row's value).
 template <class Op>
@@ -502,14 +559,24 @@ template <bool GATHER>
 static void launch_score(int MT, dim3 grid, hipStream_t st, const uint8_t* ic, const uint8_t* is,
                          int64_t cap, const int32_t* len, const int32_t* pool,
                          const int32_t* pool_len, int pool_cap, const uint16_t* q, const float* w,
-                         int H, float* scores, int64_t sstride, float* bmax, int64_t bstride,
-                         int stpw) {
+                         int H, float* scores, int64_t sstride, float* bmax, int64_t bstride) {
   if (MT == 1)
-    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
   else if (MT == 2)
-    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
   else
-    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, stpw);
+    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
+}
+
+// Workgroups per sequence for `items` scored entries: enough resident waves
+// to cover the chip, never more than one super-tile per wave.
+static unsigned score_wgs(int64_t items, int B) {
+  const int64_t tiles = (items + kSuperTile - 1) / kSuperTile;
+  int64_t waves = kScoreWaves / (B > 0 ? B : 1);
+  if (waves < 4) waves = 4;
+  if (waves > tiles) waves = tiles;
+  const int64_t wgs = (waves + 3) / 4;
+  return (unsigned)(wgs > 0 ? wgs : 1);
 }
 
 int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
@@ -522,12 +589,10 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   float* bmax = reinterpret_cast<float*>((char*)ws + l.bmax_off);
   const int64_t nbk = (cap + block - 1) / block;
   const int MT = (H + 15) / 16;
-  const int stpw = 2;
-  const int64_t chunk = 4LL * stpw * kSuperTile;
-  dim3 grid((unsigned)((cap + chunk - 1) / chunk), (unsigned)B);
+  dim3 grid(score_wgs(cap, B), (unsigned)B);
   if (cap > 0)
     launch_score<false>(MT, grid, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
-                        H, scores, cap, bmax, nbk, stpw);
+                        H, scores, cap, bmax, nbk);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
 #define CSA2_SELFULL(NT, EB, EP) \
@@ -554,12 +619,10 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   if (B == 0) return 0;
   float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>(ws);
   const int MT = (H + 15) / 16;
-  const int stpw = 2;
-  const int64_t chunk = 4LL * stpw * kSuperTile;
-  dim3 grid((unsigned)((pool_cap + chunk - 1) / chunk), (unsigned)B);
+  dim3 grid(score_wgs(pool_cap, B), (unsigned)B);
   if (pool_cap > 0)
     launch_score<true>(MT, grid, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
-                       w, H, ps, pool_cap, nullptr, 0, stpw);
+                       w, H, ps, pool_cap, nullptr, 0);
   if (hipGetLastError() != hipSuccess) return -1;
   if (pool_cap <= 4 * 1024)
     select_pool_kernel<1024, 4><<<B, 1024, 0, st>>>(ps, pool, pool_len, pool_cap, k, topk);
