@@ -112,8 +112,8 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
   if (!idx_codes || !idx_scales || !len || !pool || !pool_len || !q || !w || !topk)
     return CSA2_ERR_NULL;
   if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
-  if (!pool_scores_opt && (!ws || ws_bytes < csa2_index_pool_workspace(B, pool_cap, k)))
-    return CSA2_ERR_WORKSPACE;
+  const size_t need = csa2_index_pool_workspace(B, pool_cap, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   return launched(csa2::launch_index_pool(idx_codes, idx_scales, cap, len, B, pool, pool_len,
                                           pool_cap, q, w, H, k, topk, pool_scores_opt, ws,
                                           as_stream(stream)));

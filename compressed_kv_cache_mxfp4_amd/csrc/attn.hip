@@ -353,22 +353,21 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   float2* ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
                                          ((n * 512 * sizeof(float) + 255) & ~(size_t)255));
   const size_t smem = sizeof(AttnSmem);
-  static bool attr_done[2] = {false, false};
   const int pairs8 = (B * S + 7) / 8;
   const unsigned grid = (unsigned)(pairs8 * 8 * (H / 16));
-  if (main_fmt == 0) {
-    if (!attr_done[0]) {
-      hipFuncSetAttribute((const void*)attn_split_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      attr_done[0] = true;
+  auto go = [&](auto kern) -> bool {
+    static bool attr_done = false;  // one per instantiation
+    if (!attr_done) {
+      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+        return false;
+      attr_done = true;
     }
-    attn_split_kernel<0><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S, part, ml);
-  } else {
-    if (!attr_done[1]) {
-      hipFuncSetAttribute((const void*)attn_split_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      attr_done[1] = true;
-    }
-    attn_split_kernel<1><<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S, part, ml);
-  }
+    kern<<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
+                                           swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
+                                           part, ml);
+    return true;
+  };
+  if (!(main_fmt == 0 ? go(attn_split_kernel<0>) : go(attn_split_kernel<1>))) return -1;
   const int BH = B * H;
   attn_combine_kernel<<<(unsigned)((BH + 3) / 4), 256, 0, st>>>(part, ml, BH, S, out, lse_opt);
   return hipGetLastError() == hipSuccess ? 0 : -1;

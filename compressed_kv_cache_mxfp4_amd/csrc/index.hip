@@ -231,10 +231,11 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
         const int64_t it = bs + lane;
         const bool mine_ok = (ok >> g) & 1u;
         if (it < N) scores_b[it] = mine_ok ? sc : __uint_as_float(0x7FC00000u);
-        if (!GATHER) {
-          const float bm = max8_lanes(it < N ? sc : -INFINITY);
-          if ((lane & 7) == 0 && it < N) bmax[(int64_t)b * bmax_stride + (it >> 3)] = bm;
-        }
+        // maximum of each group of 8 consecutive items (a cache block, or 8
+        // pool entries); a group with no visible item gets NaN (absent)
+        const float bm = max8_lanes((it < N && mine_ok) ? sc : -INFINITY);
+        if ((lane & 7) == 0 && it < N)
+          bmax[(int64_t)b * bmax_stride + (it >> 3)] = bm == -INFINITY ? __uint_as_float(0x7FC00000u) : bm;
       }
     }
   }
@@ -283,8 +284,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
-struct SelScratch {
-  uint32_t hist[2048];
+struct __align__(16) SelScratch {
+  uint32_t hist[2][2048];  // double-buffered: one is cleared while the other is filled
   uint32_t wred[3][16];
   uint32_t bc[4];
 };
@@ -320,13 +321,56 @@ __device__ __forceinline__ void load_keys(KeyRegs<EPT>& K, const Src& src, int n
   }
 }
 
-// Top-k of the n candidates (key 0 = absent): calls emit(i, rank) for the
-// winners in ascending i, rank = 0, 1, ...; returns min(k, #present).
-template <int NT, int EPT, class Src, class Emit>
+// Bin of histogram h (2048 bins, ascending key order; bins past the used
+// range are zero) that holds the need-th largest counted key.  Thread t scans
+// bins 2047-TB*t .. 2048-TB*(t+1) in descending order; a block scan of the
+// per-thread sums locates the owner, which writes (bin, count above the bin)
+// to bc[0..1].  Ends with a barrier, so bc is visible on return.
+template <int NT>
+__device__ __forceinline__ void find_bin_from_top(const uint32_t* h, SelScratch& sh, uint32_t need) {
+  constexpr int TB = 2048 / NT;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int top = 2047 - TB * t;
+  uint32_t hb[TB];
+  uint32_t s = 0u;
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    hb[j] = h[top - j];
+    s += hb[j];
+  }
+  const uint32_t incl = wave_incl_scan(s);
+  if (lane == 63) sh.wred[0][wave] = incl;
+  __syncthreads();
+  uint32_t excl = incl - s;
+  for (int v = 0; v < wave; ++v) excl += sh.wred[0][v];
+  if (excl < need && need <= excl + s) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      if (acc < need && need <= acc + hb[j]) {
+        sh.bc[0] = (uint32_t)(top - j);
+        sh.bc[1] = acc;
+        sh.bc[2] = hb[j];
+      }
+      acc += hb[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Top-k of the n candidates (key 0 = absent): calls emit(i, rank, j) for the
+// winners in ascending i (j = the thread's key slot holding candidate i),
+// rank = 0, 1, ...; returns min(k, #present).
+//
+// PREF: when the candidates far outnumber k, a sample (one key per thread)
+// first bounds the k-th key from below: T0 = lower edge of the histogram bin
+// holding a sample rank with a wide margin.  If at least k keys are >= T0
+// (checked exactly), the radix search only histograms keys in [T0, max];
+// otherwise it searches the full range.  Either way the result is exact.
+template <int NT, int EPT, bool PREF, class Src, class Emit>
 __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
                            Emit emit) {
   constexpr int NW = NT / 64;
-  constexpr int TB = 2048 / NT;  // histogram bins per thread in the search
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int E = EPT > 0 ? EPT : (n + NT - 1) / NT;
   auto KEY = [&](int j) -> uint32_t {
@@ -370,6 +414,34 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
   if (target == 0u) return 0;
 
   uint32_t lo = mn, hi = mx, above = 0u, T;
+  bool take_all_eq = false;
+  int buf = 0;  // histogram buffer of the next pass; both start cleared
+  for (int i = t; i < 2 * 2048; i += NT) (&sh.hist[0][0])[i] = 0u;
+  __syncthreads();
+  if (PREF && lo != hi && cnt > 4096u && cnt >= 8u * target) {
+    const uint32_t span = hi - lo;
+    const int nbits = 32 - __clz((int)span);
+    const int shift = nbits > 11 ? nbits - 11 : 0;
+    const uint32_t smp = KEY(0);
+    if (smp) atomicAdd(&sh.hist[0][(smp - lo) >> shift], 1u);
+    if (t == 0) sh.bc[0] = 0xFFFFFFFFu;
+    __syncthreads();
+    // sample rank: 1.5x the expected share of the k winners, plus 16
+    const uint32_t r = min((uint32_t)NT, 16u + (uint32_t)((3ull * target * NT + 2ull * cnt - 1) / (2ull * cnt)));
+    find_bin_from_top<NT>(sh.hist[0], sh, r);
+    const uint32_t tb = sh.bc[0];
+    const uint32_t T0 = tb == 0xFFFFFFFFu ? lo : lo + (tb << shift);
+    for (int i = t; i < 2048; i += NT) sh.hist[0][i] = 0u;
+    uint32_t c0 = 0u;
+#pragma unroll UNR
+    for (int j = 0; j < E; ++j) c0 += (uint32_t)__popcll(__ballot(KEY(j) >= T0));
+    if (lane == 0) sh.wred[1][wave] = c0;
+    __syncthreads();
+    c0 = 0u;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) c0 += sh.wred[1][v];
+    if (c0 >= target) lo = T0;
+  }
   for (;;) {
     if (lo == hi) {
       T = lo;
@@ -378,54 +450,35 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     const uint32_t span = hi - lo;
     const int nbits = 32 - __clz((int)span);
     const int shift = nbits > 11 ? nbits - 11 : 0;
-    const int nb = (int)(span >> shift) + 1;
-    for (int i = t; i < nb; i += NT) sh.hist[i] = 0u;
-    __syncthreads();
+    uint32_t* h = sh.hist[buf];
 #pragma unroll UNR
     for (int j = 0; j < E; ++j) {
       const uint32_t kk = KEY(j);
-      if (kk >= lo && kk <= hi) atomicAdd(&sh.hist[(kk - lo) >> shift], 1u);
+      if (kk >= lo && kk <= hi) atomicAdd(&h[(kk - lo) >> shift], 1u);
     }
+    uint32_t* hn = sh.hist[buf ^ 1];
+    for (int i = t; i < 2048; i += NT) hn[i] = 0u;  // the next pass's buffer
     __syncthreads();
-    // thread t owns bins top, top-1, ..., top-TB+1 (descending score order)
-    const int top = nb - 1 - TB * t;
-    uint32_t hb[TB];
-    uint32_t s = 0u;
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      hb[j] = (top - j) >= 0 ? sh.hist[top - j] : 0u;
-      s += hb[j];
+    find_bin_from_top<NT>(h, sh, target - above);
+    const uint32_t tb = sh.bc[0], gt = sh.bc[1], in_bin = sh.bc[2];
+    if (target - above - gt == in_bin) {
+      // every key of the boundary bin is selected: take all keys >= its lower edge
+      T = lo + (tb << shift);
+      take_all_eq = true;
+      break;
     }
-    const uint32_t incl = wave_incl_scan(s);
-    if (lane == 63) sh.wred[0][wave] = incl;
-    __syncthreads();
-    uint32_t excl = incl - s;
-    for (int v = 0; v < wave; ++v) excl += sh.wred[0][v];
-    const uint32_t need = target - above;
-    if (excl < need && need <= excl + s) {
-      uint32_t acc = excl;
-#pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        if (acc < need && need <= acc + hb[j]) {
-          sh.bc[0] = (uint32_t)(top - j);
-          sh.bc[1] = acc;
-        }
-        acc += hb[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t tb = sh.bc[0], gt = sh.bc[1];
     above += gt;
     const uint32_t nlo = lo + (tb << shift);
     const uint32_t width = (1u << shift) - 1u;
     hi = (hi - nlo < width) ? hi : nlo + width;
     lo = nlo;
+    buf ^= 1;
     if (shift == 0) {
       T = lo;
       break;
     }
   }
-  const uint32_t need_eq = target - above;
+  const uint32_t need_eq = take_all_eq ? 0xFFFFFFFFu : target - above;
 
   // per-wave counts above / equal to the threshold, then ordered emission
   uint32_t wgt = 0u, weq = 0u;
@@ -457,7 +510,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     const uint32_t eq_rank = r_eq + (uint32_t)__popcll(eqb & below);
     const bool sel = kk > T || (eq && eq_rank < need_eq);
     const uint64_t selb = __ballot(sel);
-    if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)));
+    if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
     r_eq += (uint32_t)__popcll(eqb);
     r_sel += (uint32_t)__popcll(selb);
   }
@@ -470,29 +523,53 @@ struct KeysFromArray {
   __device__ uint32_t key(int i) const { return float_key(p[i]); }
 };
 
-constexpr int kBlock = 8;
-
-// Positions of candidate blocks: candidate i is position blk[i/8]*8 + i%8.
-struct KeysFromBlocks {
-  const float* scores;
-  const int32_t* blk;
-  __device__ uint32_t key(int i) const { return float_key(scores[blk[i >> 3] * kBlock + (i & 7)]); }
+struct KeysFromLds {
+  const uint32_t* p;
+  __device__ uint32_t key(int i) const { return p[i]; }
 };
 
+constexpr int kBlock = 8;
+
+// Items of candidate groups: candidate i is item grp[i/8]*8 + i%8.
+struct KeysFromGroups {
+  const float* scores;
+  const int32_t* grp;
+  __device__ int item(int i) const { return grp[i >> 3] * kBlock + (i & 7); }
+  __device__ uint32_t key(int i) const { return float_key(scores[item(i)]); }
+};
+
+// Group selection prunes item selection exactly: take contiguous groups of
+// items (8 positions of a cache block, or 8 consecutive pool entries) ranked
+// by (group max desc, group index asc).  Every group ranked ahead of the
+// group of an item p holds a distinct item ranked ahead of p (its maximum:
+// larger, or equal and at a lower index), so an item of rank < k lies in a
+// group of rank < k.  The item top-k is therefore exact over the items of the
+// top-k groups.
+
+// Number of items covered by the first ng selected groups (the last group of
+// the n items may be partial).
+__device__ __forceinline__ int group_items(const int32_t* grp, int ng, int n_items) {
+  int nc = ng * kBlock;
+  const int last = (n_items + kBlock - 1) / kBlock - 1;
+  if (ng > 0 && grp[ng - 1] == last) nc -= last * kBlock + kBlock - n_items;
+  return nc;
+}
+
 // Full-mode selection for one sequence (grid = B):
-//  1. block top-n_blocks -> pool (ascending positions);
-//  2. block top-k -> candidate positions: every position of rank <= k lies in a
-//     block of rank <= k (each block ranked ahead of it holds a distinct
-//     position ranked ahead of it), so the position top-k is exact over the
-//     positions of the top-k blocks;
-//  3. position top-k over those candidates.
-template <int NT, int EPT_B, int EPT_P>
+//  1. block top-n_blocks -> pool (ascending positions), with the sampled
+//     prefilter (2048 of 16,384 blocks at 128K);
+//  2. block top-k -> candidate blocks, among the pool blocks when
+//     n_blocks >= k (the top-k blocks are among the top-n_blocks blocks),
+//     otherwise among all blocks;
+//  3. position top-k over the positions of those blocks (group pruning).
+template <int NT, int EPT_B, int EPT_C, int EPT_P>
 __global__ __launch_bounds__(NT) void select_full_kernel(
     const float* __restrict__ scores, int64_t sstride, const float* __restrict__ bmax,
     int64_t bstride, const int32_t* __restrict__ len, int64_t cap, int k, int n_blocks,
     int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len) {
   __shared__ SelScratch sh;
   __shared__ int32_t blk[CSA2_POOL_BLOCKS];
+  __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
   __shared__ int32_t cblk[CSA2_MAX_TOPK];
   const int b = blockIdx.x;
   int64_t L = len[b];
@@ -503,41 +580,74 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   KeysFromArray bsrc{bmax + (int64_t)b * bstride};
   KeyRegs<EPT_B> kb;
   load_keys<NT, EPT_B>(kb, bsrc, nb);
+  int ncb;
   if (n_blocks > 0) {
-    const int nsel = select_core<NT, EPT_B>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r) { blk[r] = i; });
-    int pl = nsel * kBlock;
-    if (nsel > 0 && blk[nsel - 1] == nb - 1) pl -= nb * kBlock - (int)L;
+    const int nsel = select_core<NT, EPT_B, true>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r, int j) {
+      blk[r] = i;
+      if constexpr (EPT_B > 0) blkkey[r] = kb.r[j]; else blkkey[r] = bsrc.key(i);
+    });
+    const int pl = group_items(blk, nsel, (int)L);
     int32_t* pb = pool + (int64_t)b * n_blocks * kBlock;
     for (int i = threadIdx.x; i < n_blocks * kBlock; i += NT)
       pb[i] = i < pl ? blk[i >> 3] * kBlock + (i & 7) : -1;
     if (threadIdx.x == 0) pool_len[b] = pl;
   }
-  const int ncb = select_core<NT, EPT_B>(kb, bsrc, nb, k, sh, [&](int i, int r) { cblk[r] = i; });
-  int nc = ncb * kBlock;
-  if (ncb > 0 && cblk[ncb - 1] == nb - 1) nc -= nb * kBlock - (int)L;
-  KeysFromBlocks psrc{sc, cblk};
+  if (n_blocks >= k) {
+    // top-k among the selected pool blocks (keys kept in LDS, ascending blocks)
+    const int nsel = min(n_blocks, nb);
+    KeysFromLds csrc{blkkey};
+    KeyRegs<EPT_C> kc;
+    load_keys<NT, EPT_C>(kc, csrc, nsel);
+    ncb = select_core<NT, EPT_C, false>(kc, csrc, nsel, k, sh, [&](int i, int r, int) { cblk[r] = blk[i]; });
+  } else {
+    ncb = select_core<NT, EPT_B, true>(kb, bsrc, nb, k, sh, [&](int i, int r, int) { cblk[r] = i; });
+  }
+  const int nc = group_items(cblk, ncb, (int)L);
+  KeysFromGroups psrc{sc, cblk};
   KeyRegs<EPT_P> kp;
   load_keys<NT, EPT_P>(kp, psrc, nc);
-  const int cnt = select_core<NT, EPT_P>(kp, psrc, nc, k, sh,
-                                         [&](int i, int r) { tk[r] = cblk[i >> 3] * kBlock + (i & 7); });
+  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh,
+                                               [&](int i, int r, int) { tk[r] = psrc.item(i); });
   for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
 }
 
-// Reindex selection: top-k of the pool scores (NaN = masked entry).
-template <int NT, int EPT>
+// Reindex selection: top-k of the pool scores (NaN = masked entry) through
+// the top-k groups of 8 consecutive pool entries (group maxima written by the
+// scoring kernel).  The pool positions of the candidates are loaded with
+// their keys, so emission needs no further memory round trip.
+template <int NT, int EPT_G, int EPT_P>
 __global__ __launch_bounds__(NT) void select_pool_kernel(
-    const float* __restrict__ pool_scores, const int32_t* __restrict__ pool,
-    const int32_t* __restrict__ pool_len, int pool_cap, int k, int32_t* __restrict__ topk) {
+    const float* __restrict__ pool_scores, const float* __restrict__ gmax,
+    const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_len, int pool_cap, int k,
+    int32_t* __restrict__ topk) {
   __shared__ SelScratch sh;
+  __shared__ int32_t cgrp[CSA2_MAX_TOPK];
   const int b = blockIdx.x;
   int n = pool_len[b];
   n = n < 0 ? 0 : (n > pool_cap ? pool_cap : n);
+  const int ng = (n + kBlock - 1) / kBlock;
   const int32_t* pb = pool + (int64_t)b * pool_cap;
   int32_t* tk = topk + (int64_t)b * k;
-  KeysFromArray src{pool_scores + (int64_t)b * pool_cap};
-  KeyRegs<EPT> kr;
-  load_keys<NT, EPT>(kr, src, n);
-  const int cnt = select_core<NT, EPT>(kr, src, n, k, sh, [&](int i, int r) { tk[r] = pb[i]; });
+  KeysFromArray gsrc{gmax + (int64_t)b * ((pool_cap + kBlock - 1) / kBlock)};
+  KeyRegs<EPT_G> kg;
+  load_keys<NT, EPT_G>(kg, gsrc, ng);
+  const int ncg = select_core<NT, EPT_G, false>(kg, gsrc, ng, k, sh, [&](int i, int r, int) { cgrp[r] = i; });
+  const int nc = group_items(cgrp, ncg, n);
+  KeysFromGroups psrc{pool_scores + (int64_t)b * pool_cap, cgrp};
+  KeyRegs<EPT_P> kp;
+  int32_t pos[EPT_P > 0 ? EPT_P : 1];
+  if constexpr (EPT_P > 0) {
+#pragma unroll
+    for (int j = 0; j < EPT_P; ++j) {
+      const int i = sel_index<NT, EPT_P>(nc, j);
+      const int item = i < nc ? psrc.item(i) : 0;
+      kp.r[j] = i < nc ? float_key(psrc.scores[item]) : 0u;
+      pos[j] = i < nc ? pb[item] : -1;
+    }
+  }
+  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh, [&](int i, int r, int j) {
+    if constexpr (EPT_P > 0) tk[r] = pos[j]; else tk[r] = pb[psrc.item(i)];
+  });
   for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
 }
 
@@ -595,39 +705,58 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                         H, scores, cap, bmax, nbk);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
-#define CSA2_SELFULL(NT, EB, EP) \
-  select_full_kernel<NT, EB, EP><<<B, NT, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, pool_len)
+  // keys per thread: all blocks (EB), the pool blocks (2), candidate positions (EP)
+#define CSA2_SELFULL(EB, EP) \
+  select_full_kernel<1024, EB, 2, EP><<<B, 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, pool_len)
   if (nbk <= 4 * 1024) {
-    if (kbig) CSA2_SELFULL(1024, 4, 16); else CSA2_SELFULL(1024, 4, 4);
+    if (kbig) CSA2_SELFULL(4, 16); else CSA2_SELFULL(4, 4);
   } else if (nbk <= 16 * 1024) {
-    if (kbig) CSA2_SELFULL(1024, 16, 16); else CSA2_SELFULL(1024, 16, 4);
+    if (kbig) CSA2_SELFULL(16, 16); else CSA2_SELFULL(16, 4);
   } else if (nbk <= 32 * 1024) {
-    if (kbig) CSA2_SELFULL(1024, 32, 16); else CSA2_SELFULL(1024, 32, 4);
+    if (kbig) CSA2_SELFULL(32, 16); else CSA2_SELFULL(32, 4);
   } else {
-    if (kbig) CSA2_SELFULL(1024, 0, 16); else CSA2_SELFULL(1024, 0, 4);
+    if (kbig) CSA2_SELFULL(0, 16); else CSA2_SELFULL(0, 4);
   }
 #undef CSA2_SELFULL
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-size_t index_pool_ws_bytes(int B, int pool_cap) { return align256((size_t)B * (size_t)pool_cap * 4); }
+// Workspace of the Reindex call: pool scores (unless the caller supplies the
+// buffer), then the maxima of groups of 8 pool entries.
+struct IndexPoolWs {
+  size_t scores_off, gmax_off, total;
+};
+
+static IndexPoolWs index_pool_ws_layout(int B, int pool_cap) {
+  IndexPoolWs l;
+  l.scores_off = 0;
+  l.gmax_off = align256((size_t)B * (size_t)pool_cap * 4);
+  l.total = l.gmax_off + align256((size_t)B * (size_t)((pool_cap + kBlock - 1) / kBlock) * 4);
+  return l;
+}
+
+size_t index_pool_ws_bytes(int B, int pool_cap) { return index_pool_ws_layout(B, pool_cap).total; }
 
 int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
                       const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
                       int pool_cap, const uint16_t* q, const float* w, int H, int k,
                       int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st) {
   if (B == 0) return 0;
-  float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>(ws);
+  const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
+  float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
+  float* gmax = reinterpret_cast<float*>((char*)ws + l.gmax_off);
+  const int64_t ngs = (pool_cap + kBlock - 1) / kBlock;
   const int MT = (H + 15) / 16;
   dim3 grid(score_wgs(pool_cap, B), (unsigned)B);
   if (pool_cap > 0)
     launch_score<true>(MT, grid, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
-                       w, H, ps, pool_cap, nullptr, 0);
+                       w, H, ps, pool_cap, gmax, ngs);
   if (hipGetLastError() != hipSuccess) return -1;
-  if (pool_cap <= 4 * 1024)
-    select_pool_kernel<1024, 4><<<B, 1024, 0, st>>>(ps, pool, pool_len, pool_cap, k, topk);
+  // keys per thread: groups (<= 2048 -> 2), candidate positions (8 per selected group)
+  if (k <= 512)
+    select_pool_kernel<1024, 2, 4><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk);
   else
-    select_pool_kernel<1024, 16><<<B, 1024, 0, st>>>(ps, pool, pool_len, pool_cap, k, topk);
+    select_pool_kernel<1024, 2, 16><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -174,6 +174,12 @@ int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
  *              the lower position.
  *   pool_scores_opt : optional out fp32 [B][pool_cap] (score of pool[b][i]).
  *   H, k as for csa2_index_full; pool_cap <= 16384.
+ *   ws, ws_bytes : workspace of at least csa2_index_pool_workspace(...) bytes
+ *              (pool scores unless pool_scores_opt is given, and the maxima
+ *              of groups of 8 consecutive pool entries); required in every
+ *              call with pool_cap > 0; no initial contents needed.
+ * Selection goes through the top-k groups of 8 consecutive pool entries
+ * (group score = max); the position top-k is exact over their entries.
  */
 size_t csa2_index_pool_workspace(int32_t B, int32_t pool_cap, int32_t k);
 int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,

@@ -112,6 +112,30 @@ def test_attention_long_selection(k, W):
     say(f"  worst relative error {worst:.2e}")
 
 
+def test_attention_workspace_reuse_deterministic():
+    """Repeated calls on one workspace give identical bits and match the oracle."""
+    fmt = 0
+    B, cap, k, W, H = 3, 2000, 512, 128, 64
+    c, s, rc, rs = _make_cache(B, cap, fmt, 21)
+    g = np.random.default_rng(21)
+    topk = torch.from_numpy(np.stack([g.choice(cap, k, replace=False) for _ in range(B)]).astype(np.int32)).to(DEV)
+    lens = torch.full((B,), cap, dtype=torch.int32, device=DEV)
+    swl = torch.full((B,), W, dtype=torch.int32, device=DEV)
+    q = syn.as_bf16_bits(torch.randn(B, H, 512, generator=torch.Generator().manual_seed(21))).to(DEV)
+    nbytes = K.lib().csa2_attn_workspace(B, H, k, W)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)  # no initial contents needed
+    outs = []
+    for _ in range(3):
+        o = K.sparse_attn_decode(q, c, s, lens, topk, fmt, swa_codes=c, swa_scales=s, swa_len=swl,
+                                 swa_stride=cap, swa_cap=W, swa_row0=cap - W, _ws=ws)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    ref = np.stack([oracle.attention(q[b].cpu().numpy(), rc[b], rs[b], cap, fmt, topk[b].cpu().numpy(),
+                                     rc[b, cap - W:], rs[b, cap - W:], W, 1 / np.sqrt(512))[0] for b in range(B)])
+    attn_close(outs[0].cpu(), ref)
+
+
 def test_attention_window_only_separate_buffer():
     fmt = 1
     B, cap, W = 2, 64, 128

@@ -120,10 +120,13 @@ def test_duplicate_rows_tie_exactly_and_prefer_lower_index():
 def test_determinism_two_runs_bitwise():
     wl = syn.small("det", 9, B=2, cap=20000, H_idx=64, k=512, n_blocks=2048)
     cache = build_gpu_cache(wl, 0)
-    a = _run_full(wl, cache, [20000, 15000])
-    b = _run_full(wl, cache, [20000, 15000])
-    for x, y in zip(a[2:], b[2:]):
-        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    lens = [20000, 15000]
+    a = _run_full(wl, cache, lens)
+    b = _run_full(wl, cache, lens)
+    for x, y in zip(a[2:5], b[2:5]):   # top-k, pool, pool_len
+        assert np.array_equal(x, y)
+    for i, n in enumerate(lens):       # scores: only the visible positions are defined
+        assert np.array_equal(a[5][i, :n].view(np.uint32), b[5][i, :n].view(np.uint32))
 
 
 def test_index_pool_matches_oracle_and_reproduces_full_topk():
