@@ -35,20 +35,21 @@
 
 namespace csa2 {
 
-constexpr int kChunk = 128;            // row slots per workgroup (8 waves x 16)
-constexpr int kAttnWaves = 8;
-constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kChunk = 128;            // row slots per workgroup at most 8 waves (sizes the workspace)
 constexpr int kHLd = 264;              // R half-row stride in bf16 (256 + pad)
-constexpr int kPLd = 136;              // P row stride in bf16 (128 + pad)
 constexpr int kQLd = 520;              // query row stride in bf16 (512 + pad)
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
+// WAVES waves take 16 rows each: a chunk of 16*WAVES row slots.
+template <int WAVES>
 struct AttnSmem {
-  uint16_t R[kChunk * kHLd];  // also holds the 16 x kQLd query tile before the first barrier
+  static constexpr int kRows = 16 * WAVES;
+  static constexpr int kPLd = kRows + 8;  // P row stride in bf16
+  uint16_t R[kRows * kHLd];  // also holds the 16 x kQLd query tile before the first barrier
   uint16_t P[16 * kPLd];
-  float red_m[kAttnWaves][16];
-  float red_l[kAttnWaves][16];
+  float red_m[WAVES][16];
+  float red_l[WAVES][16];
 };
 
 // Eight E2M1 values of one code dword -> bf16x8 (exact).
@@ -139,15 +140,21 @@ __device__ __forceinline__ bf16x8 row_step(const RowFetch& f, int ks) {
   return dequant8<FMT>(cwd, sbyte);
 }
 
-// O(16 heads x 32 dims of half h, wave w) += P . R_half  (4 K steps of 32 rows)
-__device__ __forceinline__ void pv_half(const AttnSmem& sm, int w, int g, int n, floatx4 (&O)[2]) {
+// O(16 heads x the wave's 16-dim tiles of one R half) += P . R_half.  Wave w
+// takes tiles w, w + WAVES (16 tiles per half); K steps of 32 rows.
+template <int WAVES>
+__device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g, int n, floatx4 (&O)[2]) {
+  constexpr int NK = AttnSmem<WAVES>::kRows / 32;
+  constexpr int LD = AttnSmem<WAVES>::kPLd;
   const int ta = n & 3, tj = n >> 2;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sm.P[n * kPLd + 32 * ks + 8 * g]);
+  for (int ks = 0; ks < NK; ++ks) {
+    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sm.P[n * LD + 32 * ks + 8 * g]);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int col = 32 * w + 16 * nt + 4 * ta;
+      const int tile = w + WAVES * nt;
+      if (tile >= 16) break;  // wave-uniform
+      const int col = 16 * tile + 4 * ta;
       const int r0 = 32 * ks + 8 * g + tj;
       const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kHLd + col]));
@@ -161,12 +168,12 @@ __device__ __forceinline__ void pv_half(const AttnSmem& sm, int w, int g, int n,
   }
 }
 
-// One (sequence, 16 heads, 128-slot chunk).  Grid: XCD-aware linear order in
-// which the head groups of one (sequence, chunk) share an XCD (and its L2
-// copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512] (fp32, relative
-// to the chunk max) and ml[(b*H+h)*S + s] = (max, sum).
-template <int FMT>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
+// One (sequence, 16 heads, chunk of 16*WAVES row slots).  Grid: XCD-aware
+// linear order in which the head groups of one (sequence, chunk) share an XCD
+// (and its L2 copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512]
+// (fp32, relative to the chunk max) and ml[(b*H+h)*S + s] = (max, sum).
+template <int FMT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_kernel(
     const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
@@ -174,7 +181,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
     const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
     float* __restrict__ part, float2* __restrict__ ml) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  using Smem = AttnSmem<WAVES>;
+  constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
+  static_assert(16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int HG = H >> 4;
   const int id = blockIdx.x;
   const int xcd = id & 7, j = id >> 3;
@@ -190,11 +200,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
 
   // ---- loads: index entry and the 16 queries (to LDS, 32 B per thread), then the row
-  const int slot = kChunk * sidx + 16 * w + n;
+  const int slot = kRows * sidx + 16 * w + n;
   int32_t pidx = -1;
   if (slot < k) pidx = topk[(int64_t)b * k + slot];
   const uint4* qg = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
-  const uint4 qv0 = qg[tid], qv1 = qg[tid + kAttnThreads];
+  constexpr int kQv = (1024 + kThreads - 1) / kThreads;  // 16 heads x 64 pieces of 16 B
+  uint4 qv[kQv];
+#pragma unroll
+  for (int j2 = 0; j2 < kQv; ++j2) {
+    const int e = tid + kThreads * j2;
+    qv[j2] = e < 1024 ? qg[e] : make_uint4(0u, 0u, 0u, 0u);
+  }
   RowFetch row;
   {
     const RowSrc src = locate_row(slot, pidx, nslots, b, k, L, SL, cap, swa_stride, main_codes,
@@ -203,8 +219,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
   }
   // the query tile borrows the R buffer, which is not written before the max barrier
   uint16_t* Q = sm.R;
-  *reinterpret_cast<uint4*>(&Q[(tid >> 6) * kQLd + 8 * (tid & 63)]) = qv0;
-  *reinterpret_cast<uint4*>(&Q[((tid >> 6) + 8) * kQLd + 8 * (tid & 63)]) = qv1;
+#pragma unroll
+  for (int j2 = 0; j2 < kQv; ++j2) {
+    const int e = tid + kThreads * j2;
+    if (e < 1024) *reinterpret_cast<uint4*>(&Q[(e >> 6) * kQLd + 8 * (e & 63)]) = qv[j2];
+  }
   __syncthreads();
 
   // ---- logits of the wave's 16 rows (every row dequantised once, kept for P.R)
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
   __syncthreads();  // also: every wave is done reading the query tile
   float M = sm.red_m[0][n];
 #pragma unroll
-  for (int v = 1; v < kAttnWaves; ++v) M = fmaxf(M, sm.red_m[v][n]);
+  for (int v = 1; v < WAVES; ++v) M = fmaxf(M, sm.red_m[v][n]);
   float lw = 0.f;
   uint32_t pb[4];
 #pragma unroll
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
   if (w == 0 && g == 0) {
     float l = 0.f;
 #pragma unroll
-    for (int v = 0; v < kAttnWaves; ++v) l += sm.red_l[v][n];
+    for (int v = 0; v < WAVES; ++v) l += sm.red_l[v][n];
     ml[((int64_t)b * H + 16 * hg + n) * S + sidx] = make_float2(M, l);
   }
 #pragma unroll
@@ -266,18 +285,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
       __syncthreads();
     }
     floatx4 O[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    pv_half(sm, w, g, n, O);
-    // lane (g, n): heads 4g+i, dims 256h + 32w + 16nt + n
+    pv_half<WAVES>(sm, w, g, n, O);
+    // lane (g, n): heads 4g+i, dims 256h + 16*tile + n, tile = w + WAVES*nt
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 32 * w + n;
+      float* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 16 * w + n;
       dst[0] = O[0][i];
-      dst[16] = O[1][i];
+      if (w + WAVES < 16) dst[16 * WAVES] = O[1][i];
     }
   }
 }
-
-static_assert(16 * kQLd <= kChunk * kHLd, "query tile must fit in the R buffer");
 
 // Merge the S chunk partials of each (sequence, head): one wave per head,
 // 8 dims per lane; chunk loads are issued four at a time.
@@ -347,27 +364,39 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const int32_t* swa_len, float sm_scale, uint16_t* out, float* lse_opt,
                        void* ws, hipStream_t st) {
   if (B == 0) return 0;
-  const int S = attn_splits(k, swa_cap);
-  const size_t n = (size_t)B * H * S;
+  const int nslots = k + swa_cap;
+  // Chunk shape: 8 waves (128 rows, two workgroups per CU) or 10 waves (160
+  // rows, one per CU); take the smaller row load of the busiest CU.
+  const int64_t HG = H / 16;
+  const int64_t wg8 = B * HG * ((nslots + 127) / 128), wg10 = B * HG * ((nslots + 159) / 160);
+  const bool ten = ((wg10 + 255) / 256) * 160 <= ((wg8 + 255) / 256) * 128;
+  const int S = ten ? (nslots + 159) / 160 : (nslots + 127) / 128;
   float* part = reinterpret_cast<float*>(ws);
+  const size_t n_ws = (size_t)B * H * attn_splits(k, swa_cap);  // workspace sized for 128-row chunks
   float2* ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
-                                         ((n * 512 * sizeof(float) + 255) & ~(size_t)255));
-  const size_t smem = sizeof(AttnSmem);
+                                         ((n_ws * 512 * sizeof(float) + 255) & ~(size_t)255));
   const int pairs8 = (B * S + 7) / 8;
-  const unsigned grid = (unsigned)(pairs8 * 8 * (H / 16));
-  auto go = [&](auto kern) -> bool {
+  const unsigned grid = (unsigned)(pairs8 * 8 * HG);
+  auto go = [&](auto kern, int waves, size_t smem) -> bool {
     static bool attr_done = false;  // one per instantiation
     if (!attr_done) {
       if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
         return false;
       attr_done = true;
     }
-    kern<<<grid, kAttnThreads, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
-                                           swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
-                                           part, ml);
+    kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
+                                         swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
+                                         part, ml);
     return true;
   };
-  if (!(main_fmt == 0 ? go(attn_split_kernel<0>) : go(attn_split_kernel<1>))) return -1;
+  bool ok;
+  if (ten)
+    ok = main_fmt == 0 ? go(attn_split_kernel<0, 10>, 10, sizeof(AttnSmem<10>))
+                       : go(attn_split_kernel<1, 10>, 10, sizeof(AttnSmem<10>));
+  else
+    ok = main_fmt == 0 ? go(attn_split_kernel<0, 8>, 8, sizeof(AttnSmem<8>))
+                       : go(attn_split_kernel<1, 8>, 8, sizeof(AttnSmem<8>));
+  if (!ok) return -1;
   const int BH = B * H;
   attn_combine_kernel<<<(unsigned)((BH + 3) / 4), 256, 0, st>>>(part, ml, BH, S, out, lse_opt);
   return hipGetLastError() == hipSuccess ? 0 : -1;

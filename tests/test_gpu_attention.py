@@ -136,6 +136,33 @@ def test_attention_workspace_reuse_deterministic():
     attn_close(outs[0].cpu(), ref)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_attention_decode_batch_shape(fmt):
+    """16 sequences x 64 heads x (512 + 128) rows: the one-workgroup-per-CU chunking."""
+    say(f"attention at the decode-step shape fmt={fmt}")
+    B, cap, k, W, H = 16, 1500, 512, 128, 64
+    c, s, rc, rs = _make_cache(B, cap, fmt, 31 + fmt)
+    g = np.random.default_rng(31)
+    topk = np.stack([g.choice(cap, k, replace=False) for _ in range(B)]).astype(np.int32)
+    topk[3, :40] = -1
+    lens = np.full(B, cap, np.int32)
+    swa_len = np.full(B, W, np.int32)
+    swa_len[5] = 7
+    q = syn.as_bf16_bits(torch.randn(B, H, 512, generator=torch.Generator().manual_seed(31)) * 0.6)
+    out, lse = K.sparse_attn_decode(q.to(DEV), c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV),
+                                    fmt, swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV),
+                                    swa_stride=cap, swa_cap=W, swa_row0=cap - W, return_lse=True)
+    torch.cuda.synchronize()
+    ref = np.zeros((B, H, 512), np.float32)
+    rl = np.zeros((B, H), np.float32)
+    for b in range(B):
+        ref[b], rl[b] = oracle.attention(q[b].numpy(), rc[b], rs[b], lens[b], fmt, topk[b],
+                                         rc[b, cap - W:], rs[b, cap - W:], swa_len[b], 1 / np.sqrt(512))
+    worst = attn_close(out.cpu(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=1e-4, rtol=0)
+    say(f"  worst relative error {worst:.2e}")
+
+
 def test_attention_window_only_separate_buffer():
     fmt = 1
     B, cap, W = 2, 64, 128
