@@ -105,11 +105,11 @@ int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, u
 }
 
 // ------------------------------------------------------------- cache write
-// Grid (entry tiles of 16, 4 column tiles of 32).  Every workgroup pools and
-// normalises its 16 entries (one wave per entry at a time); the column-tile-0
-// workgroup writes the main-KV FP4.  Each workgroup then projects onto its 32
+// Grid (entry tiles of 4, 4 column tiles of 32).  Every workgroup pools and
+// normalises its 4 entries (one wave per entry); the column-tile-0 workgroup
+// writes the main-KV FP4.  Each workgroup then projects onto its 32
 // indexer-K columns -- exactly one E8M0 group -- and quantises them.
-constexpr int kWriteEntries = 16;
+constexpr int kWriteEntries = 4;   // entries per workgroup (one per wave)
 constexpr int kWriteColTiles = 4;
 
 template <int FMT>
@@ -118,13 +118,28 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     int m, const float* __restrict__ gamma, float eps, const float* __restrict__ w_idx,
     uint8_t* __restrict__ main_codes, uint8_t* __restrict__ main_scales,
     uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales) {
-  __shared__ float yT[512][kWriteEntries];  // latent after RMSNorm, channel-major
-  __shared__ float kb[kWriteEntries][33];   // projected keys of this column tile
+  __shared__ __align__(16) float yT[512][kWriteEntries];  // latent after RMSNorm, channel-major
+  __shared__ float part[8][kWriteEntries][33];  // projection partial sums per channel slice
+  __shared__ float kb[kWriteEntries][33];       // projected keys of this column tile
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ct = blockIdx.y;
   const int64_t e0 = (int64_t)blockIdx.x * kWriteEntries;
+  constexpr int kEpw = kWriteEntries / 4;  // entries per wave
+  static_assert(kWriteEntries % 4 == 0, "whole entries per wave");
 
-  for (int ei = wave; ei < kWriteEntries; ei += 4) {
+  // ratio 1: every latent load of the wave is issued before any arithmetic
+  uint4 xpre[kEpw];
+  if (m == 1) {
+#pragma unroll
+    for (int j = 0; j < kEpw; ++j) {
+      const int64_t e = e0 + wave + 4 * j;
+      xpre[j] = e < n_entries ? *reinterpret_cast<const uint4*>(latent + e * 512 + 8 * lane)
+                              : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kEpw; ++j) {
+    const int ei = wave + 4 * j;
     const int64_t e = e0 + ei;
     if (e >= n_entries) {
 #pragma unroll
@@ -133,8 +148,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     }
     float pooled[8];
     if (m == 1) {
-      uint4 xv = *reinterpret_cast<const uint4*>(latent + e * 512 + 8 * lane);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t xw[4] = {xpre[j].x, xpre[j].y, xpre[j].z, xpre[j].w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) pooled[c] = bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
     } else {
@@ -187,28 +201,48 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = y[c];
   }
-  __syncthreads();
 
-  // projection k[e][d] = sum_c y[e][c] * W[c][d] for d in this column tile;
-  // thread: one column, two entries
+  // projection k[e][d] = sum_c y[e][c] * W[c][d] for the 32 columns d of this
+  // tile: thread = (channel slice cs of 64 channels, column); its 64 weights
+  // are loaded at once (before the barrier), then 8 slice sums per entry are
+  // reduced through LDS.
+  const int cs = threadIdx.x >> 5, col = threadIdx.x & 31;
+  const int d = 32 * ct + col;
+  float wv[64];
+#pragma unroll
+  for (int c = 0; c < 64; ++c) wv[c] = w_idx[(64 * cs + c) * 128 + d];
+  __syncthreads();
   {
-    const int d = 32 * ct + (threadIdx.x & 31);
-    const int e2 = 2 * (threadIdx.x >> 5);
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll 16
-    for (int c = 0; c < 512; ++c) {
-      const float wv = w_idx[c * 128 + d];
-      const float2 yv = *reinterpret_cast<const float2*>(&yT[c][e2]);
-      a0 += yv.x * wv;
-      a1 += yv.y * wv;
+    float acc[kWriteEntries];
+#pragma unroll
+    for (int e2 = 0; e2 < kWriteEntries; ++e2) acc[e2] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      const float4* yr = reinterpret_cast<const float4*>(&yT[64 * cs + c][0]);
+#pragma unroll
+      for (int q4 = 0; q4 < kWriteEntries / 4; ++q4) {
+        const float4 yv = yr[q4];
+        acc[4 * q4 + 0] += yv.x * wv[c];
+        acc[4 * q4 + 1] += yv.y * wv[c];
+        acc[4 * q4 + 2] += yv.z * wv[c];
+        acc[4 * q4 + 3] += yv.w * wv[c];
+      }
     }
-    kb[e2][threadIdx.x & 31] = a0;
-    kb[e2 + 1][threadIdx.x & 31] = a1;
+#pragma unroll
+    for (int e2 = 0; e2 < kWriteEntries; ++e2) part[cs][e2][col] = acc[e2];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < kWriteEntries * 32; o += 256) {
+    const int e2 = o >> 5, c2 = o & 31;
+    float v = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) v += part[s8][e2][c2];
+    kb[e2][c2] = v;
   }
   __syncthreads();
 
   // indexer-K FP4 of this column tile: thread = (entry, 8 consecutive dims)
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < 4 * kWriteEntries) {
     const int ei = threadIdx.x >> 2, ch = threadIdx.x & 3;
     const int64_t e = e0 + ei;
     float v[8];
