@@ -88,13 +88,15 @@ _WS = {}
 
 
 def workspace(nbytes: int, dev: torch.device, kind: str = "index") -> torch.Tensor:
-    """A cached uint8 device buffer of at least nbytes, one per (device,
-    stream, kind).  Calls on one stream are ordered, so they may share it;
-    the kernels need no particular initial contents."""
+    """A cached, zero-initialised uint8 device buffer of at least nbytes, one
+    per (device, stream, kind).  Calls on one stream are ordered, so they may
+    share it.  The attention workspace starts with completion counters that
+    must be zero and that every call leaves at zero, so it is never shared
+    with the indexer's scratch."""
     key = (dev, torch.cuda.current_stream(dev).cuda_stream, kind)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _WS[key] = buf
     return buf
 

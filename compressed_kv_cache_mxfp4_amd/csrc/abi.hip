@@ -134,6 +134,7 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
   if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
   if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
   if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
   if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
   if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;

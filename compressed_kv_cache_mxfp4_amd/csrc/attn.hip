@@ -30,6 +30,7 @@
 //    with the gfx950 transpose read (ds_read_b64_tr_b16): within a 16-lane
 //    group, source lane a+4j points at R[r0+j][d0+4a] and lane n receives
 //    R[r0..r0+3][d0+n], i.e. four K slots of the MFMA B operand.
+#include "csa2.h"
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -38,6 +39,11 @@ namespace csa2 {
 constexpr int kChunk = 128;            // row slots per workgroup at most 8 waves (sizes the workspace)
 constexpr int kHLd = 264;              // R half-row stride in bf16 (256 + pad)
 constexpr int kQLd = 520;              // query row stride in bf16 (512 + pad)
+// s_getreg operand for HW_REG_XCC_ID (register 20, bits 3:0): the XCD a wave runs on
+constexpr int kHwRegXccId = (3 << 11) | 20;
+// completion counters: one per (sequence, head group), in a fixed region at
+// the start of the workspace so that no call shape ever overlays them
+constexpr int kMaxAttnGroups = 65536;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -50,6 +56,7 @@ struct AttnSmem {
   uint16_t P[16 * kPLd];
   float red_m[WAVES][16];
   float red_l[WAVES][16];
+  int last;  // this workgroup merges its (sequence, head group)
 };
 
 // Eight E2M1 values of one code dword -> bf16x8 (exact).
@@ -179,19 +186,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
-    float* __restrict__ part, float2* __restrict__ ml) {
+    float* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
   static_assert(16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int HG = H >> 4;
+  // group gi = (sequence, head group); its S chunks get ids congruent mod 8,
+  // i.e. one XCD, whose L2 then holds every partial the merge reads
   const int id = blockIdx.x;
-  const int xcd = id & 7, j = id >> 3;
-  const int hg = j % HG;
-  const int t = (j / HG) * 8 + xcd;
-  if (t >= B * S) return;  // workgroup-uniform
-  const int b = t / S, sidx = t - b * S;
+  const int xcd = id & 7, r8 = id >> 3;
+  const int gi = (r8 / S) * 8 + xcd, sidx = r8 % S;
+  if (gi >= B * HG) return;  // workgroup-uniform
+  const int b = gi / HG, hg = gi - b * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int nslots = k + swa_cap;
   int64_t L = len ? len[b] : 0;
@@ -270,11 +279,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   __syncthreads();
 
   float* prow = part + ((int64_t)b * H + 16 * hg) * S * 512;
+  const uint32_t my_xcc = __builtin_amdgcn_s_getreg(kHwRegXccId);
   if (w == 0 && g == 0) {
     float l = 0.f;
 #pragma unroll
     for (int v = 0; v < WAVES; ++v) l += sm.red_l[v][n];
-    ml[((int64_t)b * H + 16 * hg + n) * S + sidx] = make_float2(M, l);
+    ml[((int64_t)b * H + 16 * hg + n) * S + sidx] = make_float4(M, l, __uint_as_float(my_xcc), 0.f);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -294,68 +304,106 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
       if (w + WAVES < 16) dst[16 * WAVES] = O[1][i];
     }
   }
-}
 
-// Merge the S chunk partials of each (sequence, head): one wave per head,
-// 8 dims per lane; chunk loads are issued four at a time.
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
-                                                           const float2* __restrict__ ml, int BH,
-                                                           int S, uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= BH) return;
-  const int lane = threadIdx.x & 63;
-  const float2* m = ml + (int64_t)bh * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, m[s].x);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float Lsum = 0.f;
-  if (M != -INFINITY) {
-    const float4* src = reinterpret_cast<const float4*>(part + (int64_t)bh * S * 512) + 2 * lane;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      float wgt[4];
-      float4 v[4][2];
+  // ---- the last chunk of the group to finish merges all S partials.  The
+  // stores above are complete in this XCD's L2 before the counter moves, and
+  // every chunk of the group ran on this XCD (checked below).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt + gi, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = old == (uint32_t)(S - 1);
+  }
+  __syncthreads();
+  if (!sm.last) return;  // workgroup-uniform
+  if (tid == 0) cnt[gi] = 0u;  // ready for the next call
+  if (tid < 16 * 32) {
+    // thread: head hh, dims 16*d16 .. +15.  Splits are merged four at a time
+    // with a running maximum (one round of loads per four splits).
+    const int hh = tid >> 5, d16 = tid & 31;
+    const int64_t bh = (int64_t)b * H + 16 * hg + hh;
+    const float4* mlp = ml + bh * S;
+    const float4* src = reinterpret_cast<const float4*>(part + bh * S * 512 + 16 * d16);
+    float acc[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        wgt[j] = 0.f;
-        v[j][0] = v[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (s < S) {
-          const float2 e = m[s];
-          if (e.x != -INFINITY) {
-            wgt[j] = __expf(e.x - M);
-            Lsum += wgt[j] * e.y;
-            v[j][0] = src[s * 128];
-            v[j][1] = src[s * 128 + 1];
-          }
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+    float Mx = -INFINITY, Lsum = 0.f;
+    bool same_xcd = true;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float4 e[4];
+      float4 v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u < S) {
+          e[u] = mlp[s0 + u];
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) v[u][c4] = src[(s0 + u) * 128 + c4];
+        } else {
+          e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) v[u][c4] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
+      float mg = Mx;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[0] += wgt[j] * v[j][0].x; acc[1] += wgt[j] * v[j][0].y;
-        acc[2] += wgt[j] * v[j][0].z; acc[3] += wgt[j] * v[j][0].w;
-        acc[4] += wgt[j] * v[j][1].x; acc[5] += wgt[j] * v[j][1].y;
-        acc[6] += wgt[j] * v[j][1].z; acc[7] += wgt[j] * v[j][1].w;
+      for (int u = 0; u < 4; ++u) {
+        mg = fmaxf(mg, e[u].x);
+        same_xcd &= __float_as_uint(e[u].z) == my_xcc;
+      }
+      if (mg == -INFINITY) continue;  // nothing visible so far
+      const float rs = Mx == -INFINITY ? 0.0f : __expf(Mx - mg);
+      Lsum *= rs;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] *= rs;
+      Mx = mg;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // a chunk with no visible row has max -inf and a zero partial
+        const float wgt = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx);
+        Lsum += wgt * e[u].y;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          acc[4 * c4 + 0] += wgt * v[u][c4].x;
+          acc[4 * c4 + 1] += wgt * v[u][c4].y;
+          acc[4 * c4 + 2] += wgt * v[u][c4].z;
+          acc[4 * c4 + 3] += wgt * v[u][c4].w;
+        }
       }
     }
+    float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
+    if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
+    uint32_t o8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      o8[j] = f32_to_bf16_bits(acc[2 * j] * inv) | (f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+    uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
+    op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+    op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+    if (lse && d16 == 0) lse[bh] = !same_xcd ? inv : (Lsum > 0.f ? Mx + logf(Lsum) : -INFINITY);
   }
-  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
-  uint4 o;
-  o.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
-  o.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
-  o.z = f32_to_bf16_bits(acc[4] * inv) | (f32_to_bf16_bits(acc[5] * inv) << 16);
-  o.w = f32_to_bf16_bits(acc[6] * inv) | (f32_to_bf16_bits(acc[7] * inv) << 16);
-  *reinterpret_cast<uint4*>(out + (int64_t)bh * 512 + 8 * lane) = o;
-  if (lse && lane == 0) lse[bh] = Lsum > 0.f ? M + logf(Lsum) : -INFINITY;
 }
 
 static int attn_splits(int k, int swa_cap) { return (k + swa_cap + kChunk - 1) / kChunk; }
 
-size_t attn_ws_bytes(int B, int H, int k, int swa_cap) {
+struct AttnWs {
+  size_t cnt_off, part_off, ml_off, total;
+};
+
+// [counters: kMaxAttnGroups x u32][partials: B*H*S x 512 fp32][(max, sum, xcd): B*H*S x 16 B],
+// sized for 128-row chunks (the larger S).
+static AttnWs attn_ws_layout(int B, int H, int k, int swa_cap) {
   const size_t n = (size_t)B * H * attn_splits(k, swa_cap);
-  const size_t part = (n * 512 * sizeof(float) + 255) & ~(size_t)255;
-  return part + ((n * sizeof(float2) + 255) & ~(size_t)255) + 256;
+  AttnWs l;
+  l.cnt_off = 0;
+  l.part_off = (size_t)kMaxAttnGroups * sizeof(uint32_t);
+  l.ml_off = l.part_off + ((n * 512 * sizeof(float) + 255) & ~(size_t)255);
+  l.total = l.ml_off + ((n * sizeof(float4) + 255) & ~(size_t)255);
+  return l;
 }
+
+size_t attn_ws_bytes(int B, int H, int k, int swa_cap) { return attn_ws_layout(B, H, k, swa_cap).total; }
+
+size_t attn_ws_counter_bytes() { return (size_t)kMaxAttnGroups * sizeof(uint32_t); }
 
 int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,
@@ -365,18 +413,20 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        void* ws, hipStream_t st) {
   if (B == 0) return 0;
   const int nslots = k + swa_cap;
+  const int64_t HG = H / 16;
+  const int64_t groups = (int64_t)B * HG;
+  if (groups > kMaxAttnGroups) return -1;
   // Chunk shape: 8 waves (128 rows, two workgroups per CU) or 10 waves (160
   // rows, one per CU); take the smaller row load of the busiest CU.
-  const int64_t HG = H / 16;
-  const int64_t wg8 = B * HG * ((nslots + 127) / 128), wg10 = B * HG * ((nslots + 159) / 160);
+  const int64_t wg8 = groups * ((nslots + 127) / 128), wg10 = groups * ((nslots + 159) / 160);
   const bool ten = ((wg10 + 255) / 256) * 160 <= ((wg8 + 255) / 256) * 128;
   const int S = ten ? (nslots + 159) / 160 : (nslots + 127) / 128;
-  float* part = reinterpret_cast<float*>(ws);
-  const size_t n_ws = (size_t)B * H * attn_splits(k, swa_cap);  // workspace sized for 128-row chunks
-  float2* ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
-                                         ((n_ws * 512 * sizeof(float) + 255) & ~(size_t)255));
-  const int pairs8 = (B * S + 7) / 8;
-  const unsigned grid = (unsigned)(pairs8 * 8 * HG);
+  const AttnWs l = attn_ws_layout(B, H, k, swa_cap);
+  char* wsb = reinterpret_cast<char*>(ws);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + l.cnt_off);
+  float* part = reinterpret_cast<float*>(wsb + l.part_off);
+  float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
+  const unsigned grid = (unsigned)(((groups + 7) / 8) * S * 8);
   auto go = [&](auto kern, int waves, size_t smem) -> bool {
     static bool attr_done = false;  // one per instantiation
     if (!attr_done) {
@@ -386,7 +436,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     }
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                          swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
-                                         part, ml);
+                                         part, ml, cnt, out, lse_opt);
     return true;
   };
   bool ok;
@@ -397,8 +447,6 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     ok = main_fmt == 0 ? go(attn_split_kernel<0, 8>, 8, sizeof(AttnSmem<8>))
                        : go(attn_split_kernel<1, 8>, 8, sizeof(AttnSmem<8>));
   if (!ok) return -1;
-  const int BH = B * H;
-  attn_combine_kernel<<<(unsigned)((BH + 3) / 4), 256, 0, st>>>(part, ml, BH, S, out, lse_opt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -56,7 +56,8 @@ class DecodeStep:
                                    dtype=torch.uint8, device=dev)
         self.ws_pool = torch.empty(max(L.csa2_index_pool_workspace(B, max(n_blocks * 8, 1), k), 256),
                                    dtype=torch.uint8, device=dev)
-        self.ws_attn = torch.empty(max(L.csa2_attn_workspace(B, H_attn, k, swa_cap), 256),
+        # zero-filled once: the attention calls keep their completion counters at zero
+        self.ws_attn = torch.zeros(max(L.csa2_attn_workspace(B, H_attn, k, swa_cap), 256),
                                    dtype=torch.uint8, device=dev)
 
     def schedule(self) -> List[Tuple[str, int]]:

@@ -78,6 +78,8 @@ extern "C" {
 #define CSA2_MAX_TOPK 2048
 #define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
 #define CSA2_MAX_CACHE_ROWS 1048576 /* entries per sequence accepted by index_full */
+#define CSA2_ATTN_MAX_GROUPS 65536  /* B * H / 16 accepted by csa2_sparse_attn_decode  */
+#define CSA2_ATTN_WS_COUNTER_BYTES (CSA2_ATTN_MAX_GROUPS * 4) /* leading zeroed region */
 
 typedef enum {
   CSA2_OK = 0,
@@ -206,13 +208,22 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
  *   out      : out bf16 bits [B][H][512].
  *   lse_opt  : optional out fp32 [B][H], natural-log sum of exp(sm_scale*logits);
  *              -inf (and a zero output row) when a sequence attends no row.
- *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes
- *              (B*H*ceil((k+swa_cap)/128) partial outputs of 512 fp32 plus a
- *              (max, sum) pair each); no initial contents needed, contents
- *              undefined afterwards.
- * Two kernels on `stream`: per 128-row chunk partial attention, then an exact
- * merge of the chunks of each (sequence, head).  The result is deterministic
- * (no atomics; fixed reduction order).
+ *   ws, ws_bytes : workspace of at least csa2_attn_workspace(...) bytes.
+ *              Its first CSA2_ATTN_WS_COUNTER_BYTES bytes hold completion
+ *              counters that must be zero before the first call (zero-fill
+ *              the workspace once after allocating it); every call leaves
+ *              them zero.  The rest (partial outputs, maxima, sums) needs no
+ *              initial contents.  Calls sharing a workspace must be ordered
+ *              on one stream; concurrent calls on one workspace race.
+ *              B*H/16 must not exceed CSA2_ATTN_MAX_GROUPS.
+ * One kernel on `stream`: a workgroup attends one chunk of 128 or 160 row
+ * slots for 16 heads and leaves its partial (unnormalised output, max, sum)
+ * in the workspace; the last chunk of each (sequence, head group) to finish
+ * merges all of them exactly.  The chunks of one group are placed on one XCD
+ * (workgroup ids congruent mod 8), so the partials meet in that XCD's L2; a
+ * merge that finds a chunk from another XCD writes NaN rather than a wrong
+ * value.  The result is deterministic (fixed merge order; the counters only
+ * decide which workgroup merges).
  */
 size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap);
 int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_codes,
