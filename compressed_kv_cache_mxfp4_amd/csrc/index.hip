@@ -34,7 +34,8 @@ namespace csa2 {
 // ======================================================================
 constexpr int kScoreThreads = 256;
 constexpr int kSuperTile = 64;
-constexpr int kScoreWaves = 2048;  // resident waves targeted per launch (2 per SIMD)
+constexpr int kScoreWaves = 3072;     // full mode: resident waves per launch (3 per SIMD)
+constexpr int kScoreWavesPool = 2048;  // pool mode holds more registers (2 per SIMD)
 
 template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t old) {
@@ -140,7 +141,7 @@ __device__ __forceinline__ float max8_lanes(float v) {
 // super-tiles are in flight while one is computed.  With GATHER the items
 // are pool[b][i], otherwise positions i; the pool entries of a super-tile
 // are read one ring step before its codes.
-constexpr int kScoreStages = 3;
+constexpr int kScoreStages = 2;
 
 template <int MT, bool GATHER, int NS = kScoreStages, int OCC = 2, bool WLDS = false>
 __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
@@ -154,16 +155,39 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
-  int64_t L = len[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  int64_t N = L;
-  if (GATHER) {
-    int64_t pl = pool_len[b];
-    N = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
-  }
   const int64_t W = (int64_t)gridDim.x * 4;
   const int64_t st0 = (int64_t)blockIdx.x * 4 + wave;
-  if ((int64_t)blockIdx.x * 4 * kSuperTile >= N) return;  // workgroup-uniform
+  const int64_t step = W * kSuperTile;
+  const int64_t base0 = st0 * kSuperTile;
+  const int64_t Nmax = GATHER ? (int64_t)pool_cap : cap;  // bound of the item index
+  const uint8_t* codes_b = idx_codes + (int64_t)b * cap * 64;
+  const uint8_t* scales_b = idx_scales + (int64_t)b * cap * 4;
+  const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
+  float* scores_b = scores + (int64_t)b * score_stride;
+
+  // The first stages' loads need no length: full mode reads its rows right
+  // away (masked later), pool mode reads its pool entries.  They overlap the
+  // query staging below, and the lengths are applied after the barrier.
+  ScoreRows rows[NS];
+  ScoreStage stg[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    // raw rows: the pool entry itself (-1 past the pool), or the position
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t it = base0 + u * step + 16 * t + n;
+      const bool in = it < Nmax;
+      if (GATHER)
+        rows[u].r[t] = in ? pool_b[it] : -1;
+      else
+        rows[u].r[t] = in ? (int32_t)it : 0;
+    }
+    rows[u].ok = 0u;
+  }
+  if (!GATHER) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) score_load(stg[u], rows[u], codes_b, scales_b, g);
+  }
 
   // Query heads (zero beyond H) and head weights, staged once per workgroup.
   {
@@ -177,8 +201,15 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&qs[h * 128 + 32 * part + 8 * j]) = v[j];
     if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
   }
+  int64_t L = len[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int64_t N = L;
+  if (GATHER) {
+    int64_t pl = pool_len[b];
+    N = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
+  }
   __syncthreads();
-  if (st0 * kSuperTile >= N) return;  // wave-uniform; no barrier follows
+  if (base0 >= N) return;  // wave-uniform; no barrier follows
   // A operand: lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
   bf16x8 A[MT][4];
   float wr[MT][4];
@@ -192,22 +223,29 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
   }
   const float4* wq = reinterpret_cast<const float4*>(ws) + g;  // heads 16mt+4g .. +3 at wq[4mt]
 
-  const uint8_t* codes_b = idx_codes + (int64_t)b * cap * 64;
-  const uint8_t* scales_b = idx_scales + (int64_t)b * cap * 4;
-  const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
-  float* scores_b = scores + (int64_t)b * score_stride;
-
-  const int64_t step = W * kSuperTile;
-  const int64_t base0 = st0 * kSuperTile;
+  // apply the lengths to the early rows (pool mode: entries past pool_len or
+  // outside [0, len) are masked and read row 0)
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    rows[u].ok = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t it = base0 + u * step + 16 * t + n;
+      bool vis = it < N;
+      if (GATHER) {
+        vis = vis && rows[u].r[t] >= 0 && (int64_t)rows[u].r[t] < L;
+        rows[u].r[t] = vis ? rows[u].r[t] : 0;
+      }
+      rows[u].ok |= (vis ? 1u : 0u) << t;
+    }
+  }
+  if (GATHER) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) score_load(stg[u], rows[u], codes_b, scales_b, g);
+  }
   const int64_t iters = (N - base0 + step - 1) / step;  // >= 1
-  ScoreRows rows[NS];
-  ScoreStage stg[NS];
   // ring invariant at the top of round r (iteration i = r*NS + u handled by
   // slot u): stages hold iterations i .. i+NS-2, rows[(u+NS-1)%NS] iteration i+NS-1
-#pragma unroll
-  for (int u = 0; u < NS; ++u) score_rows<GATHER>(rows[u], base0 + u * step, N, L, pool_b, n);
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u) score_load(stg[u], rows[u], codes_b, scales_b, g);
   for (int64_t i0 = 0; i0 < iters; i0 += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -680,9 +718,9 @@ static void launch_score(int MT, dim3 grid, hipStream_t st, const uint8_t* ic, c
 
 // Workgroups per sequence for `items` scored entries: enough resident waves
 // to cover the chip, never more than one super-tile per wave.
-static unsigned score_wgs(int64_t items, int B) {
+static unsigned score_wgs(int64_t items, int B, int target_waves) {
   const int64_t tiles = (items + kSuperTile - 1) / kSuperTile;
-  int64_t waves = kScoreWaves / (B > 0 ? B : 1);
+  int64_t waves = target_waves / (B > 0 ? B : 1);
   if (waves < 4) waves = 4;
   if (waves > tiles) waves = tiles;
   const int64_t wgs = (waves + 3) / 4;
@@ -699,7 +737,7 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   float* bmax = reinterpret_cast<float*>((char*)ws + l.bmax_off);
   const int64_t nbk = (cap + block - 1) / block;
   const int MT = (H + 15) / 16;
-  dim3 grid(score_wgs(cap, B), (unsigned)B);
+  dim3 grid(score_wgs(cap, B, kScoreWaves), (unsigned)B);
   if (cap > 0)
     launch_score<false>(MT, grid, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
                         H, scores, cap, bmax, nbk);
@@ -747,7 +785,7 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   float* gmax = reinterpret_cast<float*>((char*)ws + l.gmax_off);
   const int64_t ngs = (pool_cap + kBlock - 1) / kBlock;
   const int MT = (H + 15) / 16;
-  dim3 grid(score_wgs(pool_cap, B), (unsigned)B);
+  dim3 grid(score_wgs(pool_cap, B, kScoreWavesPool), (unsigned)B);
   if (pool_cap > 0)
     launch_score<true>(MT, grid, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
                        w, H, ps, pool_cap, gmax, ngs);
