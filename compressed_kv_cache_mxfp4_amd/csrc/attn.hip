@@ -56,6 +56,7 @@ struct AttnSmem {
   uint16_t P[16 * kPLd];
   float red_m[WAVES][16];
   float red_l[WAVES][16];
+  float red_v[WAVES];  // per-wave bound of |dequantised value| (partial scaling)
   int last;  // this workgroup merges its (sequence, head group)
 };
 
@@ -186,20 +187,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
-    float* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
   static_assert(16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int HG = H >> 4;
-  // group gi = (sequence, head group); its S chunks get ids congruent mod 8,
-  // i.e. one XCD, whose L2 then holds every partial the merge reads
+  // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
+  // otherwise one (sequence, head group).  A unit's workgroups get ids
+  // congruent mod 8, i.e. one XCD: its L2 then holds the rows shared by the
+  // head groups and every partial the merge reads.
   const int id = blockIdx.x;
   const int xcd = id & 7, r8 = id >> 3;
-  const int gi = (r8 / S) * 8 + xcd, sidx = r8 % S;
-  if (gi >= B * HG) return;  // workgroup-uniform
+  const int per_unit = seq_units ? HG * S : S;
+  const int unit = (r8 / per_unit) * 8 + xcd, within = r8 % per_unit;
+  if (unit >= (seq_units ? B : B * HG)) return;  // workgroup-uniform
+  const int gi = seq_units ? unit * HG + within / S : unit;  // (sequence, head group)
+  const int sidx = within % S;
   const int b = gi / HG, hg = gi - b * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int nslots = k + swa_cap;
@@ -256,6 +262,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   mw = fmaxf(mw, shfl_xor_f(mw, 16));
   mw = fmaxf(mw, shfl_xor_f(mw, 32));
   if (g == 0) sm.red_m[w][n] = mw;
+  {
+    // largest scale byte of the lane's 128 values -> bound of |value| (6 x scale)
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) {
+      const uint32_t by = (row.s[q4 >> 2] >> (8 * (q4 & 3))) & 0xFFu;
+      mb = max(mb, FMT == 0 ? by : (by & 0x7Fu));  // positive E4M3 bytes order like values
+    }
+    float vb = row.ok ? 6.0f * (FMT == 0 ? e8m0_value(mb) : e4m3_value(mb)) : 0.0f;
+    if (!(vb <= 3.0e38f)) vb = 3.0e38f;  // NaN/inf scale bytes: clamp the bound
+    vb = wave_max(vb);
+    if (lane == 0) sm.red_v[w] = vb;
+  }
   __syncthreads();  // also: every wave is done reading the query tile
   float M = sm.red_m[0][n];
 #pragma unroll
@@ -278,13 +297,34 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
   __syncthreads();
 
-  float* prow = part + ((int64_t)b * H + 16 * hg) * S * 512;
+  uint16_t* prow = part + ((int64_t)b * H + 16 * hg) * S * 512;
   const uint32_t my_xcc = __builtin_amdgcn_s_getreg(kHwRegXccId);
+  // The partial is stored as fp16 of (output / sum) * 2^-e: a convex
+  // combination of the chunk's rows, so |.| <= vmax, and 2^e brings vmax
+  // just under 2^15 (fp16 keeps 11 significant bits).
+  float vmax = sm.red_v[0];
+#pragma unroll
+  for (int v = 1; v < WAVES; ++v) vmax = fmaxf(vmax, sm.red_v[v]);
+  int e_sc = 0;  // vmax < 2^(e_sc + 15)
+  if (vmax > 0.0f) {
+    int ex;
+    (void)frexpf(vmax, &ex);
+    e_sc = ex - 15;
+  }
   if (w == 0 && g == 0) {
     float l = 0.f;
 #pragma unroll
     for (int v = 0; v < WAVES; ++v) l += sm.red_l[v][n];
-    ml[((int64_t)b * H + 16 * hg + n) * S + sidx] = make_float4(M, l, __uint_as_float(my_xcc), 0.f);
+    ml[((int64_t)b * H + 16 * hg + n) * S + sidx] =
+        make_float4(M, l, __uint_as_float(my_xcc), __int_as_float(e_sc));
+  }
+  float scl[4];  // 1 / sum for heads 4g+i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) l += sm.red_l[v][4 * g + i];
+    scl[i] = l > 0.f ? 1.0f / l : 0.0f;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -299,9 +339,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
     // lane (g, n): heads 4g+i, dims 256h + 16*tile + n, tile = w + WAVES*nt
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 16 * w + n;
-      dst[0] = O[0][i];
-      if (w + WAVES < 16) dst[16 * WAVES] = O[1][i];
+      uint16_t* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 16 * w + n;
+      dst[0] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[0][i] * scl[i], -e_sc));
+      if (w + WAVES < 16)
+        dst[16 * WAVES] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[1][i] * scl[i], -e_sc));
     }
   }
 
@@ -323,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
     const int hh = tid >> 5, d16 = tid & 31;
     const int64_t bh = (int64_t)b * H + 16 * hg + hh;
     const float4* mlp = ml + bh * S;
-    const float4* src = reinterpret_cast<const float4*>(part + bh * S * 512 + 16 * d16);
+    const uint4* src = reinterpret_cast<const uint4*>(part + bh * S * 512 + 16 * d16);
     float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
@@ -331,17 +372,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
     bool same_xcd = true;
     for (int s0 = 0; s0 < S; s0 += 4) {
       float4 e[4];
-      float4 v[4][4];
+      uint4 v[4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (s0 + u < S) {
           e[u] = mlp[s0 + u];
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) v[u][c4] = src[(s0 + u) * 128 + c4];
+          v[u][0] = src[(s0 + u) * 64];
+          v[u][1] = src[(s0 + u) * 64 + 1];
         } else {
           e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) v[u][c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+          v[u][0] = v[u][1] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
       float mg = Mx;
@@ -359,14 +399,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         // a chunk with no visible row has max -inf and a zero partial
-        const float wgt = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx);
-        Lsum += wgt * e[u].y;
+        const float wl = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx) * e[u].y;
+        Lsum += wl;
+        const float wgt = ldexpf(wl, __float_as_int(e[u].w));  // undo the partial's 2^-e
+        const uint32_t hw[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                                v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          acc[4 * c4 + 0] += wgt * v[u][c4].x;
-          acc[4 * c4 + 1] += wgt * v[u][c4].y;
-          acc[4 * c4 + 2] += wgt * v[u][c4].z;
-          acc[4 * c4 + 3] += wgt * v[u][c4].w;
+        for (int j = 0; j < 8; ++j) {
+          acc[2 * j] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] & 0xFFFFu));
+          acc[2 * j + 1] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] >> 16));
         }
       }
     }
@@ -389,14 +430,14 @@ struct AttnWs {
   size_t cnt_off, part_off, ml_off, total;
 };
 
-// [counters: kMaxAttnGroups x u32][partials: B*H*S x 512 fp32][(max, sum, xcd): B*H*S x 16 B],
+// [counters: kMaxAttnGroups x u32][partials: B*H*S x 512 fp16][(max, sum, xcd, e): B*H*S x 16 B],
 // sized for 128-row chunks (the larger S).
 static AttnWs attn_ws_layout(int B, int H, int k, int swa_cap) {
   const size_t n = (size_t)B * H * attn_splits(k, swa_cap);
   AttnWs l;
   l.cnt_off = 0;
   l.part_off = (size_t)kMaxAttnGroups * sizeof(uint32_t);
-  l.ml_off = l.part_off + ((n * 512 * sizeof(float) + 255) & ~(size_t)255);
+  l.ml_off = l.part_off + ((n * 512 * sizeof(uint16_t) + 255) & ~(size_t)255);
   l.total = l.ml_off + ((n * sizeof(float4) + 255) & ~(size_t)255);
   return l;
 }
@@ -424,9 +465,11 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   const AttnWs l = attn_ws_layout(B, H, k, swa_cap);
   char* wsb = reinterpret_cast<char*>(ws);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + l.cnt_off);
-  float* part = reinterpret_cast<float*>(wsb + l.part_off);
+  uint16_t* part = reinterpret_cast<uint16_t*>(wsb + l.part_off);
   float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
-  const unsigned grid = (unsigned)(((groups + 7) / 8) * S * 8);
+  const int seq_units = B >= 8 ? 1 : 0;
+  const int64_t units = seq_units ? B : groups;
+  const unsigned grid = (unsigned)(((units + 7) / 8) * (seq_units ? HG : 1) * S * 8);
   auto go = [&](auto kern, int waves, size_t smem) -> bool {
     static bool attr_done = false;  // one per instantiation
     if (!attr_done) {
@@ -436,7 +479,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     }
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                          swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
-                                         part, ml, cnt, out, lse_opt);
+                                         part, ml, cnt, out, lse_opt, seq_units);
     return true;
   };
   bool ok;
