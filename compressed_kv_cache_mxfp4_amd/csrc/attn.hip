@@ -10,11 +10,13 @@
 // 另外三笔账]: 512 selected + 128 window rows per query.
 //
 // Split-rows design (flash decoding).  The row slots of a sequence (top-k
-// entries, then window entries) are cut into 128-slot chunks; one workgroup
-// (8 waves) takes one (sequence, 16 heads, chunk), so a decode call with 16
-// sequences, 64 heads and 512 + 128 rows runs 320 workgroups rather than 64.
-// Each workgroup leaves an unnormalised partial output with its own max and
-// sum; a combine kernel merges the chunks of each (sequence, head) exactly.
+// entries, then window entries) are cut into chunks of 16*WAVES slots (128 or
+// 160); one workgroup takes one (sequence, 16 heads, chunk), so a decode call
+// with 16 sequences, 64 heads and 512 + 128 rows runs 256-320 workgroups
+// rather than 64.  Each workgroup leaves a partial output (normalised by its
+// own sum, stored as fp16 scaled by a power of two) with its max and sum; the
+// last workgroup of a (sequence, head group) to finish merges the chunks
+// exactly, in a fixed order.
 //  * Q.R^T: wave w takes rows 16w..16w+15 of the chunk.  Lane (g, m) holds the
 //    code bytes of row m for dims 64g..64g+63 and 256+64g..256+64g+63 and
 //    their 8 scale bytes, and dequantises them straight into the A operand of
@@ -24,9 +26,9 @@
 //    them per wave from global memory would move 8x the bytes through the
 //    CU's vector-memory path).  Every row is dequantised exactly once; the
 //    bf16 values stay in registers until their half of R is staged.
-//  * P.R: each 256-dim half of R lives in LDS in turn (67 KB, so two
-//    workgroups share a CU); wave w takes dims 32w..32w+31 of the half for the
-//    16 heads.  P comes from LDS; the row-major R tile is read column-wise
+//  * P.R: each 256-dim half of R lives in LDS in turn (67 KB at 8 waves, so
+//    two workgroups share a CU); of the half's sixteen 16-dim tiles wave w
+//    takes tiles w and w+WAVES (when below 16) for the 16 heads.  P comes from LDS; the row-major R tile is read column-wise
 //    with the gfx950 transpose read (ds_read_b64_tr_b16): within a 16-lane
 //    group, source lane a+4j points at R[r0+j][d0+4a] and lane n receives
 //    R[r0..r0+3][d0+n], i.e. four K slots of the MFMA B operand.
