@@ -49,15 +49,20 @@ constexpr int kMaxAttnGroups = 65536;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-// WAVES waves take 16 rows each: a chunk of 16*WAVES row slots.
+// WAVES waves take 16 rows each: a chunk of 16*WAVES row slots.  With more
+// than 8 waves one workgroup fills a CU, and the query tile gets a region of
+// its own so that each wave can stage its rows as soon as its logits are
+// done; with 8 waves (two workgroups per CU) the query tile borrows R.
 template <int WAVES>
 struct AttnSmem {
   static constexpr int kRows = 16 * WAVES;
   static constexpr int kPLd = kRows + 8;  // P row stride in bf16
-  uint16_t R[kRows * kHLd];  // also holds the 16 x kQLd query tile before the first barrier
+  static constexpr bool kQOwn = WAVES > 8;
+  uint16_t R[kRows * kHLd];
+  uint16_t Qown[kQOwn ? 16 * kQLd : 8];
   uint16_t P[16 * kPLd];
-  float red_m[WAVES][16];
-  float red_l[WAVES][16];
+  __align__(16) float red_m[WAVES][16];
+  __align__(16) float red_l[WAVES][16];
   float red_v[WAVES];  // per-wave bound of |dequantised value| (partial scaling)
   int last;  // this workgroup merges its (sequence, head group)
 };
@@ -151,29 +156,47 @@ __device__ __forceinline__ bf16x8 row_step(const RowFetch& f, int ks) {
 }
 
 // O(16 heads x the wave's 16-dim tiles of one R half) += P . R_half.  Wave w
-// takes tiles w, w + WAVES (16 tiles per half); K steps of 32 rows.
+// takes tiles w and w + WAVES (16 tiles per half); K steps of 32 rows.  The
+// LDS reads of KB K steps are issued before their products (all of them with
+// one workgroup per CU; two at a time at 8 waves, where registers are
+// scarcer), so a wave does not wait for LDS once per K step.  A wave without
+// a second tile reads and multiplies its first tile twice and drops O[1].
 template <int WAVES>
 __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g, int n, floatx4 (&O)[2]) {
   constexpr int NK = AttnSmem<WAVES>::kRows / 32;
   constexpr int LD = AttnSmem<WAVES>::kPLd;
+  constexpr int KB = AttnSmem<WAVES>::kQOwn ? NK : 2;
+  static_assert(NK % KB == 0, "K steps must split into whole batches");
   const int ta = n & 3, tj = n >> 2;
+  const int t1 = w + WAVES < 16 ? w + WAVES : w;
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sm.P[n * LD + 32 * ks + 8 * g]);
+  for (int k0 = 0; k0 < NK; k0 += KB) {
+    bf16x8 pa[KB];
+    shortx4 lo[2][KB], hi[2][KB];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int tile = w + WAVES * nt;
-      if (tile >= 16) break;  // wave-uniform
-      const int col = 16 * tile + 4 * ta;
-      const int r0 = 32 * ks + 8 * g + tj;
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kHLd + col]));
-      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) shortx4*)(&sm.R[(r0 + 4) * kHLd + col]));
-      shortx8 bv;
-      bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-      bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bv), O[nt], 0, 0, 0);
+    for (int j = 0; j < KB; ++j) pa[j] = *reinterpret_cast<const bf16x8*>(&sm.P[n * LD + 32 * (k0 + j) + 8 * g]);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = 16 * (nt ? t1 : w) + 4 * ta;
+        const int r0 = 32 * (k0 + j) + 8 * g + tj;
+        lo[nt][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kHLd + col]));
+        hi[nt][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(&sm.R[(r0 + 4) * kHLd + col]));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        shortx8 bv;
+        bv[0] = lo[nt][j][0]; bv[1] = lo[nt][j][1]; bv[2] = lo[nt][j][2]; bv[3] = lo[nt][j][3];
+        bv[4] = hi[nt][j][0]; bv[5] = hi[nt][j][1]; bv[6] = hi[nt][j][2]; bv[7] = hi[nt][j][3];
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j], __builtin_bit_cast(bf16x8, bv), O[nt], 0, 0, 0);
+      }
     }
   }
 }
@@ -183,7 +206,7 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
 // (and its L2 copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512]
 // (fp32, relative to the chunk max) and ml[(b*H+h)*S + s] = (max, sum).
 template <int FMT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_kernel(
+__global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_kernel(
     const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
@@ -194,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
-  static_assert(16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
+  static_assert(Smem::kQOwn || 16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int HG = H >> 4;
   // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
@@ -234,8 +257,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
                                   main_scales, swa_codes, swa_scales);
     fetch_row(row, src, g);
   }
-  // the query tile borrows the R buffer, which is not written before the max barrier
-  uint16_t* Q = sm.R;
+  // with 8 waves the query tile borrows the R buffer, which is then not
+  // written before the max barrier
+  uint16_t* Q = Smem::kQOwn ? sm.Qown : sm.R;
 #pragma unroll
   for (int j2 = 0; j2 < kQv; ++j2) {
     const int e = tid + kThreads * j2;
@@ -246,11 +270,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   // ---- logits of the wave's 16 rows (every row dequantised once, kept for P.R)
   floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
   bf16x8 ra[16];
+  // query fragments of kQB K steps are read before their products (fewer at
+  // 8 waves, where four waves share a SIMD and registers are scarcer)
+  constexpr int kQB = Smem::kQOwn ? 8 : 4;
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    ra[ks] = row_step<FMT>(row, ks);
-    const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + step_dim(ks, g)]);
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[ks], qf, sacc, 0, 0, 0);
+  for (int kb = 0; kb < 16; kb += kQB) {
+    bf16x8 qf[kQB];
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + step_dim(kb + j, g)]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      ra[kb + j] = row_step<FMT>(row, kb + j);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[kb + j], qf[j], sacc, 0, 0, 0);
+    }
+  }
+  uint16_t* rrow = &sm.R[(16 * w + n) * kHLd + 64 * g];
+  if (Smem::kQOwn) {
+    // the first half of the wave's rows goes to LDS now (R is not shared with Q)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
   }
   // lane (g, n): rows 4g+i of the wave's tile, head n
   const uint64_t vmask = __ballot(row.ok != 0u);
@@ -294,9 +333,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
   if (g == 0) sm.red_l[w][n] = lw;
   *reinterpret_cast<uint2*>(&sm.P[n * kPLd + 16 * w + 4 * g]) =
       make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
-  uint16_t* rrow = &sm.R[(16 * w + n) * kHLd + 64 * g];
+  if (!Smem::kQOwn) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
+    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
+  }
   __syncthreads();
 
   uint16_t* prow = part + ((int64_t)b * H + 16 * hg) * S * 512;
@@ -321,12 +361,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 2 : 1) void attn_split_ker
         make_float4(M, l, __uint_as_float(my_xcc), __int_as_float(e_sc));
   }
   float scl[4];  // 1 / sum for heads 4g+i
+  {
+    float4 ls[WAVES];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float l = 0.f;
+    for (int v = 0; v < WAVES; ++v) ls[v] = *reinterpret_cast<const float4*>(&sm.red_l[v][4 * g]);
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < WAVES; ++v) l += sm.red_l[v][4 * g + i];
-    scl[i] = l > 0.f ? 1.0f / l : 0.0f;
+    for (int v = 0; v < WAVES; ++v) {
+      l4[0] += ls[v].x;
+      l4[1] += ls[v].y;
+      l4[2] += ls[v].z;
+      l4[3] += ls[v].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scl[i] = l4[i] > 0.f ? 1.0f / l4[i] : 0.0f;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
