@@ -359,6 +359,15 @@ __device__ __forceinline__ void load_keys(KeyRegs<EPT>& K, const Src& src, int n
   }
 }
 
+// Sum of the per-wave values w[0 .. wave-1] (wave < 16): lane v < wave reads
+// w[v], then one 16-lane reduction.  One LDS round trip, a few VALU ops.
+__device__ __forceinline__ uint32_t wave_prefix(const uint32_t* w, int wave) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v = lane < wave ? w[lane] : 0u;
+  v = row_reduce(v, [](uint32_t x, uint32_t y) { return x + y; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+}
+
 // Bin of histogram h (2048 bins, ascending key order; bins past the used
 // range are zero) that holds the need-th largest counted key.  Thread t scans
 // bins 2047-TB*t .. 2048-TB*(t+1) in descending order; a block scan of the
@@ -379,8 +388,7 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* h, SelScratch&
   const uint32_t incl = wave_incl_scan(s);
   if (lane == 63) sh.wred[0][wave] = incl;
   __syncthreads();
-  uint32_t excl = incl - s;
-  for (int v = 0; v < wave; ++v) excl += sh.wred[0][v];
+  uint32_t excl = incl - s + wave_prefix(sh.wred[0], wave);
   if (excl < need && need <= excl + s) {
     uint32_t acc = excl;
 #pragma unroll
@@ -409,6 +417,7 @@ template <int NT, int EPT, bool PREF, class Src, class Emit>
 __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
                            Emit emit) {
   constexpr int NW = NT / 64;
+  static_assert(NW <= 16, "per-wave partials hold at most 16 waves");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int E = EPT > 0 ? EPT : (n + NT - 1) / NT;
   auto KEY = [&](int j) -> uint32_t {
@@ -531,12 +540,16 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     sh.wred[2][wave] = weq;
   }
   __syncthreads();
-  uint32_t eq_pref = 0u, out_pref = 0u;
-  for (int v = 0; v < wave; ++v) {
-    const uint32_t g_v = sh.wred[1][v], e_v = sh.wred[2][v];
-    const uint32_t take_v = eq_pref >= need_eq ? 0u : min(e_v, need_eq - eq_pref);
-    out_pref += g_v + take_v;
-    eq_pref += e_v;
+  // Earlier waves' totals: G (keys above T) and E (keys equal to T).  The
+  // equal keys are taken in index order up to need_eq, so the earlier waves
+  // emitted G + min(E, need_eq).  Lanes 0-15 sum wred[1], lanes 16-31 wred[2].
+  uint32_t eq_pref, out_pref;
+  {
+    uint32_t v = lane < wave ? sh.wred[1][lane] : ((lane >= 16 && lane - 16 < wave) ? sh.wred[2][lane - 16] : 0u);
+    v = row_reduce(v, [](uint32_t x, uint32_t y) { return x + y; });
+    const uint32_t G = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    eq_pref = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    out_pref = G + min(eq_pref, need_eq);
   }
   const uint64_t below = (1ull << lane) - 1ull;
   uint32_t r_sel = out_pref, r_eq = eq_pref;
