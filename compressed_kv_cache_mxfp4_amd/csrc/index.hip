@@ -359,6 +359,28 @@ __device__ __forceinline__ void load_keys(KeyRegs<EPT>& K, const Src& src, int n
   }
 }
 
+// Keys of a float array in two steps, so that the loads need not wait for
+// the candidate count: load_raw reads every slot below n_alloc (the array's
+// allocated length), finish_keys then turns slots below n into keys and the
+// rest into 0 (absent).
+template <int NT, int EPT>
+__device__ __forceinline__ void load_raw(KeyRegs<EPT>& K, const float* p, int n_alloc) {
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = sel_index<NT, EPT>(0, j);
+    K.r[j] = i < n_alloc ? __float_as_uint(p[i]) : 0x7FC00000u;
+  }
+}
+
+template <int NT, int EPT>
+__device__ __forceinline__ void finish_keys(KeyRegs<EPT>& K, int n) {
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = sel_index<NT, EPT>(0, j);
+    K.r[j] = i < n ? float_key(__uint_as_float(K.r[j])) : 0u;
+  }
+}
+
 // Sum of the per-wave values w[0 .. wave-1] (wave < 16): lane v < wave reads
 // w[v], then one 16-lane reduction.  One LDS round trip, a few VALU ops.
 __device__ __forceinline__ uint32_t wave_prefix(const uint32_t* w, int wave) {
@@ -430,6 +452,9 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
   };
   constexpr int UNR = EPT > 0 ? EPT : 1;
 
+  // both histogram buffers start cleared; the barrier after the reduction
+  // below orders these stores before any histogram update
+  for (int i = t; i < 2 * 2048; i += NT) (&sh.hist[0][0])[i] = 0u;
   uint32_t cnt = 0u, mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll UNR
   for (int j = 0; j < E; ++j) {
@@ -456,15 +481,18 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     mn = min(mn, sh.wred[1][v]);
     mx = max(mx, sh.wred[2][v]);
   }
-  __syncthreads();  // every wave has read the partials before they are reused
+  // No barrier here: the prefilter and every pass synchronise before they
+  // write wred; only the emission can follow directly (synced == false).
   const uint32_t target = min((uint32_t)k, cnt);
-  if (target == 0u) return 0;
+  bool synced = false;  // a barrier has passed since the partials were read
+  if (target == 0u) {
+    __syncthreads();  // every wave has read the partials before a later call reuses them
+    return 0;
+  }
 
   uint32_t lo = mn, hi = mx, above = 0u, T;
   bool take_all_eq = false;
-  int buf = 0;  // histogram buffer of the next pass; both start cleared
-  for (int i = t; i < 2 * 2048; i += NT) (&sh.hist[0][0])[i] = 0u;
-  __syncthreads();
+  int buf = 0;  // histogram buffer of the next pass
   if (PREF && lo != hi && cnt > 4096u && cnt >= 8u * target) {
     const uint32_t span = hi - lo;
     const int nbits = 32 - __clz((int)span);
@@ -473,6 +501,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     if (smp) atomicAdd(&sh.hist[0][(smp - lo) >> shift], 1u);
     if (t == 0) sh.bc[0] = 0xFFFFFFFFu;
     __syncthreads();
+    synced = true;
     // sample rank: 1.5x the expected share of the k winners, plus 16
     const uint32_t r = min((uint32_t)NT, 16u + (uint32_t)((3ull * target * NT + 2ull * cnt - 1) / (2ull * cnt)));
     find_bin_from_top<NT>(sh.hist[0], sh, r);
@@ -482,11 +511,13 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     uint32_t c0 = 0u;
 #pragma unroll UNR
     for (int j = 0; j < E; ++j) c0 += (uint32_t)__popcll(__ballot(KEY(j) >= T0));
-    if (lane == 0) sh.wred[1][wave] = c0;
+    // wred[0]: read by find_bin above before its last barrier; the emission
+    // below writes only wred[1] and wred[2]
+    if (lane == 0) sh.wred[0][wave] = c0;
     __syncthreads();
     c0 = 0u;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) c0 += sh.wred[1][v];
+    for (int v = 0; v < NW; ++v) c0 += sh.wred[0][v];
     if (c0 >= target) lo = T0;
   }
   for (;;) {
@@ -506,6 +537,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     uint32_t* hn = sh.hist[buf ^ 1];
     for (int i = t; i < 2048; i += NT) hn[i] = 0u;  // the next pass's buffer
     __syncthreads();
+    synced = true;
     find_bin_from_top<NT>(h, sh, target - above);
     const uint32_t tb = sh.bc[0], gt = sh.bc[1], in_bin = sh.bc[2];
     if (target - above - gt == in_bin) {
@@ -535,6 +567,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     wgt += (uint32_t)__popcll(__ballot(kk > T));
     weq += (uint32_t)__popcll(__ballot(kk == T));
   }
+  if (!synced) __syncthreads();  // workgroup-uniform: all keys were equal
   if (lane == 0) {
     sh.wred[1][wave] = wgt;
     sh.wred[2][wave] = weq;
@@ -556,14 +589,18 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
 #pragma unroll UNR
   for (int j = 0; j < E; ++j) {
     const uint32_t kk = KEY(j);
-    const bool eq = kk == T;
-    const uint64_t eqb = __ballot(eq);
-    const uint32_t eq_rank = r_eq + (uint32_t)__popcll(eqb & below);
-    const bool sel = kk > T || (eq && eq_rank < need_eq);
+    bool sel = kk > T;
+    const uint64_t eqb = __ballot(kk == T);
+    if (eqb) {  // wave-uniform: rare, only around the threshold
+      const uint32_t eq_rank = r_eq + (uint32_t)__popcll(eqb & below);
+      sel = sel || (kk == T && eq_rank < need_eq);
+      r_eq += (uint32_t)__popcll(eqb);
+    }
     const uint64_t selb = __ballot(sel);
-    if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
-    r_eq += (uint32_t)__popcll(eqb);
-    r_sel += (uint32_t)__popcll(selb);
+    if (selb) {  // wave-uniform
+      if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
+      r_sel += (uint32_t)__popcll(selb);
+    }
   }
   __syncthreads();
   return (int)target;
@@ -623,14 +660,15 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
   __shared__ int32_t cblk[CSA2_MAX_TOPK];
   const int b = blockIdx.x;
+  KeysFromArray bsrc{bmax + (int64_t)b * bstride};
+  KeyRegs<EPT_B> kb;
+  if constexpr (EPT_B > 0) load_raw<NT, EPT_B>(kb, bsrc.p, (int)bstride);  // overlaps the length load
   int64_t L = len[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nb = (int)((L + kBlock - 1) / kBlock);
   const float* sc = scores + (int64_t)b * sstride;
   int32_t* tk = topk + (int64_t)b * k;
-  KeysFromArray bsrc{bmax + (int64_t)b * bstride};
-  KeyRegs<EPT_B> kb;
-  load_keys<NT, EPT_B>(kb, bsrc, nb);
+  if constexpr (EPT_B > 0) finish_keys<NT, EPT_B>(kb, nb);
   int ncb;
   if (n_blocks > 0) {
     const int nsel = select_core<NT, EPT_B, true>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r, int j) {
@@ -639,8 +677,24 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
     });
     const int pl = group_items(blk, nsel, (int)L);
     int32_t* pb = pool + (int64_t)b * n_blocks * kBlock;
-    for (int i = threadIdx.x; i < n_blocks * kBlock; i += NT)
-      pb[i] = i < pl ? blk[i >> 3] * kBlock + (i & 7) : -1;
+    // a thread writes whole groups (8 entries: two 16-byte stores when the
+    // caller's buffer allows it)
+    const bool vec = (reinterpret_cast<uintptr_t>(pb) & 15u) == 0u;
+    for (int gi = threadIdx.x; gi < n_blocks; gi += NT) {
+      const int base = gi * kBlock;
+      const int p0 = gi < nsel ? blk[gi] * kBlock : 0;
+      int e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = base + j < pl ? p0 + j : -1;
+      if (vec) {
+        int4* dst = reinterpret_cast<int4*>(pb + base);
+        dst[0] = make_int4(e[0], e[1], e[2], e[3]);
+        dst[1] = make_int4(e[4], e[5], e[6], e[7]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[base + j] = e[j];
+      }
+    }
     if (threadIdx.x == 0) pool_len[b] = pl;
   }
   if (n_blocks >= k) {
@@ -674,14 +728,16 @@ __global__ __launch_bounds__(NT) void select_pool_kernel(
   __shared__ SelScratch sh;
   __shared__ int32_t cgrp[CSA2_MAX_TOPK];
   const int b = blockIdx.x;
+  const int ngs = (pool_cap + kBlock - 1) / kBlock;
+  KeysFromArray gsrc{gmax + (int64_t)b * ngs};
+  KeyRegs<EPT_G> kg;
+  load_raw<NT, EPT_G>(kg, gsrc.p, ngs);  // overlaps the pool length load
   int n = pool_len[b];
   n = n < 0 ? 0 : (n > pool_cap ? pool_cap : n);
   const int ng = (n + kBlock - 1) / kBlock;
   const int32_t* pb = pool + (int64_t)b * pool_cap;
   int32_t* tk = topk + (int64_t)b * k;
-  KeysFromArray gsrc{gmax + (int64_t)b * ((pool_cap + kBlock - 1) / kBlock)};
-  KeyRegs<EPT_G> kg;
-  load_keys<NT, EPT_G>(kg, gsrc, ng);
+  finish_keys<NT, EPT_G>(kg, ng);
   const int ncg = select_core<NT, EPT_G, false>(kg, gsrc, ng, k, sh, [&](int i, int r, int) { cgrp[r] = i; });
   const int nc = group_items(cgrp, ncg, n);
   KeysFromGroups psrc{pool_scores + (int64_t)b * pool_cap, cgrp};

@@ -117,6 +117,31 @@ def test_duplicate_rows_tie_exactly_and_prefer_lower_index():
     assert list(p2[:16]) == list(range(0, 8)) + list(range(96, 104))
 
 
+def test_all_scores_equal_take_lowest_indices():
+    """Every key equal (all-zero codes score exactly 0): the selection takes
+    the lowest indices, and its radix search ends before any histogram pass."""
+    wl = syn.small("eq", 29, B=2, cap=65536, H_idx=64, k=512, n_blocks=2048)
+    say("index_full / index_pool with every score equal, 2 x 65536")
+    cache = build_gpu_cache(wl, 0)
+    ic = torch.zeros_like(cache["idx_codes"])
+    lens = torch.tensor([65536, 40001], dtype=torch.int32, device=DEV)
+    q = syn.index_query(wl, 0, DEV)
+    w = syn.index_weights(wl, 0, DEV)
+    topk, pool, pool_len, scores = K.index_full(ic, cache["idx_scales"], lens, q, w, k=512, n_blocks=2048,
+                                                return_scores=True)
+    torch.cuda.synchronize()
+    assert (scores[0] == 0).all() and (scores[1, :40001] == 0).all()
+    assert (topk.cpu().numpy() == np.arange(512)).all()
+    assert (pool.cpu().numpy() == np.arange(2048 * 8)).all()
+    assert pool_len.cpu().numpy().tolist() == [2048 * 8, 2048 * 8]
+    t2 = K.index_pool(ic, cache["idx_scales"], lens, pool, pool_len, q, w, k=512)
+    assert (t2.cpu().numpy() == np.arange(512)).all()
+    # a pool of 40 entries and k = 512: every entry is taken, the rest is -1
+    pl = torch.tensor([40, 40], dtype=torch.int32, device=DEV)
+    t3 = K.index_pool(ic, cache["idx_scales"], lens, pool, pl, q, w, k=512).cpu().numpy()
+    assert (t3[:, :40] == np.arange(40)).all() and (t3[:, 40:] == -1).all()
+
+
 def test_determinism_two_runs_bitwise():
     wl = syn.small("det", 9, B=2, cap=20000, H_idx=64, k=512, n_blocks=2048)
     cache = build_gpu_cache(wl, 0)
