@@ -219,6 +219,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
   static_assert(Smem::kQOwn || 16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  // every kernel argument in SGPRs up front: one batch of argument loads and
+  // one wait, instead of a load and a wait in each branch that first uses one
+  asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
+               "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
+               "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S),
+               "s"(seq_units));
   const int HG = H >> 4;
   // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
   // otherwise one (sequence, head group).  A unit's workgroups get ids
@@ -228,29 +234,43 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   const int xcd = id & 7, r8 = id >> 3;
   const int per_unit = seq_units ? HG * S : S;
   const int unit = (r8 / per_unit) * 8 + xcd, within = r8 % per_unit;
-  if (unit >= (seq_units ? B : B * HG)) return;  // workgroup-uniform
-  const int gi = seq_units ? unit * HG + within / S : unit;  // (sequence, head group)
+  // Padding workgroups (unit past the end) load from unit 0's addresses and
+  // leave after issuing their loads: every load below is independent, and
+  // none of them waits for another or for an early exit.
+  const bool valid = unit < (seq_units ? B : B * HG);  // workgroup-uniform
+  const int gi = !valid ? 0 : (seq_units ? unit * HG + within / S : unit);  // (sequence, head group)
   const int sidx = within % S;
   const int b = gi / HG, hg = gi - b * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int nslots = k + swa_cap;
-  int64_t L = len ? len[b] : 0;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  int SL = swa_len ? swa_len[b] : 0;
-  SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
 
-  // ---- loads: index entry and the 16 queries (to LDS, 32 B per thread), then the row
+  // ---- loads: index entry, lengths and the 16 queries (to LDS, 32 B per
+  // thread), then the row.  Every load is unconditional (clamped addresses,
+  // results masked afterwards): a conditional load makes the compiler wait
+  // for it where the branches join.  The lengths are per-lane vector loads
+  // (a scalar load is waited for before the next one is issued); a NULL
+  // pointer reads the query instead and counts as 0.
+  int vzero;  // an opaque 0 in a VGPR: keeps the length loads on the vector path
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
   const int slot = kRows * sidx + 16 * w + n;
-  int32_t pidx = -1;
-  if (slot < k) pidx = topk[(int64_t)b * k + slot];
+  const int32_t* tp = k > 0 ? topk + (int64_t)b * k + min(slot, k - 1) : reinterpret_cast<const int32_t*>(q);
+  const int32_t praw = tp[0];
+  const int32_t Lraw = (len ? len + b : reinterpret_cast<const int32_t*>(q))[vzero];
+  const int32_t SLraw = (swa_len ? swa_len + b : reinterpret_cast<const int32_t*>(q))[vzero];
   const uint4* qg = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
-  constexpr int kQv = (1024 + kThreads - 1) / kThreads;  // 16 heads x 64 pieces of 16 B
-  uint4 qv[kQv];
-#pragma unroll
-  for (int j2 = 0; j2 < kQv; ++j2) {
-    const int e = tid + kThreads * j2;
-    qv[j2] = e < 1024 ? qg[e] : make_uint4(0u, 0u, 0u, 0u);
-  }
+  // 16 heads x 64 pieces of 16 B: two pieces per thread
+  static_assert(kThreads >= 512 && kThreads < 1024, "two query pieces per thread");
+  const uint4 qv0 = qg[tid];
+  const uint4 qv1 = qg[min(tid + kThreads, 1023)];
+  // all of the above in flight together: the compiler would otherwise sink
+  // each load into the branch that uses it and wait for them one by one
+  asm volatile("" ::"v"(praw), "v"(Lraw), "v"(SLraw));
+  const int32_t pidx = slot < k ? praw : -1;
+  if (!valid) return;
+  int64_t L = len ? Lraw : 0;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int SL = swa_len ? SLraw : 0;
+  SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
   RowFetch row;
   {
     const RowSrc src = locate_row(slot, pidx, nslots, b, k, L, SL, cap, swa_stride, main_codes,
@@ -260,10 +280,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   // with 8 waves the query tile borrows the R buffer, which is then not
   // written before the max barrier
   uint16_t* Q = Smem::kQOwn ? sm.Qown : sm.R;
-#pragma unroll
-  for (int j2 = 0; j2 < kQv; ++j2) {
-    const int e = tid + kThreads * j2;
-    if (e < 1024) *reinterpret_cast<uint4*>(&Q[(e >> 6) * kQLd + 8 * (e & 63)]) = qv[j2];
+  *reinterpret_cast<uint4*>(&Q[(tid >> 6) * kQLd + 8 * (tid & 63)]) = qv0;
+  if (tid + kThreads < 1024) {
+    const int e = tid + kThreads;
+    *reinterpret_cast<uint4*>(&Q[(e >> 6) * kQLd + 8 * (e & 63)]) = qv1;
   }
   __syncthreads();
 
