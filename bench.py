@@ -10,6 +10,11 @@ Default workload: 16 sequences x 131072 FP4 entries (128K context), 64 indexer
 heads, 64 attention heads x 512 dims.  Inputs are seeded synthetic tensors,
 resident in HBM before timing starts.
 
+The step is captured once into a HIP graph and the timed steps are graph
+replays (one host call per step); `ms_per_step_eager` reports the same step
+launched call by call from Python.  Per-call times come from each phase's
+own graph, timed with HIP events on the launch stream.
+
 Prints ONE JSON line on stdout.  `value` is indexer positions scored per
 second over whole steps; attention queries/s, per-call times and roofline
 fractions are reported alongside.
@@ -177,63 +182,100 @@ def main():
     torch.cuda.synchronize()
 
     only = args.only
+    n_pool = n_idx - 1
 
-    def one_step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        if only in (None, "write"):
-            K.cache_write(new_lat, None, 1, w_proj, fmt, out=staged)
-        if ev is not None:
-            ev[1].record()
-        if only in (None, "index_full", "index_pool"):
-            c = step.cache
-            if only != "index_pool":
-                q, w = idx_qw[0]
-                K.index_full(c["idx_codes"], c["idx_scales"], lengths, q, w, k=wl.k, n_blocks=wl.n_blocks,
-                             out=dict(topk=step.topk[0], pool=step.pool, pool_len=step.pool_len),
-                             _ws=step.ws_full)
-            if ev is not None:
-                ev[2].record()
-            if only != "index_full":
-                for i in range(1, n_idx):
-                    q, w = idx_qw[i]
-                    K.index_pool(c["idx_codes"], c["idx_scales"], lengths, step.pool, step.pool_len, q, w,
-                                 k=wl.k, out=dict(topk=step.topk[i]), _ws=step.ws_pool)
-        elif ev is not None:
-            ev[2].record()
-        if ev is not None:
-            ev[3].record()
-        if only in (None, "attn"):
-            step.run_attention(attn_q)
-        if ev is not None:
-            ev[4].record()
+    # ---- the step's phases (every call reads/writes preallocated buffers)
+    def ph_write():
+        K.cache_write(new_lat, None, 1, w_proj, fmt, out=staged)
 
+    def ph_full():
+        q, w = idx_qw[0]
+        c = step.cache
+        K.index_full(c["idx_codes"], c["idx_scales"], lengths, q, w, k=wl.k, n_blocks=wl.n_blocks,
+                     out=dict(topk=step.topk[0], pool=step.pool, pool_len=step.pool_len), _ws=step.ws_full)
+
+    def ph_pool():
+        c = step.cache
+        for i in range(1, n_idx):
+            q, w = idx_qw[i]
+            K.index_pool(c["idx_codes"], c["idx_scales"], lengths, step.pool, step.pool_len, q, w,
+                         k=wl.k, out=dict(topk=step.topk[i]), _ws=step.ws_pool)
+
+    def ph_attn():
+        step.run_attention(attn_q)
+
+    all_phases = [("write", ph_write), ("index_full", ph_full), ("index_pool", ph_pool), ("attn", ph_attn)]
+    phases = [(n, f) for n, f in all_phases if only is None or n == only]
     if only in ("index_pool", "attn"):
-        one_step_full = only
-        only = None
-        one_step()          # produce pool/top-k once
-        only = one_step_full
+        ph_full()           # produce pool/top-k once
+        if only == "attn":
+            ph_pool()
+
+    def one_step():
+        for _, f in phases:
+            f()
+
+    # eager warm-up (also sets each kernel's launch attributes before capture)
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
     pool_len = step.pool_len.cpu().tolist()
     log(f"[bench] warmup done; pool_len={pool_len[0]}")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # The step is launched as one HIP graph (torch.cuda.CUDAGraph): the same
+    # kernels on the same buffers, one host call per step.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    g_step = capture(one_step)
+    # a phase graph repeats its phase until it holds about 20 launches, so that
+    # the per-call time is not dominated by the replay's own launch cost
+    launches = dict(write=1, index_full=2, index_pool=2 * n_pool, attn=step.n_attn)
+    reps = {n: max(1, -(-20 // max(launches[n], 1))) for n, _ in phases}
+
+    def repeated(f, r):
+        def g():
+            for _ in range(r):
+                f()
+        return g
+
+    g_phase = {n: capture(repeated(f, reps[n])) for n, f in phases}
+    for _ in range(2):
+        g_step.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        one_step(evs[s])
+    for _ in range(args.steps):
+        g_step.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    seg = [[evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i in range(4)]
-    avg = [sum(x) / len(x) for x in seg]  # ms per step for each phase
-    n_pool = n_idx - 1
-    per_call_us = dict(write=avg[0] * 1e3, index_full=avg[1] * 1e3,
-                       index_pool=(avg[2] * 1e3 / n_pool) if n_pool else 0.0,
-                       attn=avg[3] * 1e3 / step.n_attn)
+
+    # ---- per-call times: each phase's graph replayed on its own, HIP events
+    # on the launch stream around K replays
+    per_call_us = {}
     calls = dict(write=1, index_full=1, index_pool=n_pool, attn=step.n_attn)
+    for n, g in g_phase.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call_us[n] = e0.elapsed_time(e1) * 1e3 / args.steps / reps[n] / max(calls[n], 1)
+    # the same step launched call by call from Python, for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     nbytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128)
     kernels = {}
     for name in per_call_us:
@@ -261,7 +303,8 @@ def main():
                     unit="GB/s", frac=d["frac_hbm"], traffic=traffic)
     res = dict(
         metric=METRIC, value=value, unit="positions/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        ms_per_step=ms_per_step, ms_per_step_eager=ms_per_step_eager, launch="hip_graph",
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic",
         config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
                     topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,

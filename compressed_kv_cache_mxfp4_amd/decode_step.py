@@ -94,3 +94,19 @@ class DecodeStep:
         self.run_index(idx_qw)
         self.run_attention(attn_q)
         return self
+
+    def capture(self, idx_qw, attn_q) -> "torch.cuda.CUDAGraph":
+        """Record one step into a HIP graph (torch.cuda.CUDAGraph); `graph.replay()`
+        then launches the same kernels on the same buffers with one host call.
+
+        The inputs (queries, weights, cache, lengths) are read at replay time
+        from the addresses recorded here, so refill them in place.  The step
+        records no memset and allocates nothing (buffers come from __init__),
+        and the attention completion counters are left at zero by every call,
+        so replays are independent.  The first eager call of each kernel sets
+        its launch attributes, so run() once before capturing.
+        """
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(idx_qw, attn_q)
+        return graph

@@ -101,6 +101,46 @@ def _check_workload(wl, fmt):
     torch.cuda.empty_cache()
 
 
+def test_decode_step_graph_replay_matches_eager():
+    """A step captured into a HIP graph reproduces the eager step bit for bit
+    on every replay, with eager steps and host synchronisations in between."""
+    wl = syn.small("graph", 41, B=3, cap=20000, H_idx=64, k=512, n_blocks=512, n_reindex=2,
+                   reuse_per_index=2)
+    say("[graph] capture and replay a 3 x 20000 decoder step")
+    cache = build_gpu_cache(wl, 0)
+    lengths = torch.tensor([20000, 19993, 7001], dtype=torch.int32, device=DEV)
+    step = DecodeStep(cache, lengths, k=wl.k, n_blocks=wl.n_blocks, n_reindex=wl.n_reindex,
+                      reuse_per_index=wl.reuse_per_index, main_fmt=0)
+    idx_qw, attn_q = _inputs(wl)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return ([t.clone() for t in step.topk], step.pool.clone(), step.pool_len.clone(),
+                [o.clone() for o in step.out])
+
+    def same(a, b):
+        return (all(torch.equal(x, y) for x, y in zip(a[0], b[0])) and torch.equal(a[1], b[1])
+                and torch.equal(a[2], b[2]) and all(torch.equal(x, y) for x, y in zip(a[3], b[3])))
+
+    step.run(idx_qw, attn_q)
+    ref = snapshot()
+    graph = step.capture(idx_qw, attn_q)
+    for rep in range(3):
+        # clobber the outputs, replay, compare; then an eager step in between
+        for t in step.topk:
+            t.fill_(-7)
+        for o in step.out:
+            o.fill_(0)
+        graph.replay()
+        assert same(snapshot(), ref), f"replay {rep} differs from the eager step"
+        step.run(idx_qw, attn_q)
+        assert same(snapshot(), ref), f"eager step after replay {rep} differs"
+    # the completion counters of the attention workspace are back at zero
+    assert int(step.ws_attn[:65536 * 4].count_nonzero()) == 0  # CSA2_ATTN_WS_COUNTER_BYTES
+    del graph, step, cache
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_tiny_workload(fmt):
     _check_workload(syn.WORKLOADS["tiny"], fmt)
