@@ -149,14 +149,27 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     const int32_t* __restrict__ len, const int32_t* __restrict__ pool,
     const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
     const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
-    float* __restrict__ bmax, int64_t bmax_stride) {
+    float* __restrict__ bmax, int64_t bmax_stride, int B, int per_seq) {
   __shared__ __align__(16) uint16_t qs[64 * 128];
   __shared__ float ws[64];
-  const int b = blockIdx.y;
+  // Grid: per_seq workgroups for each of B sequences, in one dimension.  When
+  // B is a multiple of 8, sequence b's workgroups all get ids congruent to
+  // b mod 8, i.e. they run on XCD b mod 8 -- the XCD of the selection
+  // workgroup b that reads their output next.
+  const int id = blockIdx.x;
+  int b, x;
+  if ((B & 7) == 0) {
+    const int r = id >> 3;
+    b = (id & 7) + 8 * (r / per_seq);
+    x = r % per_seq;
+  } else {
+    b = id / per_seq;
+    x = id % per_seq;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
-  const int64_t W = (int64_t)gridDim.x * 4;
-  const int64_t st0 = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t W = (int64_t)per_seq * 4;
+  const int64_t st0 = (int64_t)x * 4 + wave;
   const int64_t step = W * kSuperTile;
   const int64_t base0 = st0 * kSuperTile;
   const int64_t Nmax = GATHER ? (int64_t)pool_cap : cap;  // bound of the item index
@@ -773,16 +786,17 @@ IndexFullWs index_full_ws_layout(int B, int64_t cap, int block) {
 }
 
 template <bool GATHER>
-static void launch_score(int MT, dim3 grid, hipStream_t st, const uint8_t* ic, const uint8_t* is,
+static void launch_score(int MT, int per_seq, int B, hipStream_t st, const uint8_t* ic, const uint8_t* is,
                          int64_t cap, const int32_t* len, const int32_t* pool,
                          const int32_t* pool_len, int pool_cap, const uint16_t* q, const float* w,
                          int H, float* scores, int64_t sstride, float* bmax, int64_t bstride) {
+  const dim3 grid((unsigned)per_seq * (unsigned)B);
   if (MT == 1)
-    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
+    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
   else if (MT == 2)
-    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
+    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
   else
-    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride);
+    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
 }
 
 // Workgroups per sequence for `items` scored entries: enough resident waves
@@ -806,9 +820,9 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   float* bmax = reinterpret_cast<float*>((char*)ws + l.bmax_off);
   const int64_t nbk = (cap + block - 1) / block;
   const int MT = (H + 15) / 16;
-  dim3 grid(score_wgs(cap, B, kScoreWaves), (unsigned)B);
+  const int per_seq = (int)score_wgs(cap, B, kScoreWaves);
   if (cap > 0)
-    launch_score<false>(MT, grid, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
+    launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
                         H, scores, cap, bmax, nbk);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
@@ -854,9 +868,9 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   float* gmax = reinterpret_cast<float*>((char*)ws + l.gmax_off);
   const int64_t ngs = (pool_cap + kBlock - 1) / kBlock;
   const int MT = (H + 15) / 16;
-  dim3 grid(score_wgs(pool_cap, B, kScoreWavesPool), (unsigned)B);
+  const int per_seq = (int)score_wgs(pool_cap, B, kScoreWavesPool);
   if (pool_cap > 0)
-    launch_score<true>(MT, grid, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
+    launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
                        w, H, ps, pool_cap, gmax, ngs);
   if (hipGetLastError() != hipSuccess) return -1;
   // keys per thread: groups (<= 2048 -> 2), candidate positions (8 per selected group)
