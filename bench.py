@@ -69,7 +69,9 @@ def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa)
     pool = sum_pool * 68 + B * (n_blocks * 8 * 4 + 4) + B * (H_idx * 128 * 2 + H_idx * 4 + 4) + B * k * 4
     rows = B * (k + swa)
     attn = rows * 288 + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8
-    write = B * 512 * 2 + 512 * 128 * 4 + B * 356
+    # cache write: T tokens (latent, plus the gate when m > 1) pooled into T/m entries
+    T, m = (wl.write_tokens, wl.write_m) if wl.write_tokens else (B, 1)
+    write = T * 512 * 2 * (2 if m > 1 else 1) + 512 * 128 * 4 + (T // m) * 356
     return dict(write=write, index_full=full, index_pool=pool, attn=attn)
 
 
@@ -171,14 +173,22 @@ def main():
     n_idx = 1 + wl.n_reindex
     idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
     attn_q = [syn.attn_query(wl, j, dev) for j in range(step.n_attn)]
-    # the step's new tokens: one per sequence, written as ratio-1 entries into a staging area
-    wl_w = syn.Workload("append", wl.seed + 100, B=B, cap=1, H_idx=8, k=1, block=8, n_blocks=0,
-                        write_tokens=B, write_m=1)
-    new_lat, _, w_proj = syn.write_inputs(wl_w, dev)
-    staged = dict(main_codes=torch.empty(B, 256, dtype=torch.uint8, device=dev),
-                  main_scales=torch.empty(B, 32, dtype=torch.uint8, device=dev),
-                  idx_codes=torch.empty(B, 64, dtype=torch.uint8, device=dev),
-                  idx_scales=torch.empty(B, 4, dtype=torch.uint8, device=dev))
+    # The step's cache write: the workload's own write stage when it has one
+    # (T tokens pooled m at a time), otherwise one new token per sequence as
+    # ratio-1 entries.  Either way into a staging area.
+    if wl.write_tokens:
+        new_lat, new_gate, w_proj = syn.write_inputs(wl, dev)
+        w_T, w_m = wl.write_tokens, wl.write_m
+    else:
+        wl_w = syn.Workload("append", wl.seed + 100, B=B, cap=1, H_idx=8, k=1, block=8, n_blocks=0,
+                            write_tokens=B, write_m=1)
+        new_lat, _, w_proj = syn.write_inputs(wl_w, dev)
+        new_gate, w_T, w_m = None, B, 1
+    n_new = w_T // w_m
+    staged = dict(main_codes=torch.empty(n_new, 256, dtype=torch.uint8, device=dev),
+                  main_scales=torch.empty(n_new, 32, dtype=torch.uint8, device=dev),
+                  idx_codes=torch.empty(n_new, 64, dtype=torch.uint8, device=dev),
+                  idx_scales=torch.empty(n_new, 4, dtype=torch.uint8, device=dev))
     torch.cuda.synchronize()
 
     only = args.only
@@ -186,7 +196,7 @@ def main():
 
     # ---- the step's phases (every call reads/writes preallocated buffers)
     def ph_write():
-        K.cache_write(new_lat, None, 1, w_proj, fmt, out=staged)
+        K.cache_write(new_lat, new_gate, w_m, w_proj, fmt, out=staged)
 
     def ph_full():
         q, w = idx_qw[0]
@@ -205,7 +215,8 @@ def main():
         step.run_attention(attn_q)
 
     all_phases = [("write", ph_write), ("index_full", ph_full), ("index_pool", ph_pool), ("attn", ph_attn)]
-    phases = [(n, f) for n, f in all_phases if only is None or n == only]
+    calls = dict(write=1, index_full=1, index_pool=n_pool, attn=step.n_attn)
+    phases = [(n, f) for n, f in all_phases if (only is None or n == only) and calls[n] > 0]
     if only in ("index_pool", "attn"):
         ph_full()           # produce pool/top-k once
         if only == "attn":
@@ -259,7 +270,6 @@ def main():
     # ---- per-call times: each phase's graph replayed on its own, HIP events
     # on the launch stream around K replays
     per_call_us = {}
-    calls = dict(write=1, index_full=1, index_pool=n_pool, attn=step.n_attn)
     for n, g in g_phase.items():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g.replay()
@@ -309,7 +319,8 @@ def main():
         config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
                     topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,
                     layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
-                    main_scale=args.fmt.upper(), only=args.only),
+                    main_scale=args.fmt.upper(), only=args.only,
+                    cache_write=f"{w_T} tokens, m={w_m}"),
         attn_queries_per_s=B * step.n_attn / (ms_per_step * 1e-3),
         kernels=kernels, roofline=roofline,
     )

@@ -376,22 +376,22 @@ __device__ __forceinline__ void load_keys(KeyRegs<EPT>& K, const Src& src, int n
 // the candidate count: load_raw reads every slot below n_alloc (the array's
 // allocated length), finish_keys then turns slots below n into keys and the
 // rest into 0 (absent).
+// Slot j of a thread is base + 64 j (sel_index), so bounds are tested as
+// 64 j < n - base against one per-thread remainder: no per-slot index stays live.
 template <int NT, int EPT>
 __device__ __forceinline__ void load_raw(KeyRegs<EPT>& K, const float* p, int n_alloc) {
+  const int base = sel_index<NT, EPT>(0, 0);
+  const int rem = n_alloc - base;
+  const float* pb = p + base;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int i = sel_index<NT, EPT>(0, j);
-    K.r[j] = i < n_alloc ? __float_as_uint(p[i]) : 0x7FC00000u;
-  }
+  for (int j = 0; j < EPT; ++j) K.r[j] = 64 * j < rem ? __float_as_uint(pb[64 * j]) : 0x7FC00000u;
 }
 
 template <int NT, int EPT>
 __device__ __forceinline__ void finish_keys(KeyRegs<EPT>& K, int n) {
+  const int rem = n - sel_index<NT, EPT>(0, 0);
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int i = sel_index<NT, EPT>(0, j);
-    K.r[j] = i < n ? float_key(__uint_as_float(K.r[j])) : 0u;
-  }
+  for (int j = 0; j < EPT; ++j) K.r[j] = 64 * j < rem ? float_key(__uint_as_float(K.r[j])) : 0u;
 }
 
 // Sum of the per-wave values w[0 .. wave-1] (wave < 16): lane v < wave reads
@@ -449,7 +449,7 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* h, SelScratch&
 // (checked exactly), the radix search only histograms keys in [T0, max];
 // otherwise it searches the full range.  Either way the result is exact.
 template <int NT, int EPT, bool PREF, class Src, class Emit>
-__device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
+__device__ __forceinline__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
                            Emit emit) {
   constexpr int NW = NT / 64;
   static_assert(NW <= 16, "per-wave partials hold at most 16 waves");
@@ -546,6 +546,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     for (int j = 0; j < E; ++j) {
       const uint32_t kk = KEY(j);
       if (kk >= lo && kk <= hi) atomicAdd(&h[(kk - lo) >> shift], 1u);
+      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound register pressure at large E
     }
     uint32_t* hn = sh.hist[buf ^ 1];
     for (int i = t; i < 2048; i += NT) hn[i] = 0u;  // the next pass's buffer
@@ -598,6 +599,7 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     out_pref = G + min(eq_pref, need_eq);
   }
   const uint64_t below = (1ull << lane) - 1ull;
+  const int ibase = sel_index<NT, EPT>(n, 0);  // slot j holds candidate ibase + 64 j
   uint32_t r_sel = out_pref, r_eq = eq_pref;
 #pragma unroll UNR
   for (int j = 0; j < E; ++j) {
@@ -611,9 +613,10 @@ __device__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, 
     }
     const uint64_t selb = __ballot(sel);
     if (selb) {  // wave-uniform
-      if (sel) emit(sel_index<NT, EPT>(n, j), (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
+      if (sel) emit(ibase + 64 * j, (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
       r_sel += (uint32_t)__popcll(selb);
     }
+    if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   return (int)target;
@@ -835,6 +838,8 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
     if (kbig) CSA2_SELFULL(16, 16); else CSA2_SELFULL(16, 4);
   } else if (nbk <= 32 * 1024) {
     if (kbig) CSA2_SELFULL(32, 16); else CSA2_SELFULL(32, 4);
+  } else if (nbk <= 64 * 1024) {
+    if (kbig) CSA2_SELFULL(64, 16); else CSA2_SELFULL(64, 4);
   } else {
     if (kbig) CSA2_SELFULL(0, 16); else CSA2_SELFULL(0, 4);
   }
