@@ -108,7 +108,10 @@ int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, u
 // Grid (entry tiles of 4, 4 column tiles of 32).  Every workgroup pools and
 // normalises its 4 entries (one wave per entry); the column-tile-0 workgroup
 // writes the main-KV FP4.  Each workgroup then projects onto its 32
-// indexer-K columns -- exactly one E8M0 group -- and quantises them.
+// indexer-K columns -- exactly one E8M0 group -- and quantises them.  (16
+// entries per workgroup, which reads each projection weight for 4x the
+// entries, measured slower on 4096-entry writes: the longer chain per
+// workgroup costs more than the weight traffic it saves.)
 constexpr int kWriteEntries = 4;   // entries per workgroup (one per wave)
 constexpr int kWriteColTiles = 4;
 
@@ -127,14 +130,21 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   constexpr int kEpw = kWriteEntries / 4;  // entries per wave
   static_assert(kWriteEntries % 4 == 0, "whole entries per wave");
 
-  // ratio 1: every latent load of the wave is issued before any arithmetic
-  uint4 xpre[kEpw];
-  if (m == 1) {
+  // ratio 1 and 2: every latent (and gate) load of the wave is issued before
+  // any arithmetic, so the wave's entries cost one memory round trip
+  uint4 xpre[kEpw][2], gpre[kEpw][2];
+  if (m <= 2) {
 #pragma unroll
     for (int j = 0; j < kEpw; ++j) {
       const int64_t e = e0 + wave + 4 * j;
-      xpre[j] = e < n_entries ? *reinterpret_cast<const uint4*>(latent + e * 512 + 8 * lane)
-                              : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool ok = e < n_entries && t < m;
+        xpre[j][t] = ok ? *reinterpret_cast<const uint4*>(latent + (e * m + t) * 512 + 8 * lane)
+                        : make_uint4(0u, 0u, 0u, 0u);
+        gpre[j][t] = ok && m > 1 ? *reinterpret_cast<const uint4*>(gate + (e * m + t) * 512 + 8 * lane)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   }
 #pragma unroll
@@ -148,9 +158,33 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     }
     float pooled[8];
     if (m == 1) {
-      const uint32_t xw[4] = {xpre[j].x, xpre[j].y, xpre[j].z, xpre[j].w};
+      const uint32_t xw[4] = {xpre[j][0].x, xpre[j][0].y, xpre[j][0].z, xpre[j][0].w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) pooled[c] = bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+    } else if (m == 2) {
+      // the same operations, in the same order, as the general loop below
+      float gmax[8], num[8], den[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { gmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t gw[4] = {gpre[j][t].x, gpre[j][t].y, gpre[j][t].z, gpre[j][t].w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) gmax[c] = fmaxf(gmax[c], bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t gw[4] = {gpre[j][t].x, gpre[j][t].y, gpre[j][t].z, gpre[j][t].w};
+        const uint32_t xw[4] = {xpre[j][t].x, xpre[j][t].y, xpre[j][t].z, xpre[j][t].w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float ex = expf(bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu) - gmax[c]);
+          num[c] += ex * bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+          den[c] += ex;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) pooled[c] = num[c] / den[c];
     } else {
       float gmax[8], num[8], den[8];
 #pragma unroll

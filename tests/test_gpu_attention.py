@@ -216,10 +216,11 @@ def _certified_code_mismatch(vals, ref_codes, ref_scales, got_codes, got_scales,
     return n_bad
 
 
-@pytest.mark.parametrize("m,fmt,gamma", [(1, 0, False), (2, 1, False), (2, 0, True), (4, 1, True)])
-def test_cache_write_parity(m, fmt, gamma):
-    say(f"cache write m={m} fmt={fmt} gamma={gamma}")
-    wl = syn.small("w", 31 + m, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=1024 * m, write_m=m)
+@pytest.mark.parametrize("m,fmt,gamma,n", [(1, 0, False, 1024), (2, 1, False, 1024), (2, 0, True, 1024),
+                                           (4, 1, True, 1024), (1, 0, False, 37), (2, 1, True, 37)])
+def test_cache_write_parity(m, fmt, gamma, n):
+    say(f"cache write m={m} fmt={fmt} gamma={gamma} entries={n}")
+    wl = syn.small("w", 31 + m, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=n * m, write_m=m)
     lat, gate, w = syn.write_inputs(wl, DEV)
     gm = (torch.linspace(0.5, 1.5, 512, device=DEV) if gamma else None)
     got = K.cache_write(lat, gate, m, w, fmt, gamma=gm, eps=1e-6)
@@ -232,6 +233,10 @@ def test_cache_write_parity(m, fmt, gamma):
     nk = _certified_code_mismatch(ref["k"], ref["idx_codes"], ref["idx_scales"], g["idx_codes"],
                                   g["idx_scales"], 32, 0)
     say(f"  certified mismatches: main {nm}, indexer {nk}")
+    if n < 100:
+        assert nm + nk <= 2
+        return
     # nearly all bytes are identical
     assert (g["main_codes"] == ref["main_codes"]).mean() > 0.999
     assert (g["idx_codes"] == ref["idx_codes"]).mean() > 0.999
+
