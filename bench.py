@@ -48,6 +48,8 @@ def parse():
                     choices=["tiny", "full128", "step128", "write1m", "stress"])
     ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
                     help="main-KV scale byte format")
+    ap.add_argument("--index-q", default="bf16", choices=["bf16", "fp4"],
+                    help="indexer query format: bf16, or MX-FP4 (quantised before the timed region)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,12 +63,13 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa):
+def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa, q_fp4=False):
     """Bytes each call must move at minimum (inputs read once, outputs written once)."""
     sum_len = int(sum(lengths))
     sum_pool = int(sum(pool_len))
-    full = sum_len * 68 + B * (H_idx * 128 * 2 + H_idx * 4 + 4) + B * (k * 4 + n_blocks * 8 * 4 + 4)
-    pool = sum_pool * 68 + B * (n_blocks * 8 * 4 + 4) + B * (H_idx * 128 * 2 + H_idx * 4 + 4) + B * k * 4
+    qb = H_idx * (68 if q_fp4 else 256)        # one indexer query head: FP4 codes + scales, or bf16
+    full = sum_len * 68 + B * (qb + H_idx * 4 + 4) + B * (k * 4 + n_blocks * 8 * 4 + 4)
+    pool = sum_pool * 68 + B * (n_blocks * 8 * 4 + 4) + B * (qb + H_idx * 4 + 4) + B * k * 4
     rows = B * (k + swa)
     attn = rows * 288 + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8
     # cache write: T tokens (latent, plus the gate when m > 1) pooled into T/m entries
@@ -172,6 +175,12 @@ def main():
                       reuse_per_index=wl.reuse_per_index, main_fmt=fmt)
     n_idx = 1 + wl.n_reindex
     idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
+    if args.index_q == "fp4":
+        # the indexer queries in MX-FP4 (E2M1 codes, E8M0 per 32 dims), quantised once here
+        def fp4q(q):
+            c, s = K.quantize_fp4(q.view(torch.bfloat16).float().reshape(-1, 128).contiguous(), 32, K.E8M0)
+            return c.view(B, wl.H_idx, 64), s.view(B, wl.H_idx, 4)
+        idx_qw = [(fp4q(q), w) for q, w in idx_qw]
     attn_q = [syn.attn_query(wl, j, dev) for j in range(step.n_attn)]
     # The step's cache write: the workload's own write stage when it has one
     # (T tokens pooled m at a time), otherwise one new token per sequence as
@@ -286,7 +295,8 @@ def main():
         one_step()
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-    nbytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128)
+    nbytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128,
+                              q_fp4=args.index_q == "fp4")
     kernels = {}
     for name in per_call_us:
         us = per_call_us[name]
@@ -319,7 +329,7 @@ def main():
         config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
                     topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,
                     layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
-                    main_scale=args.fmt.upper(), only=args.only,
+                    main_scale=args.fmt.upper(), index_query=args.index_q, only=args.only,
                     cache_write=f"{w_T} tokens, m={w_m}"),
         attn_queries_per_s=B * step.n_attn / (ms_per_step * 1e-3),
         kernels=kernels, roofline=roofline,

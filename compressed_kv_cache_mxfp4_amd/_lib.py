@@ -47,6 +47,8 @@ def lib():
     L.csa2_index_pool_workspace.restype = sz
     L.csa2_index_pool_workspace.argtypes = [i32, i32, i32]
     L.csa2_index_pool.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, i32, P, P, P, sz, P]
+    L.csa2_index_full_fp4q.argtypes = [P, P, i64, P, i32, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.csa2_index_pool_fp4q.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, P, i32, i32, P, P, P, sz, P]
     L.csa2_attn_workspace.restype = sz
     L.csa2_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
@@ -164,24 +166,38 @@ def cache_write(latent, gate, m: int, w_idx, main_fmt: int, gamma=None, eps: flo
 
 
 # -------------------------------------------------------------------- indexer
+def _index_query(q, dev, B):
+    """bf16 queries [B][H][128] -> (H, q bits, None, None); FP4 queries given as
+    (codes u8 [B][H][64], E8M0 scales u8 [B][H][4]) -> (H, None, codes, scales)."""
+    if isinstance(q, (tuple, list)):
+        qc, qs = q
+        H = qc.shape[1]
+        _req(qc, "q codes", torch.uint8, dev, (B, H, 64))
+        _req(qs, "q scales", torch.uint8, dev, (B, H, 4))
+        return H, None, qc, qs
+    q = _bits16(q)
+    H = q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    return H, q, None, None
+
+
 def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int = 2048,
                block: int = 8, return_scores: bool = False, out=None, _ws=None):
     """Full-mode indexer over B sequences.
 
     idx_codes u8 [B][cap][64], idx_scales u8 [B][cap][4], lengths int32 [B],
-    q bf16/int16 [B][H][128], w fp32 [B][H].
+    q bf16/int16 [B][H][128] -- or an FP4 query (codes u8 [B][H][64], E8M0
+    scales u8 [B][H][4]), which selects csa2_index_full_fp4q -- and w fp32 [B][H].
     Returns (topk int32 [B][k], pool int32 [B][n_blocks*block], pool_len int32 [B]
     [, scores fp32 [B][cap]]).
     """
-    q = _bits16(q)
     _req(idx_codes, "idx_codes", torch.uint8)
     dev = idx_codes.device
     B, cap = idx_codes.shape[0], idx_codes.shape[1]
     _req(idx_codes, "idx_codes", torch.uint8, dev, (B, cap, 64))
     _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
     _req(lengths, "lengths", torch.int32, dev, (B,))
-    H = q.shape[1]
-    _req(q, "q", torch.int16, dev, (B, H, 128))
+    H, q, qc, qs = _index_query(q, dev, B)
     _req(w, "w", torch.float32, dev, (B, H))
     out = out or {}
     topk = out.get("topk")
@@ -198,10 +214,17 @@ def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int
         scores = torch.empty(B, cap, dtype=torch.float32, device=dev)
     wsb = lib().csa2_index_full_workspace(B, cap, k, block, n_blocks)
     ws = _ws if _ws is not None else workspace(wsb, dev)
-    _check(lib().csa2_index_full(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, _ptr(q),
-                                 _ptr(w), H, k, block, n_blocks, _ptr(topk), _ptr(pool),
-                                 _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
-           "csa2_index_full")
+    if qc is None:
+        _check(lib().csa2_index_full(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, _ptr(q),
+                                     _ptr(w), H, k, block, n_blocks, _ptr(topk), _ptr(pool),
+                                     _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
+               "csa2_index_full")
+    else:
+        _check(lib().csa2_index_full_fp4q(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B,
+                                          _ptr(qc), _ptr(qs), _ptr(w), H, k, block, n_blocks, _ptr(topk),
+                                          _ptr(pool), _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(),
+                                          _stream(dev)),
+               "csa2_index_full_fp4q")
     pool = pool[:, : n_blocks * block]
     if return_scores:
         return topk, pool, pool_len, scores
@@ -210,8 +233,8 @@ def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int
 
 def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 512,
                return_scores: bool = False, out=None, _ws=None):
-    """Reindex mode: rescore pool [B][pool_cap] with (q, w), top-k per sequence."""
-    q = _bits16(q)
+    """Reindex mode: rescore pool [B][pool_cap] with (q, w), top-k per sequence.
+    q: bf16 [B][H][128], or an FP4 query (codes, scales) as in index_full."""
     _req(idx_codes, "idx_codes", torch.uint8)
     dev = idx_codes.device
     B, cap = idx_codes.shape[0], idx_codes.shape[1]
@@ -220,8 +243,7 @@ def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 51
     pool_cap = pool.shape[1]
     _req(pool, "pool", torch.int32, dev, (B, pool_cap))
     _req(pool_len, "pool_len", torch.int32, dev, (B,))
-    H = q.shape[1]
-    _req(q, "q", torch.int16, dev, (B, H, 128))
+    H, q, qc, qs = _index_query(q, dev, B)
     _req(w, "w", torch.float32, dev, (B, H))
     out = out or {}
     topk = out.get("topk")
@@ -232,10 +254,16 @@ def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 51
         ps = torch.empty(B, pool_cap, dtype=torch.float32, device=dev)
     wsb = lib().csa2_index_pool_workspace(B, pool_cap, k)
     ws = _ws if _ws is not None else workspace(wsb, dev, "pool")
-    _check(lib().csa2_index_pool(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B,
-                                 _ptr(pool), _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, k,
-                                 _ptr(topk), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)),
-           "csa2_index_pool")
+    if qc is None:
+        _check(lib().csa2_index_pool(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B,
+                                     _ptr(pool), _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, k,
+                                     _ptr(topk), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)),
+               "csa2_index_pool")
+    else:
+        _check(lib().csa2_index_pool_fp4q(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B,
+                                          _ptr(pool), _ptr(pool_len), pool_cap, _ptr(qc), _ptr(qs), _ptr(w),
+                                          H, k, _ptr(topk), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)),
+               "csa2_index_pool_fp4q")
     return (topk, ps) if return_scores else topk
 
 

@@ -23,8 +23,11 @@ struct IndexFullWs {
 };
 IndexFullWs index_full_ws_layout(int B, int64_t cap, int block);
 
+// q4c/q4s: FP4 queries (codes [B][H][64], E8M0 scales [B][H][4]); when
+// q4c is NULL the bf16 queries q are used.
 int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
-                      const int32_t* len, int B, const uint16_t* q, const float* w, int H, int k,
+                      const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
+                      const uint8_t* q4s, const float* w, int H, int k,
                       int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
                       float* scores_opt, void* ws, hipStream_t st);
 
@@ -32,7 +35,8 @@ size_t index_pool_ws_bytes(int B, int pool_cap);
 
 int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
                       const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
-                      int pool_cap, const uint16_t* q, const float* w, int H, int k,
+                      int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
+                      const float* w, int H, int k,
                       int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st);
 
 size_t attn_ws_bytes(int B, int H, int k, int swa_cap);

@@ -128,6 +128,43 @@ __device__ __forceinline__ float score_compute(const ScoreStage& S, const bf16x8
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// FP4 query (both operands MX-FP4, E8M0 per 32 dims): one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per (tile, 16 heads) over all 128 dims.
+// Lane (g, n) of B is entry 16t+n, dims 32g..32g+31 -- the stage's 16-byte
+// code load as it is -- with that block's scale byte; lane (g, i) of A is
+// head 16mt+i over the same dims.  D has the bf16 path's layout, so the
+// epilogue is the same.
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+template <int MT>
+__device__ __forceinline__ float score_compute_q4(const ScoreStage& S, const uint4 (&Aq)[MT],
+                                                  const uint32_t (&Asc)[MT], const float (&wr)[MT][4]) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const intx8 bv = {(int)S.cw[t].x, (int)S.cw[t].y, (int)S.cw[t].z, (int)S.cw[t].w, 0, 0, 0, 0};
+    floatx4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const intx8 av = {(int)Aq[mt].x, (int)Aq[mt].y, (int)Aq[mt].z, (int)Aq[mt].w, 0, 0, 0, 0};
+      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          av, bv, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, (int)Asc[mt], 0, (int)S.sb[t]);
+    }
+    float p = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p += wr[mt][i] * __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+    part[t] = p;
+  }
+  const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+  const float s02 = __uint_as_float(a02[0]) + __uint_as_float(a02[1]);
+  const float s13 = __uint_as_float(a13[0]) + __uint_as_float(a13[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float max8_lanes(float v) {
   v = fmaxf(v, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v), 0u)));   // xor 1
   v = fmaxf(v, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(v), 0u)));   // xor 2
@@ -143,14 +180,15 @@ __device__ __forceinline__ float max8_lanes(float v) {
 // are read one ring step before its codes.
 constexpr int kScoreStages = 2;
 
-template <int MT, bool GATHER, int NS = kScoreStages, int OCC = 2, bool WLDS = false>
+template <int MT, bool GATHER, bool Q4 = false, int NS = kScoreStages, int OCC = 2, bool WLDS = false>
 __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int64_t cap,
     const int32_t* __restrict__ len, const int32_t* __restrict__ pool,
     const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
     const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
-    float* __restrict__ bmax, int64_t bmax_stride, int B, int per_seq) {
-  __shared__ __align__(16) uint16_t qs[64 * 128];
+    float* __restrict__ bmax, int64_t bmax_stride, int B, int per_seq,
+    const uint8_t* __restrict__ q4_codes, const uint8_t* __restrict__ q4_scales) {
+  __shared__ __align__(16) uint16_t qs[Q4 ? 8 : 64 * 128];
   __shared__ float ws[64];
   // Grid: per_seq workgroups for each of B sequences, in one dimension.  When
   // B is a multiple of 8, sequence b's workgroups all get ids congruent to
@@ -202,8 +240,20 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     for (int u = 0; u < NS - 1; ++u) score_load(stg[u], rows[u], codes_b, scales_b, g);
   }
 
-  // Query heads (zero beyond H) and head weights, staged once per workgroup.
-  {
+  // Query heads (zero beyond H; bf16 queries only -- FP4 queries are read
+  // straight into their MFMA operands below) and head weights, staged once
+  // per workgroup.
+  uint4 Aq[MT];
+  uint32_t Asc[MT];
+  if constexpr (Q4) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + n;
+      Aq[mt] = h < H ? *reinterpret_cast<const uint4*>(q4_codes + ((int64_t)b * H + h) * 64 + 16 * g)
+                     : make_uint4(0u, 0u, 0u, 0u);
+      Asc[mt] = h < H ? q4_scales[((int64_t)b * H + h) * 4 + g] : 127u;
+    }
+  } else {
     const int h = threadIdx.x >> 2, part = threadIdx.x & 3;  // 64 heads x 4 pieces of 64 B
     uint4 v[4];
 #pragma unroll
@@ -212,8 +262,8 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
                    : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&qs[h * 128 + 32 * part + 8 * j]) = v[j];
-    if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
   }
+  if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
   int64_t L = len[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int64_t N = L;
@@ -223,14 +273,16 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
   }
   __syncthreads();
   if (base0 >= N) return;  // wave-uniform; no barrier follows
-  // A operand: lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
-  bf16x8 A[MT][4];
+  // A operand (bf16 queries): lane (g, m) holds head 16*mt+m, dims 32g+8ks .. +7.
+  bf16x8 A[Q4 ? 1 : MT][4];
   float wr[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    if constexpr (!Q4) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      A[mt][ks] = *reinterpret_cast<const bf16x8*>(&qs[(16 * mt + n) * 128 + 32 * g + 8 * ks]);
+      for (int ks = 0; ks < 4; ++ks)
+        A[mt][ks] = *reinterpret_cast<const bf16x8*>(&qs[(16 * mt + n) * 128 + 32 * g + 8 * ks]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[mt][i] = ws[16 * mt + 4 * g + i];
   }
@@ -278,7 +330,9 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
             wr[mt][0] = v.x; wr[mt][1] = v.y; wr[mt][2] = v.z; wr[mt][3] = v.w;
           }
         }
-        const float sc = score_compute<MT>(stg[u], A, wr);
+        float sc;
+        if constexpr (Q4) sc = score_compute_q4<MT>(stg[u], Aq, Asc, wr);
+        else sc = score_compute<MT>(stg[u], A, wr);
         const int64_t it = bs + lane;
         const bool mine_ok = (ok >> g) & 1u;
         if (it < N) scores_b[it] = mine_ok ? sc : __uint_as_float(0x7FC00000u);
@@ -788,18 +842,23 @@ IndexFullWs index_full_ws_layout(int B, int64_t cap, int block) {
   return l;
 }
 
+// q4_codes == nullptr: bf16 queries `q`; otherwise FP4 queries (codes, scales).
 template <bool GATHER>
 static void launch_score(int MT, int per_seq, int B, hipStream_t st, const uint8_t* ic, const uint8_t* is,
                          int64_t cap, const int32_t* len, const int32_t* pool,
-                         const int32_t* pool_len, int pool_cap, const uint16_t* q, const float* w,
-                         int H, float* scores, int64_t sstride, float* bmax, int64_t bstride) {
+                         const int32_t* pool_len, int pool_cap, const uint16_t* q, const uint8_t* q4c,
+                         const uint8_t* q4s, const float* w, int H, float* scores, int64_t sstride,
+                         float* bmax, int64_t bstride) {
   const dim3 grid((unsigned)per_seq * (unsigned)B);
-  if (MT == 1)
-    score_kernel<1, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
-  else if (MT == 2)
-    score_kernel<2, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
-  else
-    score_kernel<4, GATHER><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, scores, sstride, bmax, bstride, B, per_seq);
+#define CSA2_SCORE(MT_, Q4_) \
+  score_kernel<MT_, GATHER, Q4_><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, \
+                                                                 scores, sstride, bmax, bstride, B, per_seq, q4c, q4s)
+  if (q4c) {
+    if (MT == 1) CSA2_SCORE(1, true); else if (MT == 2) CSA2_SCORE(2, true); else CSA2_SCORE(4, true);
+  } else {
+    if (MT == 1) CSA2_SCORE(1, false); else if (MT == 2) CSA2_SCORE(2, false); else CSA2_SCORE(4, false);
+  }
+#undef CSA2_SCORE
 }
 
 // Workgroups per sequence for `items` scored entries: enough resident waves
@@ -814,7 +873,8 @@ static unsigned score_wgs(int64_t items, int B, int target_waves) {
 }
 
 int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
-                      const int32_t* len, int B, const uint16_t* q, const float* w, int H, int k,
+                      const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
+                      const uint8_t* q4s, const float* w, int H, int k,
                       int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
                       float* scores_opt, void* ws, hipStream_t st) {
   if (B == 0) return 0;
@@ -825,8 +885,8 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   const int MT = (H + 15) / 16;
   const int per_seq = (int)score_wgs(cap, B, kScoreWaves);
   if (cap > 0)
-    launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, w,
-                        H, scores, cap, bmax, nbk);
+    launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, q4c,
+                        q4s, w, H, scores, cap, bmax, nbk);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
   // keys per thread: all blocks (EB), the pool blocks (2), candidate positions (EP)
@@ -865,7 +925,8 @@ size_t index_pool_ws_bytes(int B, int pool_cap) { return index_pool_ws_layout(B,
 
 int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
                       const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
-                      int pool_cap, const uint16_t* q, const float* w, int H, int k,
+                      int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
+                      const float* w, int H, int k,
                       int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st) {
   if (B == 0) return 0;
   const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
@@ -875,7 +936,7 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   const int MT = (H + 15) / 16;
   const int per_seq = (int)score_wgs(pool_cap, B, kScoreWavesPool);
   if (pool_cap > 0)
-    launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q,
+    launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q, q4c, q4s,
                        w, H, ps, pool_cap, gmax, ngs);
   if (hipGetLastError() != hipSuccess) return -1;
   // keys per thread: groups (<= 2048 -> 2), candidate positions (8 per selected group)

@@ -191,6 +191,36 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                     float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_index_full_fp4q, csa2_index_pool_fp4q -- the two indexer calls with an
+ * FP4 indexer query [syt-nju.github.io, "为什么读输入只激活 8B", section
+ * FP4 主 KV 缓存: the indexer's query and keys were already FP4 through
+ * quantisation-aware training before the main KV was].  Both score operands
+ * are then MX-FP4 (E2M1 codes, one E8M0 scale per 32 dims), and the product
+ * runs on gfx950's scaled FP4 matrix instruction without dequantising.
+ *   q_codes  : u8 [B][H][64] E2M1 codes of the 128-dim queries (element 2i
+ *              in the low nibble of byte i), 16-byte aligned;
+ *   q_scales : u8 [B][H][4] E8M0 scale bytes, one per 32 dims
+ *              (csa2_quantize_fp4 with group 32 and E8M0 produces both).
+ * The score is the same formula with q = the dequantised query:
+ *   score[b][p] = sum_h w[b][h] * max(0, deq(q[b][h]) . deq(idx K[b][p])).
+ * Every other argument, the workspace, the outputs, the selection rules and
+ * the status codes are those of csa2_index_full / csa2_index_pool.  This is
+ * a numerics variant: the query is rounded to FP4 by the caller.
+ */
+int csa2_index_full_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                         const int32_t* len, int32_t B, const uint8_t* q_codes,
+                         const uint8_t* q_scales, const float* w, int32_t H, int32_t k,
+                         int32_t block, int32_t n_blocks, int32_t* topk, int32_t* pool,
+                         int32_t* pool_len, float* scores_opt, void* ws, size_t ws_bytes,
+                         void* stream);
+int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                         const int32_t* len, int32_t B, const int32_t* pool,
+                         const int32_t* pool_len, int32_t pool_cap, const uint8_t* q_codes,
+                         const uint8_t* q_scales, const float* w, int32_t H, int32_t k,
+                         int32_t* topk, float* pool_scores_opt, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
  * csa2_sparse_attn_decode -- core attention of one CSA2 layer for one decode
  * query per sequence: the selected main-KV entries concatenated with the
  * sliding-window entries, attended by the layer's own query; FP4 is storage

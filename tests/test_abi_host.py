@@ -109,6 +109,47 @@ def test_index_full_validation(lib):
     assert call(B=0) == CSA2_OK
 
 
+def test_index_fp4q_validation(lib):
+    """The FP4-query indexer calls validate like the bf16 ones, plus their two
+    query planes (codes 16-byte aligned, scales any alignment)."""
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    f = lib.csa2_index_full_fp4q
+    f.argtypes = [P, P, i64, P, i32, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    ok = dict(ic=FAKE, isc=FAKE, cap=4096, len=FAKE, B=2, qc=FAKE, qs=FAKE_ODD, w=FAKE, H=64, k=512, block=8,
+              nb=2048, topk=FAKE, pool=FAKE, pl=FAKE, sc=None, ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ic"], a["isc"], a["cap"], a["len"], a["B"], a["qc"], a["qs"], a["w"], a["H"], a["k"],
+                 a["block"], a["nb"], a["topk"], a["pool"], a["pl"], a["sc"], a["ws"], a["wsb"], None)
+
+    assert call(H=48) == ERR_UNSUP
+    assert call(block=16) == ERR_UNSUP
+    assert call(k=0) == ERR_SHAPE
+    assert call(qc=None) == ERR_NULL
+    assert call(qs=None) == ERR_NULL
+    assert call(qc=FAKE_ODD) == ERR_ALIGN
+    assert call(ws=None) == ERR_WS
+    assert call(B=0) == CSA2_OK
+    g = lib.csa2_index_pool_fp4q
+    g.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, P, i32, i32, P, P, P, sz, P]
+    base = [FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE_ODD, FAKE, 64, 512, FAKE, None, FAKE,
+            1 << 30, None]
+
+    def callp(i, v):
+        args = list(base)
+        args[i] = v
+        return g(*args)
+
+    assert callp(7, 20000) == ERR_SHAPE   # pool_cap
+    assert callp(11, 12) == ERR_UNSUP     # heads
+    assert callp(8, None) == ERR_NULL     # q codes
+    assert callp(9, None) == ERR_NULL     # q scales
+    assert callp(8, FAKE_ODD) == ERR_ALIGN
+    assert callp(16, 16) == ERR_WS
+    assert callp(4, 0) == CSA2_OK
+
+
 def test_index_pool_and_attention_validation(lib):
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     f = lib.csa2_index_pool

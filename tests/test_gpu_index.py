@@ -216,3 +216,85 @@ def test_index_pool_masks_invalid_entries():
                                 q.cpu().numpy()[0], w.cpu().numpy()[0], 8)
     score_close(ps, rps)
     assert np.array_equal(t.cpu().numpy()[0], rt)
+
+
+# ------------------------------------------------------------ FP4 indexer query
+# The query quantised to MX-FP4 (E2M1, E8M0 per 32 dims) by csa2_quantize_fp4;
+# the oracle quantises the same float query itself (bytes must agree), and
+# its dequantised values -- exactly representable in bf16 -- go into the
+# unchanged oracle scorer.
+def _fp4_query(q_bits):
+    qf = q_bits.view(torch.bfloat16).float()
+    B, H, _ = qf.shape
+    c, s = K.quantize_fp4(qf.reshape(B * H, 128).contiguous(), 32, K.E8M0)
+    return qf, c.view(B, H, 64), s.view(B, H, 4)
+
+
+def _oracle_fp4_query_bits(qf_b, qc_b, qs_b):
+    rc, rs = oracle.quantize(qf_b, 32, oracle.E8M0)
+    assert np.array_equal(rc, qc_b) and np.array_equal(rs, qs_b), "FP4 query bytes differ from the oracle's"
+    v = oracle.dequantize(rc, rs, 32, oracle.E8M0).astype(np.float32)
+    u = v.view(np.uint32)
+    assert ((u & 0xFFFF) == 0).all(), "a dequantised FP4 query value is not a bf16 value"
+    return (u >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("H", [8, 16, 64])
+def test_index_full_fp4_query_matches_oracle(H):
+    wl = syn.small("f4", 61 + H, B=3, cap=20000, H_idx=H, k=512, n_blocks=512)
+    say(f"index_full FP4 query, H={H}")
+    cache = build_gpu_cache(wl, 0)
+    lens = [20000, 19993, 7001]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = syn.index_query(wl, 0, DEV)
+    w = syn.index_weights(wl, 0, DEV)
+    qf, qc, qs = _fp4_query(q)
+    topk, pool, pool_len, scores = K.index_full(cache["idx_codes"], cache["idx_scales"], lt, (qc, qs), w,
+                                                k=512, n_blocks=512, return_scores=True)
+    torch.cuda.synchronize()
+    topk, pool, pool_len, scores = (t.cpu().numpy() for t in (topk, pool, pool_len, scores))
+    qfn, qcn, qsn, wn = qf.cpu().numpy(), qc.cpu().numpy(), qs.cpu().numpy(), w.cpu().numpy()
+    certified = 0
+    for b, L in enumerate(lens):
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        qb = _oracle_fp4_query_bits(qfn[b], qcn[b], qsn[b])
+        rt, rp, rpl, rs = oracle.index_full(ref["idx_codes"][:L], ref["idx_scales"][:L], L, qb, wn[b], 512, 8, 512)
+        gs = scores[b, :L]
+        score_close(gs, rs)
+        assert np.array_equal(topk[b], brute_topk(gs, 512))
+        bp, bpl, _ = brute_pool(gs, 512)
+        assert pool_len[b] == bpl == rpl and np.array_equal(pool[b], bp)
+        certified += certify_topk(topk[b], rt, rs, 512)
+    say(f"  certified near-ties: {certified}")
+
+
+def test_index_pool_fp4_query_matches_oracle_and_bf16_selection_rules():
+    wl = syn.small("p4", 71, B=2, cap=30000, H_idx=64, k=512, n_blocks=1024, n_reindex=1)
+    say("index_pool FP4 query")
+    cache = build_gpu_cache(wl, 0)
+    lens = [30000, 12345]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q0, w0 = syn.index_query(wl, 0, DEV), syn.index_weights(wl, 0, DEV)
+    _, pool, pool_len = K.index_full(cache["idx_codes"], cache["idx_scales"], lt, q0, w0, k=512, n_blocks=1024)
+    q1, w1 = syn.index_query(wl, 1, DEV), syn.index_weights(wl, 1, DEV)
+    qf, qc, qs = _fp4_query(q1)
+    # masked entries: one invalid position per sequence
+    pool[0, 5] = -1
+    pool[1, 9] = 40000
+    t, ps = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool, pool_len, (qc, qs), w1, k=512,
+                         return_scores=True)
+    torch.cuda.synchronize()
+    t, ps, pooln, pln = t.cpu().numpy(), ps.cpu().numpy(), pool.cpu().numpy(), pool_len.cpu().numpy()
+    for b, L in enumerate(lens):
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        qb = _oracle_fp4_query_bits(qf.cpu().numpy()[b], qc.cpu().numpy()[b], qs.cpu().numpy()[b])
+        n = int(pln[b])
+        rt, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], L, pooln[b], n, qb, w1.cpu().numpy()[b], 512)
+        score_close(ps[b, :n], rps)
+        assert np.array_equal(t[b], brute_topk(ps[b, :n], 512, pooln[b, :n]))
+        pos_scores = {int(p): float(s) for p, s in zip(pooln[b, :n], rps) if not np.isnan(s)}
+        diff = set(t[b].tolist()) ^ set(rt.tolist())
+        kth = np.sort(rps[~np.isnan(rps)])[::-1][511]
+        for p in diff:
+            if p >= 0:
+                assert abs(pos_scores[p] - kth) <= 2e-5 * abs(kth) + 1e-7 * np.nanmax(np.abs(rps))
