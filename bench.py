@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="instead of the benchmark, run a plain device copy of this many MB "
                          "(to calibrate HBM byte counters) and exit")
+    ap.add_argument("--attn-sweep", default=None, metavar="B1,B2,...",
+                    help="instead of the step, time one sparse-attention call per batch size "
+                         "(64 heads x 512 dims over 512 selected + 128 window rows, 32,768-entry "
+                         "caches) and print one JSON line with the sweep")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     return ap.parse_args()
@@ -76,6 +80,64 @@ def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa,
     T, m = (wl.write_tokens, wl.write_m) if wl.write_tokens else (B, 1)
     write = T * 512 * 2 * (2 if m > 1 else 1) + 512 * 128 * 4 + (T // m) * 356
     return dict(write=write, index_full=full, index_pool=pool, attn=attn)
+
+
+def attn_sweep(batches, fmt_name, steps):
+    """Sparse-attention decode call at several batch sizes: where the kernel
+    stops being latency-bound.  One seeded 32,768-entry cache per sequence,
+    512 distinct random positions selected, the last 128 entries as the window."""
+    import torch
+    import csa2_synth as syn
+    import compressed_kv_cache_mxfp4_amd as K
+    dev = torch.device("cuda:0")
+    fmt = K.E8M0 if fmt_name == "e8m0" else K.E4M3
+    cap, k, swa = 32768, 512, 128
+    L = K.lib()
+    rows = []
+    for B in batches:
+        wl = syn.Workload("attn_sweep", 5, B=B, cap=cap, H_idx=8, k=k, block=8, n_blocks=0)
+        codes = torch.empty(B, cap, 256, dtype=torch.uint8, device=dev)
+        scales = torch.empty(B, cap, 32, dtype=torch.uint8, device=dev)
+        for b in range(B):
+            K.quantize_fp4(syn.main_values(wl, b, dev), 16, fmt, codes[b], scales[b])
+        topk = torch.stack([torch.sort(syn.randperm(cap, wl.seed, "sweep_topk", b)[:k]).values
+                            for b in range(B)]).to(torch.int32).to(dev)
+        lengths = torch.full((B,), cap, dtype=torch.int32, device=dev)
+        swa_len = torch.full((B,), swa, dtype=torch.int32, device=dev)
+        q = syn.attn_query(wl, 0, dev)
+        out = torch.empty(B, 64, 512, dtype=torch.int16, device=dev)
+        ws = torch.zeros(max(L.csa2_attn_workspace(B, 64, k, swa), 256), dtype=torch.uint8, device=dev)
+
+        def call():
+            K.sparse_attn_decode(q, codes, scales, lengths, topk, fmt, swa_codes=codes, swa_scales=scales,
+                                 swa_len=swa_len, swa_stride=cap, swa_cap=swa, swa_row0=cap - swa,
+                                 out=dict(out=out), _ws=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        reps = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                call()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps / reps
+        nbytes = B * ((k + swa) * 288 + 64 * 512 * 2 * 2 + k * 4 + 8)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append(dict(B=B, us_per_call=round(us, 3), bytes_per_call=nbytes, achieved_GBs=round(gbs, 1),
+                         frac_hbm=round(gbs / HBM_PEAK_GBS, 4), queries_per_s=round(B / (us * 1e-6))))
+        log(f"[sweep] B={B}: {us:.2f} us, {gbs:.0f} GB/s")
+        del codes, scales, topk, q, out, ws, g
+        torch.cuda.empty_cache()
+    print(json.dumps(dict(metric="sparse attention decode call, batch sweep", unit="us per call",
+                          main_scale=fmt_name.upper(), heads=64, head_dim=512, rows=k + swa,
+                          entries_per_sequence=cap, peak_GBs=HBM_PEAK_GBS, sweep=rows)), flush=True)
 
 
 def copy_calibration(mb: float):
@@ -147,6 +209,9 @@ def main():
 
     if args.copy_calib_mb > 0:
         copy_calibration(args.copy_calib_mb)
+        return
+    if args.attn_sweep:
+        attn_sweep([int(x) for x in args.attn_sweep.split(",")], args.fmt, args.steps)
         return
 
     import csa2_synth as syn

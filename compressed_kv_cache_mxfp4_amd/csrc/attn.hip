@@ -201,6 +201,78 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
   }
 }
 
+// The last workgroup of a group merges the S chunk partials of sequence b:
+// thread tid takes head h0 + (tid >> 5), dims 16*(tid & 31) .. +15, so 512
+// threads merge 16 heads and 256 threads 8.  Partials are fp16 of (output / sum) * 2^-e with
+// (max, sum, XCD, e) beside them; a partial written on another XCD turns the
+// output into NaN (its bytes might not be visible in this XCD's L2).
+__device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const float4* __restrict__ ml,
+                                             const uint16_t* __restrict__ part, uint16_t* __restrict__ out,
+                                             float* __restrict__ lse, uint32_t my_xcc, int tid) {
+  // thread: head hh, dims 16*d16 .. +15.  Splits are merged four at a time
+  // with a running maximum (one round of loads per four splits).
+  const int hh = tid >> 5, d16 = tid & 31;
+  const int64_t bh = (int64_t)b * H + h0 + hh;
+  const float4* mlp = ml + bh * S;
+  const uint4* src = reinterpret_cast<const uint4*>(part + bh * S * 512 + 16 * d16);
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  float Mx = -INFINITY, Lsum = 0.f;
+  bool same_xcd = true;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float4 e[4];
+    uint4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u < S) {
+        e[u] = mlp[s0 + u];
+        v[u][0] = src[(s0 + u) * 64];
+        v[u][1] = src[(s0 + u) * 64 + 1];
+      } else {
+        e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
+        v[u][0] = v[u][1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float mg = Mx;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mg = fmaxf(mg, e[u].x);
+      same_xcd &= __float_as_uint(e[u].z) == my_xcc;
+    }
+    if (mg == -INFINITY) continue;  // nothing visible so far
+    const float rs = Mx == -INFINITY ? 0.0f : __expf(Mx - mg);
+    Lsum *= rs;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] *= rs;
+    Mx = mg;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // a chunk with no visible row has max -inf and a zero partial
+      const float wl = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx) * e[u].y;
+      Lsum += wl;
+      const float wgt = ldexpf(wl, __float_as_int(e[u].w));  // undo the partial's 2^-e
+      const uint32_t hw[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                              v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[2 * j] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] & 0xFFFFu));
+        acc[2 * j + 1] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] >> 16));
+      }
+    }
+  }
+  float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
+  if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
+  uint32_t o8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    o8[j] = f32_to_bf16_bits(acc[2 * j] * inv) | (f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+  uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
+  op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+  op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+  if (lse && d16 == 0) lse[bh] = !same_xcd ? inv : (Lsum > 0.f ? Mx + logf(Lsum) : -INFINITY);
+}
+
 // One (sequence, 16 heads, chunk of 16*WAVES row slots).  Grid: XCD-aware
 // linear order in which the head groups of one (sequence, chunk) share an XCD
 // (and its L2 copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512]
@@ -428,71 +500,413 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   __syncthreads();
   if (!sm.last) return;  // workgroup-uniform
   if (tid == 0) cnt[gi] = 0u;  // ready for the next call
-  if (tid < 16 * 32) {
-    // thread: head hh, dims 16*d16 .. +15.  Splits are merged four at a time
-    // with a running maximum (one round of loads per four splits).
-    const int hh = tid >> 5, d16 = tid & 31;
-    const int64_t bh = (int64_t)b * H + 16 * hg + hh;
-    const float4* mlp = ml + bh * S;
-    const uint4* src = reinterpret_cast<const uint4*>(part + bh * S * 512 + 16 * d16);
-    float acc[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-    float Mx = -INFINITY, Lsum = 0.f;
-    bool same_xcd = true;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      float4 e[4];
-      uint4 v[4][2];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (s0 + u < S) {
-          e[u] = mlp[s0 + u];
-          v[u][0] = src[(s0 + u) * 64];
-          v[u][1] = src[(s0 + u) * 64 + 1];
-        } else {
-          e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
-          v[u][0] = v[u][1] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 16 * 32) merge_splits(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid);
+}
+
+
+// ===================================================== throughput variant
+// One workgroup per (sequence, split of 32-row chunks) takes all 64 heads,
+// so every row is dequantised and staged once (the split kernel above does it
+// once per 16-head group), and it loops over its chunks with an online
+// softmax instead of ending after one chunk.  Used where the batch alone
+// fills the chip; the split kernel keeps the decode latency at small batch.
+//  * Eight waves in two roles, one of each per SIMD.  Score waves (0..3):
+//    wave w owns heads 16w..16w+15, keeps their queries in registers as MFMA
+//    B operands (K step ks: dims 32ks + 8g..+7 in lane group g), computes
+//    S = R.Q^T from the staged rows and the online softmax, and writes P
+//    (bf16) and the per-head rescale factor to LDS.  Value waves (4..7):
+//    wave 4+v owns dims 128v..128v+127 of every head, computes
+//    O^T += R^T.P^T one chunk behind the score waves, and stages the rows.
+//    The two roles overlap on each SIMD; one barrier per chunk.
+//  * Rows live in a ring of three 32-row buffers (chunk c+1 being staged,
+//    c being scored, c-1 being multiplied).  A step takes about 1 us while a
+//    loaded row arrives 2-3 us after its index entry is known under full
+//    load, so rows are loaded three chunks ahead of staging.  Index entries
+//    are loaded seven chunks ahead: loads complete in order, so waiting for
+//    an index entry also waits for every row load issued before it, and
+//    those must be old by then.
+//  * Staged rows are 1 KB apart; 16-byte unit u of row r is stored at unit
+//    u ^ swz(r mod 16), swz(x) = x ^ ((x >> 2) << 1), which keeps the row
+//    reads of Q.R^T free of bank conflicts (measured on gfx950).
+//  * S = R.Q^T leaves lane (g, n) with rows 4g..4g+3 of each 16-row tile for
+//    head n; P is stored per head in the K-slot order of the 32-row P.R
+//    MFMA (lane group g: rows 4g + 0..3, then 16 + 4g + 0..3), so each B
+//    operand is one 16-byte read.  R^T comes from ds_read_b64_tr_b16 in the
+//    same row order.
+//  * The running maximum moves only when a chunk exceeds it by more than
+//    2^8 (P <= 256 in between), so the accumulators are rarely rescaled.
+constexpr int kTRows = 32;     // rows per chunk
+constexpr int kTRowB = 1024;   // staged row: 512 bf16
+constexpr int kTPLd = 40;      // P row stride in bf16 (32 slots + pad)
+constexpr float kTau = 8.0f;   // log2 headroom before the running max moves
+
+__device__ __forceinline__ int tswz(int r) {
+  r &= 15;
+  return r ^ ((r >> 2) << 1);
+}
+
+struct AttnTSmem {
+  uint8_t R[3][kTRows * kTRowB];
+  uint16_t P[2][64 * kTPLd];
+  float alpha[2][64];  // rescale factor per head for the chunk in P[.]
+  float mfin[64], lfin[64];
+  uint32_t vb[3];      // row validity of the chunk in R[.]
+  float red_v[4];
+  int last;
+};
+
+// The staging lane's slice of one row: 32 code bytes and 4 scale bytes.
+struct TStage {
+  uint4 c0, c1;
+  uint32_t s;
+  uint32_t ok;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(512, 1) void attn_seq_kernel(
+    const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
+    const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
+    const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
+    const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
+    const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
+    uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  AttnTSmem& sm = *reinterpret_cast<AttnTSmem*>(smem_raw);
+  asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
+               "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
+               "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S));
+  // the S workgroups of a sequence get ids congruent mod 8 (one XCD), so the
+  // partials the last one merges are in its L2
+  const int id = blockIdx.x, xcd = id & 7, r8 = id >> 3;
+  const int b = (r8 / S) * 8 + xcd, sidx = r8 % S;
+  if (b >= B) return;  // padding workgroup (uniform, before any barrier)
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const bool scorer = w < 4;  // wave-uniform role
+  const int wr = w & 3;       // index within the role
+  const int nslots = k + swa_cap;
+  const int nch = (nslots + kTRows - 1) / kTRows;
+  const int c_begin = (int)((int64_t)sidx * nch / S), c_end = (int)((int64_t)(sidx + 1) * nch / S);
+  const int nc = c_end - c_begin;
+
+  int64_t L = len ? len[b] : 0;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int SL = swa_len ? swa_len[b] : 0;
+  SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
+
+  // ---- value waves: staging role, row srow of a chunk, dims 64*ssp .. +63
+  const int srow = 16 * (wr & 1) + n, ssp = 4 * (wr >> 1) + g;
+  const int32_t* tbase = topk + (int64_t)b * k;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)b * H * 512);
+  // index-list entry of row srow of chunk c (-1 when the slot is not a
+  // selected entry); the load is unconditional (clamped), so no branch waits
+  auto load_idx = [&](int c) -> int32_t {
+    const int slot = c * kTRows + srow;
+    const int32_t v = k > 0 ? tbase[min(slot, k - 1)] : 0;
+    return (slot < k && c < c_end) ? v : -1;
+  };
+  auto load_rows = [&](int c, int32_t p) -> TStage {
+    const int slot = c * kTRows + srow;
+    const uint8_t* cp = dummy;
+    const uint8_t* scp = dummy;
+    uint32_t ok = 0u;
+    if (c < c_end) {
+      if (slot < k) {
+        if (p >= 0 && (int64_t)p < L) {
+          cp = main_codes + ((int64_t)b * cap + p) * 256;
+          scp = main_scales + ((int64_t)b * cap + p) * 32;
+          ok = 1u;
         }
-      }
-      float mg = Mx;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        mg = fmaxf(mg, e[u].x);
-        same_xcd &= __float_as_uint(e[u].z) == my_xcc;
-      }
-      if (mg == -INFINITY) continue;  // nothing visible so far
-      const float rs = Mx == -INFINITY ? 0.0f : __expf(Mx - mg);
-      Lsum *= rs;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] *= rs;
-      Mx = mg;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        // a chunk with no visible row has max -inf and a zero partial
-        const float wl = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx) * e[u].y;
-        Lsum += wl;
-        const float wgt = ldexpf(wl, __float_as_int(e[u].w));  // undo the partial's 2^-e
-        const uint32_t hw[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
-                                v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          acc[2 * j] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] & 0xFFFFu));
-          acc[2 * j + 1] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] >> 16));
-        }
+      } else if (slot < nslots && slot - k < SL) {
+        cp = swa_codes + ((int64_t)b * swa_stride + (slot - k)) * 256;
+        scp = swa_scales + ((int64_t)b * swa_stride + (slot - k)) * 32;
+        ok = 1u;
       }
     }
-    float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
-    if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
-    uint32_t o8[8];
+    TStage st;
+    const uint4* c4 = reinterpret_cast<const uint4*>(cp + 32 * ssp);
+    st.c0 = c4[0];
+    st.c1 = c4[1];
+    st.s = *reinterpret_cast<const uint32_t*>(scp + 4 * ssp);
+    st.ok = ok;
+    return st;
+  };
+  uint32_t smax = 0u;  // largest scale byte staged by this lane (bound of |value|)
+  const int wsw = tswz(srow);
+  // dequantise the lane's slice into R[buf] (invalid rows as zeros) and
+  // record the chunk's row validity
+  auto stage = [&](int buf, TStage st) {
+    const uint32_t m = 0u - st.ok;
+    st.c0 = make_uint4(st.c0.x & m, st.c0.y & m, st.c0.z & m, st.c0.w & m);
+    st.c1 = make_uint4(st.c1.x & m, st.c1.y & m, st.c1.z & m, st.c1.w & m);
+    st.s &= m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t by = (st.s >> (8 * j)) & 0xFFu;
+      smax = max(smax, FMT == 0 ? by : (by & 0x7Fu));  // positive E4M3 bytes order like values
+    }
+    const uint32_t cw[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
+    uint8_t* rowp = sm.R[buf] + srow * kTRowB;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      o8[j] = f32_to_bf16_bits(acc[2 * j] * inv) | (f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-    uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
-    op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-    op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-    if (lse && d16 == 0) lse[bh] = !same_xcd ? inv : (Lsum > 0.f ? Mx + logf(Lsum) : -INFINITY);
+      *reinterpret_cast<bf16x8*>(rowp + (((8 * ssp + j) ^ wsw) << 4)) =
+          dequant8<FMT>(cw[j], (st.s >> (8 * (j >> 1))) & 0xFFu);
+    const uint64_t bal = __ballot(st.ok != 0u);
+    if (wr < 2 && lane == 0) reinterpret_cast<uint16_t*>(&sm.vb[buf])[wr] = (uint16_t)(bal & 0xFFFFull);
+  };
+
+  // The two roles run separate loops with the same number of barriers (one
+  // per step, plus the prologue's and the final one), so each keeps only its
+  // own state live: the queries in the score waves, the output in the value
+  // waves.
+  const uint32_t my_xcc = __builtin_amdgcn_s_getreg(kHwRegXccId);
+  if (scorer) {
+    // ---- queries of heads 16wr .. +15 (lane (g, n): head 16wr + n)
+    bf16x8 qf[16];
+    {
+      const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * wr + n) * 512 + 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qp[4 * ks]);
+    }
+    float mref = -INFINITY, lsum = 0.f;  // softmax of head 16wr + n (lane partial sum)
+    const float c2 = sm_scale * 1.4426950408889634f;  // logits in log2 units
+    // row 16t + n, unit 4ks + g -> qoff[ks%4] + 256*(ks/4) + 16384t
+    int qoff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qoff[m] = n * kTRowB + (((4 * m + g) ^ tswz(n)) << 4);
+    __syncthreads();  // chunk c_begin staged
+    for (int s = 0; s <= nc; ++s) {  // step s: score chunk s
+      if (s < nc) {
+        const uint8_t* Rb = sm.R[s % 3];
+        const uint32_t vm = sm.vb[s % 3];
+        // ---- S = R . Q^T for the chunk's two 16-row tiles; reads two K steps ahead
+        floatx4 sacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 qa[3][2];
+        auto qk_read = [&](int slot, int ks) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            qa[slot][t] = *reinterpret_cast<const bf16x8*>(Rb + qoff[ks & 3] + 256 * (ks >> 2) + 16384 * t);
+        };
+        qk_read(0, 0);
+        qk_read(1, 1);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          if (ks + 2 < 16) qk_read((ks + 2) % 3, ks + 2);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks % 3][t], qf[ks], sacc[t], 0, 0, 0);
+        }
+        // ---- online softmax (lane (g, n): rows 16t + 4g + i, head 16wr + n)
+        float x[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * g + i;
+            x[4 * t + i] = ((vm >> row) & 1u) ? sacc[t][i] * c2 : -INFINITY;
+            cmax = fmaxf(cmax, x[4 * t + i]);
+          }
+        cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+        cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+        float alpha = 1.0f;
+        if (cmax > mref + kTau) {
+          alpha = mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref - cmax);
+          mref = cmax;
+          lsum *= alpha;
+        }
+        const float mu = mref == -INFINITY ? 0.0f : mref;
+        uint32_t pb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // x = -inf (masked row) gives 0; x - mu <= kTau
+          const float p = __builtin_amdgcn_exp2f(x[j] - mu);
+          lsum += p;
+          pb[j] = f32_to_bf16_bits(p);
+        }
+        // slots 8g + 4t + i = rows 16t + 4g + i
+        *reinterpret_cast<uint4*>(sm.P[s & 1] + (16 * wr + n) * kTPLd + 8 * g) =
+            make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
+        if (g == 0) sm.alpha[s & 1][16 * wr + n] = alpha;
+      }
+      __syncthreads();
+    }
+    lsum += shfl_xor_f(lsum, 16);
+    lsum += shfl_xor_f(lsum, 32);
+    if (g == 0) {
+      sm.mfin[16 * wr + n] = mref;
+      sm.lfin[16 * wr + n] = lsum;
+    }
+    __syncthreads();  // final softmax state of every head in LDS
+  } else {
+    // ---- prologue: stage chunk c_begin; rows of c_begin+1 .. +3 and index
+    // entries of c_begin+4 .. +6 in flight.  Slot j of XA/XB/XC and PA/PB/PC
+    // serves the steps s = j mod 3 (rows of chunk s+1, index entries of
+    // chunk s+4); the step loop is unrolled by three so that no register
+    // holding an outstanding load is ever copied (a copy would wait for it).
+    TStage XA, XB, XC;
+    int32_t PA, PB, PC;
+    {
+      const int32_t p0 = load_idx(c_begin);
+      const int32_t p1 = load_idx(c_begin + 1);
+      const int32_t p2 = load_idx(c_begin + 2);
+      const int32_t p3 = load_idx(c_begin + 3);
+      PA = load_idx(c_begin + 4);
+      PB = load_idx(c_begin + 5);
+      PC = load_idx(c_begin + 6);
+      const TStage st0 = load_rows(c_begin, p0);
+      XA = load_rows(c_begin + 1, p1);
+      XB = load_rows(c_begin + 2, p2);
+      XC = load_rows(c_begin + 3, p3);
+      stage(0, st0);
+    }
+    // O^T tile (dims 128wr + 16dt .., heads 16ht ..): lane (g, n) holds dims
+    // +4g..+3 of head 16ht + n
+    floatx4 O[8][4];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) O[dt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // A = R^T: row 4g + n/4 (+16), dims 128wr + 16dt + 4(n&3)
+    int toff[8];
+    {
+      const int tr = 4 * g + (n >> 2), ta = n & 3;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        toff[dt] = tr * kTRowB + 256 * wr + (((2 * dt + (ta >> 1)) ^ tswz(tr)) << 4) + 8 * (ta & 1);
+    }
+    __syncthreads();  // chunk c_begin staged
+    // step s: multiply chunk s-1, stage chunk s+1 (rows in X), load the rows
+    // of chunk s+4 (index entry in P) and the index entries of chunk s+7
+    auto vstep = [&](int s, TStage& X, int32_t& Pn) {
+      if (s >= 1) {
+        // ---- O^T(dims of this wave, all heads) += R^T . P^T for chunk s-1
+        const uint8_t* Rb = sm.R[(s - 1) % 3];
+        const uint16_t* Pb = sm.P[(s - 1) & 1];
+        float al[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) al[ht] = sm.alpha[(s - 1) & 1][16 * ht + n];
+        if (__ballot(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) != 0ull) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) O[dt][ht] *= al[ht];
+        }
+        bf16x8 pbv[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) pbv[ht] = *reinterpret_cast<const bf16x8*>(Pb + (16 * ht + n) * kTPLd + 8 * g);
+        shortx4 tq[3][2];
+        auto tr_read = [&](int slot, int dt) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            tq[slot][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) shortx4*)(Rb + toff[dt] + kTRowB * 16 * hh));
+        };
+        tr_read(0, 0);
+        tr_read(1, 1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          if (dt + 2 < 8) tr_read((dt + 2) % 3, dt + 2);
+          const shortx4 lo = tq[dt % 3][0], hi = tq[dt % 3][1];
+          shortx8 av;
+          av[0] = lo[0]; av[1] = lo[1]; av[2] = lo[2]; av[3] = lo[3];
+          av[4] = hi[0]; av[5] = hi[1]; av[6] = hi[2]; av[7] = hi[3];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+            O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pbv[ht], O[dt][ht], 0, 0, 0);
+        }
+      }
+      if (s + 1 < nc) {
+        stage((s + 1) % 3, X);
+        X = load_rows(c_begin + s + 4, Pn);
+        Pn = load_idx(c_begin + s + 7);
+      }
+      __syncthreads();
+    };
+    for (int s0 = 0; s0 <= nc; s0 += 3) {
+      vstep(s0, XA, PA);
+      if (s0 + 1 <= nc) vstep(s0 + 1, XB, PB);
+      if (s0 + 2 <= nc) vstep(s0 + 2, XC, PC);
+    }
+    if (S > 1) {
+      float vb = 6.0f * (FMT == 0 ? e8m0_value(smax) : e4m3_value(smax));
+      if (!(vb <= 3.0e38f)) vb = 3.0e38f;  // NaN/inf scale bytes: clamp the bound
+      vb = wave_max(vb);
+      if (lane == 0) sm.red_v[wr] = vb;
+    }
+    __syncthreads();  // final softmax state of every head in LDS
+    float hm[4], hl[4], inv[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      hm[ht] = sm.mfin[16 * ht + n];
+      hl[ht] = sm.lfin[16 * ht + n];
+      inv[ht] = hl[ht] > 0.f ? 1.0f / hl[ht] : 0.0f;
+    }
+    if (S == 1) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        uint16_t* orow = out + ((int64_t)b * H + 16 * ht + n) * 512 + 128 * wr + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<uint2*>(orow + 16 * dt) =
+              make_uint2(f32_to_bf16_bits(O[dt][ht][0] * inv[ht]) | (f32_to_bf16_bits(O[dt][ht][1] * inv[ht]) << 16),
+                         f32_to_bf16_bits(O[dt][ht][2] * inv[ht]) | (f32_to_bf16_bits(O[dt][ht][3] * inv[ht]) << 16));
+        if (lse && wr == 0 && g == 0)
+          lse[(int64_t)b * H + 16 * ht + n] =
+              hl[ht] > 0.f ? (hm[ht] + log2f(hl[ht])) * 0.6931471805599453f : -INFINITY;
+      }
+    } else {
+      // partial: fp16 of (output / sum) * 2^-e, |output / sum| <= vmax < 2^(e + 15)
+      const float vmax = fmaxf(fmaxf(sm.red_v[0], sm.red_v[1]), fmaxf(sm.red_v[2], sm.red_v[3]));
+      int e_sc = 0;
+      if (vmax > 0.0f) {
+        int ex;
+        (void)frexpf(vmax, &ex);
+        e_sc = ex - 15;
+      }
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const int64_t bh = (int64_t)b * H + 16 * ht + n;
+        uint16_t* prow = part + (bh * S + sidx) * 512 + 128 * wr + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          uint32_t h16[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h16[i] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[dt][ht][i] * inv[ht], -e_sc));
+          *reinterpret_cast<uint2*>(prow + 16 * dt) = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+        }
+        if (wr == 0 && g == 0)
+          ml[bh * S + sidx] = make_float4(hm[ht] == -INFINITY ? -INFINITY : hm[ht] * 0.6931471805599453f, hl[ht],
+                                          __uint_as_float(my_xcc), __int_as_float(e_sc));
+      }
+    }
   }
+  if (S == 1) return;  // uniform
+  // ---- the last split of the sequence to finish merges all S partials
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = old == (uint32_t)(S - 1);
+  }
+  __syncthreads();
+  if (!sm.last) return;  // workgroup-uniform
+  if (tid == 0) cnt[b] = 0u;  // ready for the next call
+  for (int h0 = 0; h0 < H; h0 += 16) merge_splits(b, h0, H, S, ml, part, out, lse, my_xcc, tid);  // 16 heads per round
 }
+
+// Opt a kernel in to its dynamic LDS size once (thread-safe static init;
+// one flag per kernel instantiation).
+template <auto Kern>
+static bool lds_optin(size_t bytes) {
+  static const bool ok =
+      hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess;
+  return ok;
+}
+
+// Smallest batch for the throughput variant: below it one workgroup per
+// sequence leaves too few workgroups, and the split kernel's shorter chain
+// wins.
+constexpr int kSeqMinBatch = 48;
 
 static int attn_splits(int k, int swa_cap) { return (k + swa_cap + kChunk - 1) / kChunk; }
 
@@ -537,16 +951,30 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + l.cnt_off);
   uint16_t* part = reinterpret_cast<uint16_t*>(wsb + l.part_off);
   float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
+  if (H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
+    // throughput variant: S splits per sequence, enough to give every CU a
+    // workgroup, at most one per 128 row slots (the workspace's partials)
+    const int nch = (nslots + kTRows - 1) / kTRows;
+    int Sq = B >= 256 ? 1 : 256 / (int)B;
+    Sq = std::min(Sq, std::min(nch, attn_splits(k, swa_cap)));
+    const unsigned tgrid = (unsigned)(((B + 7) / 8) * Sq * 8);
+    auto tgo = [&](auto kern, bool lds_ok) -> bool {
+      if (!lds_ok) return false;
+      kern<<<tgrid, 512, sizeof(AttnTSmem), st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
+                                                   swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, Sq,
+                                                   part, ml, cnt, out, lse_opt);
+      return true;
+    };
+    const bool ok = main_fmt == 0 ? tgo(attn_seq_kernel<0>, lds_optin<attn_seq_kernel<0>>(sizeof(AttnTSmem)))
+                                  : tgo(attn_seq_kernel<1>, lds_optin<attn_seq_kernel<1>>(sizeof(AttnTSmem)));
+    if (!ok) return -1;
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int seq_units = B >= 8 ? 1 : 0;
   const int64_t units = seq_units ? B : groups;
   const unsigned grid = (unsigned)(((units + 7) / 8) * (seq_units ? HG : 1) * S * 8);
-  auto go = [&](auto kern, int waves, size_t smem) -> bool {
-    static bool attr_done = false;  // one per instantiation
-    if (!attr_done) {
-      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-        return false;
-      attr_done = true;
-    }
+  auto go = [&](auto kern, int waves, size_t smem, bool lds_ok) -> bool {
+    if (!lds_ok) return false;
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                          swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
                                          part, ml, cnt, out, lse_opt, seq_units);
@@ -554,11 +982,11 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   };
   bool ok;
   if (ten)
-    ok = main_fmt == 0 ? go(attn_split_kernel<0, 10>, 10, sizeof(AttnSmem<10>))
-                       : go(attn_split_kernel<1, 10>, 10, sizeof(AttnSmem<10>));
+    ok = main_fmt == 0 ? go(attn_split_kernel<0, 10>, 10, sizeof(AttnSmem<10>), lds_optin<attn_split_kernel<0, 10>>(sizeof(AttnSmem<10>)))
+                       : go(attn_split_kernel<1, 10>, 10, sizeof(AttnSmem<10>), lds_optin<attn_split_kernel<1, 10>>(sizeof(AttnSmem<10>)));
   else
-    ok = main_fmt == 0 ? go(attn_split_kernel<0, 8>, 8, sizeof(AttnSmem<8>))
-                       : go(attn_split_kernel<1, 8>, 8, sizeof(AttnSmem<8>));
+    ok = main_fmt == 0 ? go(attn_split_kernel<0, 8>, 8, sizeof(AttnSmem<8>), lds_optin<attn_split_kernel<0, 8>>(sizeof(AttnSmem<8>)))
+                       : go(attn_split_kernel<1, 8>, 8, sizeof(AttnSmem<8>), lds_optin<attn_split_kernel<1, 8>>(sizeof(AttnSmem<8>)));
   if (!ok) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -166,6 +166,75 @@ def test_attention_decode_batch_shape(fmt):
     say(f"  worst relative error {worst:.2e}")
 
 
+def _big_batch_case(B, cap, k, W, fmt, seed, sample):
+    """B sequences quantised on the GPU; the oracle re-quantises the sampled
+    ones (bytes must agree) and attends with its own bytes."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = torch.randn(B, cap, 512, generator=g, device=DEV)
+    c, s = K.quantize_fp4(x, 16, fmt)
+    rng = np.random.default_rng(seed)
+    topk = np.stack([rng.choice(cap, k, replace=False) for _ in range(B)]).astype(np.int32)
+    lens = np.full(B, cap, np.int32)
+    swa_len = np.full(B, W, np.int32)
+    # edge cases on the first sequences (all of them sampled)
+    topk[0, 10] = -1
+    topk[0, 11] = cap + 7                 # out of range: masked
+    topk[1, 20] = topk[1, 21]             # duplicate: attended twice
+    topk[2, k // 3:] = -1                 # short selection
+    lens[3] = cap - 100
+    topk[3, 30] = cap - 50                # beyond len: masked
+    swa_len[4] = min(W, 7)                # short window
+    lens[5], swa_len[5] = 0, 0            # attends nothing
+    topk[6, :] = -1                       # window only
+    picks = sorted(set(range(8)) | set(rng.choice(B, min(sample, B), replace=False).tolist()))
+    q = syn.as_bf16_bits(torch.randn(B, 64, 512, generator=torch.Generator().manual_seed(seed)) * 0.6)
+    ref = {}
+    xc = x.cpu().numpy()
+    cc, scc = c.cpu().numpy(), s.cpu().numpy()
+    for b in picks:
+        rc, rs = oracle.quantize(xc[b], 16, fmt)
+        assert np.array_equal(rc, cc[b]) and np.array_equal(rs, scc[b])
+        ref[b] = oracle.attention(q[b].numpy(), rc, rs, lens[b], fmt, topk[b], rc[cap - W:] if W else None,
+                                  rs[cap - W:] if W else None, swa_len[b], 1 / np.sqrt(512))
+    args = (q.to(DEV), c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV), fmt)
+    kw = dict(swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV), swa_stride=cap, swa_cap=W,
+              swa_row0=cap - W) if W else {}
+    return args, kw, picks, ref
+
+
+@pytest.mark.parametrize("B,k,W,fmt", [(48, 512, 128, 0), (64, 512, 128, 1), (128, 600, 100, 0),
+                                       (256, 77, 0, 1), (256, 512, 128, 0)])
+def test_attention_large_batch(B, k, W, fmt):
+    """Batches that take the all-heads throughput kernel: 5, 4, 2 and 1 splits
+    per sequence (ragged chunk ranges, k not a multiple of the 32-row chunk),
+    both scale formats; masked, duplicate, out-of-range and empty selections,
+    short and missing windows.  Repeated calls on one workspace give identical
+    bits and leave the completion counters at zero."""
+    say(f"attention large batch B={B} k={k} W={W} fmt={fmt}")
+    cap = 1200
+    args, kw, picks, ref = _big_batch_case(B, cap, k, W, fmt, 100 + B + k, 16)
+    H = 64
+    nbytes = K.lib().csa2_attn_workspace(B, H, k, W)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
+    ws[:262144].zero_()
+    out, lse = K.sparse_attn_decode(*args, return_lse=True, _ws=ws, **kw)
+    out2 = K.sparse_attn_decode(*args, _ws=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert int(ws[:262144].count_nonzero()) == 0
+    o = out.cpu()
+    l = lse.cpu().numpy()
+    worst = 0.0
+    for b in picks:
+        r, rl = ref[b]
+        if b == 5:
+            assert (o[b].view(torch.bfloat16).float() == 0).all() and np.isneginf(l[b]).all()
+            continue
+        worst = max(worst, attn_close(o[b:b + 1], r[None]))
+        np.testing.assert_allclose(l[b], rl, atol=1e-4, rtol=0)
+    say(f"  {len(picks)} sequences checked, worst relative error {worst:.2e}")
+
+
 def test_attention_window_only_separate_buffer():
     fmt = 1
     B, cap, W = 2, 64, 128
