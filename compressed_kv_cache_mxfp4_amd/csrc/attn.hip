@@ -588,6 +588,9 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   const int nch = (nslots + kTRows - 1) / kTRows;
   const int c_begin = (int)((int64_t)sidx * nch / S), c_end = (int)((int64_t)(sidx + 1) * nch / S);
   const int nc = c_end - c_begin;
+  // steps of the chunk loop, rounded up to the value waves' unroll of three
+  // (the extra steps only synchronise); both roles run exactly this many
+  const int nsteps = (nc + 1 + 2) / 3 * 3;
 
   int64_t L = len ? len[b] : 0;
   L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -598,12 +601,14 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   const int srow = 16 * (wr & 1) + n, ssp = 4 * (wr >> 1) + g;
   const int32_t* tbase = topk + (int64_t)b * k;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)b * H * 512);
-  // index-list entry of row srow of chunk c (-1 when the slot is not a
-  // selected entry); the load is unconditional (clamped), so no branch waits
+  // raw index-list entry of row srow of chunk c, loaded unconditionally from
+  // a clamped address (a valid dummy when k = 0).  It is not tested here:
+  // anything computed from it right away would make the compiler wait for
+  // the load at once.  load_rows applies every validity condition.
   auto load_idx = [&](int c) -> int32_t {
     const int slot = c * kTRows + srow;
-    const int32_t v = k > 0 ? tbase[min(slot, k - 1)] : 0;
-    return (slot < k && c < c_end) ? v : -1;
+    const int32_t* ip = k > 0 ? tbase + min(slot, k - 1) : reinterpret_cast<const int32_t*>(dummy);
+    return *ip;
   };
   auto load_rows = [&](int c, int32_t p) -> TStage {
     const int slot = c * kTRows + srow;
@@ -675,7 +680,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) qoff[m] = n * kTRowB + (((4 * m + g) ^ tswz(n)) << 4);
     __syncthreads();  // chunk c_begin staged
-    for (int s = 0; s <= nc; ++s) {  // step s: score chunk s
+    for (int s = 0; s < nsteps; ++s) {  // step s: score chunk s
       if (s < nc) {
         const uint8_t* Rb = sm.R[s % 3];
         const uint32_t vm = sm.vb[s % 3];
@@ -746,17 +751,19 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     TStage XA, XB, XC;
     int32_t PA, PB, PC;
     {
+      // issue order as in the steady state (rows of chunk j, then the index
+      // entry of chunk j+3), so that the loop's waits count the same loads
       const int32_t p0 = load_idx(c_begin);
       const int32_t p1 = load_idx(c_begin + 1);
       const int32_t p2 = load_idx(c_begin + 2);
       const int32_t p3 = load_idx(c_begin + 3);
-      PA = load_idx(c_begin + 4);
-      PB = load_idx(c_begin + 5);
-      PC = load_idx(c_begin + 6);
       const TStage st0 = load_rows(c_begin, p0);
       XA = load_rows(c_begin + 1, p1);
+      PA = load_idx(c_begin + 4);
       XB = load_rows(c_begin + 2, p2);
+      PB = load_idx(c_begin + 5);
       XC = load_rows(c_begin + 3, p3);
+      PC = load_idx(c_begin + 6);
       stage(0, st0);
     }
     // O^T tile (dims 128wr + 16dt .., heads 16ht ..): lane (g, n) holds dims
@@ -775,10 +782,10 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
         toff[dt] = tr * kTRowB + 256 * wr + (((2 * dt + (ta >> 1)) ^ tswz(tr)) << 4) + 8 * (ta & 1);
     }
     __syncthreads();  // chunk c_begin staged
-    // step s: multiply chunk s-1, stage chunk s+1 (rows in X), load the rows
-    // of chunk s+4 (index entry in P) and the index entries of chunk s+7
+    // step s: multiply chunk s-1, stage chunk s+1 (rows in X), then load the
+    // rows of chunk s+4 (index entry in Pn) and the index entries of chunk s+7
     auto vstep = [&](int s, TStage& X, int32_t& Pn) {
-      if (s >= 1) {
+      if (s >= 1 && s <= nc) {
         // ---- O^T(dims of this wave, all heads) += R^T . P^T for chunk s-1
         const uint8_t* Rb = sm.R[(s - 1) % 3];
         const uint16_t* Pb = sm.P[(s - 1) & 1];
@@ -815,17 +822,18 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
             O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pbv[ht], O[dt][ht], 0, 0, 0);
         }
       }
-      if (s + 1 < nc) {
-        stage((s + 1) % 3, X);
-        X = load_rows(c_begin + s + 4, Pn);
-        Pn = load_idx(c_begin + s + 7);
-      }
+      if (s + 1 < nc) stage((s + 1) % 3, X);
+      // issued on every step (past the split they read a dummy row), so that
+      // the count of outstanding loads is the same on every path and each
+      // wait covers only the loads it needs
+      X = load_rows(c_begin + s + 4, Pn);
+      Pn = load_idx(c_begin + s + 7);
       __syncthreads();
     };
-    for (int s0 = 0; s0 <= nc; s0 += 3) {
+    for (int s0 = 0; s0 < nsteps; s0 += 3) {
       vstep(s0, XA, PA);
-      if (s0 + 1 <= nc) vstep(s0 + 1, XB, PB);
-      if (s0 + 2 <= nc) vstep(s0 + 2, XC, PC);
+      vstep(s0 + 1, XB, PB);
+      vstep(s0 + 2, XC, PC);
     }
     if (S > 1) {
       float vb = 6.0f * (FMT == 0 ? e8m0_value(smax) : e4m3_value(smax));
