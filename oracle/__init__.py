@@ -42,7 +42,8 @@ def _load():
     lib.oracle_quantize_group.argtypes = [P, i32, i32, P, P]
     lib.oracle_quantize_rows.argtypes = [P, i64, i32, i32, i32, P, P]
     lib.oracle_dequantize_rows.argtypes = [P, P, i64, i32, i32, i32, P]
-    lib.oracle_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P, P]
+    lib.oracle_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P, P, P]
+    lib.oracle_rope.argtypes = [P, i64, i32]
     lib.oracle_score.argtypes = [P, P, P, i64, P, P, i32, P]
     lib.oracle_topk_ids.restype = i64
     lib.oracle_topk_ids.argtypes = [P, P, i64, i64, P]
@@ -51,7 +52,7 @@ def _load():
     lib.oracle_index_full.restype = i64
     lib.oracle_index_full.argtypes = [P, P, i64, P, P, i32, i32, i32, i32, P, P, P]
     lib.oracle_index_pool.argtypes = [P, P, i64, P, i64, P, P, i32, i32, P, P]
-    lib.oracle_attention.argtypes = [P, i32, P, P, i64, i32, P, i32, P, P, i32, f32, P, P]
+    lib.oracle_attention.argtypes = [P, i32, P, P, i64, i32, P, i32, P, P, i32, f32, P, P, P]
     lib.oracle_num_threads.restype = i32
     _lib = lib
     return lib
@@ -101,10 +102,20 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, group: int, fmt: int) -> n
 
 
 # ----------------------------------------------------------------- cache write
-def cache_write(latent_bf16, gate_bf16, m, w_idx, main_fmt, gamma=None, eps=1e-6):
-    """latent/gate: uint16 bf16 bits [T][512]; w_idx fp32 [512][128].
+def rope(x, pos, inverse=False):
+    """Compressed RoPE of one 512-d vector (fp64 copy returned): dims 448..511
+    as 32 adjacent pairs turned by pos * 160000^(-2j/64)."""
+    v = np.array(x, dtype=np.float64, copy=True).reshape(512)
+    _load().oracle_rope(_p(v), int(pos), 1 if inverse else 0)
+    return v
 
-    Returns dict(main_codes, main_scales, idx_codes, idx_scales, y, k).
+
+def cache_write(latent_bf16, gate_bf16, m, w_idx, main_fmt, gamma=None, eps=1e-6, rope_pos=None):
+    """latent/gate: uint16 bf16 bits [T][512]; w_idx fp32 [512][128];
+    rope_pos: int64 [T/m] entry positions for the compressed RoPE, or None.
+
+    Returns dict(main_codes, main_scales, idx_codes, idx_scales, y, k); y is
+    the (rotated) main entry before quantisation, k the indexer key.
     """
     latent = _c(latent_bf16, np.uint16)
     T = latent.shape[0]
@@ -120,8 +131,11 @@ def cache_write(latent_bf16, gate_bf16, m, w_idx, main_fmt, gamma=None, eps=1e-6
         y=np.zeros((n, 512), np.float32),
         k=np.zeros((n, 128), np.float32),
     )
+    rp = None if rope_pos is None else _c(rope_pos, np.int64)
+    if rp is not None and rp.shape != (n,):
+        raise ValueError("rope_pos must hold one position per entry")
     _load().oracle_cache_write(
-        _p(latent), _p(gate), T, m, _p(g), float(eps), _p(w), main_fmt,
+        _p(latent), _p(gate), T, m, _p(g), float(eps), _p(w), main_fmt, _p(rp),
         _p(out["main_codes"]), _p(out["main_scales"]), _p(out["idx_codes"]),
         _p(out["idx_scales"]), _p(out["y"]), _p(out["k"]),
     )
@@ -198,8 +212,9 @@ def index_pool(idx_codes, idx_scales, length, pool, pool_len, q_bf16, w, k):
 
 # ------------------------------------------------------------------- attention
 def attention(q_bf16, main_codes, main_scales, length, main_fmt, topk, swa_codes, swa_scales,
-              swa_len, sm_scale):
-    """One sequence: q uint16 [H][512]. Returns (out fp32 [H][512], lse fp32 [H])."""
+              swa_len, sm_scale, q_pos=None):
+    """One sequence: q uint16 [H][512]. Returns (out fp32 [H][512], lse fp32 [H]).
+    q_pos: the query's position for Q RoPE and output inverse RoPE, or None."""
     q = _c(q_bf16, np.uint16)
     H = q.shape[0]
     mc = _c(main_codes, np.uint8)
@@ -212,6 +227,7 @@ def attention(q_bf16, main_codes, main_scales, length, main_fmt, topk, swa_codes
         sc = ss = None
     out = np.zeros((H, 512), np.float32)
     lse = np.zeros(H, np.float32)
+    qp = None if q_pos is None else np.array([q_pos], np.int64)
     _load().oracle_attention(_p(q), H, _p(mc), _p(ms), length, main_fmt, _p(t), t.shape[0],
-                             _p(sc), _p(ss), swa_len, float(sm_scale), _p(out), _p(lse))
+                             _p(sc), _p(ss), swa_len, float(sm_scale), _p(qp), _p(out), _p(lse))
     return out, lse

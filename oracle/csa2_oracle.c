@@ -6,7 +6,7 @@
  * header, table or constant generator with the HIP library; it is written from
  * the pages' description of the method:
  *   [JU] jokeuncle.pages.dev, "两张架构图里藏着 890 字节" (sections 三, 四)
- *   [WG] weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本" (sections 3.1, 3.2)
+ *   [WG] weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本" (sections 3.1, 3.2, 10)
  *   [SY] syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B"
  *        (CSA2 / Figure 4, Hierarchical Sparse Indexer / Figure 5, FP4 主 KV 缓存)
  *   [GP] ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析" (3.2, 3.3, 7)
@@ -152,6 +152,25 @@ void oracle_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Compressed RoPE                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* [GP 3.2] entries are rotated with RoPE of base 160000 after RMSNorm and
+ * before FP4 quantisation; [GP 7] the entry keeps 448 dims without position
+ * encoding and 64 with it (128 B of bf16).  Reading: the rotated dims are the
+ * last 64 (448..511), taken as 32 adjacent pairs (448+2j, 449+2j) turned by
+ * the angle pos * 160000^(-2j/64).  inverse != 0 turns by -pos.            */
+void oracle_rope(double* x, int64_t pos, int inverse) {
+  for (int j = 0; j < 32; ++j) {
+    const double ang = (double)pos * pow(160000.0, -(double)(2 * j) / 64.0) * (inverse ? -1.0 : 1.0);
+    const double c = cos(ang), s = sin(ang);
+    const double a = x[448 + 2 * j], b = x[449 + 2 * j];
+    x[448 + 2 * j] = a * c - b * s;
+    x[449 + 2 * j] = a * s + b * c;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Cache write: gated pooling, RMSNorm, FP4, indexer-K projection            */
 /* ------------------------------------------------------------------------ */
 
@@ -162,8 +181,8 @@ void oracle_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t
  * that are quantised. */
 void oracle_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int m,
                         const float* gamma, float eps, const float* w_idx, int main_fmt,
-                        uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
-                        uint8_t* idx_scales, float* y_out, float* k_out) {
+                        const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
+                        uint8_t* idx_codes, uint8_t* idx_scales, float* y_out, float* k_out) {
   const int D = 512, DK = 128;
   int64_t n = T / m;
 #pragma omp parallel for schedule(static)
@@ -192,6 +211,17 @@ void oracle_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T,
     double r = 1.0 / sqrt(ss / D + (double)eps);
     float y[512];
     for (int c = 0; c < D; ++c) y[c] = (float)(pooled[c] * r * (gamma ? (double)gamma[c] : 1.0));
+    /* the indexer key is projected from the entry without position encoding
+     * (reading of [GP 3.2]'s "no-RoPE version"); the main entry is rotated */
+    float ym[512];
+    if (rope_pos) {
+      double yr[512];
+      for (int c = 0; c < D; ++c) yr[c] = (double)y[c];
+      oracle_rope(yr, rope_pos[j], 0);
+      for (int c = 0; c < D; ++c) ym[c] = (float)yr[c];
+    } else {
+      memcpy(ym, y, sizeof y);
+    }
     float k[128];
     for (int d = 0; d < DK; ++d) {
       double acc = 0.0;
@@ -199,12 +229,12 @@ void oracle_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T,
       k[d] = (float)acc;
     }
     for (int g = 0; g < D / 16; ++g)
-      oracle_quantize_group(y + g * 16, 16, main_fmt, main_codes + j * 256 + g * 8,
+      oracle_quantize_group(ym + g * 16, 16, main_fmt, main_codes + j * 256 + g * 8,
                             main_scales + j * 32 + g);
     for (int g = 0; g < DK / 32; ++g)
       oracle_quantize_group(k + g * 32, 32, FMT_E8M0, idx_codes + j * 64 + g * 16,
                             idx_scales + j * 4 + g);
-    if (y_out) memcpy(y_out + j * D, y, sizeof y);
+    if (y_out) memcpy(y_out + j * D, ym, sizeof ym);
     if (k_out) memcpy(k_out + j * DK, k, sizeof k);
   }
 }
@@ -366,8 +396,8 @@ void oracle_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int6
 void oracle_attention(const uint16_t* q, int H, const uint8_t* main_codes,
                       const uint8_t* main_scales, int64_t len, int main_fmt,
                       const int32_t* topk, int k, const uint8_t* swa_codes,
-                      const uint8_t* swa_scales, int swa_len, float sm_scale, float* out,
-                      float* lse) {
+                      const uint8_t* swa_scales, int swa_len, float sm_scale,
+                      const int64_t* q_pos, float* out, float* lse) {
   const int D = 512;
   int nrow = 0;
   for (int j = 0; j < k; ++j)
@@ -388,20 +418,29 @@ void oracle_attention(const uint16_t* q, int H, const uint8_t* main_codes,
 #pragma omp parallel for schedule(static)
   for (int h = 0; h < H; ++h) {
     double* logit = (double*)malloc(sizeof(double) * (nrow > 0 ? nrow : 1));
+    /* [WG 10] vLLM's fused decode path rotates the query (Q RoPE) and
+     * turns the output back (inverse RoPE); reading: both at the query's
+     * position, on the same 64 dims as the entries */
+    double qh[512];
+    for (int d = 0; d < D; ++d) qh[d] = bf16_value(q[(int64_t)h * D + d]);
+    if (q_pos) oracle_rope(qh, *q_pos, 0);
     double mx = -INFINITY;
     for (int j = 0; j < nrow; ++j) {
       double dot = 0.0;
-      for (int d = 0; d < D; ++d) dot += bf16_value(q[(int64_t)h * D + d]) * rows[(int64_t)j * D + d];
+      for (int d = 0; d < D; ++d) dot += qh[d] * rows[(int64_t)j * D + d];
       logit[j] = (double)sm_scale * dot;
       if (logit[j] > mx) mx = logit[j];
     }
     double den = 0.0;
     for (int j = 0; j < nrow; ++j) den += exp(logit[j] - mx);
+    double o[512];
     for (int d = 0; d < D; ++d) {
       double acc = 0.0;
       for (int j = 0; j < nrow; ++j) acc += exp(logit[j] - mx) * rows[(int64_t)j * D + d];
-      out[(int64_t)h * D + d] = nrow > 0 ? (float)(acc / den) : 0.0f;
+      o[d] = nrow > 0 ? acc / den : 0.0;
     }
+    if (q_pos) oracle_rope(o, *q_pos, 1);
+    for (int d = 0; d < D; ++d) out[(int64_t)h * D + d] = (float)o[d];
     if (lse) lse[h] = nrow > 0 ? (float)(mx + log(den)) : -INFINITY;
     free(logit);
   }
