@@ -40,7 +40,7 @@ def lib():
     L.csa2_status_string.argtypes = [ctypes.c_int]
     L.csa2_version.restype = ctypes.c_char_p
     L.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
-    L.csa2_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P]
+    L.csa2_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P, P]
     L.csa2_index_full_workspace.restype = sz
     L.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
     L.csa2_index_full.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
@@ -52,7 +52,7 @@ def lib():
     L.csa2_attn_workspace.restype = sz
     L.csa2_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
-                                          P, f32, P, P, P, sz, P]
+                                          P, f32, P, P, P, P, sz, P]
     _lib = L
     return L
 
@@ -130,8 +130,9 @@ def quantize_fp4(x: torch.Tensor, group: int, fmt: int, codes=None, scales=None)
 
 # ---------------------------------------------------------------- cache write
 def cache_write(latent, gate, m: int, w_idx, main_fmt: int, gamma=None, eps: float = 1e-6,
-                out=None):
-    """latent/gate bf16 (or int16 bits) [T][512]; w_idx fp32 [512][128].
+                out=None, rope_pos=None):
+    """latent/gate bf16 (or int16 bits) [T][512]; w_idx fp32 [512][128];
+    rope_pos int64 [T/m] entry positions for the compressed RoPE (or None).
 
     Returns dict(main_codes [T/m][256], main_scales [T/m][32], idx_codes [T/m][64],
     idx_scales [T/m][4]); `out` may supply these tensors (e.g. views into a cache).
@@ -158,8 +159,10 @@ def cache_write(latent, gate, m: int, w_idx, main_fmt: int, gamma=None, eps: flo
         )
     for key, width in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4)):
         _req(out[key], key, torch.uint8, dev, (n, width))
+    if rope_pos is not None:
+        _req(rope_pos, "rope_pos", torch.int64, dev, (n,))
     _check(lib().csa2_cache_write(_ptr(latent), _ptr(gate), T, m, _ptr(gamma), float(eps),
-                                  _ptr(w_idx), main_fmt, _ptr(out["main_codes"]),
+                                  _ptr(w_idx), main_fmt, _ptr(rope_pos), _ptr(out["main_codes"]),
                                   _ptr(out["main_scales"]), _ptr(out["idx_codes"]),
                                   _ptr(out["idx_scales"]), _stream(dev)), "csa2_cache_write")
     return out
@@ -271,7 +274,7 @@ def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 51
 def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
                        swa_codes=None, swa_scales=None, swa_len=None, swa_stride: int = 0,
                        swa_cap: int = 0, swa_row0: int = 0, sm_scale: Optional[float] = None,
-                       return_lse: bool = False, out=None, _ws=None):
+                       return_lse: bool = False, out=None, _ws=None, q_pos=None):
     """Sparse attention over topk rows ++ window rows.
 
     q bf16/int16 [B][H][512]; main planes [B][cap][256] / [B][cap][32];
@@ -279,6 +282,7 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
     of the contiguous tensors swa_codes (rows of 256 B) / swa_scales (rows of 32 B),
     so the window may be a separate buffer or the tail of the main cache
     (swa_codes=main_codes, swa_row0=cap-128, swa_stride=cap); swa_len int32 [B].
+    q_pos int64 [B]: query positions for Q RoPE and output inverse RoPE (or None).
     Returns out bf16 bits (int16) [B][H][512] (and lse fp32 [B][H]).
     """
     q = _bits16(q)
@@ -305,6 +309,8 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
         _req(swa_len, "swa_len", torch.int32, dev, (B,))
     if sm_scale is None:
         sm_scale = 1.0 / (512 ** 0.5)
+    if q_pos is not None:
+        _req(q_pos, "q_pos", torch.int64, dev, (B,))
     o = None if out is None else out.get("out")
     if o is None:
         o = torch.empty(B, H, 512, dtype=torch.int16, device=dev)
@@ -317,6 +323,6 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
         _ptr(q), H, _ptr(main_codes), _ptr(main_scales), cap, main_fmt, _ptr(lengths), _ptr(topk), k,
         B, ctypes.c_void_p(swa_codes.data_ptr() + 256 * swa_row0) if swa_cap else None,
         ctypes.c_void_p(swa_scales.data_ptr() + 32 * swa_row0) if swa_cap else None,
-        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, float(sm_scale), _ptr(o),
+        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, float(sm_scale), _ptr(q_pos), _ptr(o),
         _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode")
     return (o, lse) if return_lse else o

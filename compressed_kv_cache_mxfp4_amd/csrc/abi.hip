@@ -47,8 +47,8 @@ int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group, 
 
 int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int32_t m,
                      const float* gamma, float eps, const float* w_idx, int32_t main_fmt,
-                     uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
-                     uint8_t* idx_scales, void* stream) {
+                     const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
+                     uint8_t* idx_codes, uint8_t* idx_scales, void* stream) {
   if (T < 0 || m < 1 || m > 8 || T % m != 0) return CSA2_ERR_SHAPE;
   if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
   if (!(eps >= 0.0f)) return CSA2_ERR_SHAPE;
@@ -56,9 +56,10 @@ int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, in
   if (!latent || (m > 1 && !gate) || !w_idx || !main_codes || !main_scales || !idx_codes || !idx_scales)
     return CSA2_ERR_NULL;
   if (!aligned16(latent) || (m > 1 && !aligned16(gate)) || !aligned16(main_codes) ||
-      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u))
+      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(rope_pos) & 7u))
     return CSA2_ERR_ALIGN;
-  return launched(csa2::launch_cache_write(latent, gate, T, m, gamma, eps, w_idx, main_fmt,
+  return launched(csa2::launch_cache_write(latent, gate, T, m, gamma, eps, w_idx, main_fmt, rope_pos,
                                            main_codes, main_scales, idx_codes, idx_scales,
                                            as_stream(stream)));
 }
@@ -172,8 +173,8 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
                             const uint8_t* swa_codes, const uint8_t* swa_scales,
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
-                            float sm_scale, uint16_t* out, float* lse_opt, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            float sm_scale, const int64_t* q_pos, uint16_t* out, float* lse_opt,
+                            void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
   if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
   if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
@@ -186,12 +187,13 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
   if (k > 0 && (!main_codes || !main_scales || !len || !topk)) return CSA2_ERR_NULL;
   if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
   if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
-  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)))
+  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
+      (reinterpret_cast<uintptr_t>(q_pos) & 7u))
     return CSA2_ERR_ALIGN;
   if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
   return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
                                            k, B, swa_codes, swa_scales, swa_stride, swa_cap,
-                                           swa_len, sm_scale, out, lse_opt, ws,
+                                           swa_len, sm_scale, q_pos, out, lse_opt, ws,
                                            as_stream(stream)));
 }
 

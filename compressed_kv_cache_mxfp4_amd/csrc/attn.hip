@@ -67,6 +67,22 @@ struct AttnSmem {
   int last;  // this workgroup merges its (sequence, head group)
 };
 
+// Compressed RoPE of 8 consecutive bf16 dims starting at dim d0 (a multiple
+// of 8, >= 448): the 4 pairs turn by +angle at `pos`; the result is rounded
+// back to bf16 (nearest-even).
+__device__ __forceinline__ uint4 rope_bf16x8(uint4 v, int d0, int64_t pos) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = bf16_bits_to_f32(w[i] & 0xFFFFu), b = bf16_bits_to_f32(w[i] >> 16);
+    float c, sn;
+    rope_cos_sin(pos, (d0 - 448) / 2 + i, c, sn);
+    rope_pair<false>(a, b, c, sn);
+    w[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Eight E2M1 values of one code dword -> bf16x8 (exact).
 template <int FMT>
 __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, uint32_t sbyte) {
@@ -208,7 +224,8 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
 // output into NaN (its bytes might not be visible in this XCD's L2).
 __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const float4* __restrict__ ml,
                                              const uint16_t* __restrict__ part, uint16_t* __restrict__ out,
-                                             float* __restrict__ lse, uint32_t my_xcc, int tid) {
+                                             float* __restrict__ lse, uint32_t my_xcc, int tid,
+                                             const int64_t* __restrict__ q_pos) {
   // thread: head hh, dims 16*d16 .. +15.  Splits are merged four at a time
   // with a running maximum (one round of loads per four splits).
   const int hh = tid >> 5, d16 = tid & 31;
@@ -263,6 +280,16 @@ __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const 
   }
   float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
   if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
+  if (q_pos && d16 >= 28) {
+    // output inverse RoPE: dims 16*d16 .. +15 are pairs 8*(d16-28) .. +7
+    const int64_t pos = q_pos[b];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c, sn;
+      rope_cos_sin(pos, 8 * (d16 - 28) + i, c, sn);
+      rope_pair<true>(acc[2 * i], acc[2 * i + 1], c, sn);
+    }
+  }
   uint32_t o8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -283,7 +310,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
-    const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
+    const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
     uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -296,7 +323,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
                "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
                "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S),
-               "s"(seq_units));
+               "s"(seq_units), "s"(q_pos));
   const int HG = H >> 4;
   // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
   // otherwise one (sequence, head group).  A unit's workgroups get ids
@@ -332,11 +359,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   const uint4* qg = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
   // 16 heads x 64 pieces of 16 B: two pieces per thread
   static_assert(kThreads >= 512 && kThreads < 1024, "two query pieces per thread");
-  const uint4 qv0 = qg[tid];
-  const uint4 qv1 = qg[min(tid + kThreads, 1023)];
+  uint4 qv0 = qg[tid];
+  uint4 qv1 = qg[min(tid + kThreads, 1023)];
+  const int64_t qpos = (q_pos ? q_pos + b : reinterpret_cast<const int64_t*>(q))[vzero];
   // all of the above in flight together: the compiler would otherwise sink
   // each load into the branch that uses it and wait for them one by one
-  asm volatile("" ::"v"(praw), "v"(Lraw), "v"(SLraw));
+  asm volatile("" ::"v"(praw), "v"(Lraw), "v"(SLraw), "v"(qpos));
   const int32_t pidx = slot < k ? praw : -1;
   if (!valid) return;
   int64_t L = len ? Lraw : 0;
@@ -352,6 +380,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   // with 8 waves the query tile borrows the R buffer, which is then not
   // written before the max barrier
   uint16_t* Q = Smem::kQOwn ? sm.Qown : sm.R;
+  if (q_pos) {  // Q RoPE: pieces 56..63 of a head hold dims 448..511
+    if ((tid & 63) >= 56) qv0 = rope_bf16x8(qv0, 8 * (tid & 63), qpos);
+    if (((tid + kThreads) & 63) >= 56) qv1 = rope_bf16x8(qv1, 8 * ((tid + kThreads) & 63), qpos);
+  }
   *reinterpret_cast<uint4*>(&Q[(tid >> 6) * kQLd + 8 * (tid & 63)]) = qv0;
   if (tid + kThreads < 1024) {
     const int e = tid + kThreads;
@@ -500,7 +532,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   __syncthreads();
   if (!sm.last) return;  // workgroup-uniform
   if (tid == 0) cnt[gi] = 0u;  // ready for the next call
-  if (tid < 16 * 32) merge_splits(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid);
+  if (tid < 16 * 32) merge_splits(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid, q_pos);
 }
 
 
@@ -568,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
     const int32_t* __restrict__ topk, int k, const uint8_t* __restrict__ swa_codes,
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
-    const int32_t* __restrict__ swa_len, float sm_scale, int B, int S,
+    const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -672,6 +704,12 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * wr + n) * 512 + 8 * g);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qp[4 * ks]);
+      if (q_pos) {  // Q RoPE: K steps 14 and 15 hold dims 448..511
+        const int64_t pos = q_pos[b];
+#pragma unroll
+        for (int ks = 14; ks < 16; ++ks)
+          qf[ks] = __builtin_bit_cast(bf16x8, rope_bf16x8(__builtin_bit_cast(uint4, qf[ks]), 32 * ks + 8 * g, pos));
+      }
     }
     float mref = -INFINITY, lsum = 0.f;  // softmax of head 16wr + n (lane partial sum)
     const float c2 = sm_scale * 1.4426950408889634f;  // logits in log2 units
@@ -850,6 +888,24 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       inv[ht] = hl[ht] > 0.f ? 1.0f / hl[ht] : 0.0f;
     }
     if (S == 1) {
+      if (q_pos && wr == 3) {
+        // output inverse RoPE: dims 448 + 16(dt-4) + 4g + 0..3 are pairs 8(dt-4) + 2g + 0..1
+        const int64_t pos = q_pos[b];
+#pragma unroll
+        for (int dt = 4; dt < 8; ++dt)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            float c, sn;
+            rope_cos_sin(pos, 8 * (dt - 4) + 2 * g + i, c, sn);
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+              float x0 = O[dt][ht][2 * i], x1 = O[dt][ht][2 * i + 1];
+              rope_pair<true>(x0, x1, c, sn);
+              O[dt][ht][2 * i] = x0;
+              O[dt][ht][2 * i + 1] = x1;
+            }
+          }
+      }
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         uint16_t* orow = out + ((int64_t)b * H + 16 * ht + n) * 512 + 128 * wr + 4 * g;
@@ -899,7 +955,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   __syncthreads();
   if (!sm.last) return;  // workgroup-uniform
   if (tid == 0) cnt[b] = 0u;  // ready for the next call
-  for (int h0 = 0; h0 < H; h0 += 16) merge_splits(b, h0, H, S, ml, part, out, lse, my_xcc, tid);  // 16 heads per round
+  for (int h0 = 0; h0 < H; h0 += 16) merge_splits(b, h0, H, S, ml, part, out, lse, my_xcc, tid, q_pos);  // 16 heads per round
 }
 
 // Opt a kernel in to its dynamic LDS size once (thread-safe static init;
@@ -942,8 +998,8 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
-                       const int32_t* swa_len, float sm_scale, uint16_t* out, float* lse_opt,
-                       void* ws, hipStream_t st) {
+                       const int32_t* swa_len, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                       float* lse_opt, void* ws, hipStream_t st) {
   if (B == 0) return 0;
   const int nslots = k + swa_cap;
   const int64_t HG = H / 16;
@@ -969,7 +1025,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     auto tgo = [&](auto kern, bool lds_ok) -> bool {
       if (!lds_ok) return false;
       kern<<<tgrid, 512, sizeof(AttnTSmem), st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
-                                                   swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, Sq,
+                                                   swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, Sq,
                                                    part, ml, cnt, out, lse_opt);
       return true;
     };
@@ -984,7 +1040,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   auto go = [&](auto kern, int waves, size_t smem, bool lds_ok) -> bool {
     if (!lds_ok) return false;
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
-                                         swa_scales, swa_stride, swa_cap, swa_len, sm_scale, B, S,
+                                         swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, S,
                                          part, ml, cnt, out, lse_opt, seq_units);
     return true;
   };

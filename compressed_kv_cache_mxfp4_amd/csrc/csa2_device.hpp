@@ -75,6 +75,31 @@ __device__ __forceinline__ void fp4x8_to_f32(uint32_t codes, float out[8]) {
   out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
 }
 
+// ------------------------------------------------------------ compressed RoPE
+// [ggaaooppeenngg.github.io, "架构解析：KV Cache 压缩的极限在哪里", 3.2 and 7]:
+// base 160000; 64 of the 512 dims carry position.  These are dims 448..511
+// as 32 adjacent pairs; pair j turns by pos * 160000^(-2j/64).  The angle is
+// formed and reduced in fp64 (positions reach millions, where an fp32 angle
+// is off by tenths of a radian); the rotation itself is fp32.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, float& c, float& s) {
+  const double ang = (double)pos * pow(160000.0, -(double)(2 * j) / 64.0);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// Turn the pair (a, b) = (x[2j], x[2j+1]) of the RoPE dims by +angle, or by
+// -angle when INV.
+template <bool INV>
+__device__ __forceinline__ void rope_pair(float& a, float& b, float c, float s) {
+  const float sn = INV ? -s : s;
+  const float x = a * c - b * sn;
+  const float y = a * sn + b * c;
+  a = x;
+  b = y;
+}
+
 // ------------------------------------------------------------ wave helpers
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {

@@ -14,8 +14,8 @@ int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, u
 
 int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int m,
                        const float* gamma, float eps, const float* w_idx, int main_fmt,
-                       uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
-                       uint8_t* idx_scales, hipStream_t st);
+                       const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
+                       uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t st);
 
 // Workspace layout of the indexer calls (bytes, 256-aligned pieces).
 struct IndexFullWs {
@@ -45,7 +45,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
-                       const int32_t* swa_len, float sm_scale, uint16_t* out, float* lse_opt,
-                       void* ws, hipStream_t st);
+                       const int32_t* swa_len, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                       float* lse_opt, void* ws, hipStream_t st);
 
 }  // namespace csa2

@@ -11,7 +11,10 @@
 // softmax pooling over the m tokens of a group, fp32 when m > 1),
 // [ggaaooppeenngg.github.io, section 3.2 "Z"] (pooled -> RMSNorm -> FP4) and
 // [syt-nju.github.io, "为什么读输入只激活 8B", section CSA2] (indexer K projected
-// from the main-KV entry).
+// from the main-KV entry).  With entry positions given, the main entry's
+// dims 448..511 are rotated by the compressed RoPE before FP4 [same
+// ggaaooppeenngg.github.io page, 3.2]; the indexer key is projected from the
+// entry before rotation.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -119,8 +122,9 @@ template <int FMT>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ gate, int64_t n_entries,
     int m, const float* __restrict__ gamma, float eps, const float* __restrict__ w_idx,
-    uint8_t* __restrict__ main_codes, uint8_t* __restrict__ main_scales,
-    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales) {
+    const int64_t* __restrict__ rope_pos, uint8_t* __restrict__ main_codes,
+    uint8_t* __restrict__ main_scales, uint8_t* __restrict__ idx_codes,
+    uint8_t* __restrict__ idx_scales) {
   __shared__ __align__(16) float yT[512][kWriteEntries];  // latent after RMSNorm, channel-major
   __shared__ float part[8][kWriteEntries][33];  // projection partial sums per channel slice
   __shared__ float kb[kWriteEntries][33];       // projected keys of this column tile
@@ -218,7 +222,20 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     float y[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) y[c] = pooled[c] * r * (gamma ? gamma[8 * lane + c] : 1.0f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = y[c];
     if (ct == 0) {
+      // compressed RoPE of the main entry: lanes 56..63 hold dims 448..511,
+      // pairs (c, c+1) of the lane's 8 channels
+      if (rope_pos && lane >= 56) {
+        const int64_t pos = rope_pos[e];
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+          float cs, sn;
+          rope_cos_sin(pos, 4 * (lane - 56) + c / 2, cs, sn);
+          rope_pair<false>(y[c], y[c + 1], cs, sn);
+        }
+      }
       // main-KV FP4: a group of 16 channels spans two lanes
       float amax = 0.f;
 #pragma unroll
@@ -232,8 +249,6 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
       *reinterpret_cast<uint32_t*>(main_codes + e * 256 + 4 * lane) = word;
       if ((lane & 1) == 0) main_scales[e * 32 + lane / 2] = (uint8_t)b;
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = y[c];
   }
 
   // projection k[e][d] = sum_c y[e][c] * W[c][d] for the 32 columns d of this
@@ -301,18 +316,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 
 int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int m,
                        const float* gamma, float eps, const float* w_idx, int main_fmt,
-                       uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
-                       uint8_t* idx_scales, hipStream_t st) {
+                       const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
+                       uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t st) {
   const int64_t n = T / m;
   if (n == 0) return 0;
   const int64_t blocks = (n + kWriteEntries - 1) / kWriteEntries;
   const dim3 grid((unsigned)blocks, kWriteColTiles);
   if (main_fmt == 0)
-    cache_write_kernel<0><<<grid, 256, 0, st>>>(
-        latent, gate, n, m, gamma, eps, w_idx, main_codes, main_scales, idx_codes, idx_scales);
+    cache_write_kernel<0><<<grid, 256, 0, st>>>(latent, gate, n, m, gamma, eps, w_idx, rope_pos,
+                                                main_codes, main_scales, idx_codes, idx_scales);
   else
-    cache_write_kernel<1><<<grid, 256, 0, st>>>(
-        latent, gate, n, m, gamma, eps, w_idx, main_codes, main_scales, idx_codes, idx_scales);
+    cache_write_kernel<1><<<grid, 256, 0, st>>>(latent, gate, n, m, gamma, eps, w_idx, rope_pos,
+                                                main_codes, main_scales, idx_codes, idx_scales);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -4,7 +4,7 @@
  *
  * Sources (web pages on DeepSeek V4.1 Flash; cited by host, title and section):
  *   [JU]  jokeuncle.pages.dev, "两张架构图里藏着 890 字节", sections 二, 三, 四
- *   [WG]  weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本", sections 3.1, 3.2, 4
+ *   [WG]  weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本", sections 3.1, 3.2, 4, 10
  *   [SY]  syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B",
  *         sections "CSA2" (Figure 4), "Hierarchical Sparse Indexer" (Figure 5),
  *         "FP4 主 KV 缓存" (Figure 1(b))
@@ -124,6 +124,13 @@ int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group,
  *   m            : tokens per entry, 1..8; T must be a multiple of m.
  *   gamma        : fp32 [512] RMSNorm weight, NULL = all ones.
  *   w_idx        : fp32 [512][128] indexer-K projection (row c, column d).
+ *   rope_pos     : int64 [T/m] position of each written entry, or NULL.  With
+ *                  positions, the main entry's dims 448..511 are rotated by the
+ *                  compressed RoPE before FP4 [GP 3.2 (RMSNorm -> RoPE base
+ *                  160000 -> FP4), GP 7 (448 dims without position, 64 with)]:
+ *                  32 adjacent pairs (448+2j, 449+2j) turned by
+ *                  pos * 160000^(-2j/64).  The indexer key is projected from the
+ *                  entry before rotation.  8-byte aligned.
  *   main_codes/main_scales/idx_codes/idx_scales : out, rows [T/m] of the
  *                  planes above, i.e. pointers to the destination entry.
  * Errors: NULL pointer, T < 0, T % m != 0, m outside 1..8, bad main_fmt,
@@ -131,8 +138,8 @@ int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group,
  */
 int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, int32_t m,
                      const float* gamma, float eps, const float* w_idx, int32_t main_fmt,
-                     uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes,
-                     uint8_t* idx_scales, void* stream);
+                     const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
+                     uint8_t* idx_codes, uint8_t* idx_scales, void* stream);
 
 /*
  * csa2_index_full -- Full-mode hierarchical sparse indexer: one scoring pass
@@ -235,6 +242,13 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  *   swa_codes/swa_scales : window planes, sequence b at row offset b*swa_stride,
  *              same format as main; swa_len : int32 [B] rows used (<= swa_cap).
  *   swa_cap  : 0..128; may be 0 (then swa pointers may be NULL).
+ *   q_pos    : int64 [B] query positions, or NULL.  With positions, each
+ *              query's dims 448..511 are rotated by the compressed RoPE at
+ *              q_pos[b] before the products, and the output's dims 448..511
+ *              are turned back by -q_pos[b] (the fused Q RoPE and output
+ *              inverse RoPE of [WG 10]); the rows are read as written, i.e.
+ *              rotated at their own positions by csa2_cache_write.  8-byte
+ *              aligned.
  *   out      : out bf16 bits [B][H][512].
  *   lse_opt  : optional out fp32 [B][H], natural-log sum of exp(sm_scale*logits);
  *              -inf (and a zero output row) when a sequence attends no row.
@@ -246,10 +260,13 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  *              initial contents.  Calls sharing a workspace must be ordered
  *              on one stream; concurrent calls on one workspace race.
  *              B*H/16 must not exceed CSA2_ATTN_MAX_GROUPS.
- * One kernel on `stream`: a workgroup attends one chunk of 128 or 160 row
- * slots for 16 heads and leaves its partial (unnormalised output, max, sum)
- * in the workspace; the last chunk of each (sequence, head group) to finish
- * merges all of them exactly.  The chunks of one group are placed on one XCD
+ * One kernel on `stream`.  Below 48 sequences (or H < 64) a workgroup attends
+ * one chunk of 128 or 160 row slots for 16 heads and leaves its partial
+ * (unnormalised output, max, sum) in the workspace; the last chunk of each
+ * (sequence, head group) to finish merges all of them exactly.  From 48
+ * sequences with H = 64, a workgroup takes all heads of a sequence over a
+ * range of 32-row chunks with an online softmax (one range per sequence from
+ * 256 sequences), and the last range of a sequence merges the others.  The chunks of one group are placed on one XCD
  * (workgroup ids congruent mod 8), so the partials meet in that XCD's L2; a
  * merge that finds a chunk from another XCD writes NaN rather than a wrong
  * value.  The result is deterministic (fixed merge order; the counters only
@@ -261,8 +278,8 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
                             const uint8_t* swa_codes, const uint8_t* swa_scales,
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
-                            float sm_scale, uint16_t* out, float* lse_opt, void* ws,
-                            size_t ws_bytes, void* stream);
+                            float sm_scale, const int64_t* q_pos, uint16_t* out, float* lse_opt,
+                            void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

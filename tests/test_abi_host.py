@@ -66,12 +66,13 @@ def test_quantize_validation(lib):
 
 def test_cache_write_validation(lib):
     f = lib.csa2_cache_write
-    f.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_int32, P, P, P, P, P]
-    assert f(FAKE, FAKE, 7, 2, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # T % m
-    assert f(FAKE, FAKE, 8, 9, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # m
-    assert f(FAKE, None, 8, 2, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_NULL  # gate
-    assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 5, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUP
-    assert f(FAKE_ODD, None, 8, 1, None, 1e-6, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN
+    f.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_int32, P, P, P, P, P, P]
+    assert f(FAKE, FAKE, 7, 2, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # T % m
+    assert f(FAKE, FAKE, 8, 9, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE  # m
+    assert f(FAKE, None, 8, 2, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_NULL  # gate
+    assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 5, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUP
+    assert f(FAKE_ODD, None, 8, 1, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN
+    assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 0, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN  # positions
 
 
 def _index_full(lib):
@@ -159,10 +160,10 @@ def test_index_pool_and_attention_validation(lib):
     assert f(FAKE, FAKE, 4096, FAKE, 2, None, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 1 << 30, None) == ERR_NULL
     assert f(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 16, None) == ERR_WS
     a = lib.csa2_sparse_attn_decode
-    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, ctypes.c_float, P, P, P,
+    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, ctypes.c_float, P, P, P, P,
                   ctypes.c_size_t, P]
-    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0.04, FAKE, None,
-            FAKE, 1 << 40, None]
+    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0.04, None, FAKE,
+            None, FAKE, 1 << 40, None]
 
     def call(i, v):
         args = list(base)
@@ -177,5 +178,6 @@ def test_index_pool_and_attention_validation(lib):
     assert call(15, float("nan")) == ERR_SHAPE
     assert call(0, None) == ERR_NULL
     assert call(10, None) == ERR_NULL    # window planes missing
-    assert call(19, 8) == ERR_WS
+    assert call(20, 8) == ERR_WS
     assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(16, FAKE_ODD) == ERR_ALIGN  # query positions

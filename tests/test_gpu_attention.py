@@ -23,6 +23,19 @@ from gpu_common import DEV, attn_close, say
 pytestmark = pytest.mark.gpu
 
 
+def _rope_lse_tol(q_bits, rows, qpos, sm_scale=1 / np.sqrt(512)):
+    """Log-sum-exp tolerance when the query is rotated by the compressed RoPE.
+    The kernels round the rotated query to bf16 (their MFMA operand), the
+    oracle keeps it exact: each logit may move by up to 2^-9 of
+    sm_scale * sum over the 64 rotated dims of |q_rot[d] * row[d]|; 2^-8 of
+    the largest such sum over heads and rows bounds the lse difference, on
+    top of the 1e-4 accumulation tolerance."""
+    qf = (np.asarray(q_bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qr = np.stack([oracle.rope(qf[h], qpos) for h in range(qf.shape[0])])[:, 448:]
+    worst = (np.abs(qr) @ np.abs(np.asarray(rows, np.float64)[:, 448:]).T).max() if len(rows) else 0.0
+    return 1e-4 + 2.0 ** -8 * sm_scale * worst
+
+
 def _make_cache(B, cap, fmt, seed):
     g = torch.Generator(device=DEV).manual_seed(seed)
     x = torch.randn(B, cap, 512, generator=g, device=DEV)
@@ -33,10 +46,10 @@ def _make_cache(B, cap, fmt, seed):
     return c, s, rc, rs
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("H", [16, 64])
-def test_attention_parity_with_window(fmt, H):
-    say(f"attention parity fmt={fmt} H={H}")
+@pytest.mark.parametrize("fmt,H,rope", [(0, 16, False), (1, 16, False), (0, 64, False), (1, 64, False),
+                                         (0, 64, True), (1, 32, True)])
+def test_attention_parity_with_window(fmt, H, rope):
+    say(f"attention parity fmt={fmt} H={H} rope={rope}")
     B, cap, k, W = 3, 3000, 512, 128
     c, s, rc, rs = _make_cache(B, cap, fmt, 1 + fmt + H)
     g = np.random.default_rng(5)
@@ -50,17 +63,25 @@ def test_attention_parity_with_window(fmt, H):
     swa_len = np.array([128, 100, 0], np.int32)
     q = syn.as_bf16_bits(torch.randn(B, H, 512, generator=torch.Generator().manual_seed(9)) * 0.5)
     qd = q.to(DEV)
+    qpos = np.array([3000, 400, 1 << 30], np.int64) if rope else None
     out, lse = K.sparse_attn_decode(qd, c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV),
                                     fmt, swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV),
-                                    swa_stride=cap, swa_cap=W, swa_row0=cap - W, return_lse=True)
+                                    swa_stride=cap, swa_cap=W, swa_row0=cap - W, return_lse=True,
+                                    q_pos=None if qpos is None else torch.from_numpy(qpos).to(DEV))
     torch.cuda.synchronize()
     ref = np.zeros((B, H, 512), np.float32)
     rl = np.zeros((B, H), np.float32)
     for b in range(B):
         ref[b], rl[b] = oracle.attention(q[b].numpy(), rc[b], rs[b], lens[b], fmt, topk[b],
-                                         rc[b, cap - W:], rs[b, cap - W:], swa_len[b], 1 / np.sqrt(512))
+                                         rc[b, cap - W:], rs[b, cap - W:], swa_len[b], 1 / np.sqrt(512),
+                                         q_pos=None if qpos is None else int(qpos[b]))
     worst = attn_close(out.cpu(), ref)
-    np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=1e-4, rtol=0)
+    for b in range(B):
+        tol = 1e-4
+        if rope:
+            sel = [p for p in topk[b] if 0 <= p < lens[b]] + list(range(cap - W, cap - W + swa_len[b]))
+            tol = _rope_lse_tol(q[b].numpy(), oracle.dequantize(rc[b][sel], rs[b][sel], 16, fmt), int(qpos[b]))
+        np.testing.assert_allclose(lse.cpu().numpy()[b], rl[b], atol=tol, rtol=0)
     say(f"  worst relative error {worst:.2e}")
 
 
@@ -166,7 +187,7 @@ def test_attention_decode_batch_shape(fmt):
     say(f"  worst relative error {worst:.2e}")
 
 
-def _big_batch_case(B, cap, k, W, fmt, seed, sample):
+def _big_batch_case(B, cap, k, W, fmt, seed, sample, rope=False):
     """B sequences quantised on the GPU; the oracle re-quantises the sampled
     ones (bytes must agree) and attends with its own bytes."""
     g = torch.Generator(device=DEV).manual_seed(seed)
@@ -188,31 +209,42 @@ def _big_batch_case(B, cap, k, W, fmt, seed, sample):
     topk[6, :] = -1                       # window only
     picks = sorted(set(range(8)) | set(rng.choice(B, min(sample, B), replace=False).tolist()))
     q = syn.as_bf16_bits(torch.randn(B, 64, 512, generator=torch.Generator().manual_seed(seed)) * 0.6)
+    qpos = rng.integers(0, 1 << 31, B, dtype=np.int64) if rope else None
     ref = {}
+    tols = {}
     xc = x.cpu().numpy()
     cc, scc = c.cpu().numpy(), s.cpu().numpy()
     for b in picks:
         rc, rs = oracle.quantize(xc[b], 16, fmt)
         assert np.array_equal(rc, cc[b]) and np.array_equal(rs, scc[b])
+        tols[b] = 1e-4
+        if qpos is not None:
+            sel = [p for p in topk[b] if 0 <= p < lens[b]] + list(range(cap - W, cap - W + swa_len[b]))
+            tols[b] = _rope_lse_tol(q[b].numpy(), oracle.dequantize(rc[sel], rs[sel], 16, fmt), int(qpos[b]))
         ref[b] = oracle.attention(q[b].numpy(), rc, rs, lens[b], fmt, topk[b], rc[cap - W:] if W else None,
-                                  rs[cap - W:] if W else None, swa_len[b], 1 / np.sqrt(512))
+                                  rs[cap - W:] if W else None, swa_len[b], 1 / np.sqrt(512),
+                                  q_pos=None if qpos is None else int(qpos[b]))
     args = (q.to(DEV), c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV), fmt)
     kw = dict(swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV), swa_stride=cap, swa_cap=W,
               swa_row0=cap - W) if W else {}
-    return args, kw, picks, ref
+    if qpos is not None:
+        kw["q_pos"] = torch.from_numpy(qpos).to(DEV)
+    return args, kw, picks, ref, tols
 
 
-@pytest.mark.parametrize("B,k,W,fmt", [(48, 512, 128, 0), (64, 512, 128, 1), (128, 600, 100, 0),
-                                       (256, 77, 0, 1), (256, 512, 128, 0)])
-def test_attention_large_batch(B, k, W, fmt):
+@pytest.mark.parametrize("B,k,W,fmt,rope", [(48, 512, 128, 0, False), (64, 512, 128, 1, False),
+                                            (128, 600, 100, 0, False), (256, 77, 0, 1, False),
+                                            (256, 512, 128, 0, False), (64, 512, 128, 0, True),
+                                            (256, 512, 128, 1, True)])
+def test_attention_large_batch(B, k, W, fmt, rope):
     """Batches that take the all-heads throughput kernel: 5, 4, 2 and 1 splits
     per sequence (ragged chunk ranges, k not a multiple of the 32-row chunk),
     both scale formats; masked, duplicate, out-of-range and empty selections,
     short and missing windows.  Repeated calls on one workspace give identical
     bits and leave the completion counters at zero."""
-    say(f"attention large batch B={B} k={k} W={W} fmt={fmt}")
+    say(f"attention large batch B={B} k={k} W={W} fmt={fmt} rope={rope}")
     cap = 1200
-    args, kw, picks, ref = _big_batch_case(B, cap, k, W, fmt, 100 + B + k, 16)
+    args, kw, picks, ref, tols = _big_batch_case(B, cap, k, W, fmt, 100 + B + k, 16, rope)
     H = 64
     nbytes = K.lib().csa2_attn_workspace(B, H, k, W)
     ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
@@ -231,7 +263,7 @@ def test_attention_large_batch(B, k, W, fmt):
             assert (o[b].view(torch.bfloat16).float() == 0).all() and np.isneginf(l[b]).all()
             continue
         worst = max(worst, attn_close(o[b:b + 1], r[None]))
-        np.testing.assert_allclose(l[b], rl, atol=1e-4, rtol=0)
+        np.testing.assert_allclose(l[b], rl, atol=tols[b], rtol=0)
     say(f"  {len(picks)} sequences checked, worst relative error {worst:.2e}")
 
 
@@ -285,17 +317,31 @@ def _certified_code_mismatch(vals, ref_codes, ref_scales, got_codes, got_scales,
     return n_bad
 
 
-@pytest.mark.parametrize("m,fmt,gamma,n", [(1, 0, False, 1024), (2, 1, False, 1024), (2, 0, True, 1024),
-                                           (4, 1, True, 1024), (1, 0, False, 37), (2, 1, True, 37)])
-def test_cache_write_parity(m, fmt, gamma, n):
-    say(f"cache write m={m} fmt={fmt} gamma={gamma} entries={n}")
+def _rope_positions(n, seed):
+    """Entry positions for the compressed RoPE: 0, small, 400 (pair 16 turns by
+    1 rad), and large values up to 2^31 - 1."""
+    g = np.random.default_rng(seed)
+    p = g.integers(0, 1 << 31, n, dtype=np.int64)
+    p[: min(n, 4)] = [0, 1, 400, (1 << 31) - 1][: min(n, 4)]
+    return p
+
+
+@pytest.mark.parametrize("m,fmt,gamma,n,rope", [(1, 0, False, 1024, False), (2, 1, False, 1024, False),
+                                                (2, 0, True, 1024, False), (4, 1, True, 1024, False),
+                                                (1, 0, False, 37, False), (2, 1, True, 37, False),
+                                                (1, 0, False, 1024, True), (2, 1, True, 1024, True),
+                                                (1, 1, False, 37, True)])
+def test_cache_write_parity(m, fmt, gamma, n, rope):
+    say(f"cache write m={m} fmt={fmt} gamma={gamma} entries={n} rope={rope}")
     wl = syn.small("w", 31 + m, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=n * m, write_m=m)
     lat, gate, w = syn.write_inputs(wl, DEV)
     gm = (torch.linspace(0.5, 1.5, 512, device=DEV) if gamma else None)
-    got = K.cache_write(lat, gate, m, w, fmt, gamma=gm, eps=1e-6)
+    pos = _rope_positions(n, 7 + n) if rope else None
+    got = K.cache_write(lat, gate, m, w, fmt, gamma=gm, eps=1e-6,
+                        rope_pos=None if pos is None else torch.from_numpy(pos).to(DEV))
     torch.cuda.synchronize()
     ref = oracle.cache_write(lat.cpu().numpy(), gate.cpu().numpy(), m, w.cpu().numpy(), fmt,
-                             gamma=None if gm is None else gm.cpu().numpy(), eps=1e-6)
+                             gamma=None if gm is None else gm.cpu().numpy(), eps=1e-6, rope_pos=pos)
     g = {k_: v.cpu().numpy() for k_, v in got.items()}
     nm = _certified_code_mismatch(ref["y"], ref["main_codes"], ref["main_scales"], g["main_codes"],
                                   g["main_scales"], 16, fmt)
