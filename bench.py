@@ -353,6 +353,31 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         per_call_us[n] = e0.elapsed_time(e1) * 1e3 / args.steps / reps[n] / max(calls[n], 1)
+    # decode-time append (not part of the step above, which writes into a
+    # staging area): one token per sequence into a cache with free rows, m = 1
+    # with RoPE, 20 appends per graph, HIP events around K replays
+    app_cap = 20 * (args.steps + 4) + 8
+    app_cache = {k_: torch.zeros(B, app_cap, wd, dtype=torch.uint8, device=dev)
+                 for k_, wd in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4))}
+    app_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    app_tok = new_lat[:B] if new_lat.shape[0] >= B else new_lat.repeat(B, 1)[:B]
+
+    def ph_append():
+        for _ in range(20):
+            K.cache_append(app_tok, None, 1, w_proj, fmt, app_cache, app_len, rope=True)
+
+    ph_append()
+    g_app = capture(ph_append)
+    g_app.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g_app.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) * 1e3 / args.steps / 20
+    assert int(app_len.max()) <= app_cap
+    del app_cache, g_app
     # the same step launched call by call from Python, for reference
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -397,6 +422,8 @@ def main():
                     main_scale=args.fmt.upper(), index_query=args.index_q, only=args.only,
                     cache_write=f"{w_T} tokens, m={w_m}"),
         attn_queries_per_s=B * step.n_attn / (ms_per_step * 1e-3),
+        cache_append_us=dict(us_per_call=round(append_us, 3), tokens=B, m=1, rope=True,
+                             note="decode-time append of one token per sequence into the cache; not in the step"),
         kernels=kernels, roofline=roofline,
     )
     if not args.no_cpu_baseline and args.only is None:

@@ -7,6 +7,8 @@ from ._lib import (  # noqa: F401
     E4M3,
     E8M0,
     Csa2Error,
+    append_state,
+    cache_append,
     cache_write,
     index_full,
     index_pool,

@@ -41,6 +41,9 @@ def lib():
     L.csa2_version.restype = ctypes.c_char_p
     L.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
     L.csa2_cache_write.argtypes = [P, P, i64, i32, P, f32, P, i32, P, P, P, P, P, P]
+    L.csa2_append_state_bytes.restype = sz
+    L.csa2_append_state_bytes.argtypes = [i32]
+    L.csa2_cache_append.argtypes = [P, P, i32, i32, P, f32, P, i32, i32, P, P, P, P, i64, P, P, P]
     L.csa2_index_full_workspace.restype = sz
     L.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
     L.csa2_index_full.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
@@ -169,6 +172,51 @@ def cache_write(latent, gate, m: int, w_idx, main_fmt: int, gamma=None, eps: flo
 
 
 # -------------------------------------------------------------------- indexer
+def append_state(B: int, device) -> torch.Tensor:
+    """Zero-filled state for cache_append with m = 2 (held first tokens)."""
+    return torch.zeros(max(int(lib().csa2_append_state_bytes(B)), 256), dtype=torch.uint8, device=device)
+
+
+def cache_append(latent, gate, m: int, w_idx, main_fmt: int, cache: dict, lengths, state=None,
+                 gamma=None, eps: float = 1e-6, rope: bool = False):
+    """Decode-time append of one token per sequence into the cache planes.
+
+    latent/gate bf16 (or int16 bits) [B][512]; cache: dict of the planes
+    main_codes [B][cap][256], main_scales [B][cap][32], idx_codes [B][cap][64],
+    idx_scales [B][cap][4]; lengths int32 [B] (advanced in place); state from
+    append_state(B) when m == 2.  With rope, each entry is rotated at its row index.
+    """
+    latent = _bits16(latent)
+    _req(latent, "latent", torch.int16)
+    dev = latent.device
+    B = latent.shape[0]
+    _req(latent, "latent", torch.int16, dev, (B, 512))
+    if m not in (1, 2):
+        raise ValueError("m must be 1 or 2")
+    if m == 2:
+        gate = _bits16(gate)
+        _req(gate, "gate", torch.int16, dev, (B, 512))
+        if state is None:
+            raise ValueError("m == 2 needs the append state")
+        _req(state, "state", torch.uint8, dev)
+        if state.numel() < lib().csa2_append_state_bytes(B):
+            raise ValueError("append state too small")
+    else:
+        gate = None
+    _req(w_idx, "w_idx", torch.float32, dev, (512, 128))
+    if gamma is not None:
+        _req(gamma, "gamma", torch.float32, dev, (512,))
+    cap = cache["main_codes"].shape[1]
+    for key, width in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4)):
+        _req(cache[key], key, torch.uint8, dev, (B, cap, width))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    _check(lib().csa2_cache_append(_ptr(latent), _ptr(gate), B, m, _ptr(gamma), float(eps), _ptr(w_idx),
+                                   main_fmt, 1 if rope else 0, _ptr(cache["main_codes"]),
+                                   _ptr(cache["main_scales"]), _ptr(cache["idx_codes"]),
+                                   _ptr(cache["idx_scales"]), cap, _ptr(lengths),
+                                   _ptr(state) if m == 2 else None, _stream(dev)), "csa2_cache_append")
+
+
 def _index_query(q, dev, B):
     """bf16 queries [B][H][128] -> (H, q bits, None, None); FP4 queries given as
     (codes u8 [B][H][64], E8M0 scales u8 [B][H][4]) -> (H, None, codes, scales)."""

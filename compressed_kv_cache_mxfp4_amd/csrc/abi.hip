@@ -64,6 +64,28 @@ int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, in
                                            as_stream(stream)));
 }
 
+size_t csa2_append_state_bytes(int32_t B) { return B <= 0 ? 0 : csa2::append_state_bytes(B); }
+
+int csa2_cache_append(const uint16_t* latent, const uint16_t* gate, int32_t B, int32_t m,
+                      const float* gamma, float eps, const float* w_idx, int32_t main_fmt, int32_t rope,
+                      uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales,
+                      int64_t cap, int32_t* len, void* state, void* stream) {
+  if (B < 0 || m < 1 || m > 2 || cap < 1 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!latent || (m == 2 && (!gate || !state)) || !w_idx || !main_codes || !main_scales || !idx_codes ||
+      !idx_scales || !len)
+    return CSA2_ERR_NULL;
+  if (!aligned16(latent) || (m == 2 && (!aligned16(gate) || !aligned16(state))) || !aligned16(main_codes) ||
+      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(len) & 3u))
+    return CSA2_ERR_ALIGN;
+  return launched(csa2::launch_cache_append(latent, gate, B, m, gamma, eps, w_idx, main_fmt, rope ? 1 : 0,
+                                            main_codes, main_scales, idx_codes, idx_scales, cap, len, state,
+                                            as_stream(stream)));
+}
+
 size_t csa2_index_full_workspace(int32_t B, int64_t cap, int32_t k, int32_t block,
                                  int32_t n_blocks) {
   (void)k;

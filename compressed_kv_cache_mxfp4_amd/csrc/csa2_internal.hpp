@@ -17,6 +17,12 @@ int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, 
                        const int64_t* rope_pos, uint8_t* main_codes, uint8_t* main_scales,
                        uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t st);
 
+size_t append_state_bytes(int B);
+int launch_cache_append(const uint16_t* latent, const uint16_t* gate, int B, int m, const float* gamma,
+                        float eps, const float* w_idx, int main_fmt, int rope, uint8_t* main_codes,
+                        uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales, int64_t cap,
+                        int32_t* len, void* state, hipStream_t st);
+
 // Workspace layout of the indexer calls (bytes, 256-aligned pieces).
 struct IndexFullWs {
   size_t scores_off, bmax_off, total;

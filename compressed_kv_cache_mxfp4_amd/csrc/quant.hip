@@ -331,4 +331,181 @@ int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// ------------------------------------------------------------ decode append
+// [jokeuncle.pages.dev, "两张架构图里藏着 890 字节", section 四 item 1;
+// ggaaooppeenngg.github.io, "架构解析：KV Cache 压缩的极限在哪里", 3.2]: a decoder
+// layer (m = 1) writes one compressed entry per generated token; a layer with
+// m = 2 writes one every second token, holding the first token of each group
+// until its partner arrives.  One new token per sequence per call; the entry
+// goes to row len[b] of the sequence's planes (with RoPE at position len[b]
+// when asked) and len[b] advances.  Two launches: the write, then the
+// advance (so that no workgroup of the write reads a length already moved).
+// State for m = 2 (caller-owned, zero-filled once): int32 count[B] (tokens
+// held, 0 or 1), then bf16 latent[B][512] and gate[B][512] of the held token.
+struct AppendState {
+  int32_t* count;
+  uint16_t* lat;
+  uint16_t* gate;
+};
+
+static AppendState append_state(void* st, int B) {
+  char* p = reinterpret_cast<char*>(st);
+  const size_t c = ((size_t)B * 4 + 255) & ~(size_t)255;
+  return AppendState{reinterpret_cast<int32_t*>(p), reinterpret_cast<uint16_t*>(p + c),
+                     reinterpret_cast<uint16_t*>(p + c + (size_t)B * 1024)};
+}
+
+size_t append_state_bytes(int B) { return (((size_t)B * 4 + 255) & ~(size_t)255) + (size_t)B * 2048; }
+
+// Grid (sequence, 4 column tiles), 256 threads: thread t pools and
+// normalises channels 2t, 2t+1 (the cache write's operations, in its order);
+// in column tile 0, threads 0..31 quantise the main entry (one 16-channel
+// group each, RoPE on groups 28..31); every workgroup projects onto its 32
+// indexer-K columns (one E8M0 group), 8 channel slices of 64 per column.
+template <int FMT>
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ gate, int m,
+    const float* __restrict__ gamma, float eps, const float* __restrict__ w_idx, int rope,
+    uint8_t* __restrict__ main_codes, uint8_t* __restrict__ main_scales,
+    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int64_t cap,
+    const int32_t* __restrict__ len, const int32_t* __restrict__ count,
+    const uint16_t* __restrict__ plat, const uint16_t* __restrict__ pgate) {
+  __shared__ float y[512];
+  __shared__ float kv[8][33];
+  __shared__ float red[4];
+  __shared__ uint32_t kc[32];
+  const int b = blockIdx.x, ct = blockIdx.y, t = threadIdx.x;
+  const int32_t L = len[b];
+  if (L < 0 || (int64_t)L >= cap) return;    // full: nothing is written (uniform)
+  if (m == 2 && count[b] == 0) return;      // first token of a group: the advance holds it
+  float pooled[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t i = (int64_t)b * 512 + 2 * t + c;
+    if (m == 1) {
+      pooled[c] = bf16_bits_to_f32(latent[i]);
+    } else {
+      const float g0 = bf16_bits_to_f32(pgate[i]), g1 = bf16_bits_to_f32(gate[i]);
+      const float gmax = fmaxf(fmaxf(-INFINITY, g0), g1);
+      const float e0 = expf(g0 - gmax), e1 = expf(g1 - gmax);
+      float num = 0.f, den = 0.f;
+      num += e0 * bf16_bits_to_f32(plat[i]);
+      den += e0;
+      num += e1 * bf16_bits_to_f32(latent[i]);
+      den += e1;
+      pooled[c] = num / den;
+    }
+  }
+  float ss = wave_sum(pooled[0] * pooled[0] + pooled[1] * pooled[1]);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(ss / 512.0f + eps);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) y[2 * t + c] = pooled[c] * r * (gamma ? gamma[2 * t + c] : 1.0f);
+  __syncthreads();
+  const int64_t row = (int64_t)b * cap + L;
+  if (ct == 0 && t < 32) {
+    // main entry, channel group t (16 channels), rotated first when asked
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = y[16 * t + j];
+    if (rope && t >= 28) {
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        float cs, sn;
+        rope_cos_sin(L, 8 * (t - 28) + j / 2, cs, sn);
+        rope_pair<false>(v[j], v[j + 1], cs, sn);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    const uint32_t sb = scale_code<FMT>(amax);
+    const float sc = scale_value<FMT>(sb);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w0 |= e2m1_code(v[j], sc) << (4 * j);
+      w1 |= e2m1_code(v[8 + j], sc) << (4 * j);
+    }
+    *reinterpret_cast<uint2*>(main_codes + row * 256 + 8 * t) = make_uint2(w0, w1);
+    main_scales[row * 32 + t] = (uint8_t)sb;
+  }
+  // indexer key from the unrotated entry: thread = (channel slice, column)
+  {
+    const int col = t & 31, sl = t >> 5;
+    float wv[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) wv[c] = w_idx[(64 * sl + c) * 128 + 32 * ct + col];
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) acc += y[64 * sl + c] * wv[c];
+    kv[sl][col] = acc;
+  }
+  __syncthreads();
+  if (t < 32) {
+    float v = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) v += kv[s8][t];
+    float amax = fabsf(v);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
+    const uint32_t sb = scale_code_e8m0(amax);
+    kc[t] = e2m1_code(v, e8m0_value(sb));
+    if (t == 0) idx_scales[row * 4 + ct] = (uint8_t)sb;
+  }
+  __syncthreads();
+  if (t < 4) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= kc[8 * t + j] << (4 * j);
+    *reinterpret_cast<uint32_t*>(idx_codes + row * 64 + 16 * ct + 4 * t) = w;
+  }
+}
+
+// After the write: advance len (m = 1, or the second token of an m = 2
+// group), or hold the token (first of an m = 2 group).  A full sequence is
+// left as it is.  One wave per sequence.
+__global__ __launch_bounds__(64) void cache_advance_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ gate, int m, int64_t cap,
+    int32_t* __restrict__ len, int32_t* __restrict__ count, uint16_t* __restrict__ plat,
+    uint16_t* __restrict__ pgate) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int32_t L = len[b];
+  const bool full = L < 0 || (int64_t)L >= cap;
+  const int32_t c = m == 2 ? count[b] : 1;
+  __syncthreads();  // every lane has read len and count before lane 0 moves them
+  if (full) return;
+  if (c == 0) {
+    const uint4* src = reinterpret_cast<const uint4*>(latent + (int64_t)b * 512);
+    const uint4* srg = reinterpret_cast<const uint4*>(gate + (int64_t)b * 512);
+    reinterpret_cast<uint4*>(plat + (int64_t)b * 512)[t] = src[t];
+    reinterpret_cast<uint4*>(pgate + (int64_t)b * 512)[t] = srg[t];
+    if (t == 0) count[b] = 1;
+  } else if (t == 0) {
+    if (m == 2) count[b] = 0;
+    len[b] = L + 1;
+  }
+}
+
+int launch_cache_append(const uint16_t* latent, const uint16_t* gate, int B, int m, const float* gamma,
+                        float eps, const float* w_idx, int main_fmt, int rope, uint8_t* main_codes,
+                        uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales, int64_t cap,
+                        int32_t* len, void* state, hipStream_t st) {
+  if (B == 0) return 0;
+  AppendState s{nullptr, nullptr, nullptr};
+  if (m == 2) s = append_state(state, B);
+  if (main_fmt == 0)
+    cache_append_kernel<0><<<dim3(B, 4), 256, 0, st>>>(latent, gate, m, gamma, eps, w_idx, rope, main_codes,
+                                              main_scales, idx_codes, idx_scales, cap, len, s.count, s.lat,
+                                              s.gate);
+  else
+    cache_append_kernel<1><<<dim3(B, 4), 256, 0, st>>>(latent, gate, m, gamma, eps, w_idx, rope, main_codes,
+                                              main_scales, idx_codes, idx_scales, cap, len, s.count, s.lat,
+                                              s.gate);
+  cache_advance_kernel<<<B, 64, 0, st>>>(latent, gate, m, cap, len, s.count, s.lat, s.gate);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace csa2

@@ -142,6 +142,38 @@ int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, in
                      uint8_t* idx_codes, uint8_t* idx_scales, void* stream);
 
 /*
+ * csa2_cache_append -- decode-time append [JU 四 item 1; GP 3.2]: one new
+ * token per sequence.  A decoder layer (m = 1) writes one compressed entry
+ * per token; a layer with m = 2 writes one entry per two tokens and holds
+ * the first token of each group in `state` until its partner arrives.
+ *   latent, gate : bf16 bits [B][512], the new token of each sequence (gate
+ *                  is read only when m == 2).
+ *   m            : 1 or 2.
+ *   gamma, eps, w_idx, main_fmt : as csa2_cache_write.
+ *   rope         : non-zero to rotate each written entry by the compressed
+ *                  RoPE at its own row index len[b] (csa2_cache_write's
+ *                  rope_pos, with the entry index as the position).
+ *   main_codes/main_scales/idx_codes/idx_scales : the cache planes
+ *                  [B][cap][256] / [B][cap][32] / [B][cap][64] / [B][cap][4].
+ *   len          : int32 [B], in/out.  A written entry goes to row len[b] and
+ *                  len[b] then grows by one.  A sequence with len[b] >= cap is
+ *                  full: nothing is written or held, and len[b] stays.
+ *   state        : m == 2 only (else may be NULL): csa2_append_state_bytes(B)
+ *                  bytes, zero-filled once before the first call, then owned
+ *                  by the calls (per sequence: tokens held, and the held
+ *                  token's latent and gate).  16-byte aligned.
+ * The entry written equals csa2_cache_write of the group's tokens.  Two
+ * launches on `stream` (the write, then the advance of len/state); no
+ * allocation, no memset, so it may be captured in a graph.  Calls sharing
+ * `len` or `state` must be ordered on one stream.
+ */
+size_t csa2_append_state_bytes(int32_t B);
+int csa2_cache_append(const uint16_t* latent, const uint16_t* gate, int32_t B, int32_t m,
+                      const float* gamma, float eps, const float* w_idx, int32_t main_fmt, int32_t rope,
+                      uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales,
+                      int64_t cap, int32_t* len, void* state, void* stream);
+
+/*
  * csa2_index_full -- Full-mode hierarchical sparse indexer: one scoring pass
  * over every visible entry, feeding two selections [GP 3.3; SY Figure 5; WG 3.2]:
  *   score[b][p] = sum_h w[b][h] * max(0, q[b][h] . deq(idx K[b][p]))  for p < len[b]

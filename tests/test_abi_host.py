@@ -36,7 +36,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert {"csa2_cache_write", "csa2_index_full", "csa2_index_pool", "csa2_sparse_attn_decode",
+    assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
+            "csa2_index_pool", "csa2_sparse_attn_decode",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -73,6 +74,34 @@ def test_cache_write_validation(lib):
     assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 5, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUP
     assert f(FAKE_ODD, None, 8, 1, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN
     assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 0, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN  # positions
+
+
+def test_cache_append_validation(lib):
+    f = lib.csa2_cache_append
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f.argtypes = [P, P, i32, i32, P, ctypes.c_float, P, i32, i32, P, P, P, P, i64, P, P, P]
+    lib.csa2_append_state_bytes.restype = ctypes.c_size_t
+    lib.csa2_append_state_bytes.argtypes = [i32]
+    assert lib.csa2_append_state_bytes(16) == 256 + 16 * 2048
+    assert lib.csa2_append_state_bytes(0) == 0
+    base = [FAKE, FAKE, 4, 2, None, 1e-6, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return f(*args)
+
+    assert call(3, 3) == ERR_SHAPE        # m
+    assert call(13, 0) == ERR_SHAPE       # cap
+    assert call(7, 9) == ERR_UNSUP        # scale format
+    assert call(15, None) == ERR_NULL     # state needed for m = 2
+    assert call(14, None) == ERR_NULL     # lengths
+    assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(2, 0) == CSA2_OK          # empty batch: nothing to do
+    args = list(base)
+    args[3], args[1], args[15] = 1, None, None   # m = 1: gate and state not needed
+    args[0] = None
+    assert f(*args) == ERR_NULL                  # but the latent is
 
 
 def _index_full(lib):

@@ -355,3 +355,48 @@ def test_cache_write_parity(m, fmt, gamma, n, rope):
     assert (g["main_codes"] == ref["main_codes"]).mean() > 0.999
     assert (g["idx_codes"] == ref["idx_codes"]).mean() > 0.999
 
+
+
+@pytest.mark.parametrize("m,fmt,rope", [(1, 0, False), (1, 1, True), (2, 0, True), (2, 1, False)])
+def test_cache_append_streams_like_a_batch_write(m, fmt, rope):
+    """Tokens appended one step at a time land where a batch write of the
+    same tokens puts them: rows len0.., RoPE at the row index, the first token
+    of an m = 2 group held until its partner; a sequence with one free row
+    takes one entry, a full one takes nothing; other rows are untouched."""
+    say(f"cache append m={m} fmt={fmt} rope={rope}")
+    B, cap, steps = 5, 40, 11
+    len0 = np.array([0, 3, 10, 39, 40], np.int32)
+    g = torch.Generator().manual_seed(50 + m + fmt)
+    lat = syn.as_bf16_bits(torch.randn(steps, B, 512, generator=g))
+    gate = syn.as_bf16_bits(torch.randn(steps, B, 512, generator=g))
+    w = (torch.randn(512, 128, generator=g) / np.sqrt(512)).float()
+    cache = {k_: torch.full((B, cap, wd), 0xAB, dtype=torch.uint8, device=DEV)
+             for k_, wd in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4))}
+    lengths = torch.from_numpy(len0.copy()).to(DEV)
+    state = K.append_state(B, DEV) if m == 2 else None
+    wd = w.to(DEV)
+    for t in range(steps):
+        K.cache_append(lat[t].to(DEV), gate[t].to(DEV), m, wd, fmt, cache, lengths, state=state, rope=rope)
+    torch.cuda.synchronize()
+    got = {k_: v.cpu().numpy() for k_, v in cache.items()}
+    n_entries = steps // m
+    want_len = np.minimum(cap, len0 + n_entries)
+    want_len[len0 >= cap] = len0[len0 >= cap]
+    assert np.array_equal(lengths.cpu().numpy(), want_len)
+    if m == 2:
+        held = state[:4 * B].view(torch.int32).cpu().numpy()
+        assert np.array_equal(held, np.where(len0 + n_entries <= cap, steps % 2, 0))
+    for b in range(B):
+        ne = int(want_len[b] - len0[b])
+        rows = slice(int(len0[b]), int(want_len[b]))
+        if ne > 0:
+            toks = slice(0, ne * m)
+            ref = oracle.cache_write(lat[toks, b].numpy(), gate[toks, b].numpy(), m, w.numpy(), fmt,
+                                     rope_pos=np.arange(len0[b], len0[b] + ne, dtype=np.int64) if rope else None)
+            nm = _certified_code_mismatch(ref["y"], ref["main_codes"], ref["main_scales"],
+                                          got["main_codes"][b, rows], got["main_scales"][b, rows], 16, fmt)
+            nk = _certified_code_mismatch(ref["k"], ref["idx_codes"], ref["idx_scales"],
+                                          got["idx_codes"][b, rows], got["idx_scales"][b, rows], 32, 0)
+            assert nm + nk <= 2
+        for k_ in got:
+            assert (got[k_][b, : int(len0[b])] == 0xAB).all() and (got[k_][b, int(want_len[b]):] == 0xAB).all()
