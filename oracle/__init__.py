@@ -52,7 +52,10 @@ def _load():
     lib.oracle_index_full.restype = i64
     lib.oracle_index_full.argtypes = [P, P, i64, P, P, i32, i32, i32, i32, P, P, P]
     lib.oracle_index_pool.argtypes = [P, P, i64, P, i64, P, P, i32, i32, P, P]
-    lib.oracle_attention.argtypes = [P, i32, P, P, i64, i32, P, i32, P, P, i32, f32, P, P, P]
+    lib.oracle_attention.argtypes = [P, i32, P, P, i64, i32, P, i32, P, P, i32, i32, f32, P, P, P]
+    lib.oracle_fp8_record.argtypes = [P, P, P]
+    lib.oracle_fp8_record_decode.argtypes = [P, P, i64, P]
+    lib.oracle_window_write.argtypes = [P, i64, i32, P, f32, i32, P, i32, P, P, P, P]
     lib.oracle_num_threads.restype = i32
     _lib = lib
     return lib
@@ -212,9 +215,11 @@ def index_pool(idx_codes, idx_scales, length, pool, pool_len, q_bf16, w, k):
 
 # ------------------------------------------------------------------- attention
 def attention(q_bf16, main_codes, main_scales, length, main_fmt, topk, swa_codes, swa_scales,
-              swa_len, sm_scale, q_pos=None):
+              swa_len, sm_scale, q_pos=None, swa_fmt=0):
     """One sequence: q uint16 [H][512]. Returns (out fp32 [H][512], lse fp32 [H]).
-    q_pos: the query's position for Q RoPE and output inverse RoPE, or None."""
+    q_pos: the query's position for Q RoPE and output inverse RoPE, or None.
+    swa_fmt 0: window rows in the main format ([W][256] codes, [W][32] scales);
+    swa_fmt 1: FP8 window records ([W][576] data, [W][8] scales)."""
     q = _c(q_bf16, np.uint16)
     H = q.shape[0]
     mc = _c(main_codes, np.uint8)
@@ -229,5 +234,50 @@ def attention(q_bf16, main_codes, main_scales, length, main_fmt, topk, swa_codes
     lse = np.zeros(H, np.float32)
     qp = None if q_pos is None else np.array([q_pos], np.int64)
     _load().oracle_attention(_p(q), H, _p(mc), _p(ms), length, main_fmt, _p(t), t.shape[0],
-                             _p(sc), _p(ss), swa_len, float(sm_scale), _p(qp), _p(out), _p(lse))
+                             _p(sc), _p(ss), swa_len, int(swa_fmt), float(sm_scale), _p(qp), _p(out),
+                             _p(lse))
     return out, lse
+
+
+def fp8_record(y):
+    """Rows float32 [..][512] -> FP8 window records (data u8 [..][576], scales u8 [..][8])."""
+    y = _c(y, np.float32)
+    lead = y.shape[:-1]
+    y2 = y.reshape(-1, 512)
+    data = np.zeros((y2.shape[0], 576), np.uint8)
+    sc = np.zeros((y2.shape[0], 8), np.uint8)
+    for r in range(y2.shape[0]):
+        _load().oracle_fp8_record(_p(y2[r]), _p(data[r]), _p(sc[r]))
+    return data.reshape(*lead, 576), sc.reshape(*lead, 8)
+
+
+def fp8_record_decode(data, scales):
+    """FP8 window records -> float64 rows [..][512]."""
+    d = _c(data, np.uint8)
+    s = _c(scales, np.uint8)
+    lead = d.shape[:-1]
+    out = np.zeros((int(np.prod(lead, dtype=np.int64)), 512), np.float64)
+    _load().oracle_fp8_record_decode(_p(d), _p(s), out.shape[0], _p(out))
+    return out.reshape(*lead, 512)
+
+
+def window_write(latent, pos0, W, gamma=None, eps=1e-6, rope=False, data=None, scales=None):
+    """Write tokens into the FP8 window ring.  latent bf16 bits [B][n][512];
+    pos0 int64 [B] (position of token 0); W slots.  data/scales (u8 [B][W][576],
+    [B][W][8]) are updated in place when given (else start zeroed).
+    Returns dict(data, scales, swa_len int32 [B], y float32 [B][n][512])."""
+    x = _c(latent, np.uint16)
+    B, n = x.shape[0], x.shape[1]
+    p0 = _c(pos0, np.int64)
+    if data is None:
+        data = np.zeros((B, W, 576), np.uint8)
+    if scales is None:
+        scales = np.zeros((B, W, 8), np.uint8)
+    assert data.dtype == np.uint8 and data.flags.c_contiguous and data.shape == (B, W, 576)
+    assert scales.dtype == np.uint8 and scales.flags.c_contiguous and scales.shape == (B, W, 8)
+    g = None if gamma is None else _c(gamma, np.float32)
+    swa_len = np.zeros(B, np.int32)
+    y = np.zeros((B, n, 512), np.float32)
+    _load().oracle_window_write(_p(x), B, n, _p(g), float(eps), int(bool(rope)), _p(p0), W, _p(data),
+                                _p(scales), _p(swa_len), _p(y))
+    return dict(data=data, scales=scales, swa_len=swa_len, y=y)

@@ -9,7 +9,7 @@
  *   [WG] weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本" (sections 3.1, 3.2, 10)
  *   [SY] syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B"
  *        (CSA2 / Figure 4, Hierarchical Sparse Indexer / Figure 5, FP4 主 KV 缓存)
- *   [GP] ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析" (3.2, 3.3, 7)
+ *   [GP] ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析" (3.2, 3.3, 4.1, 7)
  *
  * Style: scalar loops, double-precision accumulation, qsort for orderings,
  * OpenMP only across independent entries / heads.  Float results are the
@@ -17,7 +17,7 @@
  *
  * Parity status of each function (pins live in tests/test_oracle_*.py):
  *   decode tables, quantiser, byte accounting, scoring, top-k, block pool,
- *   reindex, attention, cache write: pinned (closed forms, library routines,
+ *   reindex, attention, cache write, RoPE, FP8 window record and ring: pinned (closed forms, library routines,
  *   brute force, invariants).  End-to-end values of a full decode step have
  *   no printed worked example on the pages: that composition is
  *   "parity unpinned" beyond the per-step pins.
@@ -240,6 +240,129 @@ void oracle_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T,
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 sliding-window record                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* [GP 4.1] each layer keeps a 128-token window whose entries stay in FP8
+ * (they are more sensitive to quantisation than the compressed entries);
+ * [GP 7] a record is 448 B of position-free dims + 128 B of RoPE dims + 8 B
+ * of scale = 584 B per token, paged with 576-B alignment; [WG 10.1] the FP8
+ * window record is kept when the compressed cache is FP4; [JU 顺便算清另外三笔账]
+ * the window cache has a constant 128 slots per sequence, overwritten as a
+ * ring.  Readings (the byte counts are the pages'; the rest is the plainest
+ * reading that fits them):
+ *   - dims 0..447: OCP E4M3 codes (bias 7, largest finite 448, the value
+ *     [GP 7] multiplies by 6 for its range argument), one UE8M0 scale byte per
+ *     64 dims: 7 bytes, then one zero pad byte = the 8 B of scale;
+ *   - dims 448..511: bf16 (64 x 2 B = the 128 B of RoPE dims);
+ *   - a slot's 576 data bytes sit at a 576-B stride, its 8 scale bytes in a
+ *     plane of their own;
+ *   - scale = the smallest 2^(b-127) with 448*scale >= max|x| of the 64 dims
+ *     (b = 0 for an all-zero group); each x/scale goes to the nearest E4M3
+ *     value, an exact tie to the even code; a zero magnitude is +0;
+ *   - bf16 dims are the value rounded to nearest, ties to even. */
+
+/* nearest bf16 of a finite float, ties to the even pattern */
+static uint16_t bf16_nearest(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  uint16_t lo = (uint16_t)(u >> 16); /* toward zero */
+  uint16_t hi = (uint16_t)(lo + 1);  /* next magnitude up */
+  double dl = fabs((double)x - bf16_value(lo)), dh = fabs(bf16_value(hi) - (double)x);
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (lo & 1) ? hi : lo;
+}
+
+/* 64 values -> 64 E4M3 codes + 1 UE8M0 scale byte */
+static void fp8_group(const float* x, uint8_t* codes, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < 64; ++i)
+    if (fabs((double)x[i]) > amax) amax = fabs((double)x[i]);
+  int b = 0;
+  if (amax > 0.0) {
+    b = 254;
+    for (int c = 0; c <= 254; ++c)
+      if (448.0 * ldexp(1.0, c - 127) >= amax) {
+        b = c;
+        break;
+      }
+  }
+  *scale = (uint8_t)b;
+  const double s = ldexp(1.0, b - 127);
+  for (int i = 0; i < 64; ++i) {
+    const double a = fabs((double)x[i]);
+    int code = 0;
+    /* codes 0..126 are the finite magnitudes in increasing order */
+    for (int c = 1; c <= 126 && a > 0.0; ++c) {
+      const double mid = 0.5 * (oracle_scale_value((uint8_t)(c - 1), FMT_E4M3) +
+                                oracle_scale_value((uint8_t)c, FMT_E4M3)) * s;
+      if (a > mid || (a == mid && (c % 2) == 0)) code = c;
+    }
+    if (code != 0 && x[i] < 0.0f) code |= 0x80;
+    codes[i] = (uint8_t)code;
+  }
+}
+
+/* one 512-dim float row -> 576 data bytes + 8 scale bytes */
+void oracle_fp8_record(const float* y, uint8_t* data, uint8_t* scales) {
+  for (int g = 0; g < 7; ++g) fp8_group(y + 64 * g, data + 64 * g, scales + g);
+  scales[7] = 0;
+  for (int d = 448; d < 512; ++d) {
+    const uint16_t h = bf16_nearest(y[d]);
+    data[448 + 2 * (d - 448)] = (uint8_t)(h & 0xFF);
+    data[449 + 2 * (d - 448)] = (uint8_t)(h >> 8);
+  }
+}
+
+/* value of dim d of a record */
+static double fp8_record_elem(const uint8_t* data, const uint8_t* scales, int d) {
+  if (d < 448) return oracle_scale_value(data[d], FMT_E4M3) * ldexp(1.0, (int)scales[d / 64] - 127);
+  const int j = 448 + 2 * (d - 448);
+  return bf16_value((uint16_t)(data[j] | (data[j + 1] << 8)));
+}
+
+void oracle_fp8_record_decode(const uint8_t* data, const uint8_t* scales, int64_t rows, double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int d = 0; d < 512; ++d) out[r * 512 + d] = fp8_record_elem(data + r * 576, scales + r * 8, d);
+}
+
+/* Window write: token i of sequence b (position pos0[b] + i) is the RMS-
+ * normalised latent (the cache write's m = 1 arithmetic: no pooling), rotated
+ * by the compressed RoPE at its position when rope != 0, stored as a record
+ * in slot (position mod W).  Tokens are written in order, so a later token
+ * overwrites an earlier one in the same slot.  swa_len[b] = min(pos0[b] + n, W):
+ * the window then holds the last min(pos0[b] + n, W) tokens.
+ * latent: bf16 [B][n][512]; data [B][W][576]; scales [B][W][8];
+ * y_out (or NULL): float [B][n][512], the rows before FP8. */
+void oracle_window_write(const uint16_t* latent, int64_t B, int n, const float* gamma, float eps,
+                         int rope, const int64_t* pos0, int W, uint8_t* data, uint8_t* scales,
+                         int32_t* swa_len, float* y_out) {
+  const int D = 512;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int i = 0; i < n; ++i) {
+      const uint16_t* x = latent + (b * n + i) * D;
+      const int64_t p = pos0[b] + i;
+      double ss = 0.0;
+      for (int c = 0; c < D; ++c) ss += bf16_value(x[c]) * bf16_value(x[c]);
+      const double r = 1.0 / sqrt(ss / D + (double)eps);
+      float y[512];
+      for (int c = 0; c < D; ++c) y[c] = (float)(bf16_value(x[c]) * r * (gamma ? (double)gamma[c] : 1.0));
+      if (rope) {
+        double yr[512];
+        for (int c = 0; c < D; ++c) yr[c] = (double)y[c];
+        oracle_rope(yr, p, 0);
+        for (int c = 0; c < D; ++c) y[c] = (float)yr[c];
+      }
+      const int64_t slot = p % W;
+      oracle_fp8_record(y, data + (b * W + slot) * 576, scales + (b * W + slot) * 8);
+      if (y_out) memcpy(y_out + (b * n + i) * D, y, sizeof y);
+    }
+    swa_len[b] = (int32_t)(pos0[b] + n < W ? pos0[b] + n : W);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Indexer scoring                                                            */
 /* ------------------------------------------------------------------------ */
 
@@ -396,7 +519,7 @@ void oracle_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int6
 void oracle_attention(const uint16_t* q, int H, const uint8_t* main_codes,
                       const uint8_t* main_scales, int64_t len, int main_fmt,
                       const int32_t* topk, int k, const uint8_t* swa_codes,
-                      const uint8_t* swa_scales, int swa_len, float sm_scale,
+                      const uint8_t* swa_scales, int swa_len, int swa_fmt, float sm_scale,
                       const int64_t* q_pos, float* out, float* lse) {
   const int D = 512;
   int nrow = 0;
@@ -412,9 +535,12 @@ void oracle_attention(const uint16_t* q, int H, const uint8_t* main_codes,
       rows[(int64_t)r * D + d] = fp4_elem(main_codes + p * 256, main_scales + p * 32, 16, main_fmt, d);
     ++r;
   }
+  /* window rows: the main format (swa_fmt 0) or FP8 records (swa_fmt 1) */
   for (int j = 0; j < swa_len; ++j, ++r)
     for (int d = 0; d < D; ++d)
-      rows[(int64_t)r * D + d] = fp4_elem(swa_codes + (int64_t)j * 256, swa_scales + (int64_t)j * 32, 16, main_fmt, d);
+      rows[(int64_t)r * D + d] =
+          swa_fmt ? fp8_record_elem(swa_codes + (int64_t)j * 576, swa_scales + (int64_t)j * 8, d)
+                  : fp4_elem(swa_codes + (int64_t)j * 256, swa_scales + (int64_t)j * 32, 16, main_fmt, d);
 #pragma omp parallel for schedule(static)
   for (int h = 0; h < H; ++h) {
     double* logit = (double*)malloc(sizeof(double) * (nrow > 0 ? nrow : 1));
