@@ -6,6 +6,8 @@ device memory and streams)."""
 from ._lib import (  # noqa: F401
     E4M3,
     E8M0,
+    SWA_FP8,
+    SWA_MAIN,
     Csa2Error,
     append_state,
     cache_append,
@@ -15,6 +17,8 @@ from ._lib import (  # noqa: F401
     lib,
     quantize_fp4,
     sparse_attn_decode,
+    window_alloc,
+    window_write,
     workspace,
 )
 

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libcsa2.so")
 
 E8M0 = 0
 E4M3 = 1
+SWA_MAIN = 0  # window rows in the main-KV format
+SWA_FP8 = 1  # window rows as FP8 records (576 + 8 B)
 
 _lib = None
 
@@ -55,7 +57,8 @@ def lib():
     L.csa2_attn_workspace.restype = sz
     L.csa2_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
-                                          P, f32, P, P, P, P, sz, P]
+                                          P, i32, f32, P, P, P, P, sz, P]
+    L.csa2_window_write.argtypes = [P, i32, i32, P, f32, i32, P, i32, P, P, P, P]
     _lib = L
     return L
 
@@ -217,6 +220,34 @@ def cache_append(latent, gate, m: int, w_idx, main_fmt: int, cache: dict, length
                                    _ptr(state) if m == 2 else None, _stream(dev)), "csa2_cache_append")
 
 
+def window_alloc(B: int, W: int = 128, device="cuda"):
+    """Zeroed FP8 window ring: data u8 [B][W][576], scales u8 [B][W][8], swa_len int32 [B]."""
+    return dict(data=torch.zeros(B, W, 576, dtype=torch.uint8, device=device),
+                scales=torch.zeros(B, W, 8, dtype=torch.uint8, device=device),
+                swa_len=torch.zeros(B, dtype=torch.int32, device=device))
+
+
+def window_write(latent, pos0, window: dict, gamma=None, eps: float = 1e-6, rope: bool = False):
+    """Write n tokens per sequence into the FP8 window ring (window_alloc's dict,
+    updated in place).  latent bf16 (or int16 bits) [B][n][512]; pos0 int64 [B]:
+    position of token 0; token at position p goes to slot p mod W."""
+    latent = _bits16(latent)
+    _req(latent, "latent", torch.int16)
+    dev = latent.device
+    B, n = latent.shape[0], latent.shape[1]
+    _req(latent, "latent", torch.int16, dev, (B, n, 512))
+    W = window["data"].shape[1]
+    _req(window["data"], "window data", torch.uint8, dev, (B, W, 576))
+    _req(window["scales"], "window scales", torch.uint8, dev, (B, W, 8))
+    _req(window["swa_len"], "swa_len", torch.int32, dev, (B,))
+    _req(pos0, "pos0", torch.int64, dev, (B,))
+    if gamma is not None:
+        _req(gamma, "gamma", torch.float32, dev, (512,))
+    _check(lib().csa2_window_write(_ptr(latent), B, n, _ptr(gamma), float(eps), 1 if rope else 0, _ptr(pos0), W,
+                                   _ptr(window["data"]), _ptr(window["scales"]), _ptr(window["swa_len"]),
+                                   _stream(dev)), "csa2_window_write")
+
+
 def _index_query(q, dev, B):
     """bf16 queries [B][H][128] -> (H, q bits, None, None); FP4 queries given as
     (codes u8 [B][H][64], E8M0 scales u8 [B][H][4]) -> (H, None, codes, scales)."""
@@ -322,14 +353,16 @@ def index_pool(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 51
 def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
                        swa_codes=None, swa_scales=None, swa_len=None, swa_stride: int = 0,
                        swa_cap: int = 0, swa_row0: int = 0, sm_scale: Optional[float] = None,
-                       return_lse: bool = False, out=None, _ws=None, q_pos=None):
+                       return_lse: bool = False, out=None, _ws=None, q_pos=None, swa_fmt: int = 0):
     """Sparse attention over topk rows ++ window rows.
 
     q bf16/int16 [B][H][512]; main planes [B][cap][256] / [B][cap][32];
     topk int32 [B][k]; window row r of sequence b is row swa_row0 + b*swa_stride + r
-    of the contiguous tensors swa_codes (rows of 256 B) / swa_scales (rows of 32 B),
-    so the window may be a separate buffer or the tail of the main cache
-    (swa_codes=main_codes, swa_row0=cap-128, swa_stride=cap); swa_len int32 [B].
+    of the contiguous tensors swa_codes / swa_scales, so the window may be a
+    separate buffer or the tail of the main cache (swa_codes=main_codes,
+    swa_row0=cap-128, swa_stride=cap); swa_len int32 [B].  swa_fmt 0: window rows
+    in the main format (rows of 256 B / 32 B); swa_fmt 1 (SWA_FP8): FP8 window
+    records (rows of 576 B / 8 B, as window_write produces).
     q_pos int64 [B]: query positions for Q RoPE and output inverse RoPE (or None).
     Returns out bf16 bits (int16) [B][H][512] (and lse fp32 [B][H]).
     """
@@ -351,8 +384,11 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
             raise ValueError("window planes on another device")
         if not (swa_codes.is_contiguous() and swa_scales.is_contiguous()):
             raise ValueError("window planes must be contiguous")
+        if swa_fmt not in (SWA_MAIN, SWA_FP8):
+            raise ValueError("swa_fmt must be 0 (main format) or 1 (FP8 records)")
+        rb, sb = (576, 8) if swa_fmt == SWA_FP8 else (256, 32)
         need = swa_row0 + (B - 1) * swa_stride + swa_cap
-        if swa_row0 < 0 or swa_codes.numel() < need * 256 or swa_scales.numel() < need * 32:
+        if swa_row0 < 0 or swa_codes.numel() < need * rb or swa_scales.numel() < need * sb:
             raise ValueError("window planes smaller than swa_row0 + B rows of swa_stride")
         _req(swa_len, "swa_len", torch.int32, dev, (B,))
     if sm_scale is None:
@@ -369,8 +405,9 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
     ws = _ws if _ws is not None else workspace(wsb, dev, "attn")
     _check(lib().csa2_sparse_attn_decode(
         _ptr(q), H, _ptr(main_codes), _ptr(main_scales), cap, main_fmt, _ptr(lengths), _ptr(topk), k,
-        B, ctypes.c_void_p(swa_codes.data_ptr() + 256 * swa_row0) if swa_cap else None,
-        ctypes.c_void_p(swa_scales.data_ptr() + 32 * swa_row0) if swa_cap else None,
-        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, float(sm_scale), _ptr(q_pos), _ptr(o),
+        B, ctypes.c_void_p(swa_codes.data_ptr() + rb * swa_row0) if swa_cap else None,
+        ctypes.c_void_p(swa_scales.data_ptr() + sb * swa_row0) if swa_cap else None,
+        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, int(swa_fmt) if swa_cap else 0,
+        float(sm_scale), _ptr(q_pos), _ptr(o),
         _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode")
     return (o, lse) if return_lse else o

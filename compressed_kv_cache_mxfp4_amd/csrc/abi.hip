@@ -86,6 +86,21 @@ int csa2_cache_append(const uint16_t* latent, const uint16_t* gate, int32_t B, i
                                             as_stream(stream)));
 }
 
+int csa2_window_write(const uint16_t* latent, int32_t B, int32_t n, const float* gamma, float eps,
+                      int32_t rope, const int64_t* pos0, int32_t W, uint8_t* win_data,
+                      uint8_t* win_scales, int32_t* swa_len, void* stream) {
+  if (B < 0 || n < 0 || W < 1 || W > CSA2_SWA) return CSA2_ERR_SHAPE;
+  if (!(eps >= 0.0f)) return CSA2_ERR_SHAPE;
+  if (B == 0 || n == 0) return CSA2_OK;
+  if (!latent || !pos0 || !win_data || !win_scales || !swa_len) return CSA2_ERR_NULL;
+  if (!aligned16(latent) || !aligned16(win_data) || (reinterpret_cast<uintptr_t>(win_scales) & 7u) ||
+      (reinterpret_cast<uintptr_t>(pos0) & 7u) || (reinterpret_cast<uintptr_t>(swa_len) & 3u) ||
+      (reinterpret_cast<uintptr_t>(gamma) & 3u))
+    return CSA2_ERR_ALIGN;
+  return launched(csa2::launch_window_write(latent, B, n, gamma, eps, rope ? 1 : 0, pos0, W, win_data,
+                                            win_scales, swa_len, as_stream(stream)));
+}
+
 size_t csa2_index_full_workspace(int32_t B, int64_t cap, int32_t k, int32_t block,
                                  int32_t n_blocks) {
   (void)k;
@@ -195,13 +210,14 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
                             const uint8_t* swa_codes, const uint8_t* swa_scales,
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
-                            float sm_scale, const int64_t* q_pos, uint16_t* out, float* lse_opt,
-                            void* ws, size_t ws_bytes, void* stream) {
+                            int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                            float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
   if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
   if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
   if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
   if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (swa_fmt != CSA2_SWA_MAIN && swa_fmt != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
   if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
   if (B == 0) return CSA2_OK;
@@ -210,12 +226,13 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
   if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
   if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
   if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
-      (reinterpret_cast<uintptr_t>(q_pos) & 7u))
+      (reinterpret_cast<uintptr_t>(q_pos) & 7u) ||
+      (swa_fmt == CSA2_SWA_FP8 && (reinterpret_cast<uintptr_t>(swa_scales) & 7u)))
     return CSA2_ERR_ALIGN;
   if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
   return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
                                            k, B, swa_codes, swa_scales, swa_stride, swa_cap,
-                                           swa_len, sm_scale, q_pos, out, lse_opt, ws,
+                                           swa_len, swa_fmt, sm_scale, q_pos, out, lse_opt, ws,
                                            as_stream(stream)));
 }
 

@@ -32,6 +32,8 @@
 //    with the gfx950 transpose read (ds_read_b64_tr_b16): within a 16-lane
 //    group, source lane a+4j points at R[r0+j][d0+4a] and lane n receives
 //    R[r0..r0+3][d0+n], i.e. four K slots of the MFMA B operand.
+#include <type_traits>
+
 #include "csa2.h"
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
@@ -105,35 +107,52 @@ struct RowFetch {
   uint4 c[4];   // code bytes: c[0..1] dims 64g..64g+63, c[2..3] dims 256+64g..256+64g+63
   uint32_t s[2];  // scale bytes: s[0] groups 4g..4g+3, s[1] groups 16+4g..16+4g+3
   uint32_t ok;  // row exists and is visible
+  // FP8 window record (lane group g): c[0..3] E4M3 dims 64g..64g+63,
+  // x[0..2] E4M3 dims 256+48g..256+48g+47, x[3..4] bf16 dims 448+16g..+15,
+  // s[0..1] the record's 8 UE8M0 bytes (byte i: dims 64i..64i+63)
+  uint4 x[5];
+  uint32_t win;  // the row is an FP8 window record
 };
 
 struct RowSrc {
   const uint8_t* codes;
   const uint8_t* scales;
   uint32_t ok;
+  uint32_t win;
 };
 
+// FP8 window record: 576 data bytes (E4M3 dims 0..447, bf16 dims 448..511)
+// and 8 scale bytes per slot.
+constexpr int kWinDataB = 576;
+constexpr int kWinScaleB = 8;
+
 // Where row slot `slot` of sequence b lives (selected entry or window entry);
-// `p` is the already-loaded index-list entry for slots below k.
-__device__ __forceinline__ RowSrc locate_row(int slot, int32_t p, int nslots, int b, int k,
+// `p` is the already-loaded index-list entry for slots below k.  Window
+// entries take slots kw.. (kw = k, or k rounded up to 16 for FP8 records, so
+// that no wave mixes the two row layouts: a wave's query fragments follow
+// one layout); slots k..kw-1 are empty.
+template <bool WF8>
+__device__ __forceinline__ RowSrc locate_row(int slot, int32_t p, int nslots, int b, int k, int kw,
                                              int64_t L, int SL, int64_t cap, int64_t swa_stride,
                                              const uint8_t* __restrict__ main_codes,
                                              const uint8_t* __restrict__ main_scales,
                                              const uint8_t* __restrict__ swa_codes,
                                              const uint8_t* __restrict__ swa_scales) {
-  RowSrc r{nullptr, nullptr, 0u};
+  RowSrc r{nullptr, nullptr, 0u, 0u};
   if (slot < k) {
     if (p >= 0 && (int64_t)p < L) {
       r.codes = main_codes + ((int64_t)b * cap + p) * 256;
       r.scales = main_scales + ((int64_t)b * cap + p) * 32;
       r.ok = 1u;
     }
-  } else if (slot < nslots) {
-    const int rr = slot - k;
+  } else if (slot >= kw && slot < nslots) {
+    const int rr = slot - kw;
     if (rr < SL) {
-      r.codes = swa_codes + ((int64_t)b * swa_stride + rr) * 256;
-      r.scales = swa_scales + ((int64_t)b * swa_stride + rr) * 32;
+      const int64_t wr = (int64_t)b * swa_stride + rr;
+      r.codes = swa_codes + wr * (WF8 ? kWinDataB : 256);
+      r.scales = swa_scales + wr * (WF8 ? kWinScaleB : 32);
       r.ok = 1u;
+      r.win = WF8 ? 1u : 0u;
     }
   }
   return r;
@@ -155,6 +174,58 @@ __device__ __forceinline__ void fetch_row(RowFetch& f, const RowSrc& r, int g) {
     f.s[0] = f.s[1] = 0u;
   }
   f.ok = r.ok;
+}
+
+// FP8 window record: the lane's slice as in RowFetch (an invisible row reads
+// as zeros).
+__device__ __forceinline__ void fetch_row_w8(RowFetch& f, const RowSrc& r, int g) {
+  if (r.ok && r.win) {
+    const uint4* lo = reinterpret_cast<const uint4*>(r.codes + 64 * g);
+    const uint4* hi = reinterpret_cast<const uint4*>(r.codes + 256 + 48 * g);
+    const uint4* rp = reinterpret_cast<const uint4*>(r.codes + 448 + 32 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.c[j] = lo[j];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) f.x[j] = hi[j];
+    f.x[3] = rp[0];
+    f.x[4] = rp[1];
+    const uint2 sc = *reinterpret_cast<const uint2*>(r.scales);
+    f.s[0] = sc.x;
+    f.s[1] = sc.y;
+  } else if (r.ok) {
+    const uint4* lo = reinterpret_cast<const uint4*>(r.codes + 32 * g);
+    const uint4* hi = reinterpret_cast<const uint4*>(r.codes + 128 + 32 * g);
+    f.c[0] = lo[0];
+    f.c[1] = lo[1];
+    f.c[2] = hi[0];
+    f.c[3] = hi[1];
+    f.s[0] = *reinterpret_cast<const uint32_t*>(r.scales + 4 * g);
+    f.s[1] = *reinterpret_cast<const uint32_t*>(r.scales + 16 + 4 * g);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.c[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) f.x[j] = make_uint4(0u, 0u, 0u, 0u);
+    f.s[0] = f.s[1] = 0u;
+  }
+  f.ok = r.ok;
+  f.win = r.ok & r.win;
+}
+
+// Dims of K step ks in lane group g for an FP8 window record: 64g+8ks
+// (ks < 8), 256+48g+8(ks-8) (ks 8..13), 448+16g+8(ks-14) (ks 14, 15).
+__device__ __forceinline__ int step_dim_w8(int ks, int g) {
+  return ks < 8 ? 64 * g + 8 * ks : (ks < 14 ? 256 + 48 * g + 8 * (ks - 8) : 448 + 16 * g + 8 * (ks - 14));
+}
+
+// K step ks of a lane's FP8 window slice as bf16x8 (exact).
+__device__ __forceinline__ bf16x8 row_step_w8(const RowFetch& f, int ks, int g) {
+  if (ks >= 14) return __builtin_bit_cast(bf16x8, f.x[3 + (ks - 14)]);
+  const uint4 u = ks < 8 ? f.c[ks >> 1] : f.x[(ks - 8) >> 1];
+  const uint32_t lo = (ks & 1) ? u.z : u.x, hi = (ks & 1) ? u.w : u.y;
+  const int grp = step_dim_w8(ks, g) >> 6;
+  const uint32_t sb = (f.s[grp >> 2] >> (8 * (grp & 3))) & 0xFFu;
+  return fp8x8_to_bf16(lo, hi, e8m0_operand(sb));
 }
 
 // Dims of K step ks in lane group g: 64g+8ks (ks < 8), 256+64g+8(ks-8).
@@ -304,7 +375,7 @@ __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const 
 // linear order in which the head groups of one (sequence, chunk) share an XCD
 // (and its L2 copy of the chunk's rows).  Writes part[(b*H+h)*S + s][512]
 // (fp32, relative to the chunk max) and ml[(b*H+h)*S + s] = (max, sum).
-template <int FMT, int WAVES>
+template <int FMT, int WAVES, bool WF8>
 __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_kernel(
     const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
@@ -341,7 +412,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   const int sidx = within % S;
   const int b = gi / HG, hg = gi - b * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int nslots = k + swa_cap;
+  const int kw = WF8 ? (k + 15) & ~15 : k;  // first window slot
+  const int nslots = kw + swa_cap;
 
   // ---- loads: index entry, lengths and the 16 queries (to LDS, 32 B per
   // thread), then the row.  Every load is unconditional (clamped addresses,
@@ -352,6 +424,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   int vzero;  // an opaque 0 in a VGPR: keeps the length loads on the vector path
   asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
   const int slot = kRows * sidx + 16 * w + n;
+  // the wave's 16 slots are all selected entries or all window records
+  // (kw is a multiple of 16): its query fragments follow that row layout,
+  // whether or not each of its rows is visible
+  const bool wwin = WF8 && kRows * sidx + 16 * w >= kw;
   const int32_t* tp = k > 0 ? topk + (int64_t)b * k + min(slot, k - 1) : reinterpret_cast<const int32_t*>(q);
   const int32_t praw = tp[0];
   const int32_t Lraw = (len ? len + b : reinterpret_cast<const int32_t*>(q))[vzero];
@@ -373,9 +449,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
   RowFetch row;
   {
-    const RowSrc src = locate_row(slot, pidx, nslots, b, k, L, SL, cap, swa_stride, main_codes,
-                                  main_scales, swa_codes, swa_scales);
-    fetch_row(row, src, g);
+    const RowSrc src = locate_row<WF8>(slot, pidx, nslots, b, k, kw, L, SL, cap, swa_stride, main_codes,
+                                       main_scales, swa_codes, swa_scales);
+    if constexpr (WF8)
+      fetch_row_w8(row, src, g);
+    else
+      fetch_row(row, src, g);
   }
   // with 8 waves the query tile borrows the R buffer, which is then not
   // written before the max barrier
@@ -401,15 +480,28 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   for (int kb = 0; kb < 16; kb += kQB) {
     bf16x8 qf[kQB];
 #pragma unroll
-    for (int j = 0; j < kQB; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + step_dim(kb + j, g)]);
+    for (int j = 0; j < kQB; ++j) {
+      const int dq = wwin ? step_dim_w8(kb + j, g) : step_dim(kb + j, g);
+      qf[j] = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + dq]);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
     for (int j = 0; j < kQB; ++j) {
-      ra[kb + j] = row_step<FMT>(row, kb + j);
+      if constexpr (WF8)
+        ra[kb + j] = wwin ? row_step_w8(row, kb + j, g) : row_step<FMT>(row, kb + j);
+      else
+        ra[kb + j] = row_step<FMT>(row, kb + j);
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[kb + j], qf[j], sacc, 0, 0, 0);
     }
   }
   uint16_t* rrow = &sm.R[(16 * w + n) * kHLd + 64 * g];
+  // offset (from rrow) of K step 8 + ks in the second half-row: dims
+  // 256+64g+8ks, or for an FP8 window record 256+48g+8ks (ks < 6) and
+  // 448+16g+8(ks-6)
+  auto h1off = [&](int ks) -> int {
+    if (wwin) return (ks < 6 ? 48 * g + 8 * ks : 192 + 16 * g + 8 * (ks - 6)) - 64 * g;
+    return 8 * ks;
+  };
   if (Smem::kQOwn) {
     // the first half of the wave's rows goes to LDS now (R is not shared with Q)
 #pragma unroll
@@ -433,9 +525,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
 #pragma unroll
     for (int q4 = 0; q4 < 8; ++q4) {
       const uint32_t by = (row.s[q4 >> 2] >> (8 * (q4 & 3))) & 0xFFu;
-      mb = max(mb, FMT == 0 ? by : (by & 0x7Fu));  // positive E4M3 bytes order like values
+      mb = max(mb, (FMT == 0 || (WF8 && row.win)) ? by : (by & 0x7Fu));  // positive E4M3 bytes order like values
     }
     float vb = row.ok ? 6.0f * (FMT == 0 ? e8m0_value(mb) : e4m3_value(mb)) : 0.0f;
+    if (WF8 && row.win) {
+      // E4M3 dims: 448 x the largest scale; bf16 dims: their own magnitudes
+      float rm = 0.0f;
+#pragma unroll
+      for (int j = 3; j < 5; ++j) {
+        const uint32_t wd[4] = {row.x[j].x, row.x[j].y, row.x[j].z, row.x[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rm = fmaxf(rm, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(wd[i] >> 16))));
+      }
+      vb = fmaxf(448.0f * e8m0_value(mb), rm);
+    }
     if (!(vb <= 3.0e38f)) vb = 3.0e38f;  // NaN/inf scale bytes: clamp the bound
     vb = wave_max(vb);
     if (lane == 0) sm.red_v[w] = vb;
@@ -505,7 +609,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     if (h == 1) {
       __syncthreads();  // every wave is done reading the first half
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[8 + ks];
+      for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + h1off(ks)) = ra[8 + ks];
       __syncthreads();
     }
     floatx4 O[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -972,7 +1076,11 @@ static bool lds_optin(size_t bytes) {
 // wins.
 constexpr int kSeqMinBatch = 48;
 
-static int attn_splits(int k, int swa_cap) { return (k + swa_cap + kChunk - 1) / kChunk; }
+// row slots: the selected entries, then (from k rounded up to 16 when the
+// window holds FP8 records) the window entries; the workspace is sized for
+// the rounded count either way
+static int attn_slots(int k, int swa_cap, bool w8) { return (w8 ? (k + 15) & ~15 : k) + swa_cap; }
+static int attn_splits(int k, int swa_cap) { return (attn_slots(k, swa_cap, true) + kChunk - 1) / kChunk; }
 
 struct AttnWs {
   size_t cnt_off, part_off, ml_off, total;
@@ -998,10 +1106,11 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
-                       const int32_t* swa_len, float sm_scale, const int64_t* q_pos, uint16_t* out,
-                       float* lse_opt, void* ws, hipStream_t st) {
+                       const int32_t* swa_len, int swa_fmt, float sm_scale, const int64_t* q_pos,
+                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st) {
   if (B == 0) return 0;
-  const int nslots = k + swa_cap;
+  const bool w8 = swa_fmt == 1 && swa_cap > 0;
+  const int nslots = attn_slots(k, swa_cap, w8);
   const int64_t HG = H / 16;
   const int64_t groups = (int64_t)B * HG;
   if (groups > kMaxAttnGroups) return -1;
@@ -1015,7 +1124,9 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + l.cnt_off);
   uint16_t* part = reinterpret_cast<uint16_t*>(wsb + l.part_off);
   float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
-  if (H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
+  // FP8 window records are read by the split kernel only: the throughput
+  // kernel's staging lanes have no registers left for a 584-byte record
+  if (!w8 && H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
     // throughput variant: S splits per sequence, enough to give every CU a
     // workgroup, at most one per 128 row slots (the workspace's partials)
     const int nch = (nslots + kTRows - 1) / kTRows;
@@ -1044,13 +1155,24 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                                          part, ml, cnt, out, lse_opt, seq_units);
     return true;
   };
+  auto pick = [&](auto fmt_c, auto w8_c) -> bool {
+    constexpr int F = decltype(fmt_c)::value;
+    constexpr bool W8 = decltype(w8_c)::value;
+    if (ten)
+      return go(attn_split_kernel<F, 10, W8>, 10, sizeof(AttnSmem<10>),
+                lds_optin<attn_split_kernel<F, 10, W8>>(sizeof(AttnSmem<10>)));
+    return go(attn_split_kernel<F, 8, W8>, 8, sizeof(AttnSmem<8>),
+              lds_optin<attn_split_kernel<F, 8, W8>>(sizeof(AttnSmem<8>)));
+  };
+  using F0 = std::integral_constant<int, 0>;
+  using F1 = std::integral_constant<int, 1>;
+  using WN = std::integral_constant<bool, false>;
+  using WY = std::integral_constant<bool, true>;
   bool ok;
-  if (ten)
-    ok = main_fmt == 0 ? go(attn_split_kernel<0, 10>, 10, sizeof(AttnSmem<10>), lds_optin<attn_split_kernel<0, 10>>(sizeof(AttnSmem<10>)))
-                       : go(attn_split_kernel<1, 10>, 10, sizeof(AttnSmem<10>), lds_optin<attn_split_kernel<1, 10>>(sizeof(AttnSmem<10>)));
+  if (w8)
+    ok = main_fmt == 0 ? pick(F0{}, WY{}) : pick(F1{}, WY{});
   else
-    ok = main_fmt == 0 ? go(attn_split_kernel<0, 8>, 8, sizeof(AttnSmem<8>), lds_optin<attn_split_kernel<0, 8>>(sizeof(AttnSmem<8>)))
-                       : go(attn_split_kernel<1, 8>, 8, sizeof(AttnSmem<8>), lds_optin<attn_split_kernel<1, 8>>(sizeof(AttnSmem<8>)));
+    ok = main_fmt == 0 ? pick(F0{}, WN{}) : pick(F1{}, WN{});
   if (!ok) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

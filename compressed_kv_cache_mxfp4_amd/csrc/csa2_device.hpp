@@ -118,6 +118,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Eight OCP E4M3 bytes (two dwords, byte i = element i) -> bf16x8, each
+// times the power of two of an E8M0 operand (exact: E4M3 values scaled by a
+// power of two fit in bf16 for every scale a window record uses).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float e8m0_op) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, e8m0_op, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, e8m0_op, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, e8m0_op, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, e8m0_op, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

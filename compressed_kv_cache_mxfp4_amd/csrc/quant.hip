@@ -508,4 +508,117 @@ int launch_cache_append(const uint16_t* latent, const uint16_t* gate, int B, int
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// ======================================================================
+// FP8 sliding-window ring
+// ======================================================================
+// Record of one window slot: 576 data bytes -- OCP E4M3 codes of dims
+// 0..447 with one UE8M0 scale per 64 dims, then dims 448..511 as bf16 -- and
+// 8 scale bytes (7 scales and a zero pad).  The window keeps the token's own
+// RMS-normalised latent (no pooling), rotated at the token's position.
+
+// smallest UE8M0 byte b with 448 * 2^(b-127) >= amax (0 for amax == 0):
+// amax = f * 2^e with f in [0.5, 1) and 448 = 0.875 * 2^9
+__device__ __forceinline__ uint32_t fp8_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 0u;
+  int e;
+  const float f = frexpf(amax, &e);
+  const int b = e + 118 + (f > 0.875f ? 1 : 0);
+  return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
+// nearest OCP E4M3 code of v (|v| <= 448), ties to the even code; +0 for a
+// zero magnitude.  With a = |v| in binade E (floored at -6, the subnormal
+// exponent) the step is 2^(E-3) and code = 8 (E + 7) + n - 8 for the rounded
+// multiple n; n = 16 moves to the next binade by itself, and E = -6 with
+// n < 8 gives the subnormal code n.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const float a = fabsf(v);
+  if (a == 0.0f) return 0u;
+  int e;
+  (void)frexpf(a, &e);
+  const int E = max(e - 1, -6);
+  const int nq = (int)rintf(ldexpf(a, 3 - E));
+  const uint32_t code = (uint32_t)(8 * (E + 7) + nq - 8);
+  return (code != 0u && v < 0.0f) ? (code | 0x80u) : code;
+}
+
+// Grid (sequence, written token), one wave: lane t takes dims 8t..8t+7.
+// Only the last min(n, W) tokens are written (earlier ones would be
+// overwritten in the ring anyway).
+__global__ __launch_bounds__(64) void window_write_kernel(
+    const uint16_t* __restrict__ latent, int n, const float* __restrict__ gamma, float eps, int rope,
+    const int64_t* __restrict__ pos0, int W, uint8_t* __restrict__ data, uint8_t* __restrict__ scales,
+    int32_t* __restrict__ swa_len) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int nw = n < W ? n : W;
+  const int i = n - nw + (int)blockIdx.y;
+  const int64_t p0 = pos0[b];
+  if (p0 < 0) return;  // not a position: the sequence is left as it is (uniform)
+  const int64_t p = p0 + i;
+  if (blockIdx.y == 0 && t == 0) swa_len[b] = (int32_t)(p0 + n < W ? p0 + n : W);
+  const uint4 raw = reinterpret_cast<const uint4*>(latent + ((int64_t)b * n + i) * 512)[t];
+  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_bits_to_f32(wd[j] & 0xFFFFu);
+    v[2 * j + 1] = bf16_bits_to_f32(wd[j] >> 16);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / 512.0f + eps);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * r * (gamma ? gamma[8 * t + j] : 1.0f);
+  uint8_t* rec = data + ((int64_t)b * W + p % W) * 576;
+  // per 64-dim group (8 lanes): the largest magnitude and its scale byte
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, shfl_xor_f(amax, 1));
+  amax = fmaxf(amax, shfl_xor_f(amax, 2));
+  amax = fmaxf(amax, shfl_xor_f(amax, 4));
+  const uint32_t sb = fp8_scale_code(amax);
+  uint32_t sbytes[8];
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) sbytes[gi] = (uint32_t)__shfl((int)sb, 8 * gi, kWave);
+  if (t < 56) {
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j >> 2] |= e4m3_code(ldexpf(v[j], 127 - (int)sb)) << (8 * (j & 3));
+    *reinterpret_cast<uint2*>(rec + 8 * t) = make_uint2(c[0], c[1]);
+  } else {
+    if (rope) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        float cs, sn;
+        rope_cos_sin(p, 4 * (t - 56) + j / 2, cs, sn);
+        rope_pair<false>(v[j], v[j + 1], cs, sn);
+      }
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = f32_to_bf16_bits(v[2 * j]) | (f32_to_bf16_bits(v[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(rec + 448 + 16 * (t - 56)) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+  if (t == 0) {
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) lo |= sbytes[gi] << (8 * gi);
+#pragma unroll
+    for (int gi = 4; gi < 7; ++gi) hi |= sbytes[gi] << (8 * (gi - 4));
+    *reinterpret_cast<uint2*>(scales + ((int64_t)b * W + p % W) * 8) = make_uint2(lo, hi);
+  }
+}
+
+int launch_window_write(const uint16_t* latent, int B, int n, const float* gamma, float eps, int rope,
+                        const int64_t* pos0, int W, uint8_t* data, uint8_t* scales, int32_t* swa_len,
+                        hipStream_t st) {
+  if (B == 0) return 0;
+  const int nw = n < W ? n : W;
+  window_write_kernel<<<dim3(B, nw), 64, 0, st>>>(latent, n, gamma, eps, rope, pos0, W, data, scales, swa_len);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace csa2

@@ -8,7 +8,7 @@
  *   [SY]  syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B",
  *         sections "CSA2" (Figure 4), "Hierarchical Sparse Indexer" (Figure 5),
  *         "FP4 主 KV 缓存" (Figure 1(b))
- *   [GP]  ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", sections 3.2, 3.3, 7
+ *   [GP]  ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", sections 3.2, 3.3, 4.1, 7
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -73,6 +73,10 @@ extern "C" {
 #define CSA2_BLOCK 8               /* candidate_block_size                        */
 #define CSA2_POOL_BLOCKS 2048      /* candidate_topk_blocks                       */
 #define CSA2_SWA 128               /* sliding_window                              */
+#define CSA2_WIN_DATA_BYTES 576    /* FP8 window record: 448 E4M3 + 64 x bf16     */
+#define CSA2_WIN_SCALE_BYTES 8     /* 7 UE8M0 scales (one per 64 dims) + 1 pad    */
+#define CSA2_SWA_MAIN 0            /* window rows in the main-KV format           */
+#define CSA2_SWA_FP8 1             /* window rows as FP8 records                  */
 #define CSA2_ATTN_HEADS 64         /* query heads of the core attention           */
 
 #define CSA2_MAX_TOPK 2048
@@ -174,6 +178,39 @@ int csa2_cache_append(const uint16_t* latent, const uint16_t* gate, int32_t B, i
                       int64_t cap, int32_t* len, void* state, void* stream);
 
 /*
+ * csa2_window_write -- the FP8 sliding-window ring of one layer [GP 4.1: a
+ * 128-token window whose entries stay in FP8; GP 7: 448 B position-free + 128 B
+ * RoPE + 8 B scale = 584 B per token, 576-B aligned; WG 10.1: the FP8 window
+ * record stays beside an FP4 compressed cache; JU 顺便算清另外三笔账: 128 slots
+ * per sequence, overwritten as a ring].  Writes n new tokens per sequence.
+ *   latent   : bf16 bits [B][n][512], token i of sequence b at position
+ *              pos0[b] + i.  16-byte aligned.
+ *   gamma, eps : RMSNorm weight (fp32 [512], NULL = 1) and epsilon (>= 0): the
+ *              window row is the token's RMS-normalised latent (the m = 1
+ *              arithmetic of csa2_cache_write: no pooling).
+ *   rope     : non-zero to rotate dims 448..511 by the compressed RoPE at the
+ *              token's position before storing.
+ *   pos0     : int64 [B], position of token 0 of each sequence (8-byte aligned).
+ *              A sequence with pos0[b] < 0 is left untouched.
+ *   W        : slots per sequence, 1..128; token at position p goes to slot
+ *              p mod W, so the ring holds the last min(p + 1, W) tokens.
+ *   win_data : u8 [B][W][576] records: bytes 0..447 are OCP E4M3 codes of dims
+ *              0..447 (nearest, ties to even, a zero magnitude as +0), bytes
+ *              448..575 dims 448..511 as bf16 (nearest even).  16-byte aligned.
+ *   win_scales : u8 [B][W][8]: byte i (i < 7) is the UE8M0 scale 2^(s-127) of
+ *              dims 64i..64i+63, the smallest with 448 * scale >= the group's
+ *              largest magnitude (0 for an all-zero group); byte 7 is 0.
+ *              8-byte aligned.
+ *   swa_len  : out int32 [B]: min(pos0[b] + n, W), the rows the window holds.
+ * Only the last min(n, W) tokens are written (an earlier one would be
+ * overwritten in the same call).  One launch on `stream`; no allocation.
+ * Errors: B < 0, n < 0, W outside 1..128, eps < 0, NULL or misaligned planes.
+ */
+int csa2_window_write(const uint16_t* latent, int32_t B, int32_t n, const float* gamma, float eps,
+                      int32_t rope, const int64_t* pos0, int32_t W, uint8_t* win_data,
+                      uint8_t* win_scales, int32_t* swa_len, void* stream);
+
+/*
  * csa2_index_full -- Full-mode hierarchical sparse indexer: one scoring pass
  * over every visible entry, feeding two selections [GP 3.3; SY Figure 5; WG 3.2]:
  *   score[b][p] = sum_h w[b][h] * max(0, q[b][h] . deq(idx K[b][p]))  for p < len[b]
@@ -271,9 +308,12 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  *   main_codes/main_scales : main planes [B][cap][256] / [B][cap][32], format main_fmt.
  *   len      : int32 [B] valid main entries per sequence.
  *   topk     : int32 [B][k], k <= 2048 (any order; duplicates are attended twice).
- *   swa_codes/swa_scales : window planes, sequence b at row offset b*swa_stride,
- *              same format as main; swa_len : int32 [B] rows used (<= swa_cap).
+ *   swa_codes/swa_scales : window planes, sequence b at row offset b*swa_stride;
+ *              swa_len : int32 [B] rows used (<= swa_cap), any slot order.
  *   swa_cap  : 0..128; may be 0 (then swa pointers may be NULL).
+ *   swa_fmt  : CSA2_SWA_MAIN: window rows in the main format (256 + 32 B);
+ *              CSA2_SWA_FP8: FP8 window records as csa2_window_write writes
+ *              them (576 + 8 B; swa_scales 8-byte aligned) [GP 4.1; GP 7].
  *   q_pos    : int64 [B] query positions, or NULL.  With positions, each
  *              query's dims 448..511 are rotated by the compressed RoPE at
  *              q_pos[b] before the products, and the output's dims 448..511
@@ -292,7 +332,8 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  *              initial contents.  Calls sharing a workspace must be ordered
  *              on one stream; concurrent calls on one workspace race.
  *              B*H/16 must not exceed CSA2_ATTN_MAX_GROUPS.
- * One kernel on `stream`.  Below 48 sequences (or H < 64) a workgroup attends
+ * One kernel on `stream`.  Below 48 sequences (or H < 64, or FP8 window
+ * records, which only this kernel reads) a workgroup attends
  * one chunk of 128 or 160 row slots for 16 heads and leaves its partial
  * (unnormalised output, max, sum) in the workspace; the last chunk of each
  * (sequence, head group) to finish merges all of them exactly.  From 48
@@ -310,8 +351,8 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
                             const uint8_t* swa_codes, const uint8_t* swa_scales,
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
-                            float sm_scale, const int64_t* q_pos, uint16_t* out, float* lse_opt,
-                            void* ws, size_t ws_bytes, void* stream);
+                            int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                            float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

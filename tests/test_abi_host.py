@@ -37,7 +37,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
-            "csa2_index_pool", "csa2_sparse_attn_decode",
+            "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -189,10 +189,10 @@ def test_index_pool_and_attention_validation(lib):
     assert f(FAKE, FAKE, 4096, FAKE, 2, None, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 1 << 30, None) == ERR_NULL
     assert f(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 16, None) == ERR_WS
     a = lib.csa2_sparse_attn_decode
-    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, ctypes.c_float, P, P, P, P,
-                  ctypes.c_size_t, P]
-    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0.04, None, FAKE,
-            None, FAKE, 1 << 40, None]
+    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, i32, ctypes.c_float, P, P, P,
+                  P, ctypes.c_size_t, P]
+    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0, 0.04, None,
+            FAKE, None, FAKE, 1 << 40, None]
 
     def call(i, v):
         args = list(base)
@@ -204,9 +204,37 @@ def test_index_pool_and_attention_validation(lib):
     assert call(13, 129) == ERR_SHAPE    # window > 128
     assert call(12, 100) == ERR_SHAPE    # stride < window
     assert call(8, 5000) == ERR_SHAPE    # k
-    assert call(15, float("nan")) == ERR_SHAPE
+    assert call(16, float("nan")) == ERR_SHAPE
+    assert call(15, 2) == ERR_UNSUP      # window format
     assert call(0, None) == ERR_NULL
     assert call(10, None) == ERR_NULL    # window planes missing
-    assert call(20, 8) == ERR_WS
+    assert call(21, 8) == ERR_WS
     assert call(0, FAKE_ODD) == ERR_ALIGN
-    assert call(16, FAKE_ODD) == ERR_ALIGN  # query positions
+    assert call(17, FAKE_ODD) == ERR_ALIGN  # query positions
+    args = list(base)
+    args[15], args[11] = 1, P(0x1004)     # FP8 window records: scale rows need 8-byte alignment
+    assert a(*args) == ERR_ALIGN
+
+
+def test_window_write_validation(lib):
+    i32 = ctypes.c_int32
+    f = lib.csa2_window_write
+    f.argtypes = [P, i32, i32, P, ctypes.c_float, i32, P, i32, P, P, P, P]
+    base = [FAKE, 4, 1, None, 1e-6, 1, FAKE, 128, FAKE, FAKE, FAKE, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return f(*args)
+
+    assert call(7, 129) == ERR_SHAPE      # more than 128 slots
+    assert call(7, 0) == ERR_SHAPE
+    assert call(2, -1) == ERR_SHAPE       # tokens
+    assert call(4, -1.0) == ERR_SHAPE     # eps
+    assert call(1, 0) == CSA2_OK          # nothing to write
+    assert call(2, 0) == CSA2_OK
+    assert call(6, None) == ERR_NULL      # positions
+    assert call(10, None) == ERR_NULL     # swa_len
+    assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(9, P(0x1004)) == ERR_ALIGN  # scale rows: 8-byte aligned
+    assert call(6, P(0x1004)) == ERR_ALIGN  # int64 positions
