@@ -53,7 +53,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None, choices=["write", "index_full", "index_pool", "attn"],
+    ap.add_argument("--window", default="tail", choices=["tail", "fp8"],
+                    help="window rows: the last 128 entries of the main cache (the configured workload), or "
+                         "each layer's own FP8 ring (576 + 8 B records), written once per layer per step")
+    ap.add_argument("--only", default=None, choices=["write", "window", "index_full", "index_pool", "attn"],
                     help="run only one call type in the timed loop (for profiling)")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="instead of the benchmark, run a plain device copy of this many MB "
@@ -67,25 +70,27 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa, q_fp4=False):
+def algorithmic_bytes(wl, B, lengths, pool_len, k, n_blocks, H_idx, H_attn, swa, q_fp4=False, fp8_window=False):
     """Bytes each call must move at minimum (inputs read once, outputs written once)."""
     sum_len = int(sum(lengths))
     sum_pool = int(sum(pool_len))
     qb = H_idx * (68 if q_fp4 else 256)        # one indexer query head: FP4 codes + scales, or bf16
     full = sum_len * 68 + B * (qb + H_idx * 4 + 4) + B * (k * 4 + n_blocks * 8 * 4 + 4)
     pool = sum_pool * 68 + B * (n_blocks * 8 * 4 + 4) + B * (qb + H_idx * 4 + 4) + B * k * 4
-    rows = B * (k + swa)
-    attn = rows * 288 + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8
+    attn = B * k * 288 + B * swa * (584 if fp8_window else 288) + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8
     # cache write: T tokens (latent, plus the gate when m > 1) pooled into T/m entries
     T, m = (wl.write_tokens, wl.write_m) if wl.write_tokens else (B, 1)
     write = T * 512 * 2 * (2 if m > 1 else 1) + 512 * 128 * 4 + (T // m) * 356
-    return dict(write=write, index_full=full, index_pool=pool, attn=attn)
+    # FP8 window write: one token per sequence per layer (latent in, record out)
+    window = B * (512 * 2 + 584 + 8 + 4) if fp8_window else 0
+    return dict(write=write, index_full=full, index_pool=pool, attn=attn, window=window)
 
 
-def attn_sweep(batches, fmt_name, steps):
+def attn_sweep(batches, fmt_name, steps, window="tail"):
     """Sparse-attention decode call at several batch sizes: where the kernel
     stops being latency-bound.  One seeded 32,768-entry cache per sequence,
-    512 distinct random positions selected, the last 128 entries as the window."""
+    512 distinct random positions selected, the last 128 entries as the window
+    (or, with window="fp8", a 128-slot FP8 ring per sequence)."""
     import torch
     import csa2_synth as syn
     import compressed_kv_cache_mxfp4_amd as K
@@ -107,11 +112,19 @@ def attn_sweep(batches, fmt_name, steps):
         q = syn.attn_query(wl, 0, dev)
         out = torch.empty(B, 64, 512, dtype=torch.int16, device=dev)
         ws = torch.zeros(max(L.csa2_attn_workspace(B, 64, k, swa), 256), dtype=torch.uint8, device=dev)
+        if window == "fp8":
+            ring = K.window_alloc(B, swa, dev)
+            lat = torch.randn(B, swa, 512, generator=torch.Generator(device=dev).manual_seed(B), device=dev)
+            K.window_write(lat.to(torch.bfloat16), torch.full((B,), 2 * cap - swa, dtype=torch.int64, device=dev),
+                           ring, rope=True)
+            wkw = dict(swa_codes=ring["data"], swa_scales=ring["scales"], swa_len=ring["swa_len"], swa_stride=swa,
+                       swa_cap=swa, swa_fmt=K.SWA_FP8)
+        else:
+            wkw = dict(swa_codes=codes, swa_scales=scales, swa_len=swa_len, swa_stride=cap, swa_cap=swa,
+                       swa_row0=cap - swa)
 
         def call():
-            K.sparse_attn_decode(q, codes, scales, lengths, topk, fmt, swa_codes=codes, swa_scales=scales,
-                                 swa_len=swa_len, swa_stride=cap, swa_cap=swa, swa_row0=cap - swa,
-                                 out=dict(out=out), _ws=ws)
+            K.sparse_attn_decode(q, codes, scales, lengths, topk, fmt, out=dict(out=out), _ws=ws, **wkw)
         for _ in range(3):
             call()
         torch.cuda.synchronize()
@@ -128,7 +141,7 @@ def attn_sweep(batches, fmt_name, steps):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps / reps
-        nbytes = B * ((k + swa) * 288 + 64 * 512 * 2 * 2 + k * 4 + 8)
+        nbytes = B * (k * 288 + swa * (584 if window == "fp8" else 288) + 64 * 512 * 2 * 2 + k * 4 + 8)
         gbs = nbytes / (us * 1e-6) / 1e9
         rows.append(dict(B=B, us_per_call=round(us, 3), bytes_per_call=nbytes, achieved_GBs=round(gbs, 1),
                          frac_hbm=round(gbs / HBM_PEAK_GBS, 4), queries_per_s=round(B / (us * 1e-6))))
@@ -136,7 +149,7 @@ def attn_sweep(batches, fmt_name, steps):
         del codes, scales, topk, q, out, ws, g
         torch.cuda.empty_cache()
     print(json.dumps(dict(metric="sparse attention decode call, batch sweep", unit="us per call",
-                          main_scale=fmt_name.upper(), heads=64, head_dim=512, rows=k + swa,
+                          main_scale=fmt_name.upper(), window=window, heads=64, head_dim=512, rows=k + swa,
                           entries_per_sequence=cap, peak_GBs=HBM_PEAK_GBS, sweep=rows)), flush=True)
 
 
@@ -211,7 +224,7 @@ def main():
         copy_calibration(args.copy_calib_mb)
         return
     if args.attn_sweep:
-        attn_sweep([int(x) for x in args.attn_sweep.split(",")], args.fmt, args.steps)
+        attn_sweep([int(x) for x in args.attn_sweep.split(",")], args.fmt, args.steps, args.window)
         return
 
     import csa2_synth as syn
@@ -236,8 +249,29 @@ def main():
         K.quantize_fp4(syn.main_values(wl, b, dev), 16, fmt, cache["main_codes"][b], cache["main_scales"][b])
         K.quantize_fp4(syn.idx_values(wl, b, dev), 32, K.E8M0, cache["idx_codes"][b], cache["idx_scales"][b])
     lengths = torch.full((B,), cap, dtype=torch.int32, device=dev)
+    fp8w = args.window == "fp8"
+    n_attn = (1 + wl.n_reindex) * (1 + wl.reuse_per_index)
+    rings = None
+    if fp8w:
+        # each attention layer's own FP8 window ring, holding the 128 tokens
+        # before the new one (positions 2*cap-128 .. 2*cap-1; the entries are
+        # m = 2 groups of those tokens), written by the window kernel
+        rings = []
+        gw = torch.Generator(device=dev).manual_seed(wl.seed + 300)
+        pos_fill = torch.full((B,), 2 * cap - 128, dtype=torch.int64, device=dev)
+        for _ in range(n_attn):
+            r = K.window_alloc(B, 128, dev)
+            lat = torch.randn(B, 128, 512, generator=gw, device=dev).to(torch.bfloat16)
+            K.window_write(lat, pos_fill, r, rope=True)
+            rings.append(dict(codes=r["data"], scales=r["scales"], row0=0, stride=128, length=r["swa_len"],
+                              fmt=K.SWA_FP8))
+        win_tok = [torch.randn(B, 1, 512, generator=gw, device=dev).to(torch.bfloat16) for _ in range(n_attn)]
+        win_pos = torch.full((B,), 2 * cap, dtype=torch.int64, device=dev)
+        # the step's window writes go to copies, so the rings the attention
+        # reads keep their contents from step to step
+        win_dst = [K.window_alloc(B, 128, dev) for _ in range(n_attn)]
     step = DecodeStep(cache, lengths, k=wl.k, n_blocks=wl.n_blocks, n_reindex=wl.n_reindex,
-                      reuse_per_index=wl.reuse_per_index, main_fmt=fmt)
+                      reuse_per_index=wl.reuse_per_index, main_fmt=fmt, swa=rings)
     n_idx = 1 + wl.n_reindex
     idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
     if args.index_q == "fp4":
@@ -272,6 +306,10 @@ def main():
     def ph_write():
         K.cache_write(new_lat, new_gate, w_m, w_proj, fmt, out=staged)
 
+    def ph_window():
+        for j in range(n_attn):
+            K.window_write(win_tok[j], win_pos, win_dst[j], rope=True)
+
     def ph_full():
         q, w = idx_qw[0]
         c = step.cache
@@ -289,7 +327,9 @@ def main():
         step.run_attention(attn_q)
 
     all_phases = [("write", ph_write), ("index_full", ph_full), ("index_pool", ph_pool), ("attn", ph_attn)]
-    calls = dict(write=1, index_full=1, index_pool=n_pool, attn=step.n_attn)
+    if fp8w:
+        all_phases.insert(1, ("window", ph_window))
+    calls = dict(write=1, window=n_attn if fp8w else 0, index_full=1, index_pool=n_pool, attn=step.n_attn)
     phases = [(n, f) for n, f in all_phases if (only is None or n == only) and calls[n] > 0]
     if only in ("index_pool", "attn"):
         ph_full()           # produce pool/top-k once
@@ -318,7 +358,7 @@ def main():
     g_step = capture(one_step)
     # a phase graph repeats its phase until it holds about 20 launches, so that
     # the per-call time is not dominated by the replay's own launch cost
-    launches = dict(write=1, index_full=2, index_pool=2 * n_pool, attn=step.n_attn)
+    launches = dict(write=1, window=n_attn, index_full=2, index_pool=2 * n_pool, attn=step.n_attn)
     reps = {n: max(1, -(-20 // max(launches[n], 1))) for n, _ in phases}
 
     def repeated(f, r):
@@ -386,7 +426,7 @@ def main():
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     nbytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128,
-                              q_fp4=args.index_q == "fp4")
+                              q_fp4=args.index_q == "fp4", fp8_window=fp8w)
     kernels = {}
     for name in per_call_us:
         us = per_call_us[name]
@@ -418,6 +458,7 @@ def main():
         data="synthetic",
         config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
                     topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,
+                    window_rows="per-layer FP8 ring, written each step" if fp8w else "last 128 cache entries",
                     layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
                     main_scale=args.fmt.upper(), index_query=args.index_q, only=args.only,
                     cache_write=f"{w_T} tokens, m={w_m}"),
@@ -426,7 +467,7 @@ def main():
                              note="decode-time append of one token per sequence into the cache; not in the step"),
         kernels=kernels, roofline=roofline,
     )
-    if not args.no_cpu_baseline and args.only is None:
+    if not args.no_cpu_baseline and args.only is None and not fp8w:
         del step, cache
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(wl, fmt, args.cpu_seconds)

@@ -698,7 +698,7 @@ struct TStage {
   uint32_t ok;
 };
 
-template <int FMT>
+template <int FMT, bool WF8>
 __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     const uint16_t* __restrict__ q, int H, const uint8_t* __restrict__ main_codes,
     const uint8_t* __restrict__ main_scales, int64_t cap, const int32_t* __restrict__ len,
@@ -721,7 +721,13 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   const bool scorer = w < 4;  // wave-uniform role
   const int wr = w & 3;       // index within the role
   const int nslots = k + swa_cap;
-  const int nch = (nslots + kTRows - 1) / kTRows;
+  // FP8 window records: the selected entries fill 32-row chunks up to kw (k
+  // rounded up to 32), then the window takes 16-row chunks -- a record is
+  // twice a main entry, so 16 lanes of 36 bytes stage one row and every
+  // staging lane keeps the same load slot
+  const int kw = WF8 ? (k + 31) & ~31 : k;
+  const int kwc = kw / kTRows;  // first window chunk (FP8 records)
+  const int nch = WF8 ? kwc + (swa_cap + 15) / 16 : (nslots + kTRows - 1) / kTRows;
   const int c_begin = (int)((int64_t)sidx * nch / S), c_end = (int)((int64_t)(sidx + 1) * nch / S);
   const int nc = c_end - c_begin;
   // steps of the chunk loop, rounded up to the value waves' unroll of three
@@ -733,17 +739,28 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   int SL = swa_len ? swa_len[b] : 0;
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
 
-  // ---- value waves: staging role, row srow of a chunk, dims 64*ssp .. +63
+  // ---- value waves: staging role, row srow of a chunk, dims 64*ssp .. +63;
+  // in an FP8 window chunk, row wrow, bytes 32*wt .. +31 and 512 + 4*wt .. +3
   const int srow = 16 * (wr & 1) + n, ssp = 4 * (wr >> 1) + g;
+  const int wrow = (64 * wr + lane) >> 4, wt = lane & 15;
   const int32_t* tbase = topk + (int64_t)b * k;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)b * H * 512);
   // raw index-list entry of row srow of chunk c, loaded unconditionally from
   // a clamped address (a valid dummy when k = 0).  It is not tested here:
   // anything computed from it right away would make the compiler wait for
   // the load at once.  load_rows applies every validity condition.
+  // In an FP8 window chunk the slot carries the scale dword holding the
+  // lane's group byte instead (group wt/2 of row wrow), from the same clamped
+  // kind of address.
   auto load_idx = [&](int c) -> int32_t {
     const int slot = c * kTRows + srow;
     const int32_t* ip = k > 0 ? tbase + min(slot, k - 1) : reinterpret_cast<const int32_t*>(dummy);
+    if (WF8 && c >= kwc) {
+      const int rr = (c - kwc) * 16 + wrow;
+      ip = rr < SL ? reinterpret_cast<const int32_t*>(swa_scales + ((int64_t)b * swa_stride + rr) * kWinScaleB +
+                                                      4 * ((wt >> 1) >> 2))
+                   : reinterpret_cast<const int32_t*>(dummy);
+    }
     return *ip;
   };
   auto load_rows = [&](int c, int32_t p) -> TStage {
@@ -758,25 +775,78 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
           scp = main_scales + ((int64_t)b * cap + p) * 32;
           ok = 1u;
         }
-      } else if (slot < nslots && slot - k < SL) {
+      } else if (!WF8 && slot < nslots && slot - k < SL) {
         cp = swa_codes + ((int64_t)b * swa_stride + (slot - k)) * 256;
         scp = swa_scales + ((int64_t)b * swa_stride + (slot - k)) * 32;
         ok = 1u;
       }
     }
+    const uint8_t* a0 = cp + 32 * ssp;
+    const uint8_t* as = scp + 4 * ssp;
+    if (WF8 && c >= kwc) {
+      // FP8 window record: bit 0 of ok = visible, bits 8..15 = the scale byte
+      const int rr = (c - kwc) * 16 + wrow;
+      const bool vis = c < c_end && rr < SL;
+      cp = vis ? swa_codes + ((int64_t)b * swa_stride + rr) * kWinDataB : dummy;
+      a0 = cp + 32 * wt;
+      as = cp + 512 + 4 * wt;
+      ok = vis ? 1u | ((((uint32_t)p >> (8 * ((wt >> 1) & 3))) & 0xFFu) << 8) : 0u;
+    }
     TStage st;
-    const uint4* c4 = reinterpret_cast<const uint4*>(cp + 32 * ssp);
+    const uint4* c4 = reinterpret_cast<const uint4*>(a0);
     st.c0 = c4[0];
     st.c1 = c4[1];
-    st.s = *reinterpret_cast<const uint32_t*>(scp + 4 * ssp);
+    st.s = *reinterpret_cast<const uint32_t*>(as);
     st.ok = ok;
     return st;
   };
   uint32_t smax = 0u;  // largest scale byte staged by this lane (bound of |value|)
+  float wmax = 0.0f;   // bound of |value| of the FP8 window records it staged
   const int wsw = tswz(srow);
+  // FP8 window chunk j: rows 0..15 of R[buf] from the records (invisible ones
+  // as zeros), rows 16..31 zero; validity from the window length
+  auto stage_win = [&](int buf, TStage st, int j) {
+    const uint32_t m = 0u - (st.ok & 1u);
+    st.c0 = make_uint4(st.c0.x & m, st.c0.y & m, st.c0.z & m, st.c0.w & m);
+    st.c1 = make_uint4(st.c1.x & m, st.c1.y & m, st.c1.z & m, st.c1.w & m);
+    st.s &= m;
+    uint8_t* rowp = sm.R[buf] + wrow * kTRowB;
+    const int sw = tswz(wrow);
+    auto bmax = [](uint32_t v) {
+      return fmaxf(fabsf(bf16_bits_to_f32(v & 0xFFFFu)), fabsf(bf16_bits_to_f32(v >> 16)));
+    };
+    if (wt < 14) {
+      const uint32_t sb = (st.ok >> 8) & 0xFFu;
+      const float op = e8m0_operand(sb);
+      const uint32_t cw[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<bf16x8*>(rowp + (((4 * wt + u) ^ sw) << 4)) = fp8x8_to_bf16(cw[2 * u], cw[2 * u + 1], op);
+      if (st.ok & 1u) wmax = fmaxf(wmax, 448.0f * e8m0_value(sb));
+    } else {
+      *reinterpret_cast<uint4*>(rowp + (((56 + 2 * (wt - 14)) ^ sw) << 4)) = st.c0;
+      *reinterpret_cast<uint4*>(rowp + (((57 + 2 * (wt - 14)) ^ sw) << 4)) = st.c1;
+      wmax = fmaxf(wmax, fmaxf(fmaxf(fmaxf(bmax(st.c0.x), bmax(st.c0.y)), fmaxf(bmax(st.c0.z), bmax(st.c0.w))),
+                               fmaxf(fmaxf(bmax(st.c1.x), bmax(st.c1.y)), fmaxf(bmax(st.c1.z), bmax(st.c1.w)))));
+    }
+    // dims 480 + 2wt, 481 + 2wt: a quarter of unit 60 + wt/4
+    *reinterpret_cast<uint32_t*>(rowp + (((60 + (wt >> 2)) ^ sw) << 4) + 4 * (wt & 3)) = st.s;
+    wmax = fmaxf(wmax, bmax(st.s));
+    uint8_t* zrow = sm.R[buf] + (16 + wrow) * kTRowB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(zrow + ((4 * wt + u) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+    if (wr == 0 && lane == 0) {
+      const int nv = min(max(SL - 16 * j, 0), 16);
+      sm.vb[buf] = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
+    }
+  };
   // dequantise the lane's slice into R[buf] (invalid rows as zeros) and
   // record the chunk's row validity
-  auto stage = [&](int buf, TStage st) {
+  auto stage = [&](int buf, TStage st, int c) {
+    if (WF8 && c >= kwc) {
+      stage_win(buf, st, c - kwc);
+      return;
+    }
     const uint32_t m = 0u - st.ok;
     st.c0 = make_uint4(st.c0.x & m, st.c0.y & m, st.c0.z & m, st.c0.w & m);
     st.c1 = make_uint4(st.c1.x & m, st.c1.y & m, st.c1.z & m, st.c1.w & m);
@@ -906,7 +976,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       PB = load_idx(c_begin + 5);
       XC = load_rows(c_begin + 3, p3);
       PC = load_idx(c_begin + 6);
-      stage(0, st0);
+      stage(0, st0, c_begin);
     }
     // O^T tile (dims 128wr + 16dt .., heads 16ht ..): lane (g, n) holds dims
     // +4g..+3 of head 16ht + n
@@ -964,7 +1034,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
             O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pbv[ht], O[dt][ht], 0, 0, 0);
         }
       }
-      if (s + 1 < nc) stage((s + 1) % 3, X);
+      if (s + 1 < nc) stage((s + 1) % 3, X, c_begin + s + 1);
       // issued on every step (past the split they read a dummy row), so that
       // the count of outstanding loads is the same on every path and each
       // wait covers only the loads it needs
@@ -979,6 +1049,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     }
     if (S > 1) {
       float vb = 6.0f * (FMT == 0 ? e8m0_value(smax) : e4m3_value(smax));
+      if (WF8) vb = fmaxf(vb, wmax);
       if (!(vb <= 3.0e38f)) vb = 3.0e38f;  // NaN/inf scale bytes: clamp the bound
       vb = wave_max(vb);
       if (lane == 0) sm.red_v[wr] = vb;
@@ -1124,12 +1195,10 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + l.cnt_off);
   uint16_t* part = reinterpret_cast<uint16_t*>(wsb + l.part_off);
   float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
-  // FP8 window records are read by the split kernel only: the throughput
-  // kernel's staging lanes have no registers left for a 584-byte record
-  if (!w8 && H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
+  if (H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
     // throughput variant: S splits per sequence, enough to give every CU a
     // workgroup, at most one per 128 row slots (the workspace's partials)
-    const int nch = (nslots + kTRows - 1) / kTRows;
+    const int nch = w8 ? (k + 31) / 32 + (swa_cap + 15) / 16 : (nslots + kTRows - 1) / kTRows;
     int Sq = B >= 256 ? 1 : 256 / (int)B;
     Sq = std::min(Sq, std::min(nch, attn_splits(k, swa_cap)));
     const unsigned tgrid = (unsigned)(((B + 7) / 8) * Sq * 8);
@@ -1140,8 +1209,13 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                                                    part, ml, cnt, out, lse_opt);
       return true;
     };
-    const bool ok = main_fmt == 0 ? tgo(attn_seq_kernel<0>, lds_optin<attn_seq_kernel<0>>(sizeof(AttnTSmem)))
-                                  : tgo(attn_seq_kernel<1>, lds_optin<attn_seq_kernel<1>>(sizeof(AttnTSmem)));
+    bool ok;
+    if (w8)
+      ok = main_fmt == 0 ? tgo(attn_seq_kernel<0, true>, lds_optin<attn_seq_kernel<0, true>>(sizeof(AttnTSmem)))
+                         : tgo(attn_seq_kernel<1, true>, lds_optin<attn_seq_kernel<1, true>>(sizeof(AttnTSmem)));
+    else
+      ok = main_fmt == 0 ? tgo(attn_seq_kernel<0, false>, lds_optin<attn_seq_kernel<0, false>>(sizeof(AttnTSmem)))
+                         : tgo(attn_seq_kernel<1, false>, lds_optin<attn_seq_kernel<1, false>>(sizeof(AttnTSmem)));
     if (!ok) return -1;
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }

@@ -38,7 +38,9 @@ class DecodeStep:
         self.main_fmt = main_fmt
         self.H_attn = H_attn
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / (512 ** 0.5)
-        # window: by default the last swa_cap entries of each sequence's main cache
+        # window: by default the last swa_cap entries of each sequence's main
+        # cache; or one dict for every layer, or a list with one per attention
+        # layer (each layer's own window, e.g. an FP8 ring: fmt=SWA_FP8)
         if swa is None:
             swa = dict(codes=cache["main_codes"], scales=cache["main_scales"], row0=cap - swa_cap,
                        stride=cap, length=torch.full((B,), swa_cap, dtype=torch.int32, device=dev))
@@ -81,14 +83,15 @@ class DecodeStep:
                          w, k=self.k, out=dict(topk=self.topk[i]), _ws=self.ws_pool)
 
     def run_attention(self, attn_q: Sequence[torch.Tensor]):
-        c, s = self.cache, self.swa
+        c = self.cache
         for j, (mode, i) in enumerate(self.schedule()):
+            s = self.swa[j] if isinstance(self.swa, (list, tuple)) else self.swa
             K.sparse_attn_decode(attn_q[j], c["main_codes"], c["main_scales"], self.lengths,
                                  self.topk[i], self.main_fmt, swa_codes=s["codes"],
                                  swa_scales=s["scales"], swa_len=s["length"],
                                  swa_stride=s["stride"], swa_cap=self.swa_cap, swa_row0=s["row0"],
-                                 sm_scale=self.sm_scale, out=dict(out=self.out[j]),
-                                 _ws=self.ws_attn)
+                                 swa_fmt=s.get("fmt", K.SWA_MAIN), sm_scale=self.sm_scale,
+                                 out=dict(out=self.out[j]), _ws=self.ws_attn)
 
     def run(self, idx_qw, attn_q):
         self.run_index(idx_qw)

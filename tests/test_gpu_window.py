@@ -6,7 +6,9 @@ E4M3 midpoint (or of a bf16 midpoint on the RoPE dims), or the group maximum
 within 1e-5 of a scale boundary (then the whole 64-dim group may differ);
 swa_len and every untouched slot are exact.
 
-Attention over FP8 window records: the window is written by the oracle; per
+Attention over FP8 window records (both kernels: the latency split kernel
+below 48 sequences, the throughput kernel from 48): the window is written by
+the oracle; per
 (sequence, head) max|o - r| / max|r| <= 1e-2 and the log-sum-exp within
 1e-4 (plus the RoPE allowance).  A single window row with no selected entry
 must come back bit for bit: the kernel's decode of every finite E4M3 code.
@@ -170,7 +172,8 @@ def _fp8_windows(B, W, seed, rope):
 
 
 @pytest.mark.parametrize("B,k,fmt,rope", [(1, 512, 0, False), (3, 500, 1, True), (16, 512, 0, True),
-                                          (64, 512, 1, False), (64, 500, 0, True)])
+                                          (64, 512, 1, False), (64, 500, 0, True), (48, 40, 1, True),
+                                          (256, 512, 0, True), (256, 480, 1, False)])
 def test_attention_fp8_window_parity(B, k, fmt, rope):
     say(f"attention over FP8 window B={B} k={k} fmt={fmt} rope={rope}")
     cap, W = 1500, 128
