@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify-q", type=int, default=0, metavar="Q",
+                    help="instead of the step: the Full indexer call for Q queries per sequence (a verify "
+                         "block) sharing each cache, against Q single-query calls")
     ap.add_argument("--window", default="tail", choices=["tail", "fp8"],
                     help="window rows: the last 128 entries of the main cache (the configured workload), or "
                          "each layer's own FP8 ring (576 + 8 B records), written once per layer per step")
@@ -153,6 +156,72 @@ def attn_sweep(batches, fmt_name, steps, window="tail"):
                           entries_per_sequence=cap, peak_GBs=HBM_PEAK_GBS, sweep=rows)), flush=True)
 
 
+def verify_bench(wl_name, Q, steps, warmup):
+    """Full indexer for Q queries per sequence (a speculative verify block): one
+    csa2_index_full_mq call against Q csa2_index_full calls, same caches and queries."""
+    import torch
+    import csa2_synth as syn
+    import compressed_kv_cache_mxfp4_amd as K
+    dev = torch.device("cuda:0")
+    wl = syn.WORKLOADS[wl_name]
+    B, cap = wl.B, wl.cap
+    ic = torch.empty(B, cap, 64, dtype=torch.uint8, device=dev)
+    isc = torch.empty(B, cap, 4, dtype=torch.uint8, device=dev)
+    for b in range(B):
+        K.quantize_fp4(syn.idx_values(wl, b, dev), 32, K.E8M0, ic[b], isc[b])
+    lengths = torch.full((B,), cap, dtype=torch.int32, device=dev)
+    q = torch.stack([syn.index_query(wl, i, dev) for i in range(Q)], 1).contiguous()
+    w = torch.stack([syn.index_weights(wl, i, dev) for i in range(Q)], 1).contiguous()
+    qs = [q[:, i].contiguous() for i in range(Q)]
+    ws_ = [w[:, i].contiguous() for i in range(Q)]
+    L = K.lib()
+    ws_mq = torch.empty(L.csa2_index_full_mq_workspace(B, Q, cap, wl.k, 8, wl.n_blocks), dtype=torch.uint8, device=dev)
+    ws_1 = torch.empty(L.csa2_index_full_workspace(B, cap, wl.k, 8, wl.n_blocks), dtype=torch.uint8, device=dev)
+    outs_mq = dict(topk=torch.empty(B, Q, wl.k, dtype=torch.int32, device=dev),
+                   pool=torch.empty(B, Q, wl.n_blocks * 8, dtype=torch.int32, device=dev),
+                   pool_len=torch.empty(B, Q, dtype=torch.int32, device=dev))
+    outs_1 = [dict(topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev),
+                   pool=torch.empty(B, wl.n_blocks * 8, dtype=torch.int32, device=dev),
+                   pool_len=torch.empty(B, dtype=torch.int32, device=dev)) for _ in range(Q)]
+
+    def mq():
+        K.index_full_mq(ic, isc, lengths, q, w, k=wl.k, n_blocks=wl.n_blocks, out=outs_mq, _ws=ws_mq)
+
+    def sep():
+        for i in range(Q):
+            K.index_full(ic, isc, lengths, qs[i], ws_[i], k=wl.k, n_blocks=wl.n_blocks, out=outs_1[i], _ws=ws_1)
+
+    res = {}
+    for name, fn in (("multi_query", mq), ("separate", sep)):
+        for _ in range(max(warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    for i in range(Q):
+        assert torch.equal(outs_mq["topk"][:, i], outs_1[i]["topk"]), "multi-query top-k differs"
+    cache_bytes = B * cap * 68
+    per_q = B * (wl.H_idx * 256 + wl.H_idx * 4 + 4) + B * (wl.k * 4 + wl.n_blocks * 8 * 4 + 4)
+    nbytes = cache_bytes + Q * per_q
+    us = res["multi_query"]
+    print(json.dumps(dict(metric="Full indexer call for a verify block (Q queries per sequence)", unit="us per call",
+                          workload=wl.name, sequences=B, entries_per_sequence=cap, queries_per_sequence=Q,
+                          indexer_heads=wl.H_idx, topk=wl.k, pool_blocks=wl.n_blocks,
+                          us_multi_query=round(us, 2), us_separate_calls=round(res["separate"], 2),
+                          positions_scored_per_s=Q * B * cap / (us * 1e-6),
+                          algorithmic_bytes=nbytes, achieved_GBs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                          frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))), flush=True)
+
+
 def copy_calibration(mb: float):
     import torch
 
@@ -222,6 +291,9 @@ def main():
 
     if args.copy_calib_mb > 0:
         copy_calibration(args.copy_calib_mb)
+        return
+    if args.verify_q:
+        verify_bench(args.workload, args.verify_q, args.steps, args.warmup)
         return
     if args.attn_sweep:
         attn_sweep([int(x) for x in args.attn_sweep.split(",")], args.fmt, args.steps, args.window)

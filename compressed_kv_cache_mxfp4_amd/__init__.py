@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     cache_append,
     cache_write,
     index_full,
+    index_full_mq,
     index_pool,
     lib,
     quantize_fp4,

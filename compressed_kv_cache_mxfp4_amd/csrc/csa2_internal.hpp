@@ -35,7 +35,7 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
                       const uint8_t* q4s, const float* w, int H, int k,
                       int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
-                      float* scores_opt, void* ws, hipStream_t st);
+                      float* scores_opt, void* ws, hipStream_t st, int qps = 1);
 
 size_t index_pool_ws_bytes(int B, int pool_cap);
 

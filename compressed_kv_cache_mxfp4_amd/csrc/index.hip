@@ -187,23 +187,31 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
     const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
     float* __restrict__ bmax, int64_t bmax_stride, int B, int per_seq,
-    const uint8_t* __restrict__ q4_codes, const uint8_t* __restrict__ q4_scales) {
+    const uint8_t* __restrict__ q4_codes, const uint8_t* __restrict__ q4_scales, int qps) {
   __shared__ __align__(16) uint16_t qs[Q4 ? 8 : 64 * 128];
   __shared__ float ws[64];
-  // Grid: per_seq workgroups for each of B sequences, in one dimension.  When
-  // B is a multiple of 8, sequence b's workgroups all get ids congruent to
-  // b mod 8, i.e. they run on XCD b mod 8 -- the XCD of the selection
-  // workgroup b that reads their output next.
+  // Grid: per_seq workgroups for each of the B query rows, in one dimension;
+  // row b scores cache b / qps (qps queries per cache, e.g. the tokens of a
+  // verify block).  Ids run in (cache, walker x, query) order, so the qps
+  // queries of a cache walk the same super-tiles side by side and all but
+  // the first find them in L2.  When the number of caches is a multiple of
+  // 8, cache c's workgroups all get ids congruent to c mod 8, i.e. they run
+  // on XCD c mod 8 (with one query per cache, the XCD of the selection
+  // workgroup that reads their output next).
   const int id = blockIdx.x;
-  int b, x;
-  if ((B & 7) == 0) {
+  const int per_c = per_seq * qps;
+  int cb, x, qi;
+  if (((B / qps) & 7) == 0) {
     const int r = id >> 3;
-    b = (id & 7) + 8 * (r / per_seq);
-    x = r % per_seq;
+    cb = (id & 7) + 8 * (r / per_c);
+    x = (r % per_c) / qps;
+    qi = r % qps;
   } else {
-    b = id / per_seq;
-    x = id % per_seq;
+    cb = id / per_c;
+    x = (id % per_c) / qps;
+    qi = id % qps;
   }
+  const int b = cb * qps + qi;  // query row
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const int64_t W = (int64_t)per_seq * 4;
@@ -211,8 +219,8 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
   const int64_t step = W * kSuperTile;
   const int64_t base0 = st0 * kSuperTile;
   const int64_t Nmax = GATHER ? (int64_t)pool_cap : cap;  // bound of the item index
-  const uint8_t* codes_b = idx_codes + (int64_t)b * cap * 64;
-  const uint8_t* scales_b = idx_scales + (int64_t)b * cap * 4;
+  const uint8_t* codes_b = idx_codes + (int64_t)cb * cap * 64;
+  const uint8_t* scales_b = idx_scales + (int64_t)cb * cap * 4;
   const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
   float* scores_b = scores + (int64_t)b * score_stride;
 
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&qs[h * 128 + 32 * part + 8 * j]) = v[j];
   }
   if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
-  int64_t L = len[b];
+  int64_t L = len[cb];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int64_t N = L;
   if (GATHER) {
@@ -724,7 +732,7 @@ template <int NT, int EPT_B, int EPT_C, int EPT_P>
 __global__ __launch_bounds__(NT) void select_full_kernel(
     const float* __restrict__ scores, int64_t sstride, const float* __restrict__ bmax,
     int64_t bstride, const int32_t* __restrict__ len, int64_t cap, int k, int n_blocks,
-    int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len) {
+    int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len, int qps) {
   __shared__ SelScratch sh;
   __shared__ int32_t blk[CSA2_POOL_BLOCKS];
   __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   KeysFromArray bsrc{bmax + (int64_t)b * bstride};
   KeyRegs<EPT_B> kb;
   if constexpr (EPT_B > 0) load_raw<NT, EPT_B>(kb, bsrc.p, (int)bstride);  // overlaps the length load
-  int64_t L = len[b];
+  int64_t L = len[b / qps];  // row b scores cache b / qps
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nb = (int)((L + kBlock - 1) / kBlock);
   const float* sc = scores + (int64_t)b * sstride;
@@ -848,11 +856,11 @@ static void launch_score(int MT, int per_seq, int B, hipStream_t st, const uint8
                          int64_t cap, const int32_t* len, const int32_t* pool,
                          const int32_t* pool_len, int pool_cap, const uint16_t* q, const uint8_t* q4c,
                          const uint8_t* q4s, const float* w, int H, float* scores, int64_t sstride,
-                         float* bmax, int64_t bstride) {
+                         float* bmax, int64_t bstride, int qps = 1) {
   const dim3 grid((unsigned)per_seq * (unsigned)B);
 #define CSA2_SCORE(MT_, Q4_) \
   score_kernel<MT_, GATHER, Q4_><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, \
-                                                                 scores, sstride, bmax, bstride, B, per_seq, q4c, q4s)
+                                                                 scores, sstride, bmax, bstride, B, per_seq, q4c, q4s, qps)
   if (q4c) {
     if (MT == 1) CSA2_SCORE(1, true); else if (MT == 2) CSA2_SCORE(2, true); else CSA2_SCORE(4, true);
   } else {
@@ -876,7 +884,7 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
                       const uint8_t* q4s, const float* w, int H, int k,
                       int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
-                      float* scores_opt, void* ws, hipStream_t st) {
+                      float* scores_opt, void* ws, hipStream_t st, int qps) {
   if (B == 0) return 0;
   const IndexFullWs l = index_full_ws_layout(B, cap, block);
   float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -886,12 +894,13 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   const int per_seq = (int)score_wgs(cap, B, kScoreWaves);
   if (cap > 0)
     launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, q4c,
-                        q4s, w, H, scores, cap, bmax, nbk);
+                        q4s, w, H, scores, cap, bmax, nbk, qps);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
   // keys per thread: all blocks (EB), the pool blocks (2), candidate positions (EP)
 #define CSA2_SELFULL(EB, EP) \
-  select_full_kernel<1024, EB, 2, EP><<<B, 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, pool_len)
+  select_full_kernel<1024, EB, 2, EP><<<B, 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, \
+                                                         pool_len, qps)
   if (nbk <= 4 * 1024) {
     if (kbig) CSA2_SELFULL(4, 16); else CSA2_SELFULL(4, 4);
   } else if (nbk <= 16 * 1024) {

@@ -4,7 +4,7 @@
  *
  * Sources (web pages on DeepSeek V4.1 Flash; cited by host, title and section):
  *   [JU]  jokeuncle.pages.dev, "两张架构图里藏着 890 字节", sections 二, 三, 四
- *   [WG]  weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本", sections 3.1, 3.2, 4, 10
+ *   [WG]  weigao.cc, "DeepSeek V4.1 Flash：从架构到推理成本", sections 3.1, 3.2, 4, 7, 10
  *   [SY]  syt-nju.github.io, "DeepSeek-V4.1-Flash：为什么读输入只激活 8B，写输出要 16B",
  *         sections "CSA2" (Figure 4), "Hierarchical Sparse Indexer" (Figure 5),
  *         "FP4 主 KV 缓存" (Figure 1(b))
@@ -81,6 +81,7 @@ extern "C" {
 
 #define CSA2_MAX_TOPK 2048
 #define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
+#define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache in csa2_index_full_mq */
 #define CSA2_MAX_CACHE_ROWS 1048576 /* entries per sequence accepted by index_full */
 #define CSA2_ATTN_MAX_GROUPS 65536  /* B * H / 16 accepted by csa2_sparse_attn_decode  */
 #define CSA2_ATTN_WS_COUNTER_BYTES (CSA2_ATTN_MAX_GROUPS * 4) /* leading zeroed region */
@@ -265,6 +266,32 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                     const int32_t* pool_len, int32_t pool_cap, const uint16_t* q,
                     const float* w, int32_t H, int32_t k, int32_t* topk,
                     float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_full_mq -- the Full-mode indexer for Q queries of each sequence
+ * at once, such as the positions of a speculative verify block [WG 7: the
+ * draft block has 5 parallel positions (dspark_block_size); JU 四 item 2: the
+ * 5-position block runs in one forward].  Query i of sequence b gets exactly
+ * what csa2_index_full gives it against cache b:
+ *   score[b][i][p] = sum_h w[b][i][h] * max(0, q[b][i][h] . deq(idx K[b][p]))  for p < len[b]
+ * with its own top-k and pool under the same rules.  The Q queries of a
+ * sequence walk the cache's entries side by side, so the cache is read from
+ * HBM about once for all of them (the others find it in L2).
+ *   B        : sequences (caches);  Q : queries per sequence, 1..16.
+ *   q        : bf16 bits [B][Q][H][128];  w : fp32 [B][Q][H].
+ *   len      : int32 [B], one length per cache (all its queries see it).
+ *   topk     : out int32 [B][Q][k];  pool, pool_len : out [B][Q][n_blocks*block], [B][Q].
+ *   scores_opt : optional out fp32 [B][Q][cap].
+ *   ws, ws_bytes : workspace of at least csa2_index_full_mq_workspace(...) bytes.
+ * Every other argument, the rules and the status codes are csa2_index_full's.
+ */
+size_t csa2_index_full_mq_workspace(int32_t B, int32_t Q, int64_t cap, int32_t k, int32_t block,
+                                    int32_t n_blocks);
+int csa2_index_full_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                       const int32_t* len, int32_t B, int32_t Q, const uint16_t* q, const float* w,
+                       int32_t H, int32_t k, int32_t block, int32_t n_blocks, int32_t* topk,
+                       int32_t* pool, int32_t* pool_len, float* scores_opt, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * csa2_index_full_fp4q, csa2_index_pool_fp4q -- the two indexer calls with an

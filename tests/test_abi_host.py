@@ -37,7 +37,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
-            "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write",
+            "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -238,3 +238,33 @@ def test_window_write_validation(lib):
     assert call(0, FAKE_ODD) == ERR_ALIGN
     assert call(9, P(0x1004)) == ERR_ALIGN  # scale rows: 8-byte aligned
     assert call(6, P(0x1004)) == ERR_ALIGN  # int64 positions
+
+
+def test_index_full_mq_validation(lib):
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f = lib.csa2_index_full_mq
+    f.argtypes = [P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.csa2_index_full_mq_workspace.restype = ctypes.c_size_t
+    lib.csa2_index_full_mq_workspace.argtypes = [i32, i32, i64, i32, i32, i32]
+    lib.csa2_index_full_workspace.restype = ctypes.c_size_t
+    lib.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
+    # the workspace is that of B*Q single-query rows
+    assert lib.csa2_index_full_mq_workspace(16, 5, 131072, 512, 8, 2048) == \
+        lib.csa2_index_full_workspace(80, 131072, 512, 8, 2048)
+    assert lib.csa2_index_full_mq_workspace(16, 17, 131072, 512, 8, 2048) == 0
+    base = [FAKE, FAKE, 4096, FAKE, 4, 5, FAKE, FAKE, 64, 512, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return f(*args)
+
+    assert call(5, 0) == ERR_SHAPE        # queries per sequence
+    assert call(5, 17) == ERR_SHAPE
+    assert call(9, 0) == ERR_SHAPE        # k
+    assert call(8, 12) == ERR_UNSUP       # heads
+    assert call(10, 16) == ERR_UNSUP      # block
+    assert call(4, 0) == CSA2_OK          # no sequences
+    assert call(6, None) == ERR_NULL
+    assert call(6, FAKE_ODD) == ERR_ALIGN
+    assert call(17, 64) == ERR_WS

@@ -298,3 +298,47 @@ def test_index_pool_fp4_query_matches_oracle_and_bf16_selection_rules():
         for p in diff:
             if p >= 0:
                 assert abs(pos_scores[p] - kth) <= 2e-5 * abs(kth) + 1e-7 * np.nanmax(np.abs(rps))
+
+
+# ------------------------------------------------- several queries per cache
+@pytest.mark.parametrize("B,Q,H,k,nb", [(8, 5, 64, 512, 64), (3, 4, 16, 100, 2048), (2, 1, 8, 64, 16)])
+def test_index_full_mq_equals_one_query_calls(B, Q, H, k, nb):
+    # each query row of the multi-query call must be bit-identical to the
+    # single-query call on its sequence's cache, and match the oracle
+    say(f"index_full_mq B={B} Q={Q} H={H} k={k} n_blocks={nb}")
+    cap = 6000
+    wl = syn.small("mq", 70 + B + Q, B=B, cap=cap, H_idx=H, k=k, n_blocks=nb)
+    cache = build_gpu_cache(wl, 0)
+    lens = [cap, cap - 11, 999, 5, 0, 4096, 3001, 64][:B]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = torch.stack([syn.index_query(wl, i, DEV) for i in range(Q)], 1).contiguous()   # [B][Q][H][128]
+    w = torch.stack([syn.index_weights(wl, i, DEV) for i in range(Q)], 1).contiguous()  # [B][Q][H]
+    topk, pool, pool_len, scores = K.index_full_mq(cache["idx_codes"], cache["idx_scales"], lt, q, w, k=k,
+                                                   n_blocks=nb, return_scores=True)
+    torch.cuda.synchronize()
+    topk, pool, pool_len, scores = (t.cpu().numpy() for t in (topk, pool, pool_len, scores))
+    for i in range(Q):
+        t1, p1, pl1, s1 = K.index_full(cache["idx_codes"], cache["idx_scales"], lt, q[:, i].contiguous(),
+                                       w[:, i].contiguous(), k=k, n_blocks=nb, return_scores=True)
+        torch.cuda.synchronize()
+        t1, p1, pl1, s1 = (t.cpu().numpy() for t in (t1, p1, pl1, s1))
+        assert np.array_equal(topk[:, i], t1) and np.array_equal(pool_len[:, i], pl1)
+        assert np.array_equal(pool[:, i], p1)
+        for b, L in enumerate(lens):
+            assert np.array_equal(scores[b, i, :L].view(np.uint32), s1[b, :L].view(np.uint32))
+    # oracle on a sample of (sequence, query) rows
+    qn, wn = q.cpu().numpy(), w.cpu().numpy()
+    certified = 0
+    for b, i in sorted({(0, 0), (0, Q - 1), (B - 1, Q // 2), (min(1, B - 1), 0)}):
+        L = lens[b]
+        if L == 0:
+            assert np.all(topk[b, i] == -1)
+            continue
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        rt, rp, rpl, rs = oracle.index_full(ref["idx_codes"][:L], ref["idx_scales"][:L], L, qn[b, i], wn[b, i],
+                                            k, 8, nb)
+        score_close(scores[b, i, :L], rs)
+        assert np.array_equal(topk[b, i], brute_topk(scores[b, i, :L], k))
+        certified += certify_topk(topk[b, i], rt, rs, k)
+        assert pool_len[b, i] == rpl
+    say(f"  certified near-ties: {certified}")
