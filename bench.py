@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step128",
-                    choices=["tiny", "full128", "step128", "write1m", "stress"])
+                    choices=["tiny", "full128", "step128", "write1m", "stress", "enc128"])
     ap.add_argument("--fmt", default="e8m0", choices=["e8m0", "e4m3"],
                     help="main-KV scale byte format")
     ap.add_argument("--index-q", default="bf16", choices=["bf16", "fp4"],

@@ -72,6 +72,9 @@ WORKLOADS = {
     "stress": Workload("stress", 4, B=64, cap=262144, H_idx=64, k=512, block=8,
                        n_blocks=2048, n_reindex=4, reuse_per_index=3, cluster_frac=0.05,
                        cluster_factor=3.0),
+    # one encoder source layer at 128K tokens: m = 2 entries, Full scoring with
+    # its own top-512 and no candidate pool, then its attention
+    "enc128": Workload("enc128", 5, B=16, cap=65536, H_idx=64, k=512, block=8, n_blocks=0),
 }
 
 

@@ -25,7 +25,7 @@ from gpu_common import (DEV, attn_close, brute_pool, brute_topk, build_gpu_cache
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"tiny": [0], "full128": [0, 15], "step128": [3], "write1m": [1], "stress": [0, 63]}
+SAMPLES = {"tiny": [0], "full128": [0, 15], "step128": [3], "write1m": [1], "stress": [0, 63], "enc128": [0, 9]}
 
 
 def _inputs(wl):
@@ -63,13 +63,16 @@ def _check_workload(wl, fmt):
         gs = scores[b].cpu().numpy()
         score_close(gs, rs)
         assert np.array_equal(topk[0][b], brute_topk(gs, wl.k))
-        bp, bpl, _ = brute_pool(gs, wl.n_blocks)
-        assert pool_len[b] == bpl == rpl
-        assert np.array_equal(pool[b], bp)
         certified += certify_topk(topk[0][b], rt0, rs, wl.k)
-        _, _, rbs = brute_pool(rs, wl.n_blocks)
-        certified += certify_topk(np.unique(pool[b][:bpl] // 8), np.unique(rpool[:rpl] // 8), rbs, wl.n_blocks)
-        same_pool = np.array_equal(pool[b], rpool)
+        same_pool = False
+        if wl.n_blocks > 0:
+            bp, bpl, _ = brute_pool(gs, wl.n_blocks)
+            assert pool_len[b] == bpl == rpl
+            assert np.array_equal(pool[b], bp)
+            _, _, rbs = brute_pool(rs, wl.n_blocks)
+            certified += certify_topk(np.unique(pool[b][:bpl] // 8), np.unique(rpool[:rpl] // 8), rbs,
+                                      wl.n_blocks)
+            same_pool = np.array_equal(pool[b], rpool)
         ref_topk = [rt0]
         for i in range(1, 1 + wl.n_reindex):
             rti, rpsi = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], L, rpool, rpl, qn[i][0], qn[i][1], wl.k)
@@ -171,3 +174,8 @@ def test_write1m_workload():
 
 def test_stress_workload():
     _check_workload(syn.WORKLOADS["stress"], 0)
+
+
+def test_enc128_workload():
+    # encoder source layer: m = 2 entries, no candidate pool
+    _check_workload(syn.WORKLOADS["enc128"], 0)
