@@ -11,13 +11,18 @@ from ._lib import (  # noqa: F401
     Csa2Error,
     append_state,
     cache_append,
+    cache_append_paged,
     cache_write,
     index_full,
     index_full_mq,
+    index_full_paged,
+    index_pool_rows,
+    paged_alloc,
     index_pool,
     lib,
     quantize_fp4,
     sparse_attn_decode,
+    sparse_attn_decode_rows,
     window_alloc,
     window_write,
     workspace,

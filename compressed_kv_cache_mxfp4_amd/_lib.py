@@ -62,6 +62,12 @@ def lib():
     L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
                                           P, i32, f32, P, P, P, P, sz, P]
     L.csa2_window_write.argtypes = [P, i32, i32, P, f32, i32, P, i32, P, P, P, P]
+    L.csa2_cache_append_paged.argtypes = [P, P, i32, i32, P, f32, P, i32, i32, P, P, P, P, i64, P, i32, i32, P, P, P]
+    L.csa2_index_full_paged.argtypes = [P, P, i64, P, i32, i32, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P,
+                                        P, sz, P]
+    L.csa2_index_pool_rows.argtypes = [P, P, i64, i32, P, P, P, i32, P, P, i32, i32, P, P, P, P, sz, P]
+    L.csa2_sparse_attn_decode_rows.argtypes = [P, i32, P, P, i64, i32, P, i32, i32, P, P, i64, i32, P, i32, f32, P,
+                                               P, P, P, sz, P]
     _lib = L
     return L
 
@@ -249,6 +255,143 @@ def window_write(latent, pos0, window: dict, gamma=None, eps: float = 1e-6, rope
     _check(lib().csa2_window_write(_ptr(latent), B, n, _ptr(gamma), float(eps), 1 if rope else 0, _ptr(pos0), W,
                                    _ptr(window["data"]), _ptr(window["scales"]), _ptr(window["swa_len"]),
                                    _stream(dev)), "csa2_window_write")
+
+
+# ---------------------------------------------------------------- paged cache
+def paged_alloc(n_pages: int, page_shift: int, device="cuda"):
+    """Zeroed pool of n_pages pages of 2^page_shift entries: the four planes
+    main_codes [R][256], main_scales [R][32], idx_codes [R][64], idx_scales [R][4]."""
+    R = n_pages << page_shift
+    return {k_: torch.zeros(R, wd, dtype=torch.uint8, device=device)
+            for k_, wd in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4))}
+
+
+def _pool_rows(pool):
+    R = pool["main_codes"].shape[0]
+    for key, width in (("main_codes", 256), ("main_scales", 32), ("idx_codes", 64), ("idx_scales", 4)):
+        _req(pool[key], key, torch.uint8, pool["main_codes"].device, (R, width))
+    return R
+
+
+def cache_append_paged(latent, gate, m: int, w_idx, main_fmt: int, pool: dict, table, page_shift: int, lengths,
+                       state=None, gamma=None, eps: float = 1e-6, rope: bool = False):
+    """cache_append into a paged pool (paged_alloc's dict); table int32 [B][max_pages]."""
+    latent = _bits16(latent)
+    dev = latent.device
+    B = latent.shape[0]
+    _req(latent, "latent", torch.int16, dev, (B, 512))
+    if m == 2:
+        gate = _bits16(gate)
+        _req(gate, "gate", torch.int16, dev, (B, 512))
+        if state is None or state.numel() < lib().csa2_append_state_bytes(B):
+            raise ValueError("m == 2 needs the append state")
+    else:
+        gate = None
+    R = _pool_rows(pool)
+    _req(table, "table", torch.int32, dev, (B, table.shape[1]))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    _check(lib().csa2_cache_append_paged(_ptr(latent), _ptr(gate), B, m, _ptr(gamma), float(eps), _ptr(w_idx),
+                                         main_fmt, 1 if rope else 0, _ptr(pool["main_codes"]),
+                                         _ptr(pool["main_scales"]), _ptr(pool["idx_codes"]), _ptr(pool["idx_scales"]),
+                                         R, _ptr(table), page_shift, table.shape[1], _ptr(lengths),
+                                         _ptr(state) if m == 2 else None, _stream(dev)), "csa2_cache_append_paged")
+
+
+def index_full_paged(pool: dict, table, page_shift: int, lengths, q, w, k: int = 512, n_blocks: int = 2048,
+                     return_scores: bool = False, out=None, _ws=None):
+    """index_full over a paged pool.  Returns (topk, topk_rows, pool, pool_rows,
+    pool_len[, scores]); positions are logical, *_rows are pool rows."""
+    q = _bits16(q)
+    dev = q.device
+    B, H = q.shape[0], q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    R = _pool_rows(pool)
+    _req(table, "table", torch.int32, dev, (B, table.shape[1]))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    cap = table.shape[1] << page_shift
+    out = out or {}
+    nb8 = max(n_blocks * 8, 1)
+    res = {}
+    for key, shape in (("topk", (B, k)), ("topk_rows", (B, k)), ("pool", (B, nb8)), ("pool_rows", (B, nb8)),
+                       ("pool_len", (B,))):
+        res[key] = out.get(key)
+        if res[key] is None:
+            res[key] = torch.empty(*shape, dtype=torch.int32, device=dev)
+    scores = out.get("scores")
+    if return_scores and scores is None:
+        scores = torch.empty(B, cap, dtype=torch.float32, device=dev)
+    ws = _ws if _ws is not None else workspace(lib().csa2_index_full_workspace(B, cap, k, 8, n_blocks), dev)
+    _check(lib().csa2_index_full_paged(_ptr(pool["idx_codes"]), _ptr(pool["idx_scales"]), R, _ptr(table), page_shift,
+                                       table.shape[1], _ptr(lengths), B, _ptr(q), _ptr(w), H, k, 8, n_blocks,
+                                       _ptr(res["topk"]), _ptr(res["topk_rows"]), _ptr(res["pool"]),
+                                       _ptr(res["pool_rows"]), _ptr(res["pool_len"]), _ptr(scores), _ptr(ws),
+                                       ws.numel(), _stream(dev)), "csa2_index_full_paged")
+    r = (res["topk"], res["topk_rows"], res["pool"][:, : n_blocks * 8], res["pool_rows"][:, : n_blocks * 8],
+         res["pool_len"])
+    return r + (scores,) if return_scores else r
+
+
+def index_pool_rows(pool: dict, cand, cand_rows, cand_len, q, w, k: int = 512, out=None, _ws=None):
+    """Reindex over a paged pool: candidates given by logical positions `cand`
+    and pool rows `cand_rows` [B][pool_cap].  Returns (topk, topk_rows)."""
+    q = _bits16(q)
+    dev = q.device
+    B, H = q.shape[0], q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    R = _pool_rows(pool)
+    pool_cap = cand.shape[1]
+    _req(cand, "pool", torch.int32, dev, (B, pool_cap))
+    _req(cand_rows, "pool_rows", torch.int32, dev, (B, pool_cap))
+    _req(cand_len, "pool_len", torch.int32, dev, (B,))
+    out = out or {}
+    topk = out.get("topk")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=dev)
+    topk_rows = out.get("topk_rows")
+    if topk_rows is None:
+        topk_rows = torch.empty(B, k, dtype=torch.int32, device=dev)
+    wsb = lib().csa2_index_pool_workspace(B, pool_cap, k)
+    ws = _ws if _ws is not None else workspace(max(wsb, 256), dev)
+    _check(lib().csa2_index_pool_rows(_ptr(pool["idx_codes"]), _ptr(pool["idx_scales"]), R, B, _ptr(cand),
+                                      _ptr(cand_rows), _ptr(cand_len), pool_cap, _ptr(q), _ptr(w), H, k, _ptr(topk),
+                                      _ptr(topk_rows), None, _ptr(ws), ws.numel(), _stream(dev)),
+           "csa2_index_pool_rows")
+    return topk, topk_rows
+
+
+def sparse_attn_decode_rows(q, pool: dict, rows, main_fmt: int, swa_codes=None, swa_scales=None, swa_len=None,
+                            swa_stride: int = 0, swa_cap: int = 0, swa_fmt: int = 0, sm_scale: Optional[float] = None,
+                            return_lse: bool = False, out=None, _ws=None, q_pos=None):
+    """sparse_attn_decode with the selected entries as pool rows [B][k] of a paged pool."""
+    q = _bits16(q)
+    dev = q.device
+    B, H = q.shape[0], q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 512))
+    R = _pool_rows(pool)
+    k = rows.shape[1]
+    _req(rows, "rows", torch.int32, dev, (B, k))
+    if swa_cap > 0:
+        _req(swa_len, "swa_len", torch.int32, dev, (B,))
+        rb, sb = (576, 8) if swa_fmt == SWA_FP8 else (256, 32)
+        if swa_codes.numel() < B * swa_stride * rb or swa_scales.numel() < B * swa_stride * sb:
+            raise ValueError("window planes smaller than B rows of swa_stride")
+    if q_pos is not None:
+        _req(q_pos, "q_pos", torch.int64, dev, (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / (512 ** 0.5)
+    o = None if out is None else out.get("out")
+    if o is None:
+        o = torch.empty(B, H, 512, dtype=torch.int16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev) if return_lse else None
+    ws = _ws if _ws is not None else workspace(lib().csa2_attn_workspace(B, H, k, swa_cap), dev, "attn")
+    _check(lib().csa2_sparse_attn_decode_rows(
+        _ptr(q), H, _ptr(pool["main_codes"]), _ptr(pool["main_scales"]), R, main_fmt, _ptr(rows), k, B,
+        _ptr(swa_codes) if swa_cap else None, _ptr(swa_scales) if swa_cap else None, swa_stride, swa_cap,
+        _ptr(swa_len) if swa_cap else None, int(swa_fmt) if swa_cap else 0, float(sm_scale), _ptr(q_pos), _ptr(o),
+        _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode_rows")
+    return (o, lse) if return_lse else o
 
 
 def _index_query(q, dev, B):

@@ -265,4 +265,122 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                                            as_stream(stream)));
 }
 
+// ------------------------------------------------------------ paged cache
+// A valid page map: pages of 2^page_shift entries (64 .. 2^20), a logical
+// capacity of at most CSA2_MAX_CACHE_ROWS entries, and a pool of whole pages
+// small enough for 32-bit byte offsets into the 64-byte indexer-K rows.
+static int paged_shape(int64_t n_rows, int32_t page_shift, int32_t max_pages) {
+  if (page_shift < CSA2_MIN_PAGE_SHIFT || page_shift > CSA2_MAX_PAGE_SHIFT || max_pages < 1) return CSA2_ERR_SHAPE;
+  if (((int64_t)max_pages << page_shift) > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (n_rows < (1 << page_shift) || n_rows > CSA2_MAX_POOL_ROWS || (n_rows & ((1 << page_shift) - 1)))
+    return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
+static csa2::PageMap page_map(const int32_t* table, int64_t n_rows, int32_t page_shift, int32_t max_pages) {
+  return csa2::PageMap{table, page_shift, max_pages, (int32_t)(n_rows >> page_shift)};
+}
+
+int csa2_cache_append_paged(const uint16_t* latent, const uint16_t* gate, int32_t B, int32_t m,
+                            const float* gamma, float eps, const float* w_idx, int32_t main_fmt, int32_t rope,
+                            uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales,
+                            int64_t n_rows, const int32_t* block_table, int32_t page_shift, int32_t max_pages,
+                            int32_t* len, void* state, void* stream) {
+  const int ps = paged_shape(n_rows, page_shift, max_pages);
+  if (ps != CSA2_OK) return ps;
+  if (B < 0 || m < 1 || m > 2) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!latent || (m == 2 && (!gate || !state)) || !w_idx || !main_codes || !main_scales || !idx_codes ||
+      !idx_scales || !len || !block_table)
+    return CSA2_ERR_NULL;
+  if (!aligned16(latent) || (m == 2 && (!aligned16(gate) || !aligned16(state))) || !aligned16(main_codes) ||
+      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(len) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return CSA2_ERR_ALIGN;
+  const int64_t cap = (int64_t)max_pages << page_shift;
+  return launched(csa2::launch_cache_append(latent, gate, B, m, gamma, eps, w_idx, main_fmt, rope ? 1 : 0,
+                                            main_codes, main_scales, idx_codes, idx_scales, cap, len, state,
+                                            as_stream(stream), page_map(block_table, n_rows, page_shift, max_pages)));
+}
+
+int csa2_index_full_paged(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t n_rows,
+                          const int32_t* block_table, int32_t page_shift, int32_t max_pages,
+                          const int32_t* len, int32_t B, const uint16_t* q, const float* w, int32_t H,
+                          int32_t k, int32_t block, int32_t n_blocks, int32_t* topk, int32_t* topk_rows,
+                          int32_t* pool, int32_t* pool_rows, int32_t* pool_len, float* scores_opt,
+                          void* ws, size_t ws_bytes, void* stream) {
+  const int ps = paged_shape(n_rows, page_shift, max_pages);
+  if (ps != CSA2_OK) return ps;
+  const int64_t cap = (int64_t)max_pages << page_shift;
+  if (B < 0) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+  if (n_blocks < 0 || n_blocks > CSA2_POOL_BLOCKS || (int64_t)n_blocks * block > CSA2_MAX_POOL)
+    return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !block_table || !len || !q || !w || !topk || !topk_rows)
+    return CSA2_ERR_NULL;
+  if (n_blocks > 0 && (!pool || !pool_rows || !pool_len)) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return CSA2_ERR_ALIGN;
+  if (!ws || ws_bytes < csa2_index_full_workspace(B, cap, k, block, n_blocks)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_full(idx_codes, idx_scales, cap, len, B, q, nullptr, nullptr, w, H, k, block,
+                                          n_blocks, topk, pool, pool_len, scores_opt, ws, as_stream(stream), 1,
+                                          page_map(block_table, n_rows, page_shift, max_pages), topk_rows,
+                                          n_blocks > 0 ? pool_rows : nullptr));
+}
+
+int csa2_index_pool_rows(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t n_rows, int32_t B,
+                         const int32_t* pool, const int32_t* pool_rows, const int32_t* pool_len,
+                         int32_t pool_cap, const uint16_t* q, const float* w, int32_t H, int32_t k,
+                         int32_t* topk, int32_t* topk_rows, float* pool_scores_opt, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (B < 0 || n_rows <= 0 || n_rows > CSA2_MAX_POOL_ROWS) return CSA2_ERR_SHAPE;
+  if (pool_cap < 0 || pool_cap > CSA2_MAX_POOL) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !pool || !pool_rows || !pool_len || !q || !w || !topk || !topk_rows)
+    return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  const size_t need = csa2_index_pool_workspace(B, pool_cap, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_pool(idx_codes, idx_scales, n_rows, nullptr, B, pool, pool_len, pool_cap, q,
+                                          nullptr, nullptr, w, H, k, topk, pool_scores_opt, ws, as_stream(stream),
+                                          pool_rows, topk_rows));
+}
+
+int csa2_sparse_attn_decode_rows(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                                 const uint8_t* main_scales, int64_t n_rows, int32_t main_fmt,
+                                 const int32_t* rows, int32_t k, int32_t B, const uint8_t* swa_codes,
+                                 const uint8_t* swa_scales, int64_t swa_stride, int32_t swa_cap,
+                                 const int32_t* swa_len, int32_t swa_fmt, float sm_scale, const int64_t* q_pos,
+                                 uint16_t* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || n_rows < 0 || n_rows > CSA2_MAX_POOL_ROWS) return CSA2_ERR_SHAPE;
+  if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
+  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (swa_fmt != CSA2_SWA_MAIN && swa_fmt != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
+  if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!q || !out) return CSA2_ERR_NULL;
+  if (k > 0 && (!main_codes || !main_scales || !rows)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
+      (reinterpret_cast<uintptr_t>(q_pos) & 7u) ||
+      (swa_fmt == CSA2_SWA_FP8 && (reinterpret_cast<uintptr_t>(swa_scales) & 7u)))
+    return CSA2_ERR_ALIGN;
+  if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, n_rows, main_fmt, nullptr, rows, k, B,
+                                           swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale,
+                                           q_pos, out, lse_opt, ws, as_stream(stream), true));
+}
+
 }  // extern "C"

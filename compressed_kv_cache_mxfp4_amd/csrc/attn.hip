@@ -133,7 +133,7 @@ constexpr int kWinScaleB = 8;
 // one layout); slots k..kw-1 are empty.
 template <bool WF8>
 __device__ __forceinline__ RowSrc locate_row(int slot, int32_t p, int nslots, int b, int k, int kw,
-                                             int64_t L, int SL, int64_t cap, int64_t swa_stride,
+                                             int64_t L, int SL, int64_t seq_stride, int64_t swa_stride,
                                              const uint8_t* __restrict__ main_codes,
                                              const uint8_t* __restrict__ main_scales,
                                              const uint8_t* __restrict__ swa_codes,
@@ -141,8 +141,8 @@ __device__ __forceinline__ RowSrc locate_row(int slot, int32_t p, int nslots, in
   RowSrc r{nullptr, nullptr, 0u, 0u};
   if (slot < k) {
     if (p >= 0 && (int64_t)p < L) {
-      r.codes = main_codes + ((int64_t)b * cap + p) * 256;
-      r.scales = main_scales + ((int64_t)b * cap + p) * 32;
+      r.codes = main_codes + ((int64_t)b * seq_stride + p) * 256;
+      r.scales = main_scales + ((int64_t)b * seq_stride + p) * 32;
       r.ok = 1u;
     }
   } else if (slot >= kw && slot < nslots) {
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units, int64_t seq_stride) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
                "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
                "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S),
-               "s"(seq_units), "s"(q_pos));
+               "s"(seq_units), "s"(q_pos), "s"(seq_stride));
   const int HG = H >> 4;
   // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
   // otherwise one (sequence, head group).  A unit's workgroups get ids
@@ -443,13 +443,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   asm volatile("" ::"v"(praw), "v"(Lraw), "v"(SLraw), "v"(qpos));
   const int32_t pidx = slot < k ? praw : -1;
   if (!valid) return;
-  int64_t L = len ? Lraw : 0;
+  int64_t L = len ? Lraw : cap;  // no lengths: absolute row ids below cap
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int SL = swa_len ? SLraw : 0;
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
   RowFetch row;
   {
-    const RowSrc src = locate_row<WF8>(slot, pidx, nslots, b, k, kw, L, SL, cap, swa_stride, main_codes,
+    const RowSrc src = locate_row<WF8>(slot, pidx, nslots, b, k, kw, L, SL, seq_stride, swa_stride, main_codes,
                                        main_scales, swa_codes, swa_scales);
     if constexpr (WF8)
       fetch_row_w8(row, src, g);
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t seq_stride) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnTSmem& sm = *reinterpret_cast<AttnTSmem*>(smem_raw);
   asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   // (the extra steps only synchronise); both roles run exactly this many
   const int nsteps = (nc + 1 + 2) / 3 * 3;
 
-  int64_t L = len ? len[b] : 0;
+  int64_t L = len ? len[b] : cap;  // no lengths: absolute row ids below cap
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int SL = swa_len ? swa_len[b] : 0;
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
@@ -771,8 +771,8 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     if (c < c_end) {
       if (slot < k) {
         if (p >= 0 && (int64_t)p < L) {
-          cp = main_codes + ((int64_t)b * cap + p) * 256;
-          scp = main_scales + ((int64_t)b * cap + p) * 32;
+          cp = main_codes + ((int64_t)b * seq_stride + p) * 256;
+          scp = main_scales + ((int64_t)b * seq_stride + p) * 32;
           ok = 1u;
         }
       } else if (!WF8 && slot < nslots && slot - k < SL) {
@@ -1178,8 +1178,11 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
                        const int32_t* swa_len, int swa_fmt, float sm_scale, const int64_t* q_pos,
-                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st) {
+                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st, bool abs_rows) {
   if (B == 0) return 0;
+  // abs_rows: the index list holds row ids into one pool of cap rows shared
+  // by all sequences (no lengths); otherwise positions into sequence b's cap rows
+  const int64_t seq_stride = abs_rows ? 0 : cap;
   const bool w8 = swa_fmt == 1 && swa_cap > 0;
   const int nslots = attn_slots(k, swa_cap, w8);
   const int64_t HG = H / 16;
@@ -1206,7 +1209,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
       if (!lds_ok) return false;
       kern<<<tgrid, 512, sizeof(AttnTSmem), st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                                    swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, Sq,
-                                                   part, ml, cnt, out, lse_opt);
+                                                   part, ml, cnt, out, lse_opt, seq_stride);
       return true;
     };
     bool ok;
@@ -1226,7 +1229,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     if (!lds_ok) return false;
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                          swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, S,
-                                         part, ml, cnt, out, lse_opt, seq_units);
+                                         part, ml, cnt, out, lse_opt, seq_units, seq_stride);
     return true;
   };
   auto pick = [&](auto fmt_c, auto w8_c) -> bool {

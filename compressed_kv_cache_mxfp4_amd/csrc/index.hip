@@ -50,6 +50,24 @@ struct ScoreRows {
   uint32_t ok;  // bit t: entry of tile t exists and is visible
 };
 
+// Paged cache, full mode: the rows of the super-tile at `base` through the
+// page table.  Its 64 entries share one page (pages hold at least 64
+// entries), so one wave-uniform (scalar) table load serves the super-tile.
+__device__ __forceinline__ void score_rows_paged(ScoreRows& R, int64_t base, int64_t N, const PageMap& pm,
+                                                 int cache, int n) {
+  const int tb = __builtin_amdgcn_readfirstlane((int)(base < N ? base >> pm.shift : 0));
+  const int32_t pbase = page_base(pm, cache, (int64_t)tb << pm.shift);
+  const int32_t mask = (1 << pm.shift) - 1;
+  R.ok = 0u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t it = base + 16 * t + n;
+    const bool in = it < N;
+    R.r[t] = in ? pbase + (int32_t)(it & mask) : 0;
+    R.ok |= (in ? 1u : 0u) << t;
+  }
+}
+
 // Loaded operands of one super-tile: tile t's codes (entry 16t+n, dims
 // 32g..32g+31) and the E8M0 byte of that (entry, group).
 struct ScoreStage {
@@ -180,14 +198,16 @@ __device__ __forceinline__ float max8_lanes(float v) {
 // are read one ring step before its codes.
 constexpr int kScoreStages = 2;
 
-template <int MT, bool GATHER, bool Q4 = false, int NS = kScoreStages, int OCC = 2, bool WLDS = false>
+template <int MT, bool GATHER, bool Q4 = false, bool PAGED = false, int NS = kScoreStages, int OCC = 2,
+          bool WLDS = false>
 __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int64_t cap,
     const int32_t* __restrict__ len, const int32_t* __restrict__ pool,
     const int32_t* __restrict__ pool_len, int pool_cap, const uint16_t* __restrict__ q,
     const float* __restrict__ w, int H, float* __restrict__ scores, int64_t score_stride,
     float* __restrict__ bmax, int64_t bmax_stride, int B, int per_seq,
-    const uint8_t* __restrict__ q4_codes, const uint8_t* __restrict__ q4_scales, int qps) {
+    const uint8_t* __restrict__ q4_codes, const uint8_t* __restrict__ q4_scales, int qps, PageMap pm,
+    int64_t seq_stride) {
   __shared__ __align__(16) uint16_t qs[Q4 ? 8 : 64 * 128];
   __shared__ float ws[64];
   // Grid: per_seq workgroups for each of the B query rows, in one dimension;
@@ -219,8 +239,9 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
   const int64_t step = W * kSuperTile;
   const int64_t base0 = st0 * kSuperTile;
   const int64_t Nmax = GATHER ? (int64_t)pool_cap : cap;  // bound of the item index
-  const uint8_t* codes_b = idx_codes + (int64_t)cb * cap * 64;
-  const uint8_t* scales_b = idx_scales + (int64_t)cb * cap * 4;
+  // seq_stride: rows between sequences' caches (0: one pool, physical rows)
+  const uint8_t* codes_b = idx_codes + (int64_t)cb * seq_stride * 64;
+  const uint8_t* scales_b = idx_scales + (int64_t)cb * seq_stride * 4;
   const int32_t* pool_b = GATHER ? pool + (int64_t)b * pool_cap : nullptr;
   float* scores_b = scores + (int64_t)b * score_stride;
 
@@ -241,6 +262,7 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
       else
         rows[u].r[t] = in ? (int32_t)it : 0;
     }
+    if (PAGED) score_rows_paged(rows[u], base0 + u * step, Nmax, pm, cb, n);
     rows[u].ok = 0u;
   }
   if (!GATHER) {
@@ -272,7 +294,7 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&qs[h * 128 + 32 * part + 8 * j]) = v[j];
   }
   if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < H ? w[(int64_t)b * H + threadIdx.x] : 0.0f;
-  int64_t L = len[cb];
+  int64_t L = len ? len[cb] : cap;  // no lengths: pool rows below cap
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int64_t N = L;
   if (GATHER) {
@@ -327,7 +349,10 @@ __global__ __launch_bounds__(kScoreThreads, OCC) void score_kernel(
       const uint32_t ok = rows[u].ok;
       // refill: stage of iteration i+NS-1 (its rows are ready), rows of i+NS
       score_load(stg[(u + NS - 1) % NS], rows[(u + NS - 1) % NS], codes_b, scales_b, g);
-      score_rows<GATHER>(rows[u], bs + NS * step, N, L, pool_b, n);
+      if (PAGED)
+        score_rows_paged(rows[u], bs + NS * step, N, pm, cb, n);
+      else
+        score_rows<GATHER>(rows[u], bs + NS * step, N, L, pool_b, n);
       if (i < iters) {
         if (WLDS) {
           // head weights re-read from LDS each super-tile (keeps 16 VGPRs free)
@@ -732,7 +757,8 @@ template <int NT, int EPT_B, int EPT_C, int EPT_P>
 __global__ __launch_bounds__(NT) void select_full_kernel(
     const float* __restrict__ scores, int64_t sstride, const float* __restrict__ bmax,
     int64_t bstride, const int32_t* __restrict__ len, int64_t cap, int k, int n_blocks,
-    int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len, int qps) {
+    int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len, int qps,
+    PageMap pm, int32_t* __restrict__ topk_rows, int32_t* __restrict__ pool_rows) {
   __shared__ SelScratch sh;
   __shared__ int32_t blk[CSA2_POOL_BLOCKS];
   __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
@@ -746,6 +772,8 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   const int nb = (int)((L + kBlock - 1) / kBlock);
   const float* sc = scores + (int64_t)b * sstride;
   int32_t* tk = topk + (int64_t)b * k;
+  // paged cache: the selections' physical rows too (row ids for the gathers)
+  int32_t* tkr = topk_rows ? topk_rows + (int64_t)b * k : nullptr;
   if constexpr (EPT_B > 0) finish_keys<NT, EPT_B>(kb, nb);
   int ncb;
   if (n_blocks > 0) {
@@ -758,6 +786,7 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
     // a thread writes whole groups (8 entries: two 16-byte stores when the
     // caller's buffer allows it)
     const bool vec = (reinterpret_cast<uintptr_t>(pb) & 15u) == 0u;
+    int32_t* pbr = pool_rows ? pool_rows + (int64_t)b * n_blocks * kBlock : nullptr;
     for (int gi = threadIdx.x; gi < n_blocks; gi += NT) {
       const int base = gi * kBlock;
       const int p0 = gi < nsel ? blk[gi] * kBlock : 0;
@@ -771,6 +800,12 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[base + j] = e[j];
+      }
+      if (pbr) {
+        // a block of 8 never straddles a page (pages hold >= 64 entries)
+        const int32_t r0 = base < pl ? page_row(pm, b / qps, p0) : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pbr[base + j] = e[j] >= 0 ? r0 + j : -1;
       }
     }
     if (threadIdx.x == 0) pool_len[b] = pl;
@@ -789,9 +824,14 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   KeysFromGroups psrc{sc, cblk};
   KeyRegs<EPT_P> kp;
   load_keys<NT, EPT_P>(kp, psrc, nc);
-  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh,
-                                               [&](int i, int r, int) { tk[r] = psrc.item(i); });
-  for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
+  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh, [&](int i, int r, int) {
+    tk[r] = psrc.item(i);
+    if (tkr) tkr[r] = page_row(pm, b / qps, psrc.item(i));
+  });
+  for (int i = cnt + threadIdx.x; i < k; i += NT) {
+    tk[i] = -1;
+    if (tkr) tkr[i] = -1;
+  }
 }
 
 // Reindex selection: top-k of the pool scores (NaN = masked entry) through
@@ -802,7 +842,7 @@ template <int NT, int EPT_G, int EPT_P>
 __global__ __launch_bounds__(NT) void select_pool_kernel(
     const float* __restrict__ pool_scores, const float* __restrict__ gmax,
     const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_len, int pool_cap, int k,
-    int32_t* __restrict__ topk) {
+    int32_t* __restrict__ topk, const int32_t* __restrict__ pool_rows, int32_t* __restrict__ topk_rows) {
   __shared__ SelScratch sh;
   __shared__ int32_t cgrp[CSA2_MAX_TOPK];
   const int b = blockIdx.x;
@@ -815,6 +855,9 @@ __global__ __launch_bounds__(NT) void select_pool_kernel(
   const int ng = (n + kBlock - 1) / kBlock;
   const int32_t* pb = pool + (int64_t)b * pool_cap;
   int32_t* tk = topk + (int64_t)b * k;
+  // the selections' physical rows too, when the pool has them
+  const int32_t* pbr = pool_rows ? pool_rows + (int64_t)b * pool_cap : nullptr;
+  int32_t* tkr = topk_rows ? topk_rows + (int64_t)b * k : nullptr;
   finish_keys<NT, EPT_G>(kg, ng);
   const int ncg = select_core<NT, EPT_G, false>(kg, gsrc, ng, k, sh, [&](int i, int r, int) { cgrp[r] = i; });
   const int nc = group_items(cgrp, ncg, n);
@@ -832,8 +875,12 @@ __global__ __launch_bounds__(NT) void select_pool_kernel(
   }
   const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh, [&](int i, int r, int j) {
     if constexpr (EPT_P > 0) tk[r] = pos[j]; else tk[r] = pb[psrc.item(i)];
+    if (tkr) tkr[r] = pbr[psrc.item(i)];
   });
-  for (int i = cnt + threadIdx.x; i < k; i += NT) tk[i] = -1;
+  for (int i = cnt + threadIdx.x; i < k; i += NT) {
+    tk[i] = -1;
+    if (tkr) tkr[i] = -1;
+  }
 }
 
 // ======================================================================
@@ -856,15 +903,24 @@ static void launch_score(int MT, int per_seq, int B, hipStream_t st, const uint8
                          int64_t cap, const int32_t* len, const int32_t* pool,
                          const int32_t* pool_len, int pool_cap, const uint16_t* q, const uint8_t* q4c,
                          const uint8_t* q4s, const float* w, int H, float* scores, int64_t sstride,
-                         float* bmax, int64_t bstride, int qps = 1) {
+                         float* bmax, int64_t bstride, int qps = 1, PageMap pm = PageMap{nullptr, 0, 0, 0},
+                         int64_t seq_stride = -1) {
   const dim3 grid((unsigned)per_seq * (unsigned)B);
-#define CSA2_SCORE(MT_, Q4_) \
-  score_kernel<MT_, GATHER, Q4_><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, w, H, \
-                                                                 scores, sstride, bmax, bstride, B, per_seq, q4c, q4s, qps)
-  if (q4c) {
-    if (MT == 1) CSA2_SCORE(1, true); else if (MT == 2) CSA2_SCORE(2, true); else CSA2_SCORE(4, true);
+  if (seq_stride < 0) seq_stride = cap;
+#define CSA2_SCORE(MT_, Q4_, PG_) \
+  score_kernel<MT_, GATHER, Q4_, PG_><<<grid, kScoreThreads, 0, st>>>(ic, is, cap, len, pool, pool_len, pool_cap, q, \
+                                                                      w, H, scores, sstride, bmax, bstride, B, per_seq, \
+                                                                      q4c, q4s, qps, pm, seq_stride)
+  if (!GATHER && pm.table) {
+    if (q4c) {
+      if (MT == 1) CSA2_SCORE(1, true, true); else if (MT == 2) CSA2_SCORE(2, true, true); else CSA2_SCORE(4, true, true);
+    } else {
+      if (MT == 1) CSA2_SCORE(1, false, true); else if (MT == 2) CSA2_SCORE(2, false, true); else CSA2_SCORE(4, false, true);
+    }
+  } else if (q4c) {
+    if (MT == 1) CSA2_SCORE(1, true, false); else if (MT == 2) CSA2_SCORE(2, true, false); else CSA2_SCORE(4, true, false);
   } else {
-    if (MT == 1) CSA2_SCORE(1, false); else if (MT == 2) CSA2_SCORE(2, false); else CSA2_SCORE(4, false);
+    if (MT == 1) CSA2_SCORE(1, false, false); else if (MT == 2) CSA2_SCORE(2, false, false); else CSA2_SCORE(4, false, false);
   }
 #undef CSA2_SCORE
 }
@@ -884,7 +940,8 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
                       const uint8_t* q4s, const float* w, int H, int k,
                       int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
-                      float* scores_opt, void* ws, hipStream_t st, int qps) {
+                      float* scores_opt, void* ws, hipStream_t st, int qps, PageMap pm, int32_t* topk_rows,
+                      int32_t* pool_rows) {
   if (B == 0) return 0;
   const IndexFullWs l = index_full_ws_layout(B, cap, block);
   float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -894,13 +951,13 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   const int per_seq = (int)score_wgs(cap, B, kScoreWaves);
   if (cap > 0)
     launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, q4c,
-                        q4s, w, H, scores, cap, bmax, nbk, qps);
+                        q4s, w, H, scores, cap, bmax, nbk, qps, pm, pm.table ? 0 : cap);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
   // keys per thread: all blocks (EB), the pool blocks (2), candidate positions (EP)
 #define CSA2_SELFULL(EB, EP) \
   select_full_kernel<1024, EB, 2, EP><<<B, 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, \
-                                                         pool_len, qps)
+                                                         pool_len, qps, pm, topk_rows, pool_rows)
   if (nbk <= 4 * 1024) {
     if (kbig) CSA2_SELFULL(4, 16); else CSA2_SELFULL(4, 4);
   } else if (nbk <= 16 * 1024) {
@@ -936,7 +993,8 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
                       int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
                       const float* w, int H, int k,
-                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st) {
+                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st,
+                      const int32_t* pool_rows, int32_t* topk_rows) {
   if (B == 0) return 0;
   const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
   float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -945,14 +1003,18 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   const int MT = (H + 15) / 16;
   const int per_seq = (int)score_wgs(pool_cap, B, kScoreWavesPool);
   if (pool_cap > 0)
-    launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, pool, pool_len, pool_cap, q, q4c, q4s,
-                       w, H, ps, pool_cap, gmax, ngs);
+    // with physical pool rows: gather from one pool of cap rows, no lengths
+    launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, pool_rows ? nullptr : len,
+                       pool_rows ? pool_rows : pool, pool_len, pool_cap, q, q4c, q4s, w, H, ps, pool_cap, gmax, ngs,
+                       1, PageMap{nullptr, 0, 0, 0}, pool_rows ? 0 : cap);
   if (hipGetLastError() != hipSuccess) return -1;
   // keys per thread: groups (<= 2048 -> 2), candidate positions (8 per selected group)
   if (k <= 512)
-    select_pool_kernel<1024, 2, 4><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk);
+    select_pool_kernel<1024, 2, 4><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk, pool_rows,
+                                                       topk_rows);
   else
-    select_pool_kernel<1024, 2, 16><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk);
+    select_pool_kernel<1024, 2, 16><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk, pool_rows,
+                                                        topk_rows);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     uint8_t* __restrict__ main_codes, uint8_t* __restrict__ main_scales,
     uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int64_t cap,
     const int32_t* __restrict__ len, const int32_t* __restrict__ count,
-    const uint16_t* __restrict__ plat, const uint16_t* __restrict__ pgate) {
+    const uint16_t* __restrict__ plat, const uint16_t* __restrict__ pgate, PageMap pm) {
   __shared__ float y[512];
   __shared__ float kv[8][33];
   __shared__ float red[4];
@@ -404,7 +404,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 #pragma unroll
   for (int c = 0; c < 2; ++c) y[2 * t + c] = pooled[c] * r * (gamma ? gamma[2 * t + c] : 1.0f);
   __syncthreads();
-  const int64_t row = (int64_t)b * cap + L;
+  // entry L of sequence b: its own region, or its page of the pool
+  const int64_t row = pm.table ? (int64_t)page_row(pm, b, L) : (int64_t)b * cap + L;
   if (ct == 0 && t < 32) {
     // main entry, channel group t (16 channels), rotated first when asked
     float v[16];
@@ -492,18 +493,18 @@ __global__ __launch_bounds__(64) void cache_advance_kernel(
 int launch_cache_append(const uint16_t* latent, const uint16_t* gate, int B, int m, const float* gamma,
                         float eps, const float* w_idx, int main_fmt, int rope, uint8_t* main_codes,
                         uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales, int64_t cap,
-                        int32_t* len, void* state, hipStream_t st) {
+                        int32_t* len, void* state, hipStream_t st, PageMap pm) {
   if (B == 0) return 0;
   AppendState s{nullptr, nullptr, nullptr};
   if (m == 2) s = append_state(state, B);
   if (main_fmt == 0)
     cache_append_kernel<0><<<dim3(B, 4), 256, 0, st>>>(latent, gate, m, gamma, eps, w_idx, rope, main_codes,
                                               main_scales, idx_codes, idx_scales, cap, len, s.count, s.lat,
-                                              s.gate);
+                                              s.gate, pm);
   else
     cache_append_kernel<1><<<dim3(B, 4), 256, 0, st>>>(latent, gate, m, gamma, eps, w_idx, rope, main_codes,
                                               main_scales, idx_codes, idx_scales, cap, len, s.count, s.lat,
-                                              s.gate);
+                                              s.gate, pm);
   cache_advance_kernel<<<B, 64, 0, st>>>(latent, gate, m, cap, len, s.count, s.lat, s.gate);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

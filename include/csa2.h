@@ -82,6 +82,9 @@ extern "C" {
 #define CSA2_MAX_TOPK 2048
 #define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
 #define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache in csa2_index_full_mq */
+#define CSA2_MIN_PAGE_SHIFT 6      /* paged cache: pages of 2^6 .. 2^20 entries    */
+#define CSA2_MAX_PAGE_SHIFT 20
+#define CSA2_MAX_POOL_ROWS (1 << 26) /* rows of a paged pool (32-bit byte offsets)  */
 #define CSA2_MAX_CACHE_ROWS 1048576 /* entries per sequence accepted by index_full */
 #define CSA2_ATTN_MAX_GROUPS 65536  /* B * H / 16 accepted by csa2_sparse_attn_decode  */
 #define CSA2_ATTN_WS_COUNTER_BYTES (CSA2_ATTN_MAX_GROUPS * 4) /* leading zeroed region */
@@ -380,6 +383,70 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
                             int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
                             float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Paged cache [GP 7: the cache is paged with 576-byte alignment].  The four
+ * planes of all sequences live in one pool of n_rows entries (row r of each
+ * plane: main codes [r][256], main scales [r][32], indexer codes [r][64],
+ * indexer scales [r][4]), in pages of P = 2^page_shift entries
+ * (CSA2_MIN_PAGE_SHIFT..CSA2_MAX_PAGE_SHIFT, so a page holds at least 64
+ * entries).  Entry i of sequence b is pool row
+ *     block_table[b * max_pages + i / P] * P + i % P,
+ * block_table : int32 [B][max_pages], page ids in [0, n_rows / P) (an id
+ * outside is clamped into the pool: a stale table reads a wrong row of the
+ * pool, never memory outside it).  Logical capacity max_pages * P <=
+ * CSA2_MAX_CACHE_ROWS; n_rows a multiple of P, at most CSA2_MAX_POOL_ROWS.
+ * Positions stay logical everywhere (lengths, top-k, pool, RoPE positions);
+ * the indexer calls also return the physical rows of what they select, and
+ * the Reindex and attention calls gather by those rows, so each index layer
+ * resolves pages once and its Reuse layers reuse the rows.
+ *
+ * csa2_cache_append_paged -- csa2_cache_append into a paged pool: the entry
+ * of sequence b goes to logical row len[b], i.e. pool row via block_table
+ * (len[b] >= max_pages * P: full).  Other arguments as csa2_cache_append.
+ *
+ * csa2_index_full_paged -- csa2_index_full over a paged cache (one page-table
+ * read per 64-entry tile of the scoring pass).  topk, pool, pool_len as
+ * csa2_index_full (logical positions); topk_rows : out int32 [B][k] and
+ * pool_rows : out int32 [B][n_blocks*block], the pool rows of the same
+ * entries (-1 where topk / pool hold -1).  The workspace is
+ * csa2_index_full_workspace(B, max_pages * P, k, block, n_blocks).
+ *
+ * csa2_index_pool_rows -- csa2_index_pool gathering by physical rows:
+ * pool_rows [B][pool_cap] (as csa2_index_full_paged writes them; -1 or a row
+ * outside [0, n_rows) is masked) scored for the ranking, pool [B][pool_cap]
+ * the same entries' logical positions for the output.  topk : out logical
+ * positions, topk_rows : out their pool rows (-1 padded).  No lengths: the
+ * rows carry visibility.  Workspace: csa2_index_pool_workspace.
+ *
+ * csa2_sparse_attn_decode_rows -- csa2_sparse_attn_decode with the selected
+ * entries given as pool rows: rows [B][k] into the main planes of n_rows
+ * entries (-1 or a row outside [0, n_rows) is masked; no lengths).  The
+ * window arguments, outputs, workspace and status codes are those of
+ * csa2_sparse_attn_decode.
+ */
+int csa2_cache_append_paged(const uint16_t* latent, const uint16_t* gate, int32_t B, int32_t m,
+                            const float* gamma, float eps, const float* w_idx, int32_t main_fmt, int32_t rope,
+                            uint8_t* main_codes, uint8_t* main_scales, uint8_t* idx_codes, uint8_t* idx_scales,
+                            int64_t n_rows, const int32_t* block_table, int32_t page_shift, int32_t max_pages,
+                            int32_t* len, void* state, void* stream);
+int csa2_index_full_paged(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t n_rows,
+                          const int32_t* block_table, int32_t page_shift, int32_t max_pages,
+                          const int32_t* len, int32_t B, const uint16_t* q, const float* w, int32_t H,
+                          int32_t k, int32_t block, int32_t n_blocks, int32_t* topk, int32_t* topk_rows,
+                          int32_t* pool, int32_t* pool_rows, int32_t* pool_len, float* scores_opt,
+                          void* ws, size_t ws_bytes, void* stream);
+int csa2_index_pool_rows(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t n_rows, int32_t B,
+                         const int32_t* pool, const int32_t* pool_rows, const int32_t* pool_len,
+                         int32_t pool_cap, const uint16_t* q, const float* w, int32_t H, int32_t k,
+                         int32_t* topk, int32_t* topk_rows, float* pool_scores_opt, void* ws, size_t ws_bytes,
+                         void* stream);
+int csa2_sparse_attn_decode_rows(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                                 const uint8_t* main_scales, int64_t n_rows, int32_t main_fmt,
+                                 const int32_t* rows, int32_t k, int32_t B, const uint8_t* swa_codes,
+                                 const uint8_t* swa_scales, int64_t swa_stride, int32_t swa_cap,
+                                 const int32_t* swa_len, int32_t swa_fmt, float sm_scale, const int64_t* q_pos,
+                                 uint16_t* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

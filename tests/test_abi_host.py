@@ -38,6 +38,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
             "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq",
+            "csa2_cache_append_paged", "csa2_index_full_paged", "csa2_index_pool_rows",
+            "csa2_sparse_attn_decode_rows",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -268,3 +270,53 @@ def test_index_full_mq_validation(lib):
     assert call(6, None) == ERR_NULL
     assert call(6, FAKE_ODD) == ERR_ALIGN
     assert call(17, 64) == ERR_WS
+
+
+def test_paged_validation(lib):
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f = lib.csa2_index_full_paged
+    f.argtypes = [P, P, i64, P, i32, i32, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    # pool of 64 pages of 2^8 entries, 16 pages per sequence
+    base = [FAKE, FAKE, 64 << 8, FAKE, 8, 16, FAKE, 4, FAKE, FAKE, 64, 512, 8, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+            None, FAKE, 1 << 40, None]
+
+    def call(i, v, fn=f, b=base):
+        args = list(b)
+        args[i] = v
+        return fn(*args)
+
+    assert call(4, 5) == ERR_SHAPE            # pages of fewer than 64 entries
+    assert call(4, 21) == ERR_SHAPE
+    assert call(2, (64 << 8) + 3) == ERR_SHAPE  # pool not whole pages
+    assert call(2, 1 << 27) == ERR_SHAPE        # pool beyond 32-bit byte offsets
+    assert call(5, 5000) == ERR_SHAPE           # logical capacity above the limit
+    assert call(3, None) == ERR_NULL            # block table
+    assert call(15, None) == ERR_NULL           # topk rows
+    assert call(17, None) == ERR_NULL           # pool rows with a pool
+    assert call(3, FAKE_ODD) == ERR_ALIGN
+    assert call(21, 64) == ERR_WS
+    assert call(7, 0) == CSA2_OK
+    a = lib.csa2_cache_append_paged
+    a.argtypes = [P, P, i32, i32, P, ctypes.c_float, P, i32, i32, P, P, P, P, i64, P, i32, i32, P, P, P]
+    ab = [FAKE, None, 4, 1, None, 1e-6, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, 64 << 8, FAKE, 8, 16, FAKE, None, None]
+    assert call(15, 3, a, ab) == ERR_SHAPE
+    assert call(14, None, a, ab) == ERR_NULL
+    assert call(3, 2, a, ab) == ERR_NULL        # m = 2 needs gate and state
+    assert call(2, 0, a, ab) == CSA2_OK
+    r = lib.csa2_index_pool_rows
+    r.argtypes = [P, P, i64, i32, P, P, P, i32, P, P, i32, i32, P, P, P, P, ctypes.c_size_t, P]
+    rb = [FAKE, FAKE, 1 << 16, 4, FAKE, FAKE, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, FAKE, None, FAKE, 1 << 40, None]
+    assert call(5, None, r, rb) == ERR_NULL     # pool rows
+    assert call(13, None, r, rb) == ERR_NULL    # topk rows
+    assert call(7, 20000, r, rb) == ERR_SHAPE
+    assert call(2, 0, r, rb) == ERR_SHAPE
+    t = lib.csa2_sparse_attn_decode_rows
+    t.argtypes = [P, i32, P, P, i64, i32, P, i32, i32, P, P, i64, i32, P, i32, ctypes.c_float, P, P, P, P,
+                  ctypes.c_size_t, P]
+    tb = [FAKE, 64, FAKE, FAKE, 1 << 16, 0, FAKE, 512, 16, FAKE, FAKE, 128, 128, FAKE, 1, 0.04, None, FAKE, None,
+          FAKE, 1 << 40, None]
+    assert call(6, None, t, tb) == ERR_NULL     # rows
+    assert call(4, 1 << 27, t, tb) == ERR_SHAPE
+    assert call(14, 3, t, tb) == ERR_UNSUP
+    assert call(10, P(0x1004), t, tb) == ERR_ALIGN  # FP8 window scales
+    assert call(20, 16, t, tb) == ERR_WS
