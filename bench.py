@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--verify-q", type=int, default=0, metavar="Q",
                     help="instead of the step: the Full indexer call for Q queries per sequence (a verify "
                          "block) sharing each cache, against Q single-query calls")
+    ap.add_argument("--paged", type=int, default=0, metavar="SHIFT",
+                    help="run the step on a paged cache: pages of 2^SHIFT entries in a seeded random order, "
+                         "through the paged entry points (Full scoring through the block table, Reindex and "
+                         "attention by pool rows)")
     ap.add_argument("--window", default="tail", choices=["tail", "fp8"],
                     help="window rows: the last 128 entries of the main cache (the configured workload), or "
                          "each layer's own FP8 ring (576 + 8 B records), written once per layer per step")
@@ -345,6 +349,26 @@ def main():
     step = DecodeStep(cache, lengths, k=wl.k, n_blocks=wl.n_blocks, n_reindex=wl.n_reindex,
                       reuse_per_index=wl.reuse_per_index, main_fmt=fmt, swa=rings)
     n_idx = 1 + wl.n_reindex
+    pg = None
+    if args.paged:
+        # the same entries in a pool of pages in a seeded random order (every
+        # sequence's window stays the main-format view of its last 128 entries)
+        shift = args.paged
+        P = 1 << shift
+        mp = (cap + P - 1) // P
+        perm = torch.randperm(B * mp, generator=torch.Generator().manual_seed(wl.seed + 400)).to(torch.int32)
+        table = perm.view(B, mp).to(dev)
+        ppool = K.paged_alloc(B * mp, shift, dev)
+        for key in ("main_codes", "main_scales", "idx_codes", "idx_scales"):
+            src = cache[key].view(B, mp, P, -1)
+            ppool[key].view(B * mp, P, -1)[perm.long()] = src.reshape(B * mp, P, -1)
+        nb8 = max(wl.n_blocks * 8, 1)
+        pg = dict(shift=shift, table=table, pool=ppool,
+                  topk=[torch.empty(B, wl.k, dtype=torch.int32, device=dev) for _ in range(n_idx)],
+                  rows=[torch.empty(B, wl.k, dtype=torch.int32, device=dev) for _ in range(n_idx)],
+                  cand=torch.empty(B, nb8, dtype=torch.int32, device=dev),
+                  cand_rows=torch.empty(B, nb8, dtype=torch.int32, device=dev),
+                  cand_len=torch.empty(B, dtype=torch.int32, device=dev))
     idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
     if args.index_q == "fp4":
         # the indexer queries in MX-FP4 (E2M1 codes, E8M0 per 32 dims), quantised once here
@@ -384,11 +408,22 @@ def main():
 
     def ph_full():
         q, w = idx_qw[0]
+        if pg is not None:
+            K.index_full_paged(pg["pool"], pg["table"], pg["shift"], lengths, q, w, k=wl.k, n_blocks=wl.n_blocks,
+                               out=dict(topk=pg["topk"][0], topk_rows=pg["rows"][0], pool=pg["cand"],
+                                        pool_rows=pg["cand_rows"], pool_len=pg["cand_len"]), _ws=step.ws_full)
+            return
         c = step.cache
         K.index_full(c["idx_codes"], c["idx_scales"], lengths, q, w, k=wl.k, n_blocks=wl.n_blocks,
                      out=dict(topk=step.topk[0], pool=step.pool, pool_len=step.pool_len), _ws=step.ws_full)
 
     def ph_pool():
+        if pg is not None:
+            for i in range(1, n_idx):
+                q, w = idx_qw[i]
+                K.index_pool_rows(pg["pool"], pg["cand"], pg["cand_rows"], pg["cand_len"], q, w, k=wl.k,
+                                  out=dict(topk=pg["topk"][i], topk_rows=pg["rows"][i]), _ws=step.ws_pool)
+            return
         c = step.cache
         for i in range(1, n_idx):
             q, w = idx_qw[i]
@@ -396,6 +431,17 @@ def main():
                          k=wl.k, out=dict(topk=step.topk[i]), _ws=step.ws_pool)
 
     def ph_attn():
+        if pg is not None:
+            s_ = step.swa
+            for j, (_, i) in enumerate(step.schedule()):
+                sw = s_[j] if isinstance(s_, (list, tuple)) else s_
+                rb, sb = (576, 8) if sw.get("fmt", 0) == K.SWA_FP8 else (256, 32)
+                K.sparse_attn_decode_rows(attn_q[j], pg["pool"], pg["rows"][i], fmt,
+                                          swa_codes=sw["codes"].view(-1)[sw["row0"] * rb:],
+                                          swa_scales=sw["scales"].view(-1)[sw["row0"] * sb:], swa_len=sw["length"],
+                                          swa_stride=sw["stride"], swa_cap=128, swa_fmt=sw.get("fmt", 0),
+                                          out=dict(out=step.out[j]), _ws=step.ws_attn)
+            return
         step.run_attention(attn_q)
 
     all_phases = [("write", ph_write), ("index_full", ph_full), ("index_pool", ph_pool), ("attn", ph_attn)]
@@ -416,7 +462,7 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    pool_len = step.pool_len.cpu().tolist()
+    pool_len = (pg["cand_len"] if pg is not None else step.pool_len).cpu().tolist()
     log(f"[bench] warmup done; pool_len={pool_len[0]}")
 
     # The step is launched as one HIP graph (torch.cuda.CUDAGraph): the same
@@ -531,6 +577,7 @@ def main():
         config=dict(workload=wl.name, sequences=B, entries_per_sequence=cap, indexer_heads=wl.H_idx,
                     topk=wl.k, pool_blocks=wl.n_blocks, block=8, attn_heads=64, head_dim=512, window=128,
                     window_rows="per-layer FP8 ring, written each step" if fp8w else "last 128 cache entries",
+                    paged_cache=(f"pages of {1 << args.paged} entries, random order" if args.paged else None),
                     layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
                     main_scale=args.fmt.upper(), index_query=args.index_q, only=args.only,
                     cache_write=f"{w_T} tokens, m={w_m}"),
@@ -539,7 +586,7 @@ def main():
                              note="decode-time append of one token per sequence into the cache; not in the step"),
         kernels=kernels, roofline=roofline,
     )
-    if not args.no_cpu_baseline and args.only is None and not fp8w:
+    if not args.no_cpu_baseline and args.only is None and not fp8w and not args.paged:
         del step, cache
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(wl, fmt, args.cpu_seconds)

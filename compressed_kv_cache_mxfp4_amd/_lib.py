@@ -375,7 +375,8 @@ def sparse_attn_decode_rows(q, pool: dict, rows, main_fmt: int, swa_codes=None, 
     if swa_cap > 0:
         _req(swa_len, "swa_len", torch.int32, dev, (B,))
         rb, sb = (576, 8) if swa_fmt == SWA_FP8 else (256, 32)
-        if swa_codes.numel() < B * swa_stride * rb or swa_scales.numel() < B * swa_stride * sb:
+        need = (B - 1) * swa_stride + swa_cap
+        if swa_codes.numel() < need * rb or swa_scales.numel() < need * sb:
             raise ValueError("window planes smaller than B rows of swa_stride")
     if q_pos is not None:
         _req(q_pos, "q_pos", torch.int64, dev, (B,))

@@ -293,10 +293,33 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
 // threads merge 16 heads and 256 threads 8.  Partials are fp16 of (output / sum) * 2^-e with
 // (max, sum, XCD, e) beside them; a partial written on another XCD turns the
 // output into NaN (its bytes might not be visible in this XCD's L2).
+// Inverse-RoPE factors of one merging thread: its dims 16*d16 .. +15 are
+// pairs 8*(d16-28) .. +7 when d16 >= 28.  They depend on the query position
+// and the dims, not on the head, so a thread that merges several head
+// groups computes them (in fp64) once.
+struct MergeRope {
+  float c[8], s[8];
+};
+
+__device__ __forceinline__ MergeRope merge_rope(int64_t pos, int d16) {
+  MergeRope r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (d16 >= 28) {
+      rope_cos_sin(pos, 8 * (d16 - 28) + i, r.c[i], r.s[i]);
+    } else {
+      r.c[i] = 1.0f;
+      r.s[i] = 0.0f;
+    }
+  }
+  return r;
+}
+
+template <bool ROPE>
 __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const float4* __restrict__ ml,
                                              const uint16_t* __restrict__ part, uint16_t* __restrict__ out,
                                              float* __restrict__ lse, uint32_t my_xcc, int tid,
-                                             const int64_t* __restrict__ q_pos) {
+                                             const MergeRope& rope) {
   // thread: head hh, dims 16*d16 .. +15.  Splits are merged four at a time
   // with a running maximum (one round of loads per four splits).
   const int hh = tid >> 5, d16 = tid & 31;
@@ -351,15 +374,10 @@ __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const 
   }
   float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
   if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
-  if (q_pos && d16 >= 28) {
+  if (ROPE && d16 >= 28) {
     // output inverse RoPE: dims 16*d16 .. +15 are pairs 8*(d16-28) .. +7
-    const int64_t pos = q_pos[b];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float c, sn;
-      rope_cos_sin(pos, 8 * (d16 - 28) + i, c, sn);
-      rope_pair<true>(acc[2 * i], acc[2 * i + 1], c, sn);
-    }
+    for (int i = 0; i < 8; ++i) rope_pair<true>(acc[2 * i], acc[2 * i + 1], rope.c[i], rope.s[i]);
   }
   uint32_t o8[8];
 #pragma unroll
@@ -636,7 +654,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   __syncthreads();
   if (!sm.last) return;  // workgroup-uniform
   if (tid == 0) cnt[gi] = 0u;  // ready for the next call
-  if (tid < 16 * 32) merge_splits(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid, q_pos);
+  if (tid < 16 * 32) {
+    if (q_pos)
+      merge_splits<true>(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid, merge_rope(q_pos[b], tid & 31));
+    else
+      merge_splits<false>(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid, MergeRope{});
+  }
 }
 
 
@@ -1130,7 +1153,13 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   __syncthreads();
   if (!sm.last) return;  // workgroup-uniform
   if (tid == 0) cnt[b] = 0u;  // ready for the next call
-  for (int h0 = 0; h0 < H; h0 += 16) merge_splits(b, h0, H, S, ml, part, out, lse, my_xcc, tid, q_pos);  // 16 heads per round
+  // 16 heads per round
+  if (q_pos) {
+    const MergeRope rope = merge_rope(q_pos[b], tid & 31);
+    for (int h0 = 0; h0 < H; h0 += 16) merge_splits<true>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, rope);
+  } else {
+    for (int h0 = 0; h0 < H; h0 += 16) merge_splits<false>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, MergeRope{});
+  }
 }
 
 // Opt a kernel in to its dynamic LDS size once (thread-safe static init;
