@@ -76,15 +76,22 @@ __device__ __forceinline__ void fp4x8_to_f32(uint32_t codes, float out[8]) {
 }
 
 // ------------------------------------------------------------ compressed RoPE
-// [ggaaooppeenngg.github.io, "架构解析：KV Cache 压缩的极限在哪里", 3.2 and 7]:
-// base 160000; 64 of the 512 dims carry position.  These are dims 448..511
-// as 32 adjacent pairs; pair j turns by pos * 160000^(-2j/64).  The angle is
-// formed and reduced in fp64 (positions reach millions, where an fp32 angle
-// is off by tenths of a radian); the rotation itself is fp32.
+// [ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", 3.2 and 7]: base
+// 160000; 64 of the 512 dims carry position.  These are dims 448..511 as 32
+// adjacent pairs; pair j turns by pos * 160000^(-2j/64).  The angle is kept
+// in fp64 (positions reach millions, where an fp32 angle is off by tenths of
+// a radian); the rotation itself is fp32.
+//
+// cos and sin of the compressed-RoPE angle of pair j at position pos:
+// pos * 160000^(-2j/64) radians.  The angle is carried in half-turns,
+// pos * theta_j / pi with theta_j / pi = 2^(-j log2(160000)/32 - log2(pi)) in
+// fp64 (within 14 ulp of exact), and sincospi drops the whole turns exactly,
+// so positions in the billions keep ~1e-6 rad; a general fp64 pow and a
+// large-argument sincos cost several times more.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, float& c, float& s) {
-  const double ang = (double)pos * pow(160000.0, -(double)(2 * j) / 64.0);
+  const double ht = (double)pos * exp2(-(double)j * (log2(160000.0) / 32.0) - log2(3.14159265358979323846));
   double sd, cd;
-  sincos(ang, &sd, &cd);
+  sincospi(ht, &sd, &cd);
   c = (float)cd;
   s = (float)sd;
 }
