@@ -694,6 +694,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
 //    same row order.
 //  * The running maximum moves only when a chunk exceeds it by more than
 //    2^8 (P <= 256 in between), so the accumulators are rarely rescaled.
+//  * FP8 window records (576 data + 8 scale bytes) are staged 16 rows per
+//    chunk, so that 16 staging lanes of 36 bytes cover a record and every
+//    lane keeps its load slot; the lane's scale byte arrives through the
+//    index-entry slot, which a window chunk does not otherwise use.
 constexpr int kTRows = 32;     // rows per chunk
 constexpr int kTRowB = 1024;   // staged row: 512 bf16
 constexpr int kTPLd = 40;      // P row stride in bf16 (32 slots + pad)

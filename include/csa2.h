@@ -362,13 +362,13 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  *              initial contents.  Calls sharing a workspace must be ordered
  *              on one stream; concurrent calls on one workspace race.
  *              B*H/16 must not exceed CSA2_ATTN_MAX_GROUPS.
- * One kernel on `stream`.  Below 48 sequences (or H < 64, or FP8 window
- * records, which only this kernel reads) a workgroup attends
+ * One kernel on `stream`.  Below 48 sequences (or H < 64) a workgroup attends
  * one chunk of 128 or 160 row slots for 16 heads and leaves its partial
  * (unnormalised output, max, sum) in the workspace; the last chunk of each
  * (sequence, head group) to finish merges all of them exactly.  From 48
  * sequences with H = 64, a workgroup takes all heads of a sequence over a
- * range of 32-row chunks with an online softmax (one range per sequence from
+ * range of 32-row chunks (FP8 window records: 16-row chunks) with an online
+ * softmax (one range per sequence from
  * 256 sequences), and the last range of a sequence merges the others.  The chunks of one group are placed on one XCD
  * (workgroup ids congruent mod 8), so the partials meet in that XCD's L2; a
  * merge that finds a chunk from another XCD writes NaN rather than a wrong
