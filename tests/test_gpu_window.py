@@ -172,18 +172,20 @@ def _fp8_windows(B, W, seed, rope):
     r = oracle.window_write(x, pos0, W, rope=rope, data=data, scales=sc)
     swa_len = r["swa_len"].copy()
     if B > 1:
-        swa_len[1] = 37
+        swa_len[1] = min(37, W - 1)
     if B > 2:
         swa_len[2] = 0
     return data, sc, swa_len, pos0 + n
 
 
-@pytest.mark.parametrize("B,k,fmt,rope", [(1, 512, 0, False), (3, 500, 1, True), (16, 512, 0, True),
-                                          (64, 512, 1, False), (64, 500, 0, True), (48, 40, 1, True),
-                                          (256, 512, 0, True), (256, 480, 1, False)])
-def test_attention_fp8_window_parity(B, k, fmt, rope):
-    say(f"attention over FP8 window B={B} k={k} fmt={fmt} rope={rope}")
-    cap, W = 1500, 128
+@pytest.mark.parametrize("B,k,fmt,rope,W", [(1, 512, 0, False, 128), (3, 500, 1, True, 128),
+                                            (16, 512, 0, True, 128), (64, 512, 1, False, 128),
+                                            (64, 500, 0, True, 128), (48, 40, 1, True, 128),
+                                            (256, 512, 0, True, 128), (256, 480, 1, False, 128),
+                                            (3, 512, 0, True, 37), (64, 500, 1, False, 37)])
+def test_attention_fp8_window_parity(B, k, fmt, rope, W):
+    say(f"attention over FP8 window B={B} k={k} fmt={fmt} rope={rope} W={W}")
+    cap = 1500
     c, s, rc, rs = _make_cache(B, cap, fmt, 40 + B + k)
     g = np.random.default_rng(B + k)
     topk = np.stack([np.sort(g.choice(cap, k, replace=False)) for _ in range(B)]).astype(np.int32)
