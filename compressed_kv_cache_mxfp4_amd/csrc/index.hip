@@ -746,7 +746,8 @@ __device__ __forceinline__ int group_items(const int32_t* grp, int ng, int n_ite
   return nc;
 }
 
-// Full-mode selection for one sequence (grid = B):
+// Full-mode selection for one sequence (grid = B; with a pool 2B, one
+// workgroup running 1 and one running 2-3, side by side):
 //  1. block top-n_blocks -> pool (ascending positions), with the sampled
 //     prefilter (2048 of 16,384 blocks at 128K);
 //  2. block top-k -> candidate blocks, among the pool blocks when
@@ -758,12 +759,27 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
     const float* __restrict__ scores, int64_t sstride, const float* __restrict__ bmax,
     int64_t bstride, const int32_t* __restrict__ len, int64_t cap, int k, int n_blocks,
     int32_t* __restrict__ topk, int32_t* __restrict__ pool, int32_t* __restrict__ pool_len, int qps,
-    PageMap pm, int32_t* __restrict__ topk_rows, int32_t* __restrict__ pool_rows) {
+    PageMap pm, int32_t* __restrict__ topk_rows, int32_t* __restrict__ pool_rows, int B, int split) {
   __shared__ SelScratch sh;
   __shared__ int32_t blk[CSA2_POOL_BLOCKS];
   __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
   __shared__ int32_t cblk[CSA2_MAX_TOPK];
-  const int b = blockIdx.x;
+  // split: two workgroups per sequence, one per selection (role 0 the pool,
+  // role 1 the top-k, which then takes its blocks from all blocks -- the
+  // same set, the pool being the top blocks by the same key), so the two
+  // run side by side.  Both get ids congruent to b mod 8 when B is a
+  // multiple of 8: the XCD whose L2 holds the sequence's scores.
+  int b, role;
+  if (!split) {
+    b = blockIdx.x;
+    role = -1;  // both
+  } else if ((B & 7) == 0) {
+    b = (int)(blockIdx.x & 7) + 8 * (int)(blockIdx.x >> 4);
+    role = (blockIdx.x >> 3) & 1;
+  } else {
+    b = blockIdx.x >> 1;
+    role = blockIdx.x & 1;
+  }
   KeysFromArray bsrc{bmax + (int64_t)b * bstride};
   KeyRegs<EPT_B> kb;
   if constexpr (EPT_B > 0) load_raw<NT, EPT_B>(kb, bsrc.p, (int)bstride);  // overlaps the length load
@@ -776,7 +792,7 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   int32_t* tkr = topk_rows ? topk_rows + (int64_t)b * k : nullptr;
   if constexpr (EPT_B > 0) finish_keys<NT, EPT_B>(kb, nb);
   int ncb;
-  if (n_blocks > 0) {
+  if (n_blocks > 0 && role != 1) {
     const int nsel = select_core<NT, EPT_B, true>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r, int j) {
       blk[r] = i;
       if constexpr (EPT_B > 0) blkkey[r] = kb.r[j]; else blkkey[r] = bsrc.key(i);
@@ -810,7 +826,8 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
     }
     if (threadIdx.x == 0) pool_len[b] = pl;
   }
-  if (n_blocks >= k) {
+  if (role == 0) return;  // workgroup-uniform: the pool was this workgroup's part
+  if (n_blocks >= k && role == -1) {
     // top-k among the selected pool blocks (keys kept in LDS, ascending blocks)
     const int nsel = min(n_blocks, nb);
     KeysFromLds csrc{blkkey};
@@ -954,10 +971,13 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                         q4s, w, H, scores, cap, bmax, nbk, qps, pm, pm.table ? 0 : cap);
   if (hipGetLastError() != hipSuccess) return -1;
   const bool kbig = k > 512;
+  // the pool and the top-k as two workgroups per sequence when there is a pool
+  const bool split = n_blocks > 0;
   // keys per thread: all blocks (EB), the pool blocks (2), candidate positions (EP)
 #define CSA2_SELFULL(EB, EP) \
-  select_full_kernel<1024, EB, 2, EP><<<B, 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, n_blocks, topk, pool, \
-                                                         pool_len, qps, pm, topk_rows, pool_rows)
+  select_full_kernel<1024, EB, 2, EP><<<B * (split ? 2 : 1), 1024, 0, st>>>(scores, cap, bmax, nbk, len, cap, k, \
+                                                         n_blocks, topk, pool, pool_len, qps, pm, topk_rows, \
+                                                         pool_rows, B, split ? 1 : 0)
   if (nbk <= 4 * 1024) {
     if (kbig) CSA2_SELFULL(4, 16); else CSA2_SELFULL(4, 4);
   } else if (nbk <= 16 * 1024) {
