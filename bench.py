@@ -160,7 +160,7 @@ def attn_sweep(batches, fmt_name, steps, window="tail"):
                           entries_per_sequence=cap, peak_GBs=HBM_PEAK_GBS, sweep=rows)), flush=True)
 
 
-def verify_bench(wl_name, Q, steps, warmup):
+def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
     """Full indexer for Q queries per sequence (a speculative verify block): one
     csa2_index_full_mq call against Q csa2_index_full calls, same caches and queries."""
     import torch
@@ -178,6 +178,12 @@ def verify_bench(wl_name, Q, steps, warmup):
     w = torch.stack([syn.index_weights(wl, i, dev) for i in range(Q)], 1).contiguous()
     qs = [q[:, i].contiguous() for i in range(Q)]
     ws_ = [w[:, i].contiguous() for i in range(Q)]
+    if index_q == "fp4":
+        # FP4 queries (E2M1 + E8M0 per 32 dims), quantised once here
+        H = wl.H_idx
+        qc, qsc = K.quantize_fp4(q.view(torch.bfloat16).float().reshape(-1, 128).contiguous(), 32, K.E8M0)
+        q = (qc.view(B, Q, H, 64), qsc.view(B, Q, H, 4))
+        qs = [(q[0][:, i].contiguous(), q[1][:, i].contiguous()) for i in range(Q)]
     L = K.lib()
     ws_mq = torch.empty(L.csa2_index_full_mq_workspace(B, Q, cap, wl.k, 8, wl.n_blocks), dtype=torch.uint8, device=dev)
     ws_1 = torch.empty(L.csa2_index_full_workspace(B, cap, wl.k, 8, wl.n_blocks), dtype=torch.uint8, device=dev)
@@ -214,11 +220,12 @@ def verify_bench(wl_name, Q, steps, warmup):
     for i in range(Q):
         assert torch.equal(outs_mq["topk"][:, i], outs_1[i]["topk"]), "multi-query top-k differs"
     cache_bytes = B * cap * 68
-    per_q = B * (wl.H_idx * 256 + wl.H_idx * 4 + 4) + B * (wl.k * 4 + wl.n_blocks * 8 * 4 + 4)
+    per_q = B * (wl.H_idx * (68 if index_q == "fp4" else 256) + wl.H_idx * 4 + 4) + B * (wl.k * 4 + wl.n_blocks * 8 * 4 + 4)
     nbytes = cache_bytes + Q * per_q
     us = res["multi_query"]
     print(json.dumps(dict(metric="Full indexer call for a verify block (Q queries per sequence)", unit="us per call",
                           workload=wl.name, sequences=B, entries_per_sequence=cap, queries_per_sequence=Q,
+                          index_query=index_q,
                           indexer_heads=wl.H_idx, topk=wl.k, pool_blocks=wl.n_blocks,
                           us_multi_query=round(us, 2), us_separate_calls=round(res["separate"], 2),
                           positions_scored_per_s=Q * B * cap / (us * 1e-6),
@@ -305,7 +312,7 @@ def main():
         copy_calibration(args.copy_calib_mb)
         return
     if args.verify_q:
-        verify_bench(args.workload, args.verify_q, args.steps, args.warmup)
+        verify_bench(args.workload, args.verify_q, args.steps, args.warmup, args.index_q)
         return
     if args.attn_sweep:
         attn_sweep([int(x) for x in args.attn_sweep.split(",")], args.fmt, args.steps, args.window)

@@ -55,6 +55,8 @@ def lib():
     L.csa2_index_full_mq_workspace.restype = sz
     L.csa2_index_full_mq_workspace.argtypes = [i32, i32, i64, i32, i32, i32]
     L.csa2_index_full_mq.argtypes = [P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.csa2_index_full_mq_fp4q.argtypes = [P, P, i64, P, i32, i32, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz,
+                                          P]
     L.csa2_index_full_fp4q.argtypes = [P, P, i64, P, i32, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     L.csa2_index_pool_fp4q.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, P, i32, i32, P, P, P, sz, P]
     L.csa2_attn_workspace.restype = sz
@@ -463,7 +465,8 @@ def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int
 def index_full_mq(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int = 2048,
                   block: int = 8, return_scores: bool = False, out=None, _ws=None):
     """Full-mode indexer for Q queries per sequence sharing the sequence's cache
-    (e.g. a verify block).  q bf16/int16 [B][Q][H][128], w fp32 [B][Q][H],
+    (e.g. a verify block).  q bf16/int16 [B][Q][H][128] -- or FP4 queries
+    (codes u8 [B][Q][H][64], E8M0 scales u8 [B][Q][H][4]) -- w fp32 [B][Q][H],
     lengths int32 [B].  Returns (topk [B][Q][k], pool [B][Q][n_blocks*block],
     pool_len [B][Q] [, scores fp32 [B][Q][cap]])."""
     _req(idx_codes, "idx_codes", torch.uint8)
@@ -472,9 +475,17 @@ def index_full_mq(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: 
     _req(idx_codes, "idx_codes", torch.uint8, dev, (B, cap, 64))
     _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
     _req(lengths, "lengths", torch.int32, dev, (B,))
-    q = _bits16(q)
-    Q, H = q.shape[1], q.shape[2]
-    _req(q, "q", torch.int16, dev, (B, Q, H, 128))
+    if isinstance(q, (tuple, list)):
+        qc, qs = q
+        Q, H = qc.shape[1], qc.shape[2]
+        _req(qc, "q codes", torch.uint8, dev, (B, Q, H, 64))
+        _req(qs, "q scales", torch.uint8, dev, (B, Q, H, 4))
+        q = None
+    else:
+        q = _bits16(q)
+        Q, H = q.shape[1], q.shape[2]
+        _req(q, "q", torch.int16, dev, (B, Q, H, 128))
+        qc = qs = None
     _req(w, "w", torch.float32, dev, (B, Q, H))
     out = out or {}
     topk = out.get("topk")
@@ -491,9 +502,15 @@ def index_full_mq(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: 
         scores = torch.empty(B, Q, cap, dtype=torch.float32, device=dev)
     wsb = lib().csa2_index_full_mq_workspace(B, Q, cap, k, block, n_blocks)
     ws = _ws if _ws is not None else workspace(wsb, dev)
-    _check(lib().csa2_index_full_mq(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q, _ptr(q), _ptr(w),
-                                    H, k, block, n_blocks, _ptr(topk), _ptr(pool), _ptr(pool_len), _ptr(scores),
-                                    _ptr(ws), ws.numel(), _stream(dev)), "csa2_index_full_mq")
+    if qc is None:
+        _check(lib().csa2_index_full_mq(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q, _ptr(q),
+                                        _ptr(w), H, k, block, n_blocks, _ptr(topk), _ptr(pool), _ptr(pool_len),
+                                        _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)), "csa2_index_full_mq")
+    else:
+        _check(lib().csa2_index_full_mq_fp4q(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q, _ptr(qc),
+                                             _ptr(qs), _ptr(w), H, k, block, n_blocks, _ptr(topk), _ptr(pool),
+                                             _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
+               "csa2_index_full_mq_fp4q")
     pool = pool[:, :, : n_blocks * block]
     if return_scores:
         return topk, pool, pool_len, scores

@@ -160,6 +160,29 @@ int csa2_index_full_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int6
                                           as_stream(stream), Q));
 }
 
+int csa2_index_full_mq_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int32_t B, int32_t Q, const uint8_t* q_codes,
+                            const uint8_t* q_scales, const float* w, int32_t H, int32_t k, int32_t block,
+                            int32_t n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len, float* scores_opt,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (Q < 1 || Q > CSA2_MAX_QUERIES_PER_SEQ) return CSA2_ERR_SHAPE;
+  if (B < 0 || (int64_t)B * Q > INT32_MAX || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+  if (n_blocks < 0 || n_blocks > CSA2_POOL_BLOCKS || (int64_t)n_blocks * block > CSA2_MAX_POOL)
+    return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !len || !q_codes || !q_scales || !w || !topk) return CSA2_ERR_NULL;
+  if (n_blocks > 0 && (!pool || !pool_len)) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q_codes)) return CSA2_ERR_ALIGN;
+  if (cap == 0) return CSA2_ERR_SHAPE;
+  if (!ws || ws_bytes < csa2_index_full_mq_workspace(B, Q, cap, k, block, n_blocks)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_full(idx_codes, idx_scales, cap, len, B * Q, nullptr, q_codes, q_scales, w,
+                                          H, k, block, n_blocks, topk, pool, pool_len, scores_opt, ws,
+                                          as_stream(stream), Q));
+}
+
 int csa2_index_full_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
                          const int32_t* len, int32_t B, const uint8_t* q_codes,
                          const uint8_t* q_scales, const float* w, int32_t H, int32_t k,

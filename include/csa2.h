@@ -295,6 +295,13 @@ int csa2_index_full_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int6
                        int32_t H, int32_t k, int32_t block, int32_t n_blocks, int32_t* topk,
                        int32_t* pool, int32_t* pool_len, float* scores_opt, void* ws, size_t ws_bytes,
                        void* stream);
+/* The same with FP4 queries (csa2_index_full_fp4q's format):
+ * q_codes u8 [B][Q][H][64] (16-byte aligned), q_scales u8 [B][Q][H][4]. */
+int csa2_index_full_mq_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int32_t B, int32_t Q, const uint8_t* q_codes,
+                            const uint8_t* q_scales, const float* w, int32_t H, int32_t k, int32_t block,
+                            int32_t n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len, float* scores_opt,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_full_fp4q, csa2_index_pool_fp4q -- the two indexer calls with an

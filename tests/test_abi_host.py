@@ -37,7 +37,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
-            "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq",
+            "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq", "csa2_index_full_mq_fp4q",
             "csa2_cache_append_paged", "csa2_index_full_paged", "csa2_index_pool_rows",
             "csa2_sparse_attn_decode_rows",
             "csa2_quantize_fp4"} <= set(names)

@@ -342,3 +342,31 @@ def test_index_full_mq_equals_one_query_calls(B, Q, H, k, nb):
         certified += certify_topk(topk[b, i], rt, rs, k)
         assert pool_len[b, i] == rpl
     say(f"  certified near-ties: {certified}")
+
+
+
+@pytest.mark.parametrize("B,Q,H", [(8, 5, 64), (3, 2, 16)])
+def test_index_full_mq_fp4_query_equals_one_query_calls(B, Q, H):
+    # FP4 queries (E2M1 + E8M0 per 32 dims): each query row of the
+    # multi-query call is bit-identical to the single-query FP4 call
+    say(f"index_full_mq FP4 query B={B} Q={Q} H={H}")
+    cap, k, nb = 5000, 512, 64
+    wl = syn.small("mq4", 80 + B + Q, B=B, cap=cap, H_idx=H, k=k, n_blocks=nb)
+    cache = build_gpu_cache(wl, 0)
+    lens = [cap, 4093, 777, 64, 0, 3000, 5000, 1][:B]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qb = torch.stack([syn.index_query(wl, i, DEV) for i in range(Q)], 1).contiguous()
+    qc, qs = K.quantize_fp4(qb.view(torch.bfloat16).float().reshape(-1, 128).contiguous(), 32, K.E8M0)
+    qc, qs = qc.view(B, Q, H, 64), qs.view(B, Q, H, 4)
+    w = torch.stack([syn.index_weights(wl, i, DEV) for i in range(Q)], 1).contiguous()
+    topk, pool, pool_len, scores = K.index_full_mq(cache["idx_codes"], cache["idx_scales"], lt, (qc, qs), w, k=k,
+                                                   n_blocks=nb, return_scores=True)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        t1, p1, pl1, s1 = K.index_full(cache["idx_codes"], cache["idx_scales"], lt,
+                                       (qc[:, i].contiguous(), qs[:, i].contiguous()), w[:, i].contiguous(), k=k,
+                                       n_blocks=nb, return_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(topk[:, i], t1) and torch.equal(pool[:, i], p1) and torch.equal(pool_len[:, i], pl1)
+        for b, L in enumerate(lens):
+            assert torch.equal(scores[b, i, :L].view(torch.int32), s1[b, :L].view(torch.int32))
