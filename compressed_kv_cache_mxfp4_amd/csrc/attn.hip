@@ -1221,10 +1221,13 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   const int64_t HG = H / 16;
   const int64_t groups = (int64_t)B * HG;
   if (groups > kMaxAttnGroups) return -1;
-  // Chunk shape: 8 waves (128 rows, two workgroups per CU) or 10 waves (160
-  // rows, one per CU); take the smaller row load of the busiest CU.
-  const int64_t wg8 = groups * ((nslots + 127) / 128), wg10 = groups * ((nslots + 159) / 160);
-  const bool ten = ((wg10 + 255) / 256) * 160 <= ((wg8 + 255) / 256) * 128;
+  // Chunk shape: 10 waves (160 rows, one workgroup per CU) when those
+  // workgroups fit the 256 CUs in one round, else 8 waves (128 rows, two
+  // workgroups resident per CU, each hiding the other's latencies).
+  // Measured: 10 waves win at 16 sequences (12.6 against 15.9 us), 8 waves
+  // from 28 to 44 (e.g. 25.7 against 31.3 us at 40).
+  const int64_t wg10 = groups * ((nslots + 159) / 160);
+  const bool ten = wg10 <= 256;
   const int S = ten ? (nslots + 159) / 160 : (nslots + 127) / 128;
   const AttnWs l = attn_ws_layout(B, H, k, swa_cap);
   char* wsb = reinterpret_cast<char*>(ws);

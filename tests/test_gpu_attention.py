@@ -235,10 +235,14 @@ def _big_batch_case(B, cap, k, W, fmt, seed, sample, rope=False):
 @pytest.mark.parametrize("B,k,W,fmt,rope", [(48, 512, 128, 0, False), (64, 512, 128, 1, False),
                                             (128, 600, 100, 0, False), (256, 77, 0, 1, False),
                                             (256, 512, 128, 0, False), (64, 512, 128, 0, True),
-                                            (256, 512, 128, 1, True)])
+                                            (256, 512, 128, 1, True),
+                                            # 8-wave split kernel (below 48 sequences, past one round of 10-wave)
+                                            (40, 512, 128, 0, True), (28, 300, 128, 1, False)])
 def test_attention_large_batch(B, k, W, fmt, rope):
     """Batches that take the all-heads throughput kernel: 5, 4, 2 and 1 splits
     per sequence (ragged chunk ranges, k not a multiple of the 32-row chunk),
+    and, below 48 sequences past one round of 10-wave workgroups, the 8-wave
+    split kernel;
     both scale formats; masked, duplicate, out-of-range and empty selections,
     short and missing windows.  Repeated calls on one workspace give identical
     bits and leave the completion counters at zero."""

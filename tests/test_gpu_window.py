@@ -182,7 +182,8 @@ def _fp8_windows(B, W, seed, rope):
                                             (16, 512, 0, True, 128), (64, 512, 1, False, 128),
                                             (64, 500, 0, True, 128), (48, 40, 1, True, 128),
                                             (256, 512, 0, True, 128), (256, 480, 1, False, 128),
-                                            (3, 512, 0, True, 37), (64, 500, 1, False, 37)])
+                                            (3, 512, 0, True, 37), (64, 500, 1, False, 37),
+                                            (40, 500, 0, True, 128)])
 def test_attention_fp8_window_parity(B, k, fmt, rope, W):
     say(f"attention over FP8 window B={B} k={k} fmt={fmt} rope={rope} W={W}")
     cap = 1500
