@@ -1221,13 +1221,17 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   const int64_t HG = H / 16;
   const int64_t groups = (int64_t)B * HG;
   if (groups > kMaxAttnGroups) return -1;
-  // Chunk shape: 10 waves (160 rows, one workgroup per CU) when those
-  // workgroups fit the 256 CUs in one round, else 8 waves (128 rows, two
-  // workgroups resident per CU, each hiding the other's latencies).
-  // Measured: 10 waves win at 16 sequences (12.6 against 15.9 us), 8 waves
-  // from 28 to 44 (e.g. 25.7 against 31.3 us at 40).
-  const int64_t wg10 = groups * ((nslots + 159) / 160);
-  const bool ten = wg10 <= 256;
+  // Chunk shape.  A placement unit (a sequence from 8 sequences, else a
+  // (sequence, head group)) runs on one XCD of 32 CUs, so what matters is the
+  // busiest XCD's workgroup count: 8 waves (128 rows) when it fits the XCD
+  // in one round; else 10 waves (160 rows, one workgroup per CU) when those
+  // fit; else 8 waves again, two workgroups resident per CU, each hiding the
+  // other's latencies.  Measured: 10 waves win at 12 and 16 sequences (12.6
+  // against 15.9 us at 16), 8 waves below (10.1 against 10.6 us at 1) and
+  // from 20 to 44 (25.7 against 31.3 us at 40).
+  const int64_t xunits = B >= 8 ? ((int64_t)B + 7) / 8 * HG : ((int64_t)B * HG + 7) / 8;
+  const int64_t x8 = xunits * ((nslots + 127) / 128), x10 = xunits * ((nslots + 159) / 160);
+  const bool ten = x8 > 32 && x10 <= 32;
   const int S = ten ? (nslots + 159) / 160 : (nslots + 127) / 128;
   const AttnWs l = attn_ws_layout(B, H, k, swa_cap);
   char* wsb = reinterpret_cast<char*>(ws);
