@@ -14,6 +14,32 @@ inline int launched(int rc) { return rc == 0 ? CSA2_OK : CSA2_ERR_HIP; }
 inline bool valid_fmt(int f) { return f == CSA2_SCALE_E8M0 || f == CSA2_SCALE_E4M3; }
 inline bool valid_index_heads(int H) { return H == 8 || H == 16 || H == 32 || H == 64; }
 
+// Argument checks shared by the attention entry points (CSA2_OK: launch).
+int check_attn(const uint16_t* q, int32_t H, const uint8_t* main_codes, const uint8_t* main_scales,
+               int64_t n_rows, int64_t max_rows, int32_t main_fmt, bool need_len, const int32_t* len,
+               const int32_t* sel, int32_t k, int32_t B, const uint8_t* swa_codes, const uint8_t* swa_scales,
+               int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len, int32_t swa_fmt, float sm_scale,
+               const int64_t* q_pos, const uint16_t* out) {
+  if (B < 0 || n_rows < 0 || n_rows > max_rows) return CSA2_ERR_SHAPE;
+  if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
+  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
+  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
+  if (swa_fmt != CSA2_SWA_MAIN && swa_fmt != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
+  if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!q || !out) return CSA2_ERR_NULL;
+  if (k > 0 && (!main_codes || !main_scales || (need_len && !len) || !sel)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
+  if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
+      (reinterpret_cast<uintptr_t>(q_pos) & 7u) ||
+      (swa_fmt == CSA2_SWA_FP8 && (reinterpret_cast<uintptr_t>(swa_scales) & 7u)))
+    return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,23 +290,9 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
                             int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
                             float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
-  if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
-  if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
-  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
-  if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
-  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
-  if (swa_fmt != CSA2_SWA_MAIN && swa_fmt != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
-  if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
-  if (B == 0) return CSA2_OK;
-  if (!q || !out) return CSA2_ERR_NULL;
-  if (k > 0 && (!main_codes || !main_scales || !len || !topk)) return CSA2_ERR_NULL;
-  if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
-  if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
-  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
-      (reinterpret_cast<uintptr_t>(q_pos) & 7u) ||
-      (swa_fmt == CSA2_SWA_FP8 && (reinterpret_cast<uintptr_t>(swa_scales) & 7u)))
-    return CSA2_ERR_ALIGN;
+  const int rc = check_attn(q, H, main_codes, main_scales, cap, CSA2_MAX_CACHE_ROWS, main_fmt, true, len, topk, k,
+                            B, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale, q_pos, out);
+  if (rc != CSA2_OK || B == 0) return rc;
   if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
   return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
                                            k, B, swa_codes, swa_scales, swa_stride, swa_cap,
@@ -383,23 +395,10 @@ int csa2_sparse_attn_decode_rows(const uint16_t* q, int32_t H, const uint8_t* ma
                                  const uint8_t* swa_scales, int64_t swa_stride, int32_t swa_cap,
                                  const int32_t* swa_len, int32_t swa_fmt, float sm_scale, const int64_t* q_pos,
                                  uint16_t* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
-  if (B < 0 || n_rows < 0 || n_rows > CSA2_MAX_POOL_ROWS) return CSA2_ERR_SHAPE;
-  if (k < 0 || k > CSA2_MAX_TOPK || swa_cap < 0 || swa_cap > CSA2_SWA) return CSA2_ERR_SHAPE;
-  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
-  if ((int64_t)B * (H / 16) > CSA2_ATTN_MAX_GROUPS) return CSA2_ERR_SHAPE;
-  if (!valid_fmt(main_fmt)) return CSA2_ERR_UNSUPPORTED;
-  if (swa_fmt != CSA2_SWA_MAIN && swa_fmt != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
-  if (k + swa_cap == 0) return CSA2_ERR_SHAPE;
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return CSA2_ERR_SHAPE;
-  if (B == 0) return CSA2_OK;
-  if (!q || !out) return CSA2_ERR_NULL;
-  if (k > 0 && (!main_codes || !main_scales || !rows)) return CSA2_ERR_NULL;
-  if (swa_cap > 0 && (!swa_codes || !swa_scales || !swa_len)) return CSA2_ERR_NULL;
-  if (swa_cap > 0 && swa_stride < swa_cap) return CSA2_ERR_SHAPE;
-  if (!aligned16(q) || (main_codes && !aligned16(main_codes)) || (swa_codes && !aligned16(swa_codes)) ||
-      (reinterpret_cast<uintptr_t>(q_pos) & 7u) ||
-      (swa_fmt == CSA2_SWA_FP8 && (reinterpret_cast<uintptr_t>(swa_scales) & 7u)))
-    return CSA2_ERR_ALIGN;
+  const int rc = check_attn(q, H, main_codes, main_scales, n_rows, CSA2_MAX_POOL_ROWS, main_fmt, false, nullptr,
+                            rows, k, B, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale,
+                            q_pos, out);
+  if (rc != CSA2_OK || B == 0) return rc;
   if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
   return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, n_rows, main_fmt, nullptr, rows, k, B,
                                            swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale,

@@ -51,6 +51,39 @@ constexpr int kMaxAttnGroups = 65536;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
+// Arrival of a workgroup at its group's completion counter, after it has
+// stored its partial; true in every thread of the workgroup that arrives last
+// (n arrivals per group), which then reads the others' partials.  Why a
+// relaxed counter suffices on gfx950, without agent-scope fences:
+//  * the grids give every workgroup of a group an id congruent mod 8, and
+//    gfx950 dispatches workgroup i of a launch to XCD i mod 8, so a group's
+//    writers and its merger share one L2 (each partial records the XCD its
+//    writer ran on, and the merge turns its output into NaN if any differs
+//    from its own -- never observed);
+//  * the vector L1 is write-through, and each wave waits for its stores to be
+//    acknowledged (s_waitcnt 0) before the barrier that precedes the counter
+//    update, so every partial is in that L2 before the counter moves;
+//  * the merger's L1 holds no stale copy: no other workgroup reads a group's
+//    partials, they occupy cache lines of their own (1 KB rows and 16-B
+//    records in runs of whole 256-B multiples), and the L1 is invalidated at
+//    kernel start.
+// The agent-scope release/acquire pair the HIP memory model asks for when
+// writers may sit on other XCDs (an L2 write-back per arriving workgroup and
+// an L2 invalidate per merge) took the decode call at batch 16 from 12.2 to
+// 18.5 us.  The last arrival resets the counter, so it is zero again when the
+// kernel ends.
+__device__ __forceinline__ bool arrive_last(uint32_t* c, uint32_t n, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == n - 1u;
+    if (old == n - 1u) *c = 0u;  // ready for the next call
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // WAVES waves take 16 rows each: a chunk of 16*WAVES row slots.  With more
 // than 8 waves one workgroup fills a CU, and the query tile gets a region of
 // its own so that each wave can stage its rows as soon as its logits are
@@ -642,18 +675,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     }
   }
 
-  // ---- the last chunk of the group to finish merges all S partials.  The
-  // stores above are complete in this XCD's L2 before the counter moves, and
-  // every chunk of the group ran on this XCD (checked below).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt + gi, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = old == (uint32_t)(S - 1);
-  }
-  __syncthreads();
-  if (!sm.last) return;  // workgroup-uniform
-  if (tid == 0) cnt[gi] = 0u;  // ready for the next call
+  // ---- the last chunk of the group to finish merges all S partials
+  if (!arrive_last(cnt + gi, (uint32_t)S, &sm.last)) return;  // workgroup-uniform
   if (tid < 16 * 32) {
     if (q_pos)
       merge_splits<true>(b, 16 * hg, H, S, ml, part, out, lse, my_xcc, tid, merge_rope(q_pos[b], tid & 31));
@@ -1148,15 +1171,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   }
   if (S == 1) return;  // uniform
   // ---- the last split of the sequence to finish merges all S partials
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = old == (uint32_t)(S - 1);
-  }
-  __syncthreads();
-  if (!sm.last) return;  // workgroup-uniform
-  if (tid == 0) cnt[b] = 0u;  // ready for the next call
+  if (!arrive_last(cnt + b, (uint32_t)S, &sm.last)) return;  // workgroup-uniform
   // 16 heads per round
   if (q_pos) {
     const MergeRope rope = merge_rope(q_pos[b], tid & 31);

@@ -42,6 +42,12 @@ class DecodeStep:
         # cache; or one dict for every layer, or a list with one per attention
         # layer (each layer's own window, e.g. an FP8 ring: fmt=SWA_FP8)
         if swa is None:
+            # the tail view is each sequence's last swa_cap entries only when
+            # every sequence is full (one host read of the lengths, here and
+            # never in run())
+            if not bool((lengths == cap).all()):
+                raise ValueError("the default window is the last swa_cap entries of a full cache: with lengths "
+                                 "below the capacity pass each sequence's window as `swa`")
             swa = dict(codes=cache["main_codes"], scales=cache["main_scales"], row0=cap - swa_cap,
                        stride=cap, length=torch.full((B,), swa_cap, dtype=torch.int32, device=dev))
         self.swa = swa

@@ -377,9 +377,10 @@ int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, in
  * range of 32-row chunks (FP8 window records: 16-row chunks) with an online
  * softmax (one range per sequence from
  * 256 sequences), and the last range of a sequence merges the others.  The chunks of one group are placed on one XCD
- * (workgroup ids congruent mod 8), so the partials meet in that XCD's L2; a
- * merge that finds a chunk from another XCD writes NaN rather than a wrong
- * value.  The result is deterministic (fixed merge order; the counters only
+ * (workgroup ids congruent mod 8; gfx950 dispatches workgroup i to XCD
+ * i mod 8), so the partials meet in that XCD's L2 and a relaxed counter
+ * orders them; a merge that finds a chunk from another XCD writes NaN rather
+ * than a wrong value.  The result is deterministic (fixed merge order; the counters only
  * decide which workgroup merges).
  */
 size_t csa2_attn_workspace(int32_t B, int32_t H, int32_t k, int32_t swa_cap);

@@ -60,6 +60,29 @@ def oracle_cache_seq(wl: syn.Workload, b: int, main_fmt: int, gpu_cache, rows: i
     return out
 
 
+def oracle_main_rows(wl: syn.Workload, b: int, main_fmt: int, gpu_cache, rows, cap: int | None = None):
+    """The oracle's quantisation of main-KV rows `rows` of sequence b (from the
+    generator's fp32 values), checked bit-identical to the same rows of the
+    GPU cache.  Quantisation is row by row, so a subset of rows is exactly the
+    corresponding subset of the whole cache's bytes."""
+    rows = np.asarray(rows, np.int64)
+    gi = torch.from_numpy(rows).to(DEV)
+    x = syn.main_values(wl, b, DEV, rows=cap or wl.cap)
+    xs = x[gi].cpu().numpy()
+    del x
+    mc, ms = oracle.quantize(xs, 16, main_fmt)
+    assert np.array_equal(mc, gpu_cache["main_codes"][b][gi].cpu().numpy()), "main codes differ"
+    assert np.array_equal(ms, gpu_cache["main_scales"][b][gi].cpu().numpy()), "main scales differ"
+    return mc, ms
+
+
+def remap_positions(sel, rows):
+    """Positions of `sel` as indices into the sorted row list `rows` (-1 stays
+    -1; a position not in `rows` is an error)."""
+    lut = {int(r): i for i, r in enumerate(rows)}
+    return np.array([lut[int(p)] if p >= 0 else -1 for p in sel], np.int32)
+
+
 # ---------------------------------------------------------------- tolerances
 def score_close(gpu, ref):
     """Scores agree within 1e-5 relative, with a floor of 1e-7 x the largest."""

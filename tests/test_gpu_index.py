@@ -370,3 +370,24 @@ def test_index_full_mq_fp4_query_equals_one_query_calls(B, Q, H):
         assert torch.equal(topk[:, i], t1) and torch.equal(pool[:, i], p1) and torch.equal(pool_len[:, i], pl1)
         for b, L in enumerate(lens):
             assert torch.equal(scores[b, i, :L].view(torch.int32), s1[b, :L].view(torch.int32))
+    # the oracle on a sample of (sequence, query) rows, scoring the dequantised
+    # FP4 query (exact in bf16)
+    topk, pool, pool_len, scores = (t.cpu().numpy() for t in (topk, pool, pool_len, scores))
+    qfn = qb.view(torch.bfloat16).float().cpu().numpy()
+    qcn, qsn, wn = qc.cpu().numpy(), qs.cpu().numpy(), w.cpu().numpy()
+    certified = 0
+    for b, i in sorted({(0, 0), (0, Q - 1), (B - 1, Q // 2), (min(1, B - 1), Q - 1), (min(2, B - 1), 0)}):
+        L = lens[b]
+        if L == 0:
+            assert np.all(topk[b, i] == -1) and pool_len[b, i] == 0
+            continue
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        qbits = _oracle_fp4_query_bits(qfn[b, i], qcn[b, i], qsn[b, i])
+        rt, rp, rpl, rs = oracle.index_full(ref["idx_codes"][:L], ref["idx_scales"][:L], L, qbits, wn[b, i], k, 8,
+                                            nb)
+        score_close(scores[b, i, :L], rs)
+        assert np.array_equal(topk[b, i], brute_topk(scores[b, i, :L], k))
+        bp, bpl, _ = brute_pool(scores[b, i, :L], nb)
+        assert pool_len[b, i] == bpl == rpl and np.array_equal(pool[b, i], bp)
+        certified += certify_topk(topk[b, i], rt, rs, k)
+    say(f"  certified near-ties against the oracle: {certified}")

@@ -8,8 +8,15 @@ pool length and scores must equal the contiguous call's; the returned pool
 rows must be exactly the table's translation of the returned positions;
 attention over the returned rows must equal attention over the positions
 (same rows, same order, so the same bits); appends must land on the rows
-the table names.  The contiguous calls themselves are checked against the
-oracle in test_gpu_index.py and test_gpu_attention.py.
+the table names.
+
+The paged results also face the oracle directly: the logical cache of each
+sequence is gathered from the pool through the table on the host, checked
+equal to the oracle's quantisation of the generator's values, and the
+oracle's index_full, index_pool and attention on it are compared with the
+paged top-k, pool, pool scores, Reindex top-k and attention outputs (scores
+within tolerance, selections exact on the GPU's own scores and equal to the
+oracle's up to certified near-ties, attention within 1e-2).
 """
 import numpy as np
 import pytest
@@ -17,7 +24,8 @@ import torch
 
 import csa2_synth as syn
 import compressed_kv_cache_mxfp4_amd as K
-from gpu_common import DEV, build_gpu_cache, say
+import oracle
+from gpu_common import DEV, attn_close, brute_pool, brute_topk, build_gpu_cache, certify_topk, say, score_close
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +52,24 @@ def _paginate(cache, lens, shift, seed, spare=7):
         used = (lens[b] + P - 1) // P
         table[b, used:] = np.where(np.arange(mp - used) % 2 == 0, -5, 1 << 30)[: mp - used]
     return pool, torch.from_numpy(table).to(DEV), table
+
+
+def _logical(pool, tabn, shift, b, L):
+    """Sequence b's first L entries gathered from the pool through the table (host)."""
+    rows = _phys(tabn, shift, b, np.arange(L))
+    return {key: pool[key].cpu().numpy()[rows] for key, _ in PLANES}
+
+
+def _oracle_planes(wl, b, L, fmt, logical):
+    """The oracle's quantisation of sequence b's first L entries, checked equal
+    to the entries the table addresses."""
+    xi = syn.idx_values(wl, b, DEV, rows=wl.cap).cpu().numpy()[:L]
+    xm = syn.main_values(wl, b, DEV, rows=wl.cap).cpu().numpy()[:L]
+    ic, isc = oracle.quantize(xi, 32, oracle.E8M0)
+    mc, ms = oracle.quantize(xm, 16, fmt)
+    for key, ref in (("idx_codes", ic), ("idx_scales", isc), ("main_codes", mc), ("main_scales", ms)):
+        assert np.array_equal(logical[key], ref), f"sequence {b}: paged {key} differ from the oracle's"
+    return dict(idx_codes=ic, idx_scales=isc, main_codes=mc, main_scales=ms)
 
 
 def _phys(table, shift, b, pos):
@@ -93,8 +119,35 @@ def test_paged_index_and_attention_equal_contiguous(shift, fmt):
     o0, l0 = K.sparse_attn_decode(qa, cache["main_codes"], cache["main_scales"], lt, torch.from_numpy(t1).to(DEV),
                                   fmt, return_lse=True, **win)
     o1, l1 = K.sparse_attn_decode_rows(qa, pool, torch.from_numpy(tr1).to(DEV), fmt, return_lse=True, **win)
+    _, ps1 = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool_t, pool_l, q2, w2, k=256,
+                          return_scores=True)
     torch.cuda.synchronize()
     assert torch.equal(o0.cpu(), o1.cpu()) and torch.equal(l0.cpu(), l1.cpu())
+
+    # ---- the paged results against the oracle on the logical cache
+    qn, wn, q2n, w2n = (x.cpu().numpy() for x in (q, w, q2, w2))
+    ps1, o1n, swl = ps1.cpu().numpy(), o1.cpu(), swa_len.cpu().numpy()
+    cert = 0
+    for b, L in enumerate(lens):
+        ref = _oracle_planes(wl, b, L, fmt, _logical(pool, tabn, shift, b, L))
+        rt, rp, rpl, rs = oracle.index_full(ref["idx_codes"], ref["idx_scales"], L, qn[b], wn[b], 256, 8, 64)
+        score_close(s1[b, :L], rs)
+        assert np.array_equal(t1[b], brute_topk(s1[b, :L], 256))
+        bp, bpl, _ = brute_pool(s1[b, :L], 64)
+        assert pl1[b] == bpl == rpl and np.array_equal(p1[b], bp)
+        cert += certify_topk(t1[b], rt, rs, 256)
+        n = int(pl1[b])
+        rti, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], L, p1[b], n, q2n[b], w2n[b], 256)
+        score_close(ps1[b, :n], rps)
+        assert np.array_equal(tk1[b], brute_topk(ps1[b, :n], 256, p1[b, :n]))
+        pos_scores = np.full(L, np.nan)
+        pos_scores[p1[b, :n]] = rps
+        cert += certify_topk(tk1[b], rti, pos_scores, 256)
+        sl = int(swl[b])
+        ro, _ = oracle.attention(qa[b].cpu().numpy(), ref["main_codes"], ref["main_scales"], L, fmt, t1[b],
+                                 ref["main_codes"][:sl], ref["main_scales"][:sl], sl, 1 / np.sqrt(512))
+        attn_close(o1n[b:b + 1], ro[None])
+    say(f"  paged against the oracle: certified near-ties {cert}")
 
 
 def test_paged_attention_throughput_kernel_equal_contiguous():
@@ -110,12 +163,12 @@ def test_paged_attention_throughput_kernel_equal_contiguous():
     topk = np.stack([g.choice(cap, k, replace=False) for _ in range(B)]).astype(np.int32)
     topk[0, :7] = -1
     rows = np.stack([_phys(tabn, shift, b, topk[b]) for b in range(B)])
-    ring = K.window_alloc(B, 128, DEV)
-    K.window_write(torch.randn(B, 128, 512, generator=torch.Generator(device=DEV).manual_seed(4),
-                               device=DEV).to(torch.bfloat16),
-                   torch.full((B,), 5000, dtype=torch.int64, device=DEV), ring, rope=True)
-    win = dict(swa_codes=ring["data"], swa_scales=ring["scales"], swa_len=ring["swa_len"], swa_stride=128,
-               swa_cap=128, swa_fmt=K.SWA_FP8)
+    # the FP8 window rings come from the oracle's ring writer (host), so the
+    # attention check below shares its inputs with the oracle
+    lat = syn.as_bf16_bits(torch.randn(B, 128, 512, generator=torch.Generator().manual_seed(4)))
+    ring = oracle.window_write(lat.numpy().view(np.uint16), np.full(B, 5000, np.int64), 128, rope=True)
+    win = dict(swa_codes=torch.from_numpy(ring["data"]).to(DEV), swa_scales=torch.from_numpy(ring["scales"]).to(DEV),
+               swa_len=torch.from_numpy(ring["swa_len"]).to(DEV), swa_stride=128, swa_cap=128, swa_fmt=K.SWA_FP8)
     qa = syn.as_bf16_bits(torch.randn(B, 64, 512, generator=torch.Generator().manual_seed(9)) * 0.5).to(DEV)
     qp = torch.arange(B, dtype=torch.int64, device=DEV) * 977 + 5128
     o0 = K.sparse_attn_decode(qa, cache["main_codes"], cache["main_scales"], lt, torch.from_numpy(topk).to(DEV), 0,
@@ -123,6 +176,16 @@ def test_paged_attention_throughput_kernel_equal_contiguous():
     o1 = K.sparse_attn_decode_rows(qa, pool, torch.from_numpy(rows).to(DEV), 0, q_pos=qp, **win)
     torch.cuda.synchronize()
     assert torch.equal(o0.cpu(), o1.cpu())
+    # against the oracle on the logical cache, one sequence of each XCD residue
+    o1n, qpn, qan = o1.cpu(), qp.cpu().numpy(), qa.cpu().numpy()
+    worst = 0.0
+    for b in (0, 9, 18, 27, 36, 45, 6, 15):  # b mod 8 = 0..7
+        ref = _oracle_planes(wl, b, cap, 0, _logical(pool, tabn, shift, b, cap))
+        ro, _ = oracle.attention(qan[b], ref["main_codes"], ref["main_scales"], cap, 0, topk[b], ring["data"][b],
+                                 ring["scales"][b], int(ring["swa_len"][b]), 1 / np.sqrt(512), q_pos=int(qpn[b]),
+                                 swa_fmt=1)
+        worst = max(worst, attn_close(o1n[b:b + 1], ro[None]))
+    say(f"  paged throughput kernel against the oracle: worst rel err {worst:.2e}")
 
 
 @pytest.mark.parametrize("m", [1, 2])
