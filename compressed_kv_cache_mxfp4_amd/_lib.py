@@ -63,6 +63,8 @@ def lib():
     L.csa2_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_sparse_attn_decode.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
                                           P, i32, f32, P, P, P, P, sz, P]
+    L.csa2_sparse_attn_decode_noalloc.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
+                                                  P, i32, f32, P, P, P, P]
     L.csa2_window_write.argtypes = [P, i32, i32, P, f32, i32, P, i32, P, P, P, P]
     L.csa2_cache_append_paged.argtypes = [P, P, i32, i32, P, f32, P, i32, i32, P, P, P, P, i64, P, i32, i32, P, P, P]
     L.csa2_index_full_paged.argtypes = [P, P, i64, P, i32, i32, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P,
@@ -615,3 +617,50 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
         float(sm_scale), _ptr(q_pos), _ptr(o),
         _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode")
     return (o, lse) if return_lse else o
+
+
+def sparse_attn_decode_noalloc(q, main_codes, main_scales, lengths, topk, main_fmt: int, out, lse=None,
+                               swa_codes=None, swa_scales=None, swa_len=None, swa_stride: int = 0,
+                               swa_cap: int = 0, swa_row0: int = 0, sm_scale: Optional[float] = None,
+                               q_pos=None, swa_fmt: int = 0):
+    """sparse_attn_decode through csa2_sparse_attn_decode_noalloc: the library's
+    own per-GPU scratch instead of a workspace, and caller-provided outputs
+    (`out` int16 [B][H][512], optional `lse` fp32 [B][H]), so that neither
+    this call nor the library allocates.  Arguments as sparse_attn_decode."""
+    q = _bits16(q)
+    _req(q, "q", torch.int16)
+    dev = q.device
+    B, H = q.shape[0], q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 512))
+    cap = main_codes.shape[1]
+    _req(main_codes, "main_codes", torch.uint8, dev, (B, cap, 256))
+    _req(main_scales, "main_scales", torch.uint8, dev, (B, cap, 32))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    k = topk.shape[1]
+    _req(topk, "topk", torch.int32, dev, (B, k))
+    _req(out, "out", torch.int16, dev, (B, H, 512))
+    if lse is not None:
+        _req(lse, "lse", torch.float32, dev, (B, H))
+    rb, sb = (576, 8) if swa_fmt == SWA_FP8 else (256, 32)
+    if swa_cap > 0:
+        if swa_codes.dtype != torch.uint8 or swa_scales.dtype != torch.uint8:
+            raise TypeError("window planes must be uint8")
+        if swa_codes.device != dev or swa_scales.device != dev:
+            raise ValueError("window planes on another device")
+        if not (swa_codes.is_contiguous() and swa_scales.is_contiguous()):
+            raise ValueError("window planes must be contiguous")
+        need = swa_row0 + (B - 1) * swa_stride + swa_cap
+        if swa_row0 < 0 or swa_codes.numel() < need * rb or swa_scales.numel() < need * sb:
+            raise ValueError("window planes smaller than swa_row0 + B rows of swa_stride")
+        _req(swa_len, "swa_len", torch.int32, dev, (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / (512 ** 0.5)
+    if q_pos is not None:
+        _req(q_pos, "q_pos", torch.int64, dev, (B,))
+    _check(lib().csa2_sparse_attn_decode_noalloc(
+        _ptr(q), H, _ptr(main_codes), _ptr(main_scales), cap, main_fmt, _ptr(lengths), _ptr(topk), k,
+        B, ctypes.c_void_p(swa_codes.data_ptr() + rb * swa_row0) if swa_cap else None,
+        ctypes.c_void_p(swa_scales.data_ptr() + sb * swa_row0) if swa_cap else None,
+        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, int(swa_fmt) if swa_cap else 0,
+        float(sm_scale), _ptr(q_pos), _ptr(out), _ptr(lse), _stream(dev)), "csa2_sparse_attn_decode_noalloc")
+    return out

@@ -3,6 +3,8 @@
 // quant.hip, index.hip and attn.hip.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "csa2.h"
 #include "csa2_internal.hpp"
 
@@ -40,6 +42,52 @@ int check_attn(const uint16_t* q, int32_t H, const uint8_t* main_codes, const ui
   return CSA2_OK;
 }
 
+// ---- library-held attention scratch for csa2_sparse_attn_decode_noalloc.
+// Each GPU holds one copy of `scratch` for the life of the process.  In host
+// code the name is only a stand-in for the device symbol: its device address
+// is taken once per device with hipGetSymbolAddress, and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[CSA2_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_rc[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The scratch address on the current device (nullptr on failure, with the
+// status in *rc).  The first call on a device also clears the completion
+// counters with a fill kernel on `st` (every attention call leaves them zero
+// afterwards).
+void* device_scratch(hipStream_t st, int* rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = CSA2_ERR_HIP;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [&] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      g_scratch_rc[dev] = CSA2_ERR_HIP;
+      return;
+    }
+    constexpr int words = CSA2_ATTN_WS_COUNTER_BYTES / 4;
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, st>>>(reinterpret_cast<uint32_t*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) {
+      g_scratch_rc[dev] = CSA2_ERR_HIP;
+      return;
+    }
+    g_scratch_ptr[dev] = ptr;
+    g_scratch_rc[dev] = CSA2_OK;
+  });
+  *rc = g_scratch_rc[dev];
+  return *rc == CSA2_OK ? g_scratch_ptr[dev] : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +101,7 @@ const char* csa2_status_string(int status) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP launch failure";
+    case CSA2_ERR_SCRATCH: return "problem larger than the library's fixed attention scratch";
     default: return "unknown status";
   }
 }
@@ -294,6 +343,26 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             B, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale, q_pos, out);
   if (rc != CSA2_OK || B == 0) return rc;
   if (!ws || ws_bytes < csa2_attn_workspace(B, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
+                                           k, B, swa_codes, swa_scales, swa_stride, swa_cap,
+                                           swa_len, swa_fmt, sm_scale, q_pos, out, lse_opt, ws,
+                                           as_stream(stream)));
+}
+
+int csa2_sparse_attn_decode_noalloc(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                                    const uint8_t* main_scales, int64_t cap, int32_t main_fmt,
+                                    const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
+                                    const uint8_t* swa_codes, const uint8_t* swa_scales,
+                                    int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
+                                    int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                                    float* lse_opt, void* stream) {
+  const int rc = check_attn(q, H, main_codes, main_scales, cap, CSA2_MAX_CACHE_ROWS, main_fmt, true, len, topk, k,
+                            B, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale, q_pos, out);
+  if (rc != CSA2_OK || B == 0) return rc;
+  if (csa2_attn_workspace(B, H, k, swa_cap) > (size_t)CSA2_ATTN_NOALLOC_SCRATCH_BYTES) return CSA2_ERR_SCRATCH;
+  int src = CSA2_OK;
+  void* ws = device_scratch(as_stream(stream), &src);
+  if (!ws) return src;
   return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk,
                                            k, B, swa_codes, swa_scales, swa_stride, swa_cap,
                                            swa_len, swa_fmt, sm_scale, q_pos, out, lse_opt, ws,

@@ -88,6 +88,7 @@ extern "C" {
 #define CSA2_MAX_CACHE_ROWS 1048576 /* entries per sequence accepted by index_full */
 #define CSA2_ATTN_MAX_GROUPS 65536  /* B * H / 16 accepted by csa2_sparse_attn_decode  */
 #define CSA2_ATTN_WS_COUNTER_BYTES (CSA2_ATTN_MAX_GROUPS * 4) /* leading zeroed region */
+#define CSA2_ATTN_NOALLOC_SCRATCH_BYTES (32 << 20) /* per-GPU scratch of csa2_sparse_attn_decode_noalloc */
 
 typedef enum {
   CSA2_OK = 0,
@@ -96,7 +97,8 @@ typedef enum {
   CSA2_ERR_ALIGN = 3,       /* a plane pointer is not 16-byte aligned            */
   CSA2_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head count)       */
   CSA2_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
-  CSA2_ERR_HIP = 6          /* a HIP launch failed                               */
+  CSA2_ERR_HIP = 6,         /* a HIP launch failed                               */
+  CSA2_ERR_SCRATCH = 7      /* larger than the library's fixed scratch (noalloc) */
 } csa2_status;
 
 typedef enum { CSA2_SCALE_E8M0 = 0, CSA2_SCALE_E4M3 = 1 } csa2_scale_fmt;
@@ -391,6 +393,30 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
                             int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
                             float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_sparse_attn_decode_noalloc -- csa2_sparse_attn_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, outputs, kernels
+ * and results, without ws/ws_bytes: the partials and completion counters live
+ * in a library-held device array of CSA2_ATTN_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * per GPU, kept until the process ends.  The call allocates nothing.
+ *   Limit: csa2_attn_workspace(B, H, k, swa_cap) must not exceed
+ *   CSA2_ATTN_NOALLOC_SCRATCH_BYTES (e.g. up to 96 sequences at H = 64,
+ *   k = 512, swa_cap = 128), else CSA2_ERR_SCRATCH and nothing is launched.
+ *   The current device must be the device of `stream` and of the buffers.
+ *   The first call on a device takes the array's device address and clears
+ *   its counters with a small kernel on `stream`; every call leaves them zero.
+ *   All calls on one GPU share the array: calls that overlap in time (on
+ *   different streams, or in graphs replayed concurrently) race.
+ */
+int csa2_sparse_attn_decode_noalloc(const uint16_t* q, int32_t H, const uint8_t* main_codes,
+                                    const uint8_t* main_scales, int64_t cap, int32_t main_fmt,
+                                    const int32_t* len, const int32_t* topk, int32_t k, int32_t B,
+                                    const uint8_t* swa_codes, const uint8_t* swa_scales,
+                                    int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
+                                    int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
+                                    float* lse_opt, void* stream);
 
 /*
  * Paged cache [GP 7: the cache is paged with 576-byte alignment].  The four

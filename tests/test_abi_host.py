@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "csa2.h")
 LIB = os.path.join(ROOT, "compressed_kv_cache_mxfp4_amd", "lib", "libcsa2.so")
 
-CSA2_OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP = range(7)
+CSA2_OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH = range(8)
 
 
 def _declared():
@@ -46,8 +46,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
-        assert lib.csa2_status_string(code)
+    for code in range(8):
+        assert lib.csa2_status_string(code) != b"unknown status"
     assert lib.csa2_status_string(99) == b"unknown status"
 
 
@@ -216,6 +216,34 @@ def test_index_pool_and_attention_validation(lib):
     args = list(base)
     args[15], args[11] = 1, P(0x1004)     # FP8 window records: scale rows need 8-byte alignment
     assert a(*args) == ERR_ALIGN
+
+
+def test_attention_noalloc_validation(lib):
+    # the no-alloc attention call validates like the workspace call, and
+    # refuses a problem larger than its fixed per-GPU scratch before touching
+    # any device (all of these fail before the scratch address is taken)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    a = lib.csa2_sparse_attn_decode_noalloc
+    a.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, i32, ctypes.c_float, P, P, P, P]
+    base = [FAKE, 64, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0, 0.04, None,
+            FAKE, None, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return a(*args)
+
+    assert lib.csa2_status_string(ERR_SCRATCH) == b"problem larger than the library's fixed attention scratch"
+    assert call(1, 40) == ERR_UNSUP
+    assert call(13, 129) == ERR_SHAPE
+    assert call(0, None) == ERR_NULL
+    assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(9, 0) == CSA2_OK                     # empty batch: nothing to do
+    # 256 sequences x 64 heads x 17 chunks of partials exceed 32 MiB
+    args = list(base)
+    args[8], args[9] = 2048, 256
+    assert a(*args) == ERR_SCRATCH
+    assert lib.csa2_attn_workspace(256, 64, 2048, 128) > (32 << 20)
 
 
 def test_window_write_validation(lib):
