@@ -72,6 +72,9 @@ def parse():
                     help="instead of the step, time one sparse-attention call per batch size "
                          "(64 heads x 512 dims over 512 selected + 128 window rows, 32,768-entry "
                          "caches) and print one JSON line with the sweep")
+    ap.add_argument("--secondary", default="step128:e4m3,write1m:e8m0,stress:e8m0",
+                    help="after the headline step, time these workload:format pairs phase by phase (scoring, "
+                         "selection and attention apart) and report them in the same JSON line; 'none' skips")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     return ap.parse_args()
@@ -233,6 +236,160 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
                           frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))), flush=True)
 
 
+def phase_bytes(wl, B, lengths, pool_len, H_idx, H_attn=64, swa=128):
+    """Algorithmic bytes of each phase when scoring and selection run as
+    separate kernels: what each phase must read and write at minimum."""
+    k, nb = wl.k, wl.n_blocks
+    sum_len, sum_pool = int(sum(lengths)), int(sum(pool_len))
+    qw = B * (H_idx * 256 + H_idx * 4 + 4)               # bf16 query heads, head weights, length
+    return dict(
+        # every visible entry's 68 B read; its score (4 B) and its block's maximum (4 B per 8) written
+        full_score=sum_len * 68 + qw + sum_len * 4 + (sum_len // 8) * 4,
+        # block maxima read; the scores of the k candidate blocks' 8 positions read; top-k, pool and its
+        # length written
+        full_select=(sum_len // 8) * 4 + B * k * 8 * 4 + B * (k * 4 + nb * 8 * 4 + 4),
+        # pool entries read, their 68 B rows gathered; pool scores and group maxima written
+        pool_score=B * nb * 8 * 4 + sum_pool * 68 + qw + sum_pool * 4 + (sum_pool // 8) * 4,
+        # group maxima read; the scores and positions of the k candidate groups' 8 entries read; top-k written
+        pool_select=(sum_pool // 8) * 4 + B * k * 8 * (4 + 4) + B * k * 4,
+        attn=B * k * 288 + B * swa * 288 + B * H_attn * 512 * 2 * 2 + B * k * 4 + B * 8,
+    )
+
+
+def secondary_workload(wl_name, fmt_name, steps, warmup):
+    """One workload's decoder step, timed phase by phase: the cache write, the
+    Full call's scoring and its selection, each Reindex call's scoring and its
+    selection, and the attention calls, each phase in its own HIP graph (HIP
+    events on the launch stream), plus the whole step (the fused calls) as one
+    graph.  Returns the per-phase record for the JSON line."""
+    import torch
+    import csa2_synth as syn
+    import compressed_kv_cache_mxfp4_amd as K
+    from compressed_kv_cache_mxfp4_amd.decode_step import DecodeStep
+
+    dev = torch.device("cuda:0")
+    wl = syn.WORKLOADS[wl_name]
+    fmt = K.E8M0 if fmt_name == "e8m0" else K.E4M3
+    B, cap = wl.B, wl.cap
+    cache = dict(
+        main_codes=torch.empty(B, cap, 256, dtype=torch.uint8, device=dev),
+        main_scales=torch.empty(B, cap, 32, dtype=torch.uint8, device=dev),
+        idx_codes=torch.empty(B, cap, 64, dtype=torch.uint8, device=dev),
+        idx_scales=torch.empty(B, cap, 4, dtype=torch.uint8, device=dev),
+    )
+    for b in range(B):
+        K.quantize_fp4(syn.main_values(wl, b, dev), 16, fmt, cache["main_codes"][b], cache["main_scales"][b])
+        K.quantize_fp4(syn.idx_values(wl, b, dev), 32, K.E8M0, cache["idx_codes"][b], cache["idx_scales"][b])
+    lengths = torch.full((B,), cap, dtype=torch.int32, device=dev)
+    step = DecodeStep(cache, lengths, k=wl.k, n_blocks=wl.n_blocks, n_reindex=wl.n_reindex,
+                      reuse_per_index=wl.reuse_per_index, main_fmt=fmt)
+    n_idx = 1 + wl.n_reindex
+    idx_qw = [(syn.index_query(wl, i, dev), syn.index_weights(wl, i, dev)) for i in range(n_idx)]
+    attn_q = [syn.attn_query(wl, j, dev) for j in range(step.n_attn)]
+    if wl.write_tokens:
+        new_lat, new_gate, w_proj = syn.write_inputs(wl, dev)
+        w_T, w_m = wl.write_tokens, wl.write_m
+    else:
+        wl_w = syn.Workload("append", wl.seed + 100, B=B, cap=1, H_idx=8, k=1, block=8, n_blocks=0,
+                            write_tokens=B, write_m=1)
+        new_lat, _, w_proj = syn.write_inputs(wl_w, dev)
+        new_gate, w_T, w_m = None, B, 1
+    n_new = w_T // w_m
+    staged = dict(main_codes=torch.empty(n_new, 256, dtype=torch.uint8, device=dev),
+                  main_scales=torch.empty(n_new, 32, dtype=torch.uint8, device=dev),
+                  idx_codes=torch.empty(n_new, 64, dtype=torch.uint8, device=dev),
+                  idx_scales=torch.empty(n_new, 4, dtype=torch.uint8, device=dev))
+    c = cache
+
+    def ph_write():
+        K.cache_write(new_lat, new_gate, w_m, w_proj, fmt, out=staged)
+
+    def ph_full_score():
+        q, w = idx_qw[0]
+        K.index_full_score(c["idx_codes"], c["idx_scales"], lengths, q, w, step.ws_full)
+
+    def ph_full_select():
+        K.index_full_select(cap, lengths, step.ws_full, k=wl.k, n_blocks=wl.n_blocks,
+                            out=dict(topk=step.topk[0], pool=step.pool, pool_len=step.pool_len))
+
+    def ph_pool_score():
+        for i in range(1, n_idx):
+            q, w = idx_qw[i]
+            K.index_pool_score(c["idx_codes"], c["idx_scales"], lengths, step.pool, step.pool_len, q, w,
+                               step.ws_pool)
+
+    def ph_pool_select():
+        for i in range(1, n_idx):
+            K.index_pool_select(step.pool, step.pool_len, step.ws_pool, k=wl.k, out=dict(topk=step.topk[i]))
+
+    def ph_attn():
+        step.run_attention(attn_q)
+
+    def one_step():
+        ph_write()
+        step.run(idx_qw, attn_q)
+
+    for _ in range(max(warmup, 1)):
+        one_step()
+        ph_full_score()
+        ph_full_select()
+        if wl.n_reindex:
+            ph_pool_score()
+            ph_pool_select()
+    torch.cuda.synchronize()
+    pool_len = step.pool_len.cpu().tolist() if wl.n_blocks else [0] * B
+
+    def capture(fn, r=1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(r):
+                fn()
+        return g
+
+    def timed(g, n):
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps / n
+
+    phases = [("write", ph_write, 1), ("full_score", ph_full_score, 1), ("full_select", ph_full_select, 1)]
+    if wl.n_reindex:
+        phases += [("pool_score", ph_pool_score, wl.n_reindex), ("pool_select", ph_pool_select, wl.n_reindex)]
+    phases.append(("attn", ph_attn, step.n_attn))
+    nbytes = phase_bytes(wl, B, [cap] * B, pool_len, wl.H_idx)
+    T_, m_ = w_T, w_m
+    nbytes["write"] = T_ * 512 * 2 * (2 if m_ > 1 else 1) + 512 * 128 * 4 + (T_ // m_) * 356
+    bound = dict(write="fp32 projection" if w_T > B else "latency", full_score="hbm", full_select="latency",
+                 pool_score="hbm", pool_select="latency", attn="hbm")
+    out = {}
+    for name, fn, n in phases:
+        reps = max(1, -(-20 // n))
+        us = timed(capture(fn, reps), reps * n)
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        out[name] = dict(calls_per_step=n, us_per_call=round(us, 3), bytes_per_call=nbytes[name],
+                         achieved_GBs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), bound=bound[name])
+    ms_step = timed(capture(one_step), 1) * 1e-3
+    full_us = out["full_score"]["us_per_call"] + out["full_select"]["us_per_call"]
+    full_bytes = algorithmic_bytes(wl, B, [cap] * B, pool_len, wl.k, wl.n_blocks, wl.H_idx, 64, 128)["index_full"]
+    res = dict(workload=wl.name, main_scale=fmt_name.upper(), sequences=B, entries_per_sequence=cap,
+               layers=f"1 Full + {wl.n_reindex} Reindex + {step.n_attn - n_idx} Reuse",
+               cache_write=f"{w_T} tokens, m={w_m}", ms_per_step=round(ms_step, 4),
+               positions_scored_per_s=(B * cap + wl.n_reindex * sum(pool_len)) / (ms_step * 1e-3),
+               attn_queries_per_s=B * step.n_attn / (ms_step * 1e-3),
+               index_full_split_us=round(full_us, 3),
+               index_full_split_frac_hbm=round(full_bytes / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+               phases=out)
+    log(f"[secondary] {wl.name}/{fmt_name}: step {ms_step:.3f} ms; " +
+        ", ".join(f"{k_} {v['us_per_call']:.1f} us" for k_, v in out.items()))
+    del cache, step, staged
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(mb: float):
     import torch
 
@@ -294,10 +451,65 @@ def cpu_baseline(wl, fmt, budget_s):
                 break
         log(f"[cpu] oracle step {step}: {spent:.1f}s so far")
         step += 1
-    return dict(value=positions / spent, unit="positions/s", cores=oracle.num_threads(), kind="oracle",
+    threads = oracle.num_threads()
+    single = single_core_oracle(dev)
+    return dict(value=positions / spent, unit="positions/s", cores=threads, kind="oracle",
                 sample=f"{seqs} sequence-steps ({wl.B} sequences per decoder step; each: full scoring, "
                        f"{n_idx - 1} pool rescorings, {wl.n_attn_calls} attention calls), "
-                       f"{spent:.1f} s of oracle time")
+                       f"{spent:.1f} s of oracle time",
+                host=host_cpu(), omp_threads=threads, single_core=single)
+
+
+def host_cpu():
+    """The host the oracle ran on: logical CPUs, the CPUs this process may use, the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return dict(nproc=os.cpu_count(), usable_cpus=usable, model=model)
+
+
+def single_core_oracle(dev):
+    """The oracle on one thread: one tiny-workload step (Full call over 4096
+    entries with 8 indexer heads, one attention call) and one full128 query
+    (Full call over 131,072 entries with 64 heads, one attention call)."""
+    import numpy as np
+    import csa2_synth as syn
+    import oracle
+
+    out = {}
+    before = oracle.num_threads()
+    try:
+        for name in ("tiny", "full128"):
+            wl = syn.WORKLOADS[name]
+            ic, isc = oracle.quantize(syn.idx_values(wl, 0, dev).cpu().numpy(), 32, oracle.E8M0)
+            mc, ms = oracle.quantize(syn.main_values(wl, 0, dev).cpu().numpy(), 16, oracle.E8M0)
+            q = syn.index_query(wl, 0, dev)[0].cpu().numpy()
+            w = syn.index_weights(wl, 0, dev)[0].cpu().numpy()
+            aq = syn.attn_query(wl, 0, dev)[0].cpu().numpy()
+            L = wl.cap
+            oracle.set_threads(1)
+            t0 = time.perf_counter()
+            topk, _, _, _ = oracle.index_full(ic, isc, L, q, w, wl.k, 8, wl.n_blocks)
+            t1 = time.perf_counter()
+            oracle.attention(aq, mc, ms, L, oracle.E8M0, topk, mc[L - 128:], ms[L - 128:], 128, 1 / np.sqrt(512))
+            t2 = time.perf_counter()
+            oracle.set_threads(before)
+            out[name] = dict(entries=L, indexer_heads=wl.H_idx, index_full_s=round(t1 - t0, 4),
+                             attention_s=round(t2 - t1, 4), positions_per_s=round(L / (t1 - t0)))
+            log(f"[cpu] single core {name}: index_full {t1 - t0:.3f} s, attention {t2 - t1:.3f} s")
+    finally:
+        oracle.set_threads(before)
+    return out
 
 
 def main():
@@ -601,9 +813,15 @@ def main():
                              note="decode-time append of one token per sequence into the cache; not in the step"),
         kernels=kernels, roofline=roofline,
     )
-    if not args.no_cpu_baseline and args.only is None and not fp8w and not args.paged:
+    headline_only = args.only is None and not fp8w and not args.paged and args.index_q == "bf16"
+    if headline_only:
+        del g_step, g_phase
         del step, cache
         torch.cuda.empty_cache()
+    if headline_only and args.secondary != "none":
+        res["secondary"] = [secondary_workload(name, f, args.steps, args.warmup)
+                            for name, f in (x.split(":") for x in args.secondary.split(","))]
+    if not args.no_cpu_baseline and headline_only:
         res["cpu_baseline"] = cpu_baseline(wl, fmt, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

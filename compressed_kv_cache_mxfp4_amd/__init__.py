@@ -14,11 +14,15 @@ from ._lib import (  # noqa: F401
     cache_append_paged,
     cache_write,
     index_full,
+    index_full_score,
+    index_full_select,
     index_full_mq,
     index_full_paged,
     index_pool_rows,
     paged_alloc,
     index_pool,
+    index_pool_score,
+    index_pool_select,
     lib,
     quantize_fp4,
     sparse_attn_decode,

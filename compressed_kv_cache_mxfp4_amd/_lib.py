@@ -49,6 +49,10 @@ def lib():
     L.csa2_index_full_workspace.restype = sz
     L.csa2_index_full_workspace.argtypes = [i32, i64, i32, i32, i32]
     L.csa2_index_full.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.csa2_index_full_score.argtypes = [P, P, i64, P, i32, P, P, i32, i32, P, P, sz, P]
+    L.csa2_index_full_select.argtypes = [i64, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.csa2_index_pool_score.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, P, P, sz, P]
+    L.csa2_index_pool_select.argtypes = [i32, P, P, i32, i32, P, P, P, sz, P]
     L.csa2_index_pool_workspace.restype = sz
     L.csa2_index_pool_workspace.argtypes = [i32, i32, i32]
     L.csa2_index_pool.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, i32, P, P, P, sz, P]
@@ -462,6 +466,88 @@ def index_full(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int
     if return_scores:
         return topk, pool, pool_len, scores
     return topk, pool, pool_len
+
+
+def index_full_score(idx_codes, idx_scales, lengths, q, w, ws, scores=None, block: int = 8):
+    """Phase 1 of index_full (csa2_index_full_score): scores (into `scores`
+    fp32 [B][cap] when given, else the workspace) and block maxima (into the
+    workspace `ws`, csa2_index_full_workspace bytes).  bf16 queries only."""
+    _req(idx_codes, "idx_codes", torch.uint8)
+    dev = idx_codes.device
+    B, cap = idx_codes.shape[0], idx_codes.shape[1]
+    _req(idx_codes, "idx_codes", torch.uint8, dev, (B, cap, 64))
+    _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    q = _bits16(q)
+    H = q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    if scores is not None:
+        _req(scores, "scores", torch.float32, dev, (B, cap))
+    _check(lib().csa2_index_full_score(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, _ptr(q), _ptr(w),
+                                       H, block, _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
+           "csa2_index_full_score")
+
+
+def index_full_select(cap: int, lengths, ws, k: int = 512, n_blocks: int = 2048, scores=None, block: int = 8,
+                      out=None):
+    """Phase 2 of index_full (csa2_index_full_select): the top-k and the pool
+    from the scores and block maxima a preceding index_full_score left in
+    `ws` (and `scores`, if it was given one).  Returns (topk, pool, pool_len)."""
+    dev = lengths.device
+    B = lengths.shape[0]
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    out = out or {}
+    topk = out.get("topk")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=dev)
+    pool = out.get("pool")
+    if pool is None:
+        pool = torch.empty(B, max(n_blocks * block, 1), dtype=torch.int32, device=dev)
+    pool_len = out.get("pool_len")
+    if pool_len is None:
+        pool_len = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib().csa2_index_full_select(cap, _ptr(lengths), B, k, block, n_blocks, _ptr(topk), _ptr(pool),
+                                        _ptr(pool_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)),
+           "csa2_index_full_select")
+    return topk, pool[:, : n_blocks * block], pool_len
+
+
+def index_pool_score(idx_codes, idx_scales, lengths, pool, pool_len, q, w, ws, pool_scores=None):
+    """Phase 1 of index_pool (csa2_index_pool_score): pool scores (into
+    `pool_scores` when given, else `ws`) and group maxima (into `ws`)."""
+    _req(idx_codes, "idx_codes", torch.uint8)
+    dev = idx_codes.device
+    B, cap = idx_codes.shape[0], idx_codes.shape[1]
+    _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    pool_cap = pool.shape[1]
+    _req(pool, "pool", torch.int32, dev, (B, pool_cap))
+    _req(pool_len, "pool_len", torch.int32, dev, (B,))
+    q = _bits16(q)
+    H = q.shape[1]
+    _req(q, "q", torch.int16, dev, (B, H, 128))
+    _req(w, "w", torch.float32, dev, (B, H))
+    if pool_scores is not None:
+        _req(pool_scores, "pool_scores", torch.float32, dev, (B, pool_cap))
+    _check(lib().csa2_index_pool_score(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, _ptr(pool),
+                                       _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, _ptr(pool_scores), _ptr(ws),
+                                       ws.numel(), _stream(dev)), "csa2_index_pool_score")
+
+
+def index_pool_select(pool, pool_len, ws, k: int = 512, pool_scores=None, out=None):
+    """Phase 2 of index_pool (csa2_index_pool_select): the layer's top-k."""
+    dev = pool.device
+    B, pool_cap = pool.shape
+    _req(pool, "pool", torch.int32, dev, (B, pool_cap))
+    _req(pool_len, "pool_len", torch.int32, dev, (B,))
+    out = out or {}
+    topk = out.get("topk")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=dev)
+    _check(lib().csa2_index_pool_select(B, _ptr(pool), _ptr(pool_len), pool_cap, k, _ptr(topk), _ptr(pool_scores),
+                                        _ptr(ws), ws.numel(), _stream(dev)), "csa2_index_pool_select")
+    return topk
 
 
 def index_full_mq(idx_codes, idx_scales, lengths, q, w, k: int = 512, n_blocks: int = 2048,

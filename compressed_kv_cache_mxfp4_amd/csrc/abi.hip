@@ -206,6 +206,38 @@ int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                                           as_stream(stream)));
 }
 
+int csa2_index_full_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                          int32_t B, const uint16_t* q, const float* w, int32_t H, int32_t block, float* scores_opt,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !len || !q || !w) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  if (cap == 0) return CSA2_ERR_SHAPE;
+  if (!ws || ws_bytes < csa2_index_full_workspace(B, cap, 1, block, 0)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_full_score(idx_codes, idx_scales, cap, len, B, q, nullptr, nullptr, w, H, block,
+                                                scores_opt, ws, as_stream(stream)));
+}
+
+int csa2_index_full_select(int64_t cap, const int32_t* len, int32_t B, int32_t k, int32_t block, int32_t n_blocks,
+                           int32_t* topk, int32_t* pool, int32_t* pool_len, const float* scores_opt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (B < 0 || cap < 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+  if (n_blocks < 0 || n_blocks > CSA2_POOL_BLOCKS || (int64_t)n_blocks * block > CSA2_MAX_POOL)
+    return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!len || !topk) return CSA2_ERR_NULL;
+  if (n_blocks > 0 && (!pool || !pool_len)) return CSA2_ERR_NULL;
+  if (cap == 0) return CSA2_ERR_SHAPE;
+  if (!ws || ws_bytes < csa2_index_full_workspace(B, cap, k, block, n_blocks)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_full_select(cap, len, B, k, block, n_blocks, topk, pool, pool_len, scores_opt,
+                                                 ws, as_stream(stream)));
+}
+
 size_t csa2_index_full_mq_workspace(int32_t B, int32_t Q, int64_t cap, int32_t k, int32_t block,
                                     int32_t n_blocks) {
   if (Q < 1 || Q > CSA2_MAX_QUERIES_PER_SEQ || B <= 0 || (int64_t)B * Q > INT32_MAX) return 0;
@@ -305,6 +337,34 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
   return launched(csa2::launch_index_pool(idx_codes, idx_scales, cap, len, B, pool, pool_len,
                                           pool_cap, q, nullptr, nullptr, w, H, k, topk, pool_scores_opt,
                                           ws, as_stream(stream)));
+}
+
+int csa2_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                          int32_t B, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                          const uint16_t* q, const float* w, int32_t H, float* pool_scores_opt, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (B < 0 || cap <= 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
+  if (pool_cap < 0 || pool_cap > CSA2_MAX_POOL) return CSA2_ERR_SHAPE;
+  if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !len || !pool || !pool_len || !q || !w) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  const size_t need = csa2_index_pool_workspace(B, pool_cap, 1);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_pool_score(idx_codes, idx_scales, cap, len, B, pool, pool_len, pool_cap, q,
+                                                nullptr, nullptr, w, H, pool_scores_opt, ws, as_stream(stream)));
+}
+
+int csa2_index_pool_select(int32_t B, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap, int32_t k,
+                           int32_t* topk, const float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || pool_cap < 0 || pool_cap > CSA2_MAX_POOL) return CSA2_ERR_SHAPE;
+  if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
+  if (B == 0) return CSA2_OK;
+  if (!pool || !pool_len || !topk) return CSA2_ERR_NULL;
+  const size_t need = csa2_index_pool_workspace(B, pool_cap, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_index_pool_select(B, pool, pool_len, pool_cap, k, topk, pool_scores_opt, ws,
+                                                 as_stream(stream)));
 }
 
 int csa2_index_pool_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,

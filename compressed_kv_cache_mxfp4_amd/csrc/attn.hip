@@ -118,20 +118,36 @@ __device__ __forceinline__ uint4 rope_bf16x8(uint4 v, int d0, int64_t pos) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Eight E2M1 values of one code dword -> bf16x8 (exact).
+// Eight E2M1 values of one code dword -> bf16x8 (exact).  E4M3 scales: the
+// scaled convert honours only the exponent of its fp32 scale, so it is given
+// the scale's power of two and the products are finished in fp32 by the
+// scale's significand (1 + m/8, or the subnormal code's m).  An E2M1 value
+// (at most 2 significant bits) times an E4M3 scale (at most 4) has at most 5
+// significant bits, so each fp32 product is a bf16 value and its upper half
+// is the bf16 encoding: the pairs are packed by a byte permute, no rounding.
 template <int FMT>
 __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, uint32_t sbyte) {
   if (FMT == 0) {
     return fp4x8_to_bf16(codes, e8m0_operand(sbyte));
   } else {
-    const float s = e4m3_value(sbyte);
-    float f[8];
-    fp4x8_to_f32(codes, f);
+    const float s = e4m3_value(sbyte);  // a normal fp32 (>= 2^-9) or NaN
+    // |s| = 2^E * sig with sig in [1, 2): the convert takes the power of two
+    // 2^E; sig carries the sign (and NaN for the NaN codes)
+    const uint32_t su = __float_as_uint(s);
+    const float sig = s != s ? s : __uint_as_float((su & 0x807FFFFFu) | 0x3F800000u);
+    const float sa = __uint_as_float(su & 0x7F800000u);
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sa, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sa, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sa, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sa, 3);
+    auto hi2 = [](float a, float b) {  // bf16(b) << 16 | bf16(a), both exact
+      return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    };
     uint4 u;
-    u.x = f32_to_bf16_bits(f[0] * s) | (f32_to_bf16_bits(f[1] * s) << 16);
-    u.y = f32_to_bf16_bits(f[2] * s) | (f32_to_bf16_bits(f[3] * s) << 16);
-    u.z = f32_to_bf16_bits(f[4] * s) | (f32_to_bf16_bits(f[5] * s) << 16);
-    u.w = f32_to_bf16_bits(f[6] * s) | (f32_to_bf16_bits(f[7] * s) << 16);
+    u.x = hi2(p0[0] * sig, p0[1] * sig);
+    u.y = hi2(p1[0] * sig, p1[1] * sig);
+    u.z = hi2(p2[0] * sig, p2[1] * sig);
+    u.w = hi2(p3[0] * sig, p3[1] * sig);
     return __builtin_bit_cast(bf16x8, u);
   }
 }

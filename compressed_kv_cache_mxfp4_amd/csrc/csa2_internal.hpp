@@ -63,7 +63,28 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       PageMap pm = PageMap{nullptr, 0, 0, 0}, int32_t* topk_rows = nullptr,
                       int32_t* pool_rows = nullptr);
 
+// The two phases of launch_index_full: scoring (scores and block maxima into
+// the workspace, or the scores into scores_opt) and the selections from them.
+int launch_index_full_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
+                            const uint8_t* q4s, const float* w, int H, int block, float* scores_opt, void* ws,
+                            hipStream_t st, int qps = 1, PageMap pm = PageMap{nullptr, 0, 0, 0});
+int launch_index_full_select(int64_t cap, const int32_t* len, int B, int k, int block, int n_blocks,
+                             int32_t* topk, int32_t* pool, int32_t* pool_len, const float* scores_opt, void* ws,
+                             hipStream_t st, int qps = 1, PageMap pm = PageMap{nullptr, 0, 0, 0},
+                             int32_t* topk_rows = nullptr, int32_t* pool_rows = nullptr);
+
 size_t index_pool_ws_bytes(int B, int pool_cap);
+
+// The two phases of launch_index_pool.
+int launch_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
+                            int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
+                            const float* w, int H, float* pool_scores_opt, void* ws, hipStream_t st,
+                            const int32_t* pool_rows = nullptr);
+int launch_index_pool_select(int B, const int32_t* pool, const int32_t* pool_len, int pool_cap, int k,
+                             int32_t* topk, const float* pool_scores_opt, void* ws, hipStream_t st,
+                             const int32_t* pool_rows = nullptr, int32_t* topk_rows = nullptr);
 
 int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
                       const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,

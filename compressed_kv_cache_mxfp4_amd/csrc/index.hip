@@ -953,12 +953,10 @@ static unsigned score_wgs(int64_t items, int B, int target_waves) {
   return (unsigned)(wgs > 0 ? wgs : 1);
 }
 
-int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
-                      const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
-                      const uint8_t* q4s, const float* w, int H, int k,
-                      int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
-                      float* scores_opt, void* ws, hipStream_t st, int qps, PageMap pm, int32_t* topk_rows,
-                      int32_t* pool_rows) {
+int launch_index_full_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
+                            const uint8_t* q4s, const float* w, int H, int block, float* scores_opt, void* ws,
+                            hipStream_t st, int qps, PageMap pm) {
   if (B == 0) return 0;
   const IndexFullWs l = index_full_ws_layout(B, cap, block);
   float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -969,7 +967,31 @@ int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
   if (cap > 0)
     launch_score<false>(MT, per_seq, B, st, idx_codes, idx_scales, cap, len, nullptr, nullptr, 0, q, q4c,
                         q4s, w, H, scores, cap, bmax, nbk, qps, pm, pm.table ? 0 : cap);
-  if (hipGetLastError() != hipSuccess) return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const uint16_t* q, const uint8_t* q4c,
+                      const uint8_t* q4s, const float* w, int H, int k,
+                      int block, int n_blocks, int32_t* topk, int32_t* pool, int32_t* pool_len,
+                      float* scores_opt, void* ws, hipStream_t st, int qps, PageMap pm, int32_t* topk_rows,
+                      int32_t* pool_rows) {
+  if (B == 0) return 0;
+  if (launch_index_full_score(idx_codes, idx_scales, cap, len, B, q, q4c, q4s, w, H, block, scores_opt, ws, st,
+                              qps, pm) != 0)
+    return -1;
+  return launch_index_full_select(cap, len, B, k, block, n_blocks, topk, pool, pool_len, scores_opt, ws, st, qps,
+                                  pm, topk_rows, pool_rows);
+}
+
+int launch_index_full_select(int64_t cap, const int32_t* len, int B, int k, int block, int n_blocks,
+                             int32_t* topk, int32_t* pool, int32_t* pool_len, const float* scores_opt, void* ws,
+                             hipStream_t st, int qps, PageMap pm, int32_t* topk_rows, int32_t* pool_rows) {
+  if (B == 0) return 0;
+  const IndexFullWs l = index_full_ws_layout(B, cap, block);
+  const float* scores = scores_opt ? scores_opt : reinterpret_cast<const float*>((char*)ws + l.scores_off);
+  const float* bmax = reinterpret_cast<const float*>((char*)ws + l.bmax_off);
+  const int64_t nbk = (cap + block - 1) / block;
   const bool kbig = k > 512;
   // the pool and the top-k as two workgroups per sequence when there is a pool
   const bool split = n_blocks > 0;
@@ -1009,12 +1031,11 @@ static IndexPoolWs index_pool_ws_layout(int B, int pool_cap) {
 
 size_t index_pool_ws_bytes(int B, int pool_cap) { return index_pool_ws_layout(B, pool_cap).total; }
 
-int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
-                      const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
-                      int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
-                      const float* w, int H, int k,
-                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st,
-                      const int32_t* pool_rows, int32_t* topk_rows) {
+int launch_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                            const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
+                            int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
+                            const float* w, int H, float* pool_scores_opt, void* ws, hipStream_t st,
+                            const int32_t* pool_rows) {
   if (B == 0) return 0;
   const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
   float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -1027,7 +1048,30 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
     launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, pool_rows ? nullptr : len,
                        pool_rows ? pool_rows : pool, pool_len, pool_cap, q, q4c, q4s, w, H, ps, pool_cap, gmax, ngs,
                        1, PageMap{nullptr, 0, 0, 0}, pool_rows ? 0 : cap);
-  if (hipGetLastError() != hipSuccess) return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap,
+                      const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
+                      int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
+                      const float* w, int H, int k,
+                      int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st,
+                      const int32_t* pool_rows, int32_t* topk_rows) {
+  if (B == 0) return 0;
+  if (launch_index_pool_score(idx_codes, idx_scales, cap, len, B, pool, pool_len, pool_cap, q, q4c, q4s, w, H,
+                              pool_scores_opt, ws, st, pool_rows) != 0)
+    return -1;
+  return launch_index_pool_select(B, pool, pool_len, pool_cap, k, topk, pool_scores_opt, ws, st, pool_rows,
+                                  topk_rows);
+}
+
+int launch_index_pool_select(int B, const int32_t* pool, const int32_t* pool_len, int pool_cap, int k,
+                             int32_t* topk, const float* pool_scores_opt, void* ws, hipStream_t st,
+                             const int32_t* pool_rows, int32_t* topk_rows) {
+  if (B == 0) return 0;
+  const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
+  const float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<const float*>((char*)ws + l.scores_off);
+  const float* gmax = reinterpret_cast<const float*>((char*)ws + l.gmax_off);
   // keys per thread: groups (<= 2048 -> 2), candidate positions (8 per selected group)
   if (k <= 512)
     select_pool_kernel<1024, 2, 4><<<B, 1024, 0, st>>>(ps, gmax, pool, pool_len, pool_cap, k, topk, pool_rows,

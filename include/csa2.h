@@ -246,6 +246,29 @@ int csa2_index_full(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                     size_t ws_bytes, void* stream);
 
 /*
+ * csa2_index_full_score / csa2_index_full_select -- the two phases of
+ * csa2_index_full as separate calls, for callers that want the scores alone,
+ * or that select from scores scored elsewhere (e.g. each GPU scoring its own
+ * share of a long sequence), or that time the phases apart.  The pages' "one
+ * scoring pass feeds both selections" [GP 3.3] is the pair called in order
+ * on one workspace; together they launch exactly the kernels of
+ * csa2_index_full and give bit-identical results.
+ *   csa2_index_full_score: arguments as csa2_index_full (no k, n_blocks or
+ *     outputs); writes every visible entry's score (to scores_opt when given,
+ *     else into ws) and the maximum of every 8-entry block (into ws).
+ *   csa2_index_full_select: the position top-k and the block pool of
+ *     csa2_index_full from those; scores_opt must be the pointer the scoring
+ *     call was given (or NULL if it had none), ws the same workspace
+ *     (csa2_index_full_workspace bytes) holding the block maxima.
+ */
+int csa2_index_full_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                          int32_t B, const uint16_t* q, const float* w, int32_t H, int32_t block, float* scores_opt,
+                          void* ws, size_t ws_bytes, void* stream);
+int csa2_index_full_select(int64_t cap, const int32_t* len, int32_t B, int32_t k, int32_t block, int32_t n_blocks,
+                           int32_t* topk, int32_t* pool, int32_t* pool_len, const float* scores_opt, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * csa2_index_pool -- Reindex mode: a layer's own indexer query rescored over
  * the shared candidate pool only, then its own top-k [SY Figure 5 (right);
  * GP 3.3; SY CSA2 Figure 4 (Reindex)].  Same score formula as index_full.
@@ -271,6 +294,21 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                     const int32_t* pool_len, int32_t pool_cap, const uint16_t* q,
                     const float* w, int32_t H, int32_t k, int32_t* topk,
                     float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_pool_score / csa2_index_pool_select -- the two phases of
+ * csa2_index_pool as separate calls (as for csa2_index_full_score/_select):
+ * the pool rescoring (pool scores to pool_scores_opt when given, else into
+ * ws, and the maxima of groups of 8 consecutive pool entries into ws), then
+ * the layer's top-k from them.  The select call takes the same pool,
+ * pool_len, pool_scores_opt and workspace.
+ */
+int csa2_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                          int32_t B, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                          const uint16_t* q, const float* w, int32_t H, float* pool_scores_opt, void* ws,
+                          size_t ws_bytes, void* stream);
+int csa2_index_pool_select(int32_t B, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap, int32_t k,
+                           int32_t* topk, const float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_full_mq -- the Full-mode indexer for Q queries of each sequence

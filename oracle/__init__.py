@@ -57,6 +57,7 @@ def _load():
     lib.oracle_fp8_record_decode.argtypes = [P, P, i64, P]
     lib.oracle_window_write.argtypes = [P, i64, i32, P, f32, i32, P, i32, P, P, P, P]
     lib.oracle_num_threads.restype = i32
+    lib.oracle_set_threads.argtypes = [i32]
     _lib = lib
     return lib
 
@@ -71,6 +72,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 # --------------------------------------------------------------------- formats

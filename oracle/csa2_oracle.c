@@ -582,3 +582,14 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads of later calls (timing of the oracle on
+ * one core beside all cores; no effect on any result). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

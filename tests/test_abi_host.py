@@ -246,6 +246,38 @@ def test_attention_noalloc_validation(lib):
     assert lib.csa2_attn_workspace(256, 64, 2048, 128) > (32 << 20)
 
 
+def test_index_phase_validation(lib):
+    # the score / select halves of the indexer calls validate like the fused calls
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    fs = lib.csa2_index_full_score
+    fs.argtypes = [P, P, i64, P, i32, P, P, i32, i32, P, P, sz, P]
+    fsel = lib.csa2_index_full_select
+    fsel.argtypes = [i64, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    ps = lib.csa2_index_pool_score
+    ps.argtypes = [P, P, i64, P, i32, P, P, i32, P, P, i32, P, P, sz, P]
+    psel = lib.csa2_index_pool_select
+    psel.argtypes = [i32, P, P, i32, i32, P, P, P, sz, P]
+    big = 1 << 40
+    assert fs(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 12, 8, None, FAKE, big, None) == ERR_UNSUP   # heads
+    assert fs(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 64, 4, None, FAKE, big, None) == ERR_UNSUP   # block
+    assert fs(FAKE, FAKE, (1 << 20) + 1, FAKE, 2, FAKE, FAKE, 64, 8, None, FAKE, big, None) == ERR_SHAPE
+    assert fs(None, FAKE, 4096, FAKE, 2, FAKE, FAKE, 64, 8, None, FAKE, big, None) == ERR_NULL
+    assert fs(FAKE_ODD, FAKE, 4096, FAKE, 2, FAKE, FAKE, 64, 8, None, FAKE, big, None) == ERR_ALIGN
+    assert fs(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 64, 8, None, FAKE, 64, None) == ERR_WS
+    assert fs(FAKE, FAKE, 4096, FAKE, 0, FAKE, FAKE, 64, 8, None, None, 0, None) == CSA2_OK      # empty batch
+    assert fsel(4096, FAKE, 2, 0, 8, 2048, FAKE, FAKE, FAKE, None, FAKE, big, None) == ERR_SHAPE  # k
+    assert fsel(4096, FAKE, 2, 512, 8, 4096, FAKE, FAKE, FAKE, None, FAKE, big, None) == ERR_SHAPE  # n_blocks
+    assert fsel(4096, FAKE, 2, 512, 8, 2048, FAKE, None, FAKE, None, FAKE, big, None) == ERR_NULL  # pool
+    assert fsel(4096, FAKE, 2, 512, 8, 2048, FAKE, FAKE, FAKE, None, FAKE, 64, None) == ERR_WS
+    assert ps(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 20000, FAKE, FAKE, 64, None, FAKE, big, None) == ERR_SHAPE
+    assert ps(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 12, None, FAKE, big, None) == ERR_UNSUP
+    assert ps(FAKE, FAKE, 4096, FAKE, 2, None, FAKE, 16384, FAKE, FAKE, 64, None, FAKE, big, None) == ERR_NULL
+    assert ps(FAKE, FAKE, 4096, FAKE, 2, FAKE, FAKE, 16384, FAKE, FAKE, 64, None, FAKE, 16, None) == ERR_WS
+    assert psel(2, FAKE, FAKE, 16384, 4096, FAKE, None, FAKE, big, None) == ERR_SHAPE             # k
+    assert psel(2, FAKE, None, 16384, 512, FAKE, None, FAKE, big, None) == ERR_NULL
+    assert psel(2, FAKE, FAKE, 16384, 512, FAKE, None, FAKE, 16, None) == ERR_WS
+
+
 def test_window_write_validation(lib):
     i32 = ctypes.c_int32
     f = lib.csa2_window_write

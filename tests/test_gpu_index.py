@@ -391,3 +391,45 @@ def test_index_full_mq_fp4_query_equals_one_query_calls(B, Q, H):
         assert pool_len[b, i] == bpl == rpl and np.array_equal(pool[b, i], bp)
         certified += certify_topk(topk[b, i], rt, rs, k)
     say(f"  certified near-ties against the oracle: {certified}")
+
+
+# ------------------------------------------------ the two phases of each call
+def test_index_phases_equal_fused_calls():
+    # scoring then selection as separate calls gives the fused calls' results
+    # bit for bit, with the scores in the workspace or in a caller buffer
+    say("index phases: score + select against the fused calls")
+    B, cap, k, nb = 3, 20000, 512, 512
+    wl = syn.small("ph", 77, B=B, cap=cap, H_idx=64, k=k, n_blocks=nb, n_reindex=1)
+    cache = build_gpu_cache(wl, 0)
+    lens = [cap, cap - 7, 7001]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ic, isc = cache["idx_codes"], cache["idx_scales"]
+    q, w = syn.index_query(wl, 0, DEV), syn.index_weights(wl, 0, DEV)
+    t0, p0, pl0, s0 = K.index_full(ic, isc, lt, q, w, k=k, n_blocks=nb, return_scores=True)
+    L = K.lib()
+    nws = L.csa2_index_full_workspace(B, cap, k, 8, nb)
+    ws1 = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    K.index_full_score(ic, isc, lt, q, w, ws1)
+    t1, p1, pl1 = K.index_full_select(cap, lt, ws1, k=k, n_blocks=nb)
+    ws2 = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    s2 = torch.empty(B, cap, dtype=torch.float32, device=DEV)
+    K.index_full_score(ic, isc, lt, q, w, ws2, scores=s2)
+    t2, p2, pl2 = K.index_full_select(cap, lt, ws2, k=k, n_blocks=nb, scores=s2)
+    q1, w1 = syn.index_query(wl, 1, DEV), syn.index_weights(wl, 1, DEV)
+    tk0, ps0 = K.index_pool(ic, isc, lt, p0, pl0, q1, w1, k=k, return_scores=True)
+    pws = torch.empty(L.csa2_index_pool_workspace(B, nb * 8, k), dtype=torch.uint8, device=DEV)
+    K.index_pool_score(ic, isc, lt, p0, pl0, q1, w1, pws)
+    tk1 = K.index_pool_select(p0, pl0, pws, k=k)
+    pws2 = torch.empty_like(pws)
+    ps2 = torch.empty(B, nb * 8, dtype=torch.float32, device=DEV)
+    K.index_pool_score(ic, isc, lt, p0, pl0, q1, w1, pws2, pool_scores=ps2)
+    tk2 = K.index_pool_select(p0, pl0, pws2, k=k, pool_scores=ps2)
+    torch.cuda.synchronize()
+    for t, p, pl in ((t1, p1, pl1), (t2, p2, pl2)):
+        assert torch.equal(t, t0) and torch.equal(p, p0) and torch.equal(pl, pl0)
+    for b, Lb in enumerate(lens):
+        assert torch.equal(s2[b, :Lb].view(torch.int32), s0[b, :Lb].view(torch.int32))
+    assert torch.equal(tk1, tk0) and torch.equal(tk2, tk0)
+    n = pl0.cpu().numpy()
+    for b in range(B):
+        assert torch.equal(ps2[b, : n[b]].view(torch.int32), ps0[b, : n[b]].view(torch.int32))
