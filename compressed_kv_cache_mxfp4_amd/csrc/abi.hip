@@ -131,8 +131,7 @@ int csa2_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, in
   if (!latent || (m > 1 && !gate) || !w_idx || !main_codes || !main_scales || !idx_codes || !idx_scales)
     return CSA2_ERR_NULL;
   if (!aligned16(latent) || (m > 1 && !aligned16(gate)) || !aligned16(main_codes) ||
-      !aligned16(idx_codes) || (reinterpret_cast<uintptr_t>(w_idx) & 3u) ||
-      (reinterpret_cast<uintptr_t>(rope_pos) & 7u))
+      !aligned16(idx_codes) || !aligned16(w_idx) || (reinterpret_cast<uintptr_t>(rope_pos) & 7u))
     return CSA2_ERR_ALIGN;
   return launched(csa2::launch_cache_write(latent, gate, T, m, gamma, eps, w_idx, main_fmt, rope_pos,
                                            main_codes, main_scales, idx_codes, idx_scales,

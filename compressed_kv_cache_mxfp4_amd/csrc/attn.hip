@@ -41,7 +41,7 @@
 namespace csa2 {
 
 constexpr int kChunk = 128;            // row slots per workgroup at most 8 waves (sizes the workspace)
-constexpr int kHLd = 264;              // R half-row stride in bf16 (256 + pad)
+constexpr int kHLd = 256;              // R half-row stride in bf16 (no pad: rows are swizzled)
 constexpr int kQLd = 520;              // query row stride in bf16 (512 + pad)
 // s_getreg operand for HW_REG_XCC_ID (register 20, bits 3:0): the XCD a wave runs on
 constexpr int kHwRegXccId = (3 << 11) | 20;
@@ -50,6 +50,38 @@ constexpr int kHwRegXccId = (3 << 11) | 20;
 constexpr int kMaxAttnGroups = 65536;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// MFMA operand type of the split kernel: bf16, or fp16 for E4M3-scaled main
+// rows (an E2M1 value times an E4M3 scale is exact in fp16 as in bf16, and
+// fp16 lets the scale's significand be applied two values per instruction).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool F16>
+struct OpT {
+  using v8 = bf16x8;
+};
+template <>
+struct OpT<true> {
+  using v8 = f16x8;
+};
+
+template <bool F16>
+__device__ __forceinline__ floatx4 mfma16(typename OpT<F16>::v8 a, typename OpT<F16>::v8 b, floatx4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Staged R half-rows are 512 B; 16-byte unit u of row r sits at unit
+// u ^ rswz(r).  Both LDS access patterns are then free of bank conflicts
+// (32 banks of 4 B): the staging writes (8 lanes write unit u of 8
+// consecutive rows: rswz takes 8 distinct values there) and the transposed
+// reads of P.R (16 lanes read units 2t, 2t+1 of 4 rows r0..r0+3, r0 a
+// multiple of 4: 2(t ^ (r & 3)) spreads them over 8 distinct bank groups).
+__device__ __forceinline__ int rswz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// bf16 index of 16-byte unit u of staged row r.
+__device__ __forceinline__ int runit(int r, int u) { return r * kHLd + ((u ^ rswz(r)) << 3); }
 
 // Arrival of a workgroup at its group's completion counter, after it has
 // stored its partial; true in every thread of the workgroup that arrives last
@@ -99,6 +131,8 @@ struct AttnSmem {
   __align__(16) float red_m[WAVES][16];
   __align__(16) float red_l[WAVES][16];
   float red_v[WAVES];  // per-wave bound of |dequantised value| (partial scaling)
+  int qk[16];          // fp16 operands: the query of head h is staged times 2^-qk[h]
+  uint2 e4lut[256];    // fp16 operands: (power of two, significand pair) of each E4M3 scale byte
   int last;  // this workgroup merges its (sequence, head group)
 };
 
@@ -113,7 +147,7 @@ __device__ __forceinline__ uint4 rope_bf16x8(uint4 v, int d0, int64_t pos) {
     float c, sn;
     rope_cos_sin(pos, (d0 - 448) / 2 + i, c, sn);
     rope_pair<false>(a, b, c, sn);
-    w[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    w[i] = pack_bf16x2(a, b);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -150,6 +184,75 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, uint32_t sbyte) {
     u.w = hi2(p3[0] * sig, p3[1] * sig);
     return __builtin_bit_cast(bf16x8, u);
   }
+}
+
+// Eight E2M1 values of one code dword with an E4M3 scale byte -> fp16x8
+// (exact): the scaled convert takes the scale's power of two, v_pk_mul_f16
+// its significand, two values per instruction.
+struct E4m3F16 {
+  float pow2;  // the scale's power of two (the scaled convert's operand)
+  f16x2 sig;   // its significand (sign, NaN) twice, for v_pk_mul_f16
+};
+
+__device__ __forceinline__ E4m3F16 e4m3_f16_scale(uint32_t sbyte) {
+  const float s = e4m3_value(sbyte);  // a normal fp32 (>= 2^-9) or NaN
+  const uint32_t su = __float_as_uint(s);
+  const _Float16 h = (_Float16)(s != s ? s : __uint_as_float((su & 0x807FFFFFu) | 0x3F800000u));
+  return E4m3F16{__uint_as_float(su & 0x7F800000u), f16x2{h, h}};
+}
+
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, const E4m3F16& sc) {
+  const float sa = sc.pow2;
+  const f16x2 sg = sc.sig;
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sa, 0) * sg;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sa, 1) * sg;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sa, 2) * sg;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sa, 3) * sg;
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// bf16x8 (8 dims of one query head) -> fp16x8 times 2^-k (exact for
+// magnitudes from 2^-14; smaller ones are rounded to fp16's subnormal grid).
+__device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 v, int k) {
+  const float m = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, k in [0, 113]
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_f16x2(bf16_bits_to_f32(wd[i] & 0xFFFFu) * m, bf16_bits_to_f32(wd[i] >> 16) * m);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Exponent shift of one query head for fp16 operands: the smallest k >= 0
+// with max|q| * 2^-k < 2^15 (the wave holds one head: 64 lanes x 8 dims).
+__device__ __forceinline__ int head_shift_f16(uint4 v) {
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(wd[i] >> 16))));
+  // 64-lane max without LDS: DPP within rows of 16, then the row swaps
+  auto dpp = [](float v, auto ctrl) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), decltype(ctrl)::value,
+                                                                 0xf, 0xf, true));
+  };
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x140>{}));  // row_mirror
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;  // zero, inf or NaN: no shift
+  int e;
+  (void)frexpf(m, &e);  // m < 2^e
+  return e > 15 ? e - 15 : 0;
 }
 
 struct RowFetch {
@@ -291,14 +394,28 @@ __device__ __forceinline__ bf16x8 row_step(const RowFetch& f, int ks) {
   return dequant8<FMT>(cwd, sbyte);
 }
 
+// The same step as fp16 (E4M3 scales); K steps 2j and 2j+1 share scale
+// byte j, whose decoded form the caller reads once from the workgroup's
+// 256-entry table (row_scale_byte gives the byte).
+__device__ __forceinline__ uint32_t row_scale_byte(const RowFetch& f, int ks) {
+  return (f.s[ks >> 3] >> (8 * ((ks >> 1) & 3))) & 0xFFu;
+}
+
+__device__ __forceinline__ f16x8 row_step_f16(const RowFetch& f, int ks, const E4m3F16& sc) {
+  const uint4 c4 = f.c[ks >> 2];
+  const uint32_t cwd = (ks & 3) == 0 ? c4.x : ((ks & 3) == 1 ? c4.y : ((ks & 3) == 2 ? c4.z : c4.w));
+  return dequant8_f16(cwd, sc);
+}
+
 // O(16 heads x the wave's 16-dim tiles of one R half) += P . R_half.  Wave w
 // takes tiles w and w + WAVES (16 tiles per half); K steps of 32 rows.  The
 // LDS reads of KB K steps are issued before their products (all of them with
 // one workgroup per CU; two at a time at 8 waves, where registers are
 // scarcer), so a wave does not wait for LDS once per K step.  A wave without
 // a second tile reads and multiplies its first tile twice and drops O[1].
-template <int WAVES>
+template <int WAVES, bool F16>
 __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g, int n, floatx4 (&O)[2]) {
+  using V8 = typename OpT<F16>::v8;
   constexpr int NK = AttnSmem<WAVES>::kRows / 32;
   constexpr int LD = AttnSmem<WAVES>::kPLd;
   constexpr int KB = AttnSmem<WAVES>::kQOwn ? NK : 2;
@@ -307,20 +424,21 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
   const int t1 = w + WAVES < 16 ? w + WAVES : w;
 #pragma unroll
   for (int k0 = 0; k0 < NK; k0 += KB) {
-    bf16x8 pa[KB];
+    V8 pa[KB];
     shortx4 lo[2][KB], hi[2][KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) pa[j] = *reinterpret_cast<const bf16x8*>(&sm.P[n * LD + 32 * (k0 + j) + 8 * g]);
+    for (int j = 0; j < KB; ++j) pa[j] = *reinterpret_cast<const V8*>(&sm.P[n * LD + 32 * (k0 + j) + 8 * g]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int col = 16 * (nt ? t1 : w) + 4 * ta;
+        // 8 bytes at dims 16*tile + 4*ta: unit 2*tile + ta/2, half ta&1
+        const int u = 2 * (nt ? t1 : w) + (ta >> 1), hb = 4 * (ta & 1);
         const int r0 = 32 * (k0 + j) + 8 * g + tj;
         lo[nt][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(&sm.R[r0 * kHLd + col]));
+            (__attribute__((address_space(3))) shortx4*)(&sm.R[runit(r0, u) + hb]));
         hi[nt][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(&sm.R[(r0 + 4) * kHLd + col]));
+            (__attribute__((address_space(3))) shortx4*)(&sm.R[runit(r0 + 4, u) + hb]));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
@@ -331,7 +449,7 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
         shortx8 bv;
         bv[0] = lo[nt][j][0]; bv[1] = lo[nt][j][1]; bv[2] = lo[nt][j][2]; bv[3] = lo[nt][j][3];
         bv[4] = hi[nt][j][0]; bv[5] = hi[nt][j][1]; bv[6] = hi[nt][j][2]; bv[7] = hi[nt][j][3];
-        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j], __builtin_bit_cast(bf16x8, bv), O[nt], 0, 0, 0);
+        O[nt] = mfma16<F16>(pa[j], __builtin_bit_cast(V8, bv), O[nt]);
       }
     }
   }
@@ -431,7 +549,7 @@ __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const 
   uint32_t o8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    o8[j] = f32_to_bf16_bits(acc[2 * j] * inv) | (f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+    o8[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
   uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
   op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
   op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
@@ -454,6 +572,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
+  // fp16 operands for E4M3-scaled main rows (FP8 window records stay bf16)
+  constexpr bool F16 = FMT == 1 && !WF8;
+  using V8 = typename OpT<F16>::v8;
   static_assert(Smem::kQOwn || 16 * kQLd <= kRows * kHLd, "query tile must fit in the R buffer");
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   // every kernel argument in SGPRs up front: one batch of argument loads and
@@ -510,6 +631,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   asm volatile("" ::"v"(praw), "v"(Lraw), "v"(SLraw), "v"(qpos));
   const int32_t pidx = slot < k ? praw : -1;
   if (!valid) return;
+  if constexpr (F16) {
+    // decoded E4M3 scale bytes, one table entry per byte value (built while
+    // the loads above are in flight; read after the query barrier)
+    if (tid < 256) {
+      const E4m3F16 e = e4m3_f16_scale((uint32_t)tid);
+      sm.e4lut[tid] = make_uint2(__float_as_uint(e.pow2), __builtin_bit_cast(uint32_t, e.sig));
+    }
+  }
   int64_t L = len ? Lraw : cap;  // no lengths: absolute row ids below cap
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int SL = swa_len ? SLraw : 0;
@@ -530,6 +659,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     if ((tid & 63) >= 56) qv0 = rope_bf16x8(qv0, 8 * (tid & 63), qpos);
     if (((tid + kThreads) & 63) >= 56) qv1 = rope_bf16x8(qv1, 8 * ((tid + kThreads) & 63), qpos);
   }
+  if constexpr (F16) {
+    // fp16 query: each wave holds whole heads (qv0: head tid/64; qv1: head
+    // (tid + kThreads)/64, for whole waves), scaled by 2^-k into fp16 range;
+    // the logits take 2^k back
+    const int k0 = head_shift_f16(qv0);
+    qv0 = bf16x8_to_f16_scaled(qv0, k0);
+    if (lane == 0) sm.qk[tid >> 6] = k0;
+    if (tid + kThreads < 1024) {  // wave-uniform
+      const int k1 = head_shift_f16(qv1);
+      qv1 = bf16x8_to_f16_scaled(qv1, k1);
+      if (lane == 0) sm.qk[(tid + kThreads) >> 6] = k1;
+    }
+  }
   *reinterpret_cast<uint4*>(&Q[(tid >> 6) * kQLd + 8 * (tid & 63)]) = qv0;
   if (tid + kThreads < 1024) {
     const int e = tid + kThreads;
@@ -538,49 +680,61 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   __syncthreads();
 
   // ---- logits of the wave's 16 rows (every row dequantised once, kept for P.R)
+  // staged row of this lane and the units of its K steps in each half-row:
+  // K step ks (< 8) is dims 64g+8ks (unit 8g+ks); K step 8+ks is dims
+  // 256+64g+8ks, or for an FP8 window record 256+48g+8ks (ks < 6) and
+  // 448+16g+8(ks-6) (units 6g+ks and 24+2g+ks-6 of the second half-row)
+  const int rr = 16 * w + n;
+  auto h0unit = [&](int ks) -> int { return 8 * g + ks; };
+  auto h1unit = [&](int ks) -> int {
+    if (wwin) return ks < 6 ? 6 * g + ks : 24 + 2 * g + (ks - 6);
+    return 8 * g + ks;
+  };
   floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 ra[16];
+  V8 ra[16];
   // query fragments of kQB K steps are read before their products (fewer at
   // 8 waves, where four waves share a SIMD and registers are scarcer)
   constexpr int kQB = Smem::kQOwn ? 8 : 4;
 #pragma unroll
   for (int kb = 0; kb < 16; kb += kQB) {
-    bf16x8 qf[kQB];
+    V8 qf[kQB];
 #pragma unroll
     for (int j = 0; j < kQB; ++j) {
       const int dq = wwin ? step_dim_w8(kb + j, g) : step_dim(kb + j, g);
-      qf[j] = *reinterpret_cast<const bf16x8*>(&Q[n * kQLd + dq]);
+      qf[j] = *reinterpret_cast<const V8*>(&Q[n * kQLd + dq]);
+    }
+    uint2 lt[kQB / 2];  // fp16 path: decoded scales of the batch's pairs of K steps
+    if constexpr (F16) {
+#pragma unroll
+      for (int j = 0; j < kQB / 2; ++j) lt[j] = sm.e4lut[row_scale_byte(row, kb + 2 * j)];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
     for (int j = 0; j < kQB; ++j) {
-      if constexpr (WF8)
+      if constexpr (F16) {
+        const E4m3F16 sc16{__uint_as_float(lt[j >> 1].x), __builtin_bit_cast(f16x2, lt[j >> 1].y)};
+        ra[kb + j] = row_step_f16(row, kb + j, sc16);
+      } else if constexpr (WF8)
         ra[kb + j] = wwin ? row_step_w8(row, kb + j, g) : row_step<FMT>(row, kb + j);
       else
         ra[kb + j] = row_step<FMT>(row, kb + j);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[kb + j], qf[j], sacc, 0, 0, 0);
+      sacc = mfma16<F16>(ra[kb + j], qf[j], sacc);
     }
   }
-  uint16_t* rrow = &sm.R[(16 * w + n) * kHLd + 64 * g];
-  // offset (from rrow) of K step 8 + ks in the second half-row: dims
-  // 256+64g+8ks, or for an FP8 window record 256+48g+8ks (ks < 6) and
-  // 448+16g+8(ks-6)
-  auto h1off = [&](int ks) -> int {
-    if (wwin) return (ks < 6 ? 48 * g + 8 * ks : 192 + 16 * g + 8 * (ks - 6)) - 64 * g;
-    return 8 * ks;
-  };
   if (Smem::kQOwn) {
     // the first half of the wave's rows goes to LDS now (R is not shared with Q)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
+    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<V8*>(&sm.R[runit(rr, h0unit(ks))]) = ra[ks];
   }
-  // lane (g, n): rows 4g+i of the wave's tile, head n
+  // lane (g, n): rows 4g+i of the wave's tile, head n; fp16 queries were
+  // staged times 2^-qk[n]
   const uint64_t vmask = __ballot(row.ok != 0u);
+  const float lsc = F16 ? ldexpf(sm_scale, sm.qk[n]) : sm_scale;
   float x[4];
   float mw = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = ((vmask >> (4 * g + i)) & 1ull) ? sacc[i] * sm_scale : -INFINITY;
+    x[i] = ((vmask >> (4 * g + i)) & 1ull) ? sacc[i] * lsc : -INFINITY;
     mw = fmaxf(mw, x[i]);
   }
   mw = fmaxf(mw, shfl_xor_f(mw, 16));
@@ -616,21 +770,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
 #pragma unroll
   for (int v = 1; v < WAVES; ++v) M = fmaxf(M, sm.red_m[v][n]);
   float lw = 0.f;
-  uint32_t pb[4];
+  float pf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p = (M == -INFINITY) ? 0.0f : __expf(x[i] - M);
-    pb[i] = f32_to_bf16_bits(p);
-    lw += p;
+    pf[i] = (M == -INFINITY) ? 0.0f : __expf(x[i] - M);
+    lw += pf[i];
   }
   lw += shfl_xor_f(lw, 16);
   lw += shfl_xor_f(lw, 32);
   if (g == 0) sm.red_l[w][n] = lw;
   *reinterpret_cast<uint2*>(&sm.P[n * kPLd + 16 * w + 4 * g]) =
-      make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+      F16 ? make_uint2(pack_f16x2(pf[0], pf[1]), pack_f16x2(pf[2], pf[3]))
+          : make_uint2(pack_bf16x2(pf[0], pf[1]), pack_bf16x2(pf[2], pf[3]));
   if (!Smem::kQOwn) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + 8 * ks) = ra[ks];
+    for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<V8*>(&sm.R[runit(rr, h0unit(ks))]) = ra[ks];
   }
   __syncthreads();
 
@@ -655,7 +809,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     ml[((int64_t)b * H + 16 * hg + n) * S + sidx] =
         make_float4(M, l, __uint_as_float(my_xcc), __int_as_float(e_sc));
   }
-  float scl[4];  // 1 / sum for heads 4g+i
+  // 1 / sum for heads 4g+i (a reciprocal: the sum is >= 1 when positive);
+  // the partial's 2^-e is applied per value (2^-e alone can exceed fp32)
+  float scl[4];
   {
     float4 ls[WAVES];
 #pragma unroll
@@ -669,18 +825,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
       l4[3] += ls[v].w;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) scl[i] = l4[i] > 0.f ? 1.0f / l4[i] : 0.0f;
+    for (int i = 0; i < 4; ++i) scl[i] = l4[i] > 0.f ? __builtin_amdgcn_rcpf(l4[i]) : 0.0f;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (h == 1) {
       __syncthreads();  // every wave is done reading the first half
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<bf16x8*>(rrow + h1off(ks)) = ra[8 + ks];
+      for (int ks = 0; ks < 8; ++ks) *reinterpret_cast<V8*>(&sm.R[runit(rr, h1unit(ks))]) = ra[8 + ks];
       __syncthreads();
     }
     floatx4 O[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    pv_half<WAVES>(sm, w, g, n, O);
+    pv_half<WAVES, F16>(sm, w, g, n, O);
     // lane (g, n): heads 4g+i, dims 256h + 16*tile + n, tile = w + WAVES*nt
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -998,17 +1154,17 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
           lsum *= alpha;
         }
         const float mu = mref == -INFINITY ? 0.0f : mref;
-        uint32_t pb[8];
+        float pf[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           // x = -inf (masked row) gives 0; x - mu <= kTau
-          const float p = __builtin_amdgcn_exp2f(x[j] - mu);
-          lsum += p;
-          pb[j] = f32_to_bf16_bits(p);
+          pf[j] = __builtin_amdgcn_exp2f(x[j] - mu);
+          lsum += pf[j];
         }
         // slots 8g + 4t + i = rows 16t + 4g + i
         *reinterpret_cast<uint4*>(sm.P[s & 1] + (16 * wr + n) * kTPLd + 8 * g) =
-            make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
+            make_uint4(pack_bf16x2(pf[0], pf[1]), pack_bf16x2(pf[2], pf[3]), pack_bf16x2(pf[4], pf[5]),
+                       pack_bf16x2(pf[6], pf[7]));
         if (g == 0) sm.alpha[s & 1][16 * wr + n] = alpha;
       }
       __syncthreads();
@@ -1126,7 +1282,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     for (int ht = 0; ht < 4; ++ht) {
       hm[ht] = sm.mfin[16 * ht + n];
       hl[ht] = sm.lfin[16 * ht + n];
-      inv[ht] = hl[ht] > 0.f ? 1.0f / hl[ht] : 0.0f;
+      inv[ht] = hl[ht] > 0.f ? __builtin_amdgcn_rcpf(hl[ht]) : 0.0f;  // the sum is >= 1 when positive
     }
     if (S == 1) {
       if (q_pos && wr == 3) {
@@ -1153,8 +1309,8 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
           *reinterpret_cast<uint2*>(orow + 16 * dt) =
-              make_uint2(f32_to_bf16_bits(O[dt][ht][0] * inv[ht]) | (f32_to_bf16_bits(O[dt][ht][1] * inv[ht]) << 16),
-                         f32_to_bf16_bits(O[dt][ht][2] * inv[ht]) | (f32_to_bf16_bits(O[dt][ht][3] * inv[ht]) << 16));
+              make_uint2(pack_bf16x2(O[dt][ht][0] * inv[ht], O[dt][ht][1] * inv[ht]),
+                         pack_bf16x2(O[dt][ht][2] * inv[ht], O[dt][ht][3] * inv[ht]));
         if (lse && wr == 0 && g == 0)
           lse[(int64_t)b * H + 16 * ht + n] =
               hl[ht] > 0.f ? (hm[ht] + log2f(hl[ht])) * 0.6931471805599453f : -INFINITY;
@@ -1172,13 +1328,12 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       for (int ht = 0; ht < 4; ++ht) {
         const int64_t bh = (int64_t)b * H + 16 * ht + n;
         uint16_t* prow = part + (bh * S + sidx) * 512 + 128 * wr + 4 * g;
+        const float sc = inv[ht];  // the partial's 2^-e is applied per value (2^-e alone can exceed fp32)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          uint32_t h16[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h16[i] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[dt][ht][i] * inv[ht], -e_sc));
-          *reinterpret_cast<uint2*>(prow + 16 * dt) = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
-        }
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<uint2*>(prow + 16 * dt) =
+              make_uint2(pack_f16x2(ldexpf(O[dt][ht][0] * sc, -e_sc), ldexpf(O[dt][ht][1] * sc, -e_sc)),
+                         pack_f16x2(ldexpf(O[dt][ht][2] * sc, -e_sc), ldexpf(O[dt][ht][3] * sc, -e_sc)));
         if (wr == 0 && g == 0)
           ml[bh * S + sidx] = make_float4(hm[ht] == -INFINITY ? -INFINITY : hm[ht] * 0.6931471805599453f, hl[ht],
                                           __uint_as_float(my_xcc), __int_as_float(e_sc));

@@ -33,17 +33,17 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
   return b == 0 ? __uint_as_float(0x00400000u) : (b == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(b << 23));
 }
 
-// Exact value of an OCP E4M3FN byte (positive codes; sign honoured).
+// Exact value of an OCP E4M3FN byte (sign honoured), without branches (it
+// sits in the inner loops, where a divergent branch per call serialises):
+// exponent e >= 1 is 2^(e-7) (1 + m/8), the fp32 with the 7 low bits moved
+// into place and the exponent rebiased by 120; e = 0 is m * 2^-9; 0x7F is NaN.
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v;
-  if (e == 0)
-    v = (float)m * 0x1p-9f;
-  else if (e == 15 && m == 7)
-    v = __uint_as_float(0x7FC00000u);
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (b & 0x80u) ? -v : v;
+  const uint32_t mag = b & 0x7Fu;
+  const float nrm = __uint_as_float((mag << 20) + (120u << 23));
+  const float sub = (float)(mag & 7u) * 0x1p-9f;
+  float v = mag < 8u ? sub : nrm;
+  v = mag == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
 }
 
 // Two E2M1 values of byte `sel` of `codes` -> bf16 pair, times 2^(b-127).
@@ -139,11 +139,23 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
   return r;
 }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
-  return r >> 16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> bf16 pair (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two fp32 values -> fp16 pair, round to nearest even: one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 r;
+  r[0] = (_Float16)lo;
+  r[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 }  // namespace csa2

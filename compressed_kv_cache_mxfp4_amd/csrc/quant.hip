@@ -108,39 +108,61 @@ int launch_quantize(const float* x, int64_t rows, int dim, int group, int fmt, u
 }
 
 // ------------------------------------------------------------- cache write
-// Grid (entry tiles of 4, 4 column tiles of 32).  Every workgroup pools and
-// normalises its 4 entries (one wave per entry); the column-tile-0 workgroup
-// writes the main-KV FP4.  Each workgroup then projects onto its 32
-// indexer-K columns -- exactly one E8M0 group -- and quantises them.  (16
-// entries per workgroup, which reads each projection weight for 4x the
-// entries, measured slower on 4096-entry writes: the longer chain per
-// workgroup costs more than the weight traffic it saves.)
-constexpr int kWriteEntries = 4;   // entries per workgroup (one per wave)
-constexpr int kWriteColTiles = 4;
+// A workgroup of 8 waves takes 16 entries.  Phase 1: each wave pools and
+// normalises 2 entries (lane: 8 channels) into LDS and, in the workgroup of
+// column split 0, quantises the main entries.  Phase 2: the indexer-K
+// projection K[16 x 128] = Y[16 x 512] . W[512 x 128] on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation), with W read
+// once per workgroup straight into the B operands.  K step ks of lane group
+// g is channel 128g + ks, so one 16-byte LDS read gives a lane its A operand
+// (Y) of four consecutive steps.  The workgroup's columns form groups of
+// CW = 64 (or 32): lane n of a group loads the CW/16 adjacent columns
+// CW/16*n .. +CW/16-1 of one W row in one load, and MFMA j takes column
+// CW/16*n + j of each lane -- a permuted 16-column tile -- so one load feeds
+// CW/16 products.  The waves of a column group split its K steps, and their
+// partial products are summed through LDS.  Phase 3: E8M0 FP4 of the keys.
+// A workgroup covers all 128 columns when there are enough entries to fill
+// the chip (T = 8 column tiles of 16); for smaller writes the columns are
+// split over 8/T workgroups per entry tile (T >= 2: a workgroup holds whole
+// 32-column scale groups).
+constexpr int kWriteEntries = 16;  // entries per workgroup
+constexpr int kWriteWaves = 8;
+constexpr int kYLd = 516;          // LDS row stride of Y (fp32): conflict-free 16-byte reads
+constexpr int kKLd = 132;          // LDS row stride of the projected keys
 
-template <int FMT>
-__global__ __launch_bounds__(256) void cache_write_kernel(
+template <int FMT, int T>
+__global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ gate, int64_t n_entries,
     int m, const float* __restrict__ gamma, float eps, const float* __restrict__ w_idx,
     const int64_t* __restrict__ rope_pos, uint8_t* __restrict__ main_codes,
     uint8_t* __restrict__ main_scales, uint8_t* __restrict__ idx_codes,
     uint8_t* __restrict__ idx_scales) {
-  __shared__ __align__(16) float yT[512][kWriteEntries];  // latent after RMSNorm, channel-major
-  __shared__ float part[8][kWriteEntries][33];  // projection partial sums per channel slice
-  __shared__ float kb[kWriteEntries][33];       // projected keys of this column tile
+  // at least one whole E8M0 group (32 columns) of the indexer key per workgroup
+  static_assert(T == 2 || T == 4 || T == 8, "column tiles per workgroup");
+  constexpr int kCW = T == 2 ? 32 : 64;          // columns of a column group
+  constexpr int kJ = kCW / 16;                   // adjacent columns per lane (and MFMAs per K step)
+  constexpr int kGroups = 16 * T / kCW;          // column groups of the workgroup
+  constexpr int kWpg = kWriteWaves / kGroups;    // waves per column group
+  constexpr int kSteps = 128 / kWpg;             // K steps per wave
+  // normalised entries (phases 1-2), then the waves' partial products (the
+  // same LDS, after a barrier)
+  __shared__ __align__(16) float ybuf[kWriteEntries * kYLd];
+  static_assert(kWriteWaves * kJ * 256 <= kWriteEntries * kYLd, "partials fit in the entry buffer");
+  float (*yS)[kYLd] = reinterpret_cast<float (*)[kYLd]>(ybuf);
+  float (*part)[kJ * 256] = reinterpret_cast<float (*)[kJ * 256]>(ybuf);
+  __shared__ __align__(16) float kS[kWriteEntries][kKLd];          // projected keys (16 T columns)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ct = blockIdx.y;
+  const int cs = blockIdx.y;                 // column split: columns 16T*cs .. 16T*cs + 16T - 1
   const int64_t e0 = (int64_t)blockIdx.x * kWriteEntries;
-  constexpr int kEpw = kWriteEntries / 4;  // entries per wave
-  static_assert(kWriteEntries % 4 == 0, "whole entries per wave");
+  constexpr int kEpw = kWriteEntries / kWriteWaves;  // entries per wave
 
-  // ratio 1 and 2: every latent (and gate) load of the wave is issued before
-  // any arithmetic, so the wave's entries cost one memory round trip
+  // ---- phase 1.  Ratio 1 and 2: every latent (and gate) load of the wave
+  // is issued before any arithmetic, so its entries cost one memory round trip.
   uint4 xpre[kEpw][2], gpre[kEpw][2];
   if (m <= 2) {
 #pragma unroll
     for (int j = 0; j < kEpw; ++j) {
-      const int64_t e = e0 + wave + 4 * j;
+      const int64_t e = e0 + wave + kWriteWaves * j;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bool ok = e < n_entries && t < m;
@@ -151,13 +173,25 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
       }
     }
   }
+  // W of this wave's first K steps in flight during the pooling
+  typedef float wvec __attribute__((ext_vector_type(kJ)));
+  const int grp = wave / kWpg, kr = wave % kWpg;        // column group, K range
+  const int g = lane >> 4, n = lane & 15;
+  const int cbase = 16 * T * cs + kCW * grp;            // first column of the group
+  const int d = cbase + kJ * n;                         // this lane's first column
+  const int ks0 = kr * kSteps;                          // first K step of this wave
+  constexpr int kPre = kSteps < 8 ? kSteps : 8;         // W loads in flight
+  wvec wpre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) wpre[i] = *reinterpret_cast<const wvec*>(w_idx + (128 * g + ks0 + i) * 128 + d);
+
 #pragma unroll
   for (int j = 0; j < kEpw; ++j) {
-    const int ei = wave + 4 * j;
+    const int ei = wave + kWriteWaves * j;
     const int64_t e = e0 + ei;
     if (e >= n_entries) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = 0.0f;
+      for (int c = 0; c < 8; ++c) yS[ei][8 * lane + c] = 0.0f;
       continue;
     }
     float pooled[8];
@@ -222,18 +256,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     float y[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) y[c] = pooled[c] * r * (gamma ? gamma[8 * lane + c] : 1.0f);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) yT[8 * lane + c][ei] = y[c];
-    if (ct == 0) {
+    *reinterpret_cast<float4*>(&yS[ei][8 * lane]) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4*>(&yS[ei][8 * lane + 4]) = make_float4(y[4], y[5], y[6], y[7]);
+    if (cs == 0) {
       // compressed RoPE of the main entry: lanes 56..63 hold dims 448..511,
       // pairs (c, c+1) of the lane's 8 channels
       if (rope_pos && lane >= 56) {
         const int64_t pos = rope_pos[e];
 #pragma unroll
         for (int c = 0; c < 8; c += 2) {
-          float cs, sn;
-          rope_cos_sin(pos, 4 * (lane - 56) + c / 2, cs, sn);
-          rope_pair<false>(y[c], y[c + 1], cs, sn);
+          float cz, sn;
+          rope_cos_sin(pos, 4 * (lane - 56) + c / 2, cz, sn);
+          rope_pair<false>(y[c], y[c + 1], cz, sn);
         }
       }
       // main-KV FP4: a group of 16 channels spans two lanes
@@ -242,74 +276,76 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
       for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(y[c]));
       amax = fmaxf(amax, shfl_xor_f(amax, 1));
       const uint32_t b = scale_code<FMT>(amax);
-      const float s = scale_value<FMT>(b);
+      const float sv = scale_value<FMT>(b);
       uint32_t word = 0;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) word |= e2m1_code(y[c], s) << (4 * c);
+      for (int c = 0; c < 8; ++c) word |= e2m1_code(y[c], sv) << (4 * c);
       *reinterpret_cast<uint32_t*>(main_codes + e * 256 + 4 * lane) = word;
       if ((lane & 1) == 0) main_scales[e * 32 + lane / 2] = (uint8_t)b;
     }
   }
+  __syncthreads();
 
-  // projection k[e][d] = sum_c y[e][c] * W[c][d] for the 32 columns d of this
-  // tile: thread = (channel slice cs of 64 channels, column); its 64 weights
-  // are loaded at once (before the barrier), then 8 slice sums per entry are
-  // reduced through LDS.
-  const int cs = threadIdx.x >> 5, col = threadIdx.x & 31;
-  const int d = 32 * ct + col;
-  float wv[64];
+  // ---- phase 2: K steps ks0 .. ks0 + kSteps - 1 of column group `grp`.
+  // A: lane (g, n) holds Y[entry n][128g + ks]; MFMA j's B: W[128g + ks][d + j];
+  // its D: lane (g, n) holds K[entries 4g .. 4g+3][d + j].
+  floatx4 acc[kJ];
 #pragma unroll
-  for (int c = 0; c < 64; ++c) wv[c] = w_idx[(64 * cs + c) * 128 + d];
-  __syncthreads();
-  {
-    float acc[kWriteEntries];
+  for (int j = 0; j < kJ; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e2 = 0; e2 < kWriteEntries; ++e2) acc[e2] = 0.f;
+  for (int s4 = 0; s4 < kSteps; s4 += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(&yS[n][128 * g + ks0 + s4]);
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-    for (int c = 0; c < 64; ++c) {
-      const float4* yr = reinterpret_cast<const float4*>(&yT[64 * cs + c][0]);
+    for (int i = 0; i < 4; ++i) {
+      const int st = s4 + i;
+      const wvec bv = wpre[st % kPre];
+      if (st + kPre < kSteps)
+        wpre[st % kPre] = *reinterpret_cast<const wvec*>(w_idx + (128 * g + ks0 + st + kPre) * 128 + d);
 #pragma unroll
-      for (int q4 = 0; q4 < kWriteEntries / 4; ++q4) {
-        const float4 yv = yr[q4];
-        acc[4 * q4 + 0] += yv.x * wv[c];
-        acc[4 * q4 + 1] += yv.y * wv[c];
-        acc[4 * q4 + 2] += yv.z * wv[c];
-        acc[4 * q4 + 3] += yv.w * wv[c];
-      }
+      for (int j = 0; j < kJ; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[j], 0, 0, 0);
     }
-#pragma unroll
-    for (int e2 = 0; e2 < kWriteEntries; ++e2) part[cs][e2][col] = acc[e2];
   }
+  // partial products of the waves of each column group, summed into kS
+  // (column c - 16T*cs of this split): part[wave][256 j + 64 i + lane]
+  __syncthreads();  // every wave is done reading Y
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][256 * j + 64 * i + lane] = acc[j][i];
   __syncthreads();
-  for (int o = threadIdx.x; o < kWriteEntries * 32; o += 256) {
-    const int e2 = o >> 5, c2 = o & 31;
+  for (int o = threadIdx.x; o < kGroups * kJ * 256; o += 64 * kWriteWaves) {
+    const int gg = o / (kJ * 256), jl = o % (kJ * 256);
+    const int j = jl >> 8, i = (jl >> 6) & 3, ln = jl & 63;
     float v = 0.f;
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) v += part[s8][e2][c2];
-    kb[e2][c2] = v;
+    for (int r = 0; r < kWpg; ++r) v += part[gg * kWpg + r][jl];
+    kS[4 * (ln >> 4) + i][kCW * gg + kJ * (ln & 15) + j] = v;
   }
   __syncthreads();
 
-  // indexer-K FP4 of this column tile: thread = (entry, 8 consecutive dims)
-  if (threadIdx.x < 4 * kWriteEntries) {
-    const int ei = threadIdx.x >> 2, ch = threadIdx.x & 3;
+  // ---- phase 3: indexer-K FP4 (E8M0, groups of 32 columns): thread ->
+  // (entry, 8 consecutive columns of this split); 4 threads share a group
+  if ((int)threadIdx.x < kWriteEntries * 2 * T) {
+    const int ei = threadIdx.x / (2 * T), ch = threadIdx.x % (2 * T);
     const int64_t e = e0 + ei;
     float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = kb[ei][8 * ch + j];
+    for (int j = 0; j < 8; ++j) v[j] = kS[ei][8 * ch + j];
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
     amax = fmaxf(amax, shfl_xor_f(amax, 1));
     amax = fmaxf(amax, shfl_xor_f(amax, 2));
     const uint32_t b = scale_code_e8m0(amax);
-    const float s = e8m0_value(b);
+    const float sv = e8m0_value(b);
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], s) << (4 * j);
+    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], sv) << (4 * j);
     if (e < n_entries) {
-      *reinterpret_cast<uint32_t*>(idx_codes + e * 64 + 16 * ct + 4 * ch) = word;
-      if (ch == 0) idx_scales[e * 4 + ct] = (uint8_t)b;
+      const int col0 = 16 * T * cs + 8 * ch;  // first column of these 8
+      *reinterpret_cast<uint32_t*>(idx_codes + e * 64 + col0 / 2) = word;
+      if ((ch & 3) == 0) idx_scales[e * 4 + col0 / 32] = (uint8_t)b;
     }
   }
 }
@@ -320,14 +356,23 @@ int launch_cache_write(const uint16_t* latent, const uint16_t* gate, int64_t T, 
                        uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t st) {
   const int64_t n = T / m;
   if (n == 0) return 0;
-  const int64_t blocks = (n + kWriteEntries - 1) / kWriteEntries;
-  const dim3 grid((unsigned)blocks, kWriteColTiles);
-  if (main_fmt == 0)
-    cache_write_kernel<0><<<grid, 256, 0, st>>>(latent, gate, n, m, gamma, eps, w_idx, rope_pos,
-                                                main_codes, main_scales, idx_codes, idx_scales);
-  else
-    cache_write_kernel<1><<<grid, 256, 0, st>>>(latent, gate, n, m, gamma, eps, w_idx, rope_pos,
-                                                main_codes, main_scales, idx_codes, idx_scales);
+  const int64_t tiles = (n + kWriteEntries - 1) / kWriteEntries;
+  // column tiles per workgroup: all 8 once the entry tiles fill the chip,
+  // else split the columns so that about 256 workgroups run (splitting a
+  // 4096-entry write over 512 workgroups measured slower: the pooling and
+  // the W reads are repeated per column split)
+  const int tpw = tiles >= 256 ? 8 : (tiles >= 128 ? 4 : 2);
+  const dim3 grid((unsigned)tiles, 8 / tpw);
+  const unsigned threads = 64 * kWriteWaves;
+#define CSA2_WRITE(F, TT)                                                                              \
+  cache_write_kernel<F, TT><<<grid, threads, 0, st>>>(latent, gate, n, m, gamma, eps, w_idx, rope_pos, \
+                                                      main_codes, main_scales, idx_codes, idx_scales)
+  if (main_fmt == 0) {
+    if (tpw == 8) CSA2_WRITE(0, 8); else if (tpw == 4) CSA2_WRITE(0, 4); else CSA2_WRITE(0, 2);
+  } else {
+    if (tpw == 8) CSA2_WRITE(1, 8); else if (tpw == 4) CSA2_WRITE(1, 4); else CSA2_WRITE(1, 2);
+  }
+#undef CSA2_WRITE
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -600,7 +645,7 @@ __global__ __launch_bounds__(64) void window_write_kernel(
     }
     uint32_t h[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = f32_to_bf16_bits(v[2 * j]) | (f32_to_bf16_bits(v[2 * j + 1]) << 16);
+    for (int j = 0; j < 4; ++j) h[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
     *reinterpret_cast<uint4*>(rec + 448 + 16 * (t - 56)) = make_uint4(h[0], h[1], h[2], h[3]);
   }
   if (t == 0) {

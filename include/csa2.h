@@ -133,7 +133,8 @@ int csa2_quantize_fp4(const float* x, int64_t rows, int32_t dim, int32_t group,
  *   latent, gate : bf16 bits [T][512]; gate is not read when m == 1 (may be NULL).
  *   m            : tokens per entry, 1..8; T must be a multiple of m.
  *   gamma        : fp32 [512] RMSNorm weight, NULL = all ones.
- *   w_idx        : fp32 [512][128] indexer-K projection (row c, column d).
+ *   w_idx        : fp32 [512][128] indexer-K projection (row c, column d),
+ *                  16-byte aligned.
  *   rope_pos     : int64 [T/m] position of each written entry, or NULL.  With
  *                  positions, the main entry's dims 448..511 are rotated by the
  *                  compressed RoPE before FP4 [GP 3.2 (RMSNorm -> RoPE base

@@ -76,6 +76,7 @@ def test_cache_write_validation(lib):
     assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 5, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUP
     assert f(FAKE_ODD, None, 8, 1, None, 1e-6, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN
     assert f(FAKE, None, 8, 1, None, 1e-6, FAKE, 0, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN  # positions
+    assert f(FAKE, None, 8, 1, None, 1e-6, P(0x1004), 0, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_ALIGN  # w_idx
 
 
 def test_cache_append_validation(lib):
