@@ -73,12 +73,16 @@ __device__ __forceinline__ floatx4 mfma16(typename OpT<F16>::v8 a, typename OpT<
 }
 
 // Staged R half-rows are 512 B; 16-byte unit u of row r sits at unit
-// u ^ rswz(r).  Both LDS access patterns are then free of bank conflicts
-// (32 banks of 4 B): the staging writes (8 lanes write unit u of 8
-// consecutive rows: rswz takes 8 distinct values there) and the transposed
-// reads of P.R (16 lanes read units 2t, 2t+1 of 4 rows r0..r0+3, r0 a
-// multiple of 4: 2(t ^ (r & 3)) spreads them over 8 distinct bank groups).
-__device__ __forceinline__ int rswz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// u ^ rswz(r).  gfx950's LDS has 64 banks of 4 B (256 B); measured there,
+// a transposed 8-byte read serves 32 lanes per cycle and a 16-byte write
+// 16.  The transposed reads of P.R give the 32 lanes of a half-wave units
+// 2t and 2t+1 of rows {0..3, 8..11} (or {4..7, 12..15}) + a multiple of 16:
+// bits 1-3 of rswz (r & 3 and bit 3 of r) send those 8 rows' 32-byte pairs
+// to 8 distinct 32-byte bank slots (2 cycles per read, against 4 with a
+// 2-way conflict).  The staging writes give the 16 lanes of a quarter-wave
+// unit 8g + ks of 16 consecutive rows; bit 0 (bit 2 of r) makes the 16
+// swizzles distinct, so those are conflict-free too.
+__device__ __forceinline__ int rswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
 
 // bf16 index of 16-byte unit u of staged row r.
 __device__ __forceinline__ int runit(int r, int u) { return r * kHLd + ((u ^ rswz(r)) << 3); }
@@ -123,11 +127,17 @@ __device__ __forceinline__ bool arrive_last(uint32_t* c, uint32_t n, int* flag) 
 template <int WAVES>
 struct AttnSmem {
   static constexpr int kRows = 16 * WAVES;
-  static constexpr int kPLd = kRows + 8;  // P row stride in bf16
+  // P plane row (one head) in bf16: kRows / 2 slots + 4 pad (8-byte reads of
+  // 16 heads then hit 16 distinct bank pairs)
+  static constexpr int kPP = kRows / 2 + 4;
   static constexpr bool kQOwn = WAVES > 8;
   uint16_t R[kRows * kHLd];
   uint16_t Qown[kQOwn ? 16 * kQLd : 8];
-  uint16_t P[16 * kPLd];
+  // P as two planes of 8-byte halves, plane 0 (row slots 8u..8u+3 of each
+  // 8-slot unit) then plane 1 (8u+4..8u+7): an MFMA operand is two 8-byte
+  // reads, which gfx950's LDS serves in 8 cycles against 16 for one 16-byte
+  // read of 64 distinct units (measured)
+  uint16_t P[2 * 16 * kPP];
   __align__(16) float red_m[WAVES][16];
   __align__(16) float red_l[WAVES][16];
   float red_v[WAVES];  // per-wave bound of |dequantised value| (partial scaling)
@@ -407,27 +417,44 @@ __device__ __forceinline__ f16x8 row_step_f16(const RowFetch& f, int ks, const E
   return dequant8_f16(cwd, sc);
 }
 
-// O(16 heads x the wave's 16-dim tiles of one R half) += P . R_half.  Wave w
-// takes tiles w and w + WAVES (16 tiles per half); K steps of 32 rows.  The
-// LDS reads of KB K steps are issued before their products (all of them with
-// one workgroup per CU; two at a time at 8 waves, where registers are
-// scarcer), so a wave does not wait for LDS once per K step.  A wave without
-// a second tile reads and multiplies its first tile twice and drops O[1].
+// A operand of P.R K step kk (32 row slots): head n, slots 32kk + 8g .. +7,
+// one 8-byte read from each P plane.
 template <int WAVES, bool F16>
-__device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g, int n, floatx4 (&O)[2]) {
-  using V8 = typename OpT<F16>::v8;
+__device__ __forceinline__ typename OpT<F16>::v8 p_operand(const AttnSmem<WAVES>& sm, int kk, int g, int n) {
+  constexpr int PP = AttnSmem<WAVES>::kPP;
+  const int e = n * PP + 4 * (4 * kk + g);
+  const uint2 lo = *reinterpret_cast<const uint2*>(&sm.P[e]);
+  const uint2 hi = *reinterpret_cast<const uint2*>(&sm.P[16 * PP + e]);
+  return __builtin_bit_cast(typename OpT<F16>::v8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// O^T(the wave's 16-dim tiles of one R half x 16 heads) += R_half^T . P^T
+// (lane (g, n) accumulates head n, dims 4g..4g+3 of each tile).  Wave w
+// takes tiles w and w + WAVES (16 tiles per half); K steps of 32 rows.  With
+// one workgroup per CU the caller reads the P operands pa once for both
+// halves; at 8 waves, where registers are scarcer, each batch reads its own.
+// The LDS reads of KB K steps are issued before their products (all of them
+// with one workgroup per CU; two at a time at 8 waves), so a wave does not
+// wait for LDS once per K step.  A wave without a second tile reads and
+// multiplies its first tile twice and drops O[1].
+template <int WAVES, bool F16>
+__device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g, int n,
+                                        const typename OpT<F16>::v8 (&pa)[AttnSmem<WAVES>::kRows / 32],
+                                        floatx4 (&O)[2]) {
   constexpr int NK = AttnSmem<WAVES>::kRows / 32;
-  constexpr int LD = AttnSmem<WAVES>::kPLd;
   constexpr int KB = AttnSmem<WAVES>::kQOwn ? NK : 2;
   static_assert(NK % KB == 0, "K steps must split into whole batches");
+  using V8 = typename OpT<F16>::v8;
   const int ta = n & 3, tj = n >> 2;
   const int t1 = w + WAVES < 16 ? w + WAVES : w;
 #pragma unroll
   for (int k0 = 0; k0 < NK; k0 += KB) {
-    V8 pa[KB];
     shortx4 lo[2][KB], hi[2][KB];
+    V8 pb[KB];
+    if constexpr (!AttnSmem<WAVES>::kQOwn) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) pa[j] = *reinterpret_cast<const V8*>(&sm.P[n * LD + 32 * (k0 + j) + 8 * g]);
+      for (int j = 0; j < KB; ++j) pb[j] = p_operand<WAVES, F16>(sm, k0 + j, g, n);
+    }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
 #pragma unroll
@@ -449,7 +476,9 @@ __device__ __forceinline__ void pv_half(const AttnSmem<WAVES>& sm, int w, int g,
         shortx8 bv;
         bv[0] = lo[nt][j][0]; bv[1] = lo[nt][j][1]; bv[2] = lo[nt][j][2]; bv[3] = lo[nt][j][3];
         bv[4] = hi[nt][j][0]; bv[5] = hi[nt][j][1]; bv[6] = hi[nt][j][2]; bv[7] = hi[nt][j][3];
-        O[nt] = mfma16<F16>(pa[j], __builtin_bit_cast(V8, bv), O[nt]);
+        // O^T tile (16 dims x 16 heads) += R^T . P^T: the same operand registers
+        // with A and B swapped, so a lane ends with 4 consecutive dims of one head
+        O[nt] = mfma16<F16>(__builtin_bit_cast(V8, bv), AttnSmem<WAVES>::kQOwn ? pa[k0 + j] : pb[j], O[nt]);
       }
     }
   }
@@ -571,7 +600,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units, int64_t seq_stride) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
-  constexpr int kRows = Smem::kRows, kPLd = Smem::kPLd, kThreads = 64 * WAVES;
+  constexpr int kRows = Smem::kRows, kPP = Smem::kPP, kThreads = 64 * WAVES;
   // fp16 operands for E4M3-scaled main rows (FP8 window records stay bf16)
   constexpr bool F16 = FMT == 1 && !WF8;
   using V8 = typename OpT<F16>::v8;
@@ -779,7 +808,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   lw += shfl_xor_f(lw, 16);
   lw += shfl_xor_f(lw, 32);
   if (g == 0) sm.red_l[w][n] = lw;
-  *reinterpret_cast<uint2*>(&sm.P[n * kPLd + 16 * w + 4 * g]) =
+  // slots 16w + 4g .. +3: unit 2w + g/2, plane g & 1
+  *reinterpret_cast<uint2*>(&sm.P[(g & 1) * 16 * kPP + n * kPP + 4 * (2 * w + (g >> 1))]) =
       F16 ? make_uint2(pack_f16x2(pf[0], pf[1]), pack_f16x2(pf[2], pf[3]))
           : make_uint2(pack_bf16x2(pf[0], pf[1]), pack_bf16x2(pf[2], pf[3]));
   if (!Smem::kQOwn) {
@@ -811,21 +841,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   }
   // 1 / sum for heads 4g+i (a reciprocal: the sum is >= 1 when positive);
   // the partial's 2^-e is applied per value (2^-e alone can exceed fp32)
-  float scl[4];
+  float scl;  // 1 / sum for head n
   {
-    float4 ls[WAVES];
+    float ln = 0.f;
 #pragma unroll
-    for (int v = 0; v < WAVES; ++v) ls[v] = *reinterpret_cast<const float4*>(&sm.red_l[v][4 * g]);
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < WAVES; ++v) ln += sm.red_l[v][n];
+    scl = ln > 0.f ? __builtin_amdgcn_rcpf(ln) : 0.0f;
+  }
+  V8 pa[kRows / 32];  // P operands, read once for both halves (one workgroup per CU)
+  if constexpr (Smem::kQOwn) {
 #pragma unroll
-    for (int v = 0; v < WAVES; ++v) {
-      l4[0] += ls[v].x;
-      l4[1] += ls[v].y;
-      l4[2] += ls[v].z;
-      l4[3] += ls[v].w;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) scl[i] = l4[i] > 0.f ? __builtin_amdgcn_rcpf(l4[i]) : 0.0f;
+    for (int kk = 0; kk < kRows / 32; ++kk) pa[kk] = p_operand<WAVES, F16>(sm, kk, g, n);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -836,14 +862,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
       __syncthreads();
     }
     floatx4 O[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    pv_half<WAVES, F16>(sm, w, g, n, O);
-    // lane (g, n): heads 4g+i, dims 256h + 16*tile + n, tile = w + WAVES*nt
+    pv_half<WAVES, F16>(sm, w, g, n, pa, O);
+    // lane (g, n): head n, dims 256h + 16*tile + 4g .. +3, tile = w + WAVES*nt:
+    // one 8-byte store per tile
+    uint2* dst = reinterpret_cast<uint2*>(prow + ((int64_t)n * S + sidx) * 512 + 256 * h + 16 * w + 4 * g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t* dst = prow + ((int64_t)(4 * g + i) * S + sidx) * 512 + 256 * h + 16 * w + n;
-      dst[0] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[0][i] * scl[i], -e_sc));
-      if (w + WAVES < 16)
-        dst[16 * WAVES] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(O[1][i] * scl[i], -e_sc));
+    for (int nt = 0; nt < 2; ++nt) {
+      if (nt == 1 && w + WAVES >= 16) break;  // wave-uniform
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = ldexpf(O[nt][i] * scl, -e_sc);
+      dst[nt * 4 * WAVES] = make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
     }
   }
 
