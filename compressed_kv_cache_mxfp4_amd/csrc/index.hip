@@ -428,6 +428,35 @@ struct __align__(16) SelScratch {
   uint32_t bc[4];
 };
 
+// Candidates that survive the prefilter, in ascending candidate order: key,
+// candidate index and one caller value each (96 KB of LDS: the prefilter's
+// sample rank leaves about 1.5 k + n / 64 survivors, 4096 for k = 2048 of
+// 65,536, so half the capacity is margin).  Compaction pays
+// off from 32 keys per thread (more than 32K candidates): it adds one pass
+// over every key (about 10 instructions per key, 16 SIMD cycles each with
+// 16 waves on 4 SIMDs) and saves the radix passes' and the emission's per-key
+// work; measured on the Full call's block selection, 65,536 blocks per
+// sequence: 34.5 -> 29.3 us and 35.5 -> 27.8 us for the two selections, and
+// at 16,384 blocks 0.5-0.9 us slower, so it is not used there.
+constexpr int kCompactCap = 8192;
+constexpr int kCompactMinEpt = 32;
+struct __align__(16) SelCompact {
+  uint32_t key[kCompactCap];
+  int32_t idx[kCompactCap];
+  uint32_t side[kCompactCap];
+};
+
+// No per-candidate caller value.
+struct NoSide {
+  __device__ uint32_t operator()(int, int) const { return 0u; }
+};
+
+// Keys of a compaction buffer.
+struct KeysFromLdsC {
+  const uint32_t* p;
+  __device__ uint32_t key(int i) const { return p[i]; }
+};
+
 // float -> uint32 key with the same order; NaN (absent) -> 0; -0 -> +0.
 __device__ __forceinline__ uint32_t float_key(float f) {
   if (f != f) return 0u;
@@ -526,18 +555,23 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* h, SelScratch&
   __syncthreads();
 }
 
-// Top-k of the n candidates (key 0 = absent): calls emit(i, rank, j) for the
-// winners in ascending i (j = the thread's key slot holding candidate i),
-// rank = 0, 1, ...; returns min(k, #present).
+// Top-k of the n candidates (key 0 = absent): calls emit(i, rank, key, side)
+// for the winners in ascending i, rank = 0, 1, ..., with side = side_fn(j, i)
+// evaluated by the thread whose key slot j holds candidate i; returns
+// min(k, #present).
 //
 // PREF: when the candidates far outnumber k, a sample (one key per thread)
 // first bounds the k-th key from below: T0 = lower edge of the histogram bin
 // holding a sample rank with a wide margin.  If at least k keys are >= T0
 // (checked exactly), the radix search only histograms keys in [T0, max];
-// otherwise it searches the full range.  Either way the result is exact.
-template <int NT, int EPT, bool PREF, class Src, class Emit>
+// otherwise it searches the full range.  With a compaction buffer cp and at
+// most kCompactCap keys >= T0, those keys are first copied to cp in
+// ascending candidate order and the search and the emission run over them
+// alone (a few keys per thread instead of all n).  Either way the result is
+// exact and the same.
+template <int NT, int EPT, bool PREF, class Src, class Emit, class Side = NoSide>
 __device__ __forceinline__ int select_core(const KeyRegs<EPT>& K, const Src& src, int n, int k, SelScratch& sh,
-                           Emit emit) {
+                           Emit emit, SelCompact* cp = nullptr, Side side_fn = Side{}) {
   constexpr int NW = NT / 64;
   static_assert(NW <= 16, "per-wave partials hold at most 16 waves");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -593,32 +627,65 @@ __device__ __forceinline__ int select_core(const KeyRegs<EPT>& K, const Src& src
   uint32_t lo = mn, hi = mx, above = 0u, T;
   bool take_all_eq = false;
   int buf = 0;  // histogram buffer of the next pass
-  if (PREF && lo != hi && cnt > 4096u && cnt >= 8u * target) {
-    const uint32_t span = hi - lo;
-    const int nbits = 32 - __clz((int)span);
-    const int shift = nbits > 11 ? nbits - 11 : 0;
-    const uint32_t smp = KEY(0);
-    if (smp) atomicAdd(&sh.hist[0][(smp - lo) >> shift], 1u);
-    if (t == 0) sh.bc[0] = 0xFFFFFFFFu;
-    __syncthreads();
-    synced = true;
-    // sample rank: 1.5x the expected share of the k winners, plus 16
-    const uint32_t r = min((uint32_t)NT, 16u + (uint32_t)((3ull * target * NT + 2ull * cnt - 1) / (2ull * cnt)));
-    find_bin_from_top<NT>(sh.hist[0], sh, r);
-    const uint32_t tb = sh.bc[0];
-    const uint32_t T0 = tb == 0xFFFFFFFFu ? lo : lo + (tb << shift);
-    for (int i = t; i < 2048; i += NT) sh.hist[0][i] = 0u;
-    uint32_t c0 = 0u;
-#pragma unroll UNR
-    for (int j = 0; j < E; ++j) c0 += (uint32_t)__popcll(__ballot(KEY(j) >= T0));
-    // wred[0]: read by find_bin above before its last barrier; the emission
-    // below writes only wred[1] and wred[2]
-    if (lane == 0) sh.wred[0][wave] = c0;
-    __syncthreads();
-    c0 = 0u;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) c0 += sh.wred[0][v];
-    if (c0 >= target) lo = T0;
+  if constexpr (PREF) {
+    if (lo != hi && cnt > 4096u && cnt >= 8u * target) {
+      const uint32_t span = hi - lo;
+      const int nbits = 32 - __clz((int)span);
+      const int shift = nbits > 11 ? nbits - 11 : 0;
+      const uint32_t smp = KEY(0);
+      if (smp) atomicAdd(&sh.hist[0][(smp - lo) >> shift], 1u);
+      if (t == 0) sh.bc[0] = 0xFFFFFFFFu;
+      __syncthreads();
+      synced = true;
+      // sample rank: 1.5x the expected share of the k winners, plus 16
+      const uint32_t r = min((uint32_t)NT, 16u + (uint32_t)((3ull * target * NT + 2ull * cnt - 1) / (2ull * cnt)));
+      find_bin_from_top<NT>(sh.hist[0], sh, r);
+      const uint32_t tb = sh.bc[0];
+      const uint32_t T0 = tb == 0xFFFFFFFFu ? lo : lo + (tb << shift);
+      for (int i = t; i < 2048; i += NT) sh.hist[0][i] = 0u;
+      uint32_t c0 = 0u;
+  #pragma unroll UNR
+      for (int j = 0; j < E; ++j) c0 += (uint32_t)__popcll(__ballot(KEY(j) >= T0));
+      // wred[0]: read by find_bin above before its last barrier; the emission
+      // below writes only wred[1] and wred[2]
+      if (lane == 0) sh.wred[0][wave] = c0;
+      __syncthreads();
+      c0 = 0u;
+  #pragma unroll
+      for (int v = 0; v < NW; ++v) c0 += sh.wred[0][v];
+      if (c0 >= target) {
+        lo = T0;
+        if (cp != nullptr && c0 <= (uint32_t)kCompactCap) {
+          // survivors to cp in candidate order: earlier waves' counts, then
+          // slot by slot through the wave's ballots
+          const uint64_t below = (1ull << lane) - 1ull;
+          uint32_t off = wave_prefix(sh.wred[0], wave);
+  #pragma unroll UNR
+          for (int j = 0; j < E; ++j) {
+            const uint32_t kk = KEY(j);
+            const bool sv = kk >= T0;
+            const uint64_t m = __ballot(sv);
+            if (sv) {
+              const uint32_t at = off + (uint32_t)__popcll(m & below);
+              const int i = sel_index<NT, EPT>(n, j);
+              cp->key[at] = kk;
+              cp->idx[at] = i;
+              cp->side[at] = side_fn(j, i);
+            }
+            off += (uint32_t)__popcll(m);
+            if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+          __syncthreads();  // also: every wave has read wred[0]
+          constexpr int EC = kCompactCap / NT;
+          KeysFromLdsC csrc{cp->key};
+          KeyRegs<EC> kc;
+          load_keys<NT, EC>(kc, csrc, (int)c0);
+          return select_core<NT, EC, false>(kc, csrc, (int)c0, k, sh, [&](int ci, int r, uint32_t key, uint32_t) {
+            emit(cp->idx[ci], r, key, cp->side[ci]);
+          });
+        }
+      }
+    }
   }
   for (;;) {
     if (lo == hi) {
@@ -700,7 +767,7 @@ __device__ __forceinline__ int select_core(const KeyRegs<EPT>& K, const Src& src
     }
     const uint64_t selb = __ballot(sel);
     if (selb) {  // wave-uniform
-      if (sel) emit(ibase + 64 * j, (int)(r_sel + (uint32_t)__popcll(selb & below)), j);
+      if (sel) emit(ibase + 64 * j, (int)(r_sel + (uint32_t)__popcll(selb & below)), kk, side_fn(j, ibase + 64 * j));
       r_sel += (uint32_t)__popcll(selb);
     }
     if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
@@ -764,6 +831,7 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   __shared__ int32_t blk[CSA2_POOL_BLOCKS];
   __shared__ uint32_t blkkey[CSA2_POOL_BLOCKS];
   __shared__ int32_t cblk[CSA2_MAX_TOPK];
+  __shared__ SelCompact cpt;
   // split: two workgroups per sequence, one per selection (role 0 the pool,
   // role 1 the top-k, which then takes its blocks from all blocks -- the
   // same set, the pool being the top blocks by the same key), so the two
@@ -793,10 +861,13 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
   if constexpr (EPT_B > 0) finish_keys<NT, EPT_B>(kb, nb);
   int ncb;
   if (n_blocks > 0 && role != 1) {
-    const int nsel = select_core<NT, EPT_B, true>(kb, bsrc, nb, n_blocks, sh, [&](int i, int r, int j) {
-      blk[r] = i;
-      if constexpr (EPT_B > 0) blkkey[r] = kb.r[j]; else blkkey[r] = bsrc.key(i);
-    });
+    const int nsel = select_core<NT, EPT_B, true>(
+        kb, bsrc, nb, n_blocks, sh,
+        [&](int i, int r, uint32_t key, uint32_t) {
+          blk[r] = i;
+          blkkey[r] = key;
+        },
+        EPT_B >= kCompactMinEpt ? &cpt : nullptr);
     const int pl = group_items(blk, nsel, (int)L);
     int32_t* pb = pool + (int64_t)b * n_blocks * kBlock;
     // a thread writes whole groups (8 entries: two 16-byte stores when the
@@ -833,18 +904,23 @@ __global__ __launch_bounds__(NT) void select_full_kernel(
     KeysFromLds csrc{blkkey};
     KeyRegs<EPT_C> kc;
     load_keys<NT, EPT_C>(kc, csrc, nsel);
-    ncb = select_core<NT, EPT_C, false>(kc, csrc, nsel, k, sh, [&](int i, int r, int) { cblk[r] = blk[i]; });
+    ncb = select_core<NT, EPT_C, false>(kc, csrc, nsel, k, sh,
+                                        [&](int i, int r, uint32_t, uint32_t) { cblk[r] = blk[i]; });
   } else {
-    ncb = select_core<NT, EPT_B, true>(kb, bsrc, nb, k, sh, [&](int i, int r, int) { cblk[r] = i; });
+    ncb = select_core<NT, EPT_B, true>(kb, bsrc, nb, k, sh, [&](int i, int r, uint32_t, uint32_t) { cblk[r] = i; },
+                                       EPT_B >= kCompactMinEpt ? &cpt : nullptr);
   }
   const int nc = group_items(cblk, ncb, (int)L);
   KeysFromGroups psrc{sc, cblk};
   KeyRegs<EPT_P> kp;
   load_keys<NT, EPT_P>(kp, psrc, nc);
-  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh, [&](int i, int r, int) {
-    tk[r] = psrc.item(i);
-    if (tkr) tkr[r] = page_row(pm, b / qps, psrc.item(i));
-  });
+  const int cnt = select_core<NT, EPT_P, true>(
+      kp, psrc, nc, k, sh,
+      [&](int i, int r, uint32_t, uint32_t) {
+        tk[r] = psrc.item(i);
+        if (tkr) tkr[r] = page_row(pm, b / qps, psrc.item(i));
+      },
+      EPT_P >= kCompactMinEpt ? &cpt : nullptr);
   for (int i = cnt + threadIdx.x; i < k; i += NT) {
     tk[i] = -1;
     if (tkr) tkr[i] = -1;
@@ -876,7 +952,7 @@ __global__ __launch_bounds__(NT) void select_pool_kernel(
   const int32_t* pbr = pool_rows ? pool_rows + (int64_t)b * pool_cap : nullptr;
   int32_t* tkr = topk_rows ? topk_rows + (int64_t)b * k : nullptr;
   finish_keys<NT, EPT_G>(kg, ng);
-  const int ncg = select_core<NT, EPT_G, false>(kg, gsrc, ng, k, sh, [&](int i, int r, int) { cgrp[r] = i; });
+  const int ncg = select_core<NT, EPT_G, false>(kg, gsrc, ng, k, sh, [&](int i, int r, uint32_t, uint32_t) { cgrp[r] = i; });
   const int nc = group_items(cgrp, ncg, n);
   KeysFromGroups psrc{pool_scores + (int64_t)b * pool_cap, cgrp};
   KeyRegs<EPT_P> kp;
@@ -890,10 +966,15 @@ __global__ __launch_bounds__(NT) void select_pool_kernel(
       pos[j] = i < nc ? pb[item] : -1;
     }
   }
-  const int cnt = select_core<NT, EPT_P, true>(kp, psrc, nc, k, sh, [&](int i, int r, int j) {
-    if constexpr (EPT_P > 0) tk[r] = pos[j]; else tk[r] = pb[psrc.item(i)];
-    if (tkr) tkr[r] = pbr[psrc.item(i)];
-  });
+  const int cnt = select_core<NT, EPT_P, true>(
+      kp, psrc, nc, k, sh,
+      [&](int i, int r, uint32_t, uint32_t side) {
+        if constexpr (EPT_P > 0) tk[r] = (int32_t)side; else tk[r] = pb[psrc.item(i)];
+        if (tkr) tkr[r] = pbr[psrc.item(i)];
+      },
+      nullptr, [&](int j, int) -> uint32_t {  // at most 16 keys per thread here: no compaction
+        if constexpr (EPT_P > 0) return (uint32_t)pos[j]; else return 0u;
+      });
   for (int i = cnt + threadIdx.x; i < k; i += NT) {
     tk[i] = -1;
     if (tkr) tkr[i] = -1;
