@@ -142,6 +142,43 @@ def test_all_scores_equal_take_lowest_indices():
     assert (t3[:, :40] == np.arange(40)).all() and (t3[:, 40:] == -1).all()
 
 
+@pytest.mark.parametrize("B,cap,kind", [(2, 262144, "random"), (2, 262144, "ties"), (2, 262144, "crowd"),
+                                         (1, 524288, "random"), (1, 524288, "ties")])
+def test_full_selection_many_blocks_exact(B, cap, kind):
+    """Selections over more than 16K blocks per sequence (32 or 64 keys per
+    thread), where the prefilter's survivors are compacted before the search:
+    the top-k and the pool are exactly the brute-force ones on the GPU's own
+    scores.  "ties": the rows are copies of 48 distinct rows, so scores take at
+    most 48 values and tie across the threshold; "crowd": a fifth of the rows
+    copy the best-scoring row, so the keys at or above the sampled bound
+    outnumber the compaction buffer and the selection falls back to the full
+    search; "random": the synthetic cache as it is."""
+    wl = syn.small("sel" + kind, 31, B=B, cap=cap, H_idx=64, k=512, n_blocks=2048)
+    say(f"index_full selection {B} x {cap}, {kind}")
+    cache = build_gpu_cache(wl, 0)
+    lens = [cap - 12345 * b for b in range(B)]
+    g = torch.Generator(device="cpu").manual_seed(1000 + cap + len(kind))
+    if kind == "ties":
+        src = torch.randint(0, cap, (48,), generator=g)
+        pick = src[torch.randint(0, 48, (cap,), generator=g)].to(DEV)
+        for key in ("idx_codes", "idx_scales"):
+            cache[key][:] = cache[key][:, pick]
+    elif kind == "crowd":
+        s0 = _run_full(wl, cache, lens)[5]
+        for b in range(B):
+            best = int(np.nanargmax(s0[b, :lens[b]]))
+            at = torch.randperm(cap, generator=g)[: cap // 5].to(DEV)
+            for key in ("idx_codes", "idx_scales"):
+                cache[key][b, at] = cache[key][b, best].clone()
+    _, _, topk, pool, pool_len, scores = _run_full(wl, cache, lens)
+    for b, L in enumerate(lens):
+        gs = scores[b, :L]
+        assert np.array_equal(topk[b], brute_topk(gs, 512)), f"seq {b}: top-k is not exact on the GPU scores"
+        bp, bpl, _ = brute_pool(gs, 2048)
+        assert pool_len[b] == bpl
+        assert np.array_equal(pool[b], bp), f"seq {b}: pool is not exact on the GPU scores"
+
+
 def test_determinism_two_runs_bitwise():
     wl = syn.small("det", 9, B=2, cap=20000, H_idx=64, k=512, n_blocks=2048)
     cache = build_gpu_cache(wl, 0)
