@@ -227,17 +227,20 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, const E4m3F16& sc)
 // bf16x8 (8 dims of one query head) -> fp16x8 times 2^-k (exact for
 // magnitudes from 2^-14; smaller ones are rounded to fp16's subnormal grid).
 __device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 v, int k) {
-  const float m = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, k in [0, 113]
   const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = pack_f16x2(bf16_bits_to_f32(wd[i] & 0xFFFFu) * m, bf16_bits_to_f32(wd[i] >> 16) * m);
+  for (int i = 0; i < 4; ++i)  // times 2^-k exactly (v_ldexp_f32: any k a bf16 head needs)
+    o[i] = pack_f16x2(ldexpf(bf16_bits_to_f32(wd[i] & 0xFFFFu), -k), ldexpf(bf16_bits_to_f32(wd[i] >> 16), -k));
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Exponent shift of one query head for fp16 operands: the smallest k >= 0
-// with max|q| * 2^-k < 2^15 (the wave holds one head: 64 lanes x 8 dims).
+// Exponent shift of one query head for fp16 operands: the k with
+// 2^14 <= max|q| * 2^-k < 2^15 (the wave holds one head: 64 lanes x 8 dims),
+// so the largest component sits at the top of fp16's range and every
+// component above 2^-28 of it stays a normal fp16, holding its 8 bf16
+// significant bits exactly.  k is negative for heads below 2^14 (down to
+// -147 for bf16's smallest subnormal) and at most 113 (bf16's largest value).
 __device__ __forceinline__ int head_shift_f16(uint4 v) {
   const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
   float m = 0.0f;
@@ -259,10 +262,10 @@ __device__ __forceinline__ int head_shift_f16(uint4 v) {
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
     m = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
   }
-  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;  // zero, inf or NaN: no shift
+  if (!(m > 0.0f) || !(m < INFINITY)) return 0;  // zero, inf or NaN: no shift
   int e;
-  (void)frexpf(m, &e);  // m < 2^e
-  return e > 15 ? e - 15 : 0;
+  (void)frexpf(m, &e);  // 2^(e-1) <= m < 2^e
+  return e - 15;
 }
 
 struct RowFetch {
@@ -758,12 +761,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   // lane (g, n): rows 4g+i of the wave's tile, head n; fp16 queries were
   // staged times 2^-qk[n]
   const uint64_t vmask = __ballot(row.ok != 0u);
-  const float lsc = F16 ? ldexpf(sm_scale, sm.qk[n]) : sm_scale;
+  // (fp16: scaled back by 2^k after sm_scale, so the logit overflows only
+  // when its true value does)
+  const int qk = F16 ? sm.qk[n] : 0;
   float x[4];
   float mw = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = ((vmask >> (4 * g + i)) & 1ull) ? sacc[i] * lsc : -INFINITY;
+    const float xs = F16 ? ldexpf(sacc[i] * sm_scale, qk) : sacc[i] * sm_scale;
+    x[i] = ((vmask >> (4 * g + i)) & 1ull) ? xs : -INFINITY;
     mw = fmaxf(mw, x[i]);
   }
   mw = fmaxf(mw, shfl_xor_f(mw, 16));

@@ -85,6 +85,52 @@ def test_attention_parity_with_window(fmt, H, rope):
     say(f"  worst relative error {worst:.2e}")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_attention_query_magnitudes_across_bf16_range(fmt):
+    """Query heads from bf16's smallest subnormal to its largest finite value
+    (the E4M3 path stages each head in fp16 times 2^-k, k chosen per head):
+    heads scaled by 2^e for e from -120 to 100, an all-zero head, a head whose
+    only non-zero component is the smallest subnormal, and heads holding one
+    or two components near the largest value the path allows.  Rows come from N(0, 1), so every logit is
+    finite in fp32 and the oracle's fp64 answer is the reference; the
+    log-sum-exp is compared relative to its size."""
+    say(f"attention query magnitudes fmt={fmt}")
+    B, cap, k, W, H = 2, 1200, 300, 64, 16
+    c, s, rc, rs = _make_cache(B, cap, fmt, 41 + fmt)
+    g = np.random.default_rng(13)
+    topk = np.stack([np.sort(g.choice(cap - W, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    lens = np.full(B, cap, np.int32)
+    swa_len = np.full(B, W, np.int32)
+    qf = torch.randn(B, H, 512, generator=torch.Generator().manual_seed(17)) * 0.5
+    exps = [-120, -60, -20, -8, 0, 6, 14, 15, 16, 30, 60, 100]
+    for h, e in enumerate(exps):
+        qf[:, h] *= 2.0 ** e
+    q = syn.as_bf16_bits(qf)
+    q[:, 12] = 0                                   # all-zero head
+    q[:, 13] = 0
+    q[:, 13, 77] = 1                               # smallest bf16 subnormal, alone
+    # near bf16's maximum: with E8M0 rows (bf16 operands, fp32 products) only
+    # up to 2^124, so that q.k itself stays within fp32; with E4M3 rows (fp16
+    # operands scaled per head) bf16's largest values
+    big, top = (0x7D80, 0x7D80) if fmt == 0 else (0x7F78, 0x7F7F)
+    q[:, 14, 5] = big                              # among N(0, 0.25) components
+    q[:, 15, 300] = top
+    q[:, 15, 301] = (top | 0x8000) - 0x10000       # and its negative (int16 bits)
+    out, lse = K.sparse_attn_decode(q.to(DEV), c, s, torch.from_numpy(lens).to(DEV), torch.from_numpy(topk).to(DEV),
+                                    fmt, swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swa_len).to(DEV),
+                                    swa_stride=cap, swa_cap=W, swa_row0=cap - W, return_lse=True)
+    torch.cuda.synchronize()
+    ref = np.zeros((B, H, 512), np.float32)
+    rl = np.zeros((B, H), np.float64)
+    for b in range(B):
+        ref[b], rl[b] = oracle.attention(q[b].numpy(), rc[b], rs[b], lens[b], fmt, topk[b],
+                                         rc[b, cap - W:], rs[b, cap - W:], swa_len[b], 1 / np.sqrt(512))
+    assert np.isfinite(rl).all()
+    worst = attn_close(out.cpu(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), rl, rtol=1e-5, atol=1e-4)
+    say(f"  worst relative error {worst:.2e}")
+
+
 def test_attention_odd_sizes_and_empty():
     fmt = 0
     B, cap, k = 2, 700, 77
