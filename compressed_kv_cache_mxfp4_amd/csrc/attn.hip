@@ -256,12 +256,7 @@ __device__ __forceinline__ int head_shift_f16(uint4 v) {
   m = fmaxf(m, dpp(m, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
   m = fmaxf(m, dpp(m, std::integral_constant<int, 0x141>{}));  // row_half_mirror
   m = fmaxf(m, dpp(m, std::integral_constant<int, 0x140>{}));  // row_mirror
-  {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-  }
+  m = rows4_max(m);
   if (!(m > 0.0f) || !(m < INFINITY)) return 0;  // zero, inf or NaN: no shift
   int e;
   (void)frexpf(m, &e);  // 2^(e-1) <= m < 2^e
@@ -782,8 +777,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     x[i] = ((vmask >> (4 * g + i)) & 1ull) ? xs : -INFINITY;
     mw = fmaxf(mw, x[i]);
   }
-  mw = fmaxf(mw, shfl_xor_f(mw, 16));
-  mw = fmaxf(mw, shfl_xor_f(mw, 32));
+  mw = rows4_max(mw);
   if (g == 0) sm.red_m[w][n] = mw;
   {
     // largest scale byte of the lane's 128 values -> bound of |value| (6 x scale)
@@ -821,8 +815,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     pf[i] = (M == -INFINITY) ? 0.0f : __expf(x[i] - M);
     lw += pf[i];
   }
-  lw += shfl_xor_f(lw, 16);
-  lw += shfl_xor_f(lw, 32);
+  lw = rows4_sum(lw);
   if (g == 0) sm.red_l[w][n] = lw;
   // slots 16w + 4g .. +3: unit 2w + g/2, plane g & 1
   *reinterpret_cast<uint2*>(&sm.P[(g & 1) * 16 * kPP + n * kPP + 4 * (2 * w + (g >> 1))]) =
@@ -1191,8 +1184,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
             x[4 * t + i] = ((vm >> row) & 1u) ? sacc[t][i] * c2 : -INFINITY;
             cmax = fmaxf(cmax, x[4 * t + i]);
           }
-        cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-        cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+        cmax = rows4_max(cmax);
         float alpha = 1.0f;
         if (cmax > mref + kTau) {
           alpha = mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref - cmax);
@@ -1215,8 +1207,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       }
       __syncthreads();
     }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
+    lsum = rows4_sum(lsum);
     if (g == 0) {
       sm.mfin[16 * wr + n] = mref;
       sm.lfin[16 * wr + n] = lsum;

@@ -113,6 +113,25 @@ __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {
   return (uint32_t)__shfl_xor((int)v, mask, kWave);
 }
 
+// Max and sum over lanes l, l^16, l^32, l^48 (one value per 16-lane row)
+// without an LDS round trip: v_permlane16_swap exchanges the odd and even
+// rows, v_permlane32_swap the two halves.  Each swap leaves the lane's own
+// value and its partner's in the two results, the same pair in every lane of
+// the pair, so the sums are bitwise equal across the four lanes.
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
