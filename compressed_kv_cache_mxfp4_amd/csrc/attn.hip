@@ -247,16 +247,7 @@ __device__ __forceinline__ int head_shift_f16(uint4 v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(wd[i] >> 16))));
-  // 64-lane max without LDS: DPP within rows of 16, then the row swaps
-  auto dpp = [](float v, auto ctrl) {
-    return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), decltype(ctrl)::value,
-                                                                 0xf, 0xf, true));
-  };
-  m = fmaxf(m, dpp(m, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
-  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
-  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x141>{}));  // row_half_mirror
-  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x140>{}));  // row_mirror
-  m = rows4_max(m);
+  m = wave_max(m);  // DPP and row swaps, no LDS
   if (!(m > 0.0f) || !(m < INFINITY)) return 0;  // zero, inf or NaN: no shift
   int e;
   (void)frexpf(m, &e);  // 2^(e-1) <= m < 2^e

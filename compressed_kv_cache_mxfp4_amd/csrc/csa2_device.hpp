@@ -132,17 +132,44 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
+// A lane's value from another lane of its 16-lane row, by a DPP control
+// (every lane reads; row and bank masks full).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum (MAX = false) or maximum over each aligned group of N lanes, N = 2 ..
+// 64, without an LDS round trip.  Partners 1 and 2 lanes away come from DPP
+// quad permutes; then, once each quad (half-row) holds one value, the row
+// half-mirror (row mirror) reads a lane of the other quad (half-row), which
+// holds what the partner 4 (8) lanes away holds; rows 16 and 32 lanes away
+// come from v_permlane16_swap and v_permlane32_swap.  Each step combines the
+// lane's value with the value its xor partner holds, so the results equal
+// those of an xor butterfly bit for bit (the combining operations are
+// commutative), and every lane of a group ends with the same value.
+template <int N, bool MAX>
+__device__ __forceinline__ float group_reduce(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (N >= 2) v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+  if constexpr (N >= 16) v = op(v, dpp_f<0x140>(v));  // row_mirror
+  if constexpr (N >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if constexpr (N >= 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return group_reduce<64, false>(v); }
+
+__device__ __forceinline__ float wave_max(float v) { return group_reduce<64, true>(v); }
 
 // Eight OCP E4M3 bytes (two dwords, byte i = element i) -> bf16x8, each
 // times the power of two of an E8M0 operand (exact: E4M3 values scaled by a

@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const bool active = i4 < n4;
   float4 v = active ? reinterpret_cast<const float4*>(x)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-  for (int m = 1; m < LPG; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
+  amax = group_reduce<LPG, true>(amax);
   const uint32_t b = scale_code<FMT>(amax);
   const float s = scale_value<FMT>(b);
   if (!active) return;
@@ -274,7 +273,7 @@ __global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
       float amax = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(y[c]));
-      amax = fmaxf(amax, shfl_xor_f(amax, 1));
+      amax = group_reduce<2, true>(amax);
       const uint32_t b = scale_code<FMT>(amax);
       const float sv = scale_value<FMT>(b);
       uint32_t word = 0;
@@ -335,8 +334,7 @@ __global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, shfl_xor_f(amax, 1));
-    amax = fmaxf(amax, shfl_xor_f(amax, 2));
+    amax = group_reduce<4, true>(amax);
     const uint32_t b = scale_code_e8m0(amax);
     const float sv = e8m0_value(b);
     uint32_t word = 0;
@@ -495,8 +493,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) v += kv[s8][t];
     float amax = fabsf(v);
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
+    amax = group_reduce<32, true>(amax);
     const uint32_t sb = scale_code_e8m0(amax);
     kc[t] = e2m1_code(v, e8m0_value(sb));
     if (t == 0) idx_scales[row * 4 + ct] = (uint8_t)sb;
@@ -622,13 +619,11 @@ __global__ __launch_bounds__(64) void window_write_kernel(
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  amax = fmaxf(amax, shfl_xor_f(amax, 1));
-  amax = fmaxf(amax, shfl_xor_f(amax, 2));
-  amax = fmaxf(amax, shfl_xor_f(amax, 4));
+  amax = group_reduce<8, true>(amax);
   const uint32_t sb = fp8_scale_code(amax);
   uint32_t sbytes[8];
 #pragma unroll
-  for (int gi = 0; gi < 8; ++gi) sbytes[gi] = (uint32_t)__shfl((int)sb, 8 * gi, kWave);
+  for (int gi = 0; gi < 8; ++gi) sbytes[gi] = (uint32_t)__builtin_amdgcn_readlane((int)sb, 8 * gi);  // uniform
   if (t < 56) {
     uint32_t c[2] = {0u, 0u};
 #pragma unroll
