@@ -58,6 +58,7 @@ __device__ __forceinline__ float scale_value(uint32_t b) {
 }
 
 // Nearest E2M1 code of x / s, ties to the even code; all products are exact.
+// (Any scale; E8M0 groups use the converts below, which give the same codes.)
 __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   float a = fabsf(x);
   if (!(a > 0.0f)) return 0u;
@@ -66,6 +67,58 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
                (uint32_t)(a > 5.0f * s);
   if (c != 0u && (__float_as_uint(x) >> 31)) c |= 8u;
   return c;
+}
+
+// E2M1 codes of values over a power-of-two scale s (an E8M0 value), two per
+// v_cvt_scalef32_pk_fp4_f32: x / s rounded to nearest, ties to even,
+// saturating at 6 -- measured on gfx950 to agree with e2m1_code for every
+// midpoint and its neighbours, every grid point, saturation, subnormal values
+// and subnormal scales, except that it gives a zero magnitude the sign of x
+// and saturates NaN.  So NaN is taken as 0 first and the sign of zero
+// magnitudes is cleared after (+0, as the rule above has it).
+__device__ __forceinline__ float nan_to_zero(float x) { return x == x ? x : 0.0f; }
+
+__device__ __forceinline__ uint32_t clear_negative_zeros(uint32_t w) {
+  const uint32_t mag = w & 0x77777777u;
+  return mag | (w & ((mag + 0x77777777u) & 0x88888888u));  // sign kept where the magnitude is not 0
+}
+
+// 8 values -> one code dword (value j in nibble j)
+__device__ __forceinline__ uint32_t e2m1x8_pow2(const float (&v)[8], float s) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, nan_to_zero(v[0]), nan_to_zero(v[1]), s, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, nan_to_zero(v[2]), nan_to_zero(v[3]), s, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, nan_to_zero(v[4]), nan_to_zero(v[5]), s, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, nan_to_zero(v[6]), nan_to_zero(v[7]), s, 3);
+  return clear_negative_zeros(w);
+}
+
+// 8 values -> one code dword with the group's scale s of format FMT
+template <int FMT>
+__device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8], float s) {
+  if constexpr (FMT == 0) {
+    return e2m1x8_pow2(v, s);
+  } else {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w |= e2m1_code(v[c], s) << (4 * c);
+    return w;
+  }
+}
+
+// Softmax pooling of a channel over two tokens (m = 2): the token with the
+// larger gate weighs 1 / (1 + e) and the other e / (1 + e), e = exp(-|g0 -
+// g1|) -- the rule's weights exp(g_t - max) / sum, whose larger term is
+// exp(0) = 1, so one exponential per channel.  e is exp2 of -|g0 - g1| log2 e
+// (v_exp_f32, 1 ulp; the product's rounding moves e by about |g0 - g1|
+// 2^-24 relative) and the quotient a hardware reciprocal: a few ulps of fp32
+// in all.  A gate of +inf gives NaN (exp(inf - inf)), as do NaN gates and
+// two -inf gates.
+__device__ __forceinline__ float pool2(float g0, float g1, float x0, float x1) {
+  const float gm = fmaxf(g0, g1);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(g0 - g1) * 1.4426950408889634f) + (gm - gm);
+  const bool first = g0 >= g1;
+  const float xa = first ? x0 : x1, xb = first ? x1 : x0;
+  return fmaf(e, xb, xa) * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ------------------------------------------------------- generic quantiser
@@ -83,8 +136,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const uint32_t b = scale_code<FMT>(amax);
   const float s = scale_value<FMT>(b);
   if (!active) return;
-  uint32_t c = e2m1_code(v.x, s) | (e2m1_code(v.y, s) << 4) | (e2m1_code(v.z, s) << 8) |
-               (e2m1_code(v.w, s) << 12);
+  uint32_t c;
+  if constexpr (FMT == 0) {
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, nan_to_zero(v.x), nan_to_zero(v.y), s, 0);
+    c = clear_negative_zeros(__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, nan_to_zero(v.z), nan_to_zero(v.w), s, 1));
+  } else {
+    c = e2m1_code(v.x, s) | (e2m1_code(v.y, s) << 4) | (e2m1_code(v.z, s) << 8) | (e2m1_code(v.w, s) << 12);
+  }
   reinterpret_cast<uint16_t*>(codes)[i4] = (uint16_t)c;
   if ((i4 % LPG) == 0) scales[i4 / LPG] = (uint8_t)b;
 }
@@ -199,29 +257,16 @@ __global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
 #pragma unroll
       for (int c = 0; c < 8; ++c) pooled[c] = bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
     } else if (m == 2) {
-      // the same operations, in the same order, as the general loop below
-      float gmax[8], num[8], den[8];
+      const uint32_t g0w[4] = {gpre[j][0].x, gpre[j][0].y, gpre[j][0].z, gpre[j][0].w};
+      const uint32_t g1w[4] = {gpre[j][1].x, gpre[j][1].y, gpre[j][1].z, gpre[j][1].w};
+      const uint32_t x0w[4] = {xpre[j][0].x, xpre[j][0].y, xpre[j][0].z, xpre[j][0].w};
+      const uint32_t x1w[4] = {xpre[j][1].x, xpre[j][1].y, xpre[j][1].z, xpre[j][1].w};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) { gmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t gw[4] = {gpre[j][t].x, gpre[j][t].y, gpre[j][t].z, gpre[j][t].w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) gmax[c] = fmaxf(gmax[c], bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu));
+      for (int c = 0; c < 8; ++c) {
+        const int sh = 16 * (c % 2);
+        pooled[c] = pool2(bf16_bits_to_f32((g0w[c / 2] >> sh) & 0xFFFFu), bf16_bits_to_f32((g1w[c / 2] >> sh) & 0xFFFFu),
+                          bf16_bits_to_f32((x0w[c / 2] >> sh) & 0xFFFFu), bf16_bits_to_f32((x1w[c / 2] >> sh) & 0xFFFFu));
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t gw[4] = {gpre[j][t].x, gpre[j][t].y, gpre[j][t].z, gpre[j][t].w};
-        const uint32_t xw[4] = {xpre[j][t].x, xpre[j][t].y, xpre[j][t].z, xpre[j][t].w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float ex = expf(bf16_bits_to_f32((gw[c / 2] >> (16 * (c % 2))) & 0xFFFFu) - gmax[c]);
-          num[c] += ex * bf16_bits_to_f32((xw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
-          den[c] += ex;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) pooled[c] = num[c] / den[c];
     } else {
       float gmax[8], num[8], den[8];
 #pragma unroll
@@ -276,9 +321,7 @@ __global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
       amax = group_reduce<2, true>(amax);
       const uint32_t b = scale_code<FMT>(amax);
       const float sv = scale_value<FMT>(b);
-      uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) word |= e2m1_code(y[c], sv) << (4 * c);
+      const uint32_t word = e2m1x8<FMT>(y, sv);
       *reinterpret_cast<uint32_t*>(main_codes + e * 256 + 4 * lane) = word;
       if ((lane & 1) == 0) main_scales[e * 32 + lane / 2] = (uint8_t)b;
     }
@@ -336,10 +379,7 @@ __global__ __launch_bounds__(64 * kWriteWaves, 2) void cache_write_kernel(
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
     amax = group_reduce<4, true>(amax);
     const uint32_t b = scale_code_e8m0(amax);
-    const float sv = e8m0_value(b);
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], sv) << (4 * j);
+    const uint32_t word = e2m1x8_pow2(v, e8m0_value(b));
     if (e < n_entries) {
       const int col0 = 16 * T * cs + 8 * ch;  // first column of these 8
       *reinterpret_cast<uint32_t*>(idx_codes + e * 64 + col0 / 2) = word;
@@ -428,15 +468,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     if (m == 1) {
       pooled[c] = bf16_bits_to_f32(latent[i]);
     } else {
-      const float g0 = bf16_bits_to_f32(pgate[i]), g1 = bf16_bits_to_f32(gate[i]);
-      const float gmax = fmaxf(fmaxf(-INFINITY, g0), g1);
-      const float e0 = expf(g0 - gmax), e1 = expf(g1 - gmax);
-      float num = 0.f, den = 0.f;
-      num += e0 * bf16_bits_to_f32(plat[i]);
-      den += e0;
-      num += e1 * bf16_bits_to_f32(latent[i]);
-      den += e1;
-      pooled[c] = num / den;
+      pooled[c] = pool2(bf16_bits_to_f32(pgate[i]), bf16_bits_to_f32(gate[i]), bf16_bits_to_f32(plat[i]),
+                        bf16_bits_to_f32(latent[i]));
     }
   }
   float ss = wave_sum(pooled[0] * pooled[0] + pooled[1] * pooled[1]);
@@ -467,13 +500,13 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
     const uint32_t sb = scale_code<FMT>(amax);
     const float sc = scale_value<FMT>(sb);
-    uint32_t w0 = 0, w1 = 0;
+    float v0[8], v1[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      w0 |= e2m1_code(v[j], sc) << (4 * j);
-      w1 |= e2m1_code(v[8 + j], sc) << (4 * j);
+      v0[j] = v[j];
+      v1[j] = v[8 + j];
     }
-    *reinterpret_cast<uint2*>(main_codes + row * 256 + 8 * t) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(main_codes + row * 256 + 8 * t) = make_uint2(e2m1x8<FMT>(v0, sc), e2m1x8<FMT>(v1, sc));
     main_scales[row * 32 + t] = (uint8_t)sb;
   }
   // indexer key from the unrotated entry: thread = (channel slice, column)
