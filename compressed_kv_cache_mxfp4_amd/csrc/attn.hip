@@ -500,6 +500,91 @@ __device__ __forceinline__ MergeRope merge_rope(int64_t pos, int d16) {
   return r;
 }
 
+// One round of a merge: the records and partial slices of up to four
+// splits s0 .. s0+3 for one thread (head bh, dims 16*d16 .. +15).
+struct MergeIn {
+  float4 e[4];
+  uint4 v[4][2];
+};
+
+__device__ __forceinline__ void merge_load(MergeIn& in, const float4* __restrict__ mlp,
+                                           const uint4* __restrict__ src, int s0, int S, uint32_t my_xcc) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (s0 + u < S) {
+      in.e[u] = mlp[s0 + u];
+      in.v[u][0] = src[(s0 + u) * 64];
+      in.v[u][1] = src[(s0 + u) * 64 + 1];
+    } else {
+      in.e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
+      in.v[u][0] = in.v[u][1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// Running state of one thread's merge (splits folded in with a running maximum).
+struct MergeAcc {
+  float acc[16];
+  float Mx, Lsum;
+  bool same_xcd;
+};
+
+__device__ __forceinline__ void merge_begin(MergeAcc& A) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) A.acc[j] = 0.f;
+  A.Mx = -INFINITY;
+  A.Lsum = 0.f;
+  A.same_xcd = true;
+}
+
+__device__ __forceinline__ void merge_fold(MergeAcc& A, const MergeIn& in, uint32_t my_xcc) {
+  float mg = A.Mx;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    mg = fmaxf(mg, in.e[u].x);
+    A.same_xcd &= __float_as_uint(in.e[u].z) == my_xcc;
+  }
+  if (mg == -INFINITY) return;  // nothing visible so far
+  const float rs = A.Mx == -INFINITY ? 0.0f : __expf(A.Mx - mg);
+  A.Lsum *= rs;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) A.acc[j] *= rs;
+  A.Mx = mg;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    // a chunk with no visible row has max -inf and a zero partial
+    const float wl = in.e[u].x == -INFINITY ? 0.0f : __expf(in.e[u].x - A.Mx) * in.e[u].y;
+    A.Lsum += wl;
+    const float wgt = ldexpf(wl, __float_as_int(in.e[u].w));  // undo the partial's 2^-e
+    const uint32_t hw[8] = {in.v[u][0].x, in.v[u][0].y, in.v[u][0].z, in.v[u][0].w,
+                            in.v[u][1].x, in.v[u][1].y, in.v[u][1].z, in.v[u][1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      A.acc[2 * j] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] & 0xFFFFu));
+      A.acc[2 * j + 1] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] >> 16));
+    }
+  }
+}
+
+template <bool ROPE>
+__device__ __forceinline__ void merge_store(MergeAcc& A, int64_t bh, int d16, uint16_t* __restrict__ out,
+                                            float* __restrict__ lse, const MergeRope& rope) {
+  float inv = A.Lsum > 0.f ? 1.0f / A.Lsum : 0.0f;
+  if (!A.same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
+  if (ROPE && d16 >= 28) {
+    // output inverse RoPE: dims 16*d16 .. +15 are pairs 8*(d16-28) .. +7
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rope_pair<true>(A.acc[2 * i], A.acc[2 * i + 1], rope.c[i], rope.s[i]);
+  }
+  uint32_t o8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o8[j] = pack_bf16x2(A.acc[2 * j] * inv, A.acc[2 * j + 1] * inv);
+  uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
+  op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+  op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+  if (lse && d16 == 0) lse[bh] = !A.same_xcd ? inv : (A.Lsum > 0.f ? A.Mx + logf(A.Lsum) : -INFINITY);
+}
+
 template <bool ROPE>
 __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const float4* __restrict__ ml,
                                              const uint16_t* __restrict__ part, uint16_t* __restrict__ out,
@@ -511,67 +596,47 @@ __device__ __forceinline__ void merge_splits(int b, int h0, int H, int S, const 
   const int64_t bh = (int64_t)b * H + h0 + hh;
   const float4* mlp = ml + bh * S;
   const uint4* src = reinterpret_cast<const uint4*>(part + bh * S * 512 + 16 * d16);
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  float Mx = -INFINITY, Lsum = 0.f;
-  bool same_xcd = true;
+  MergeAcc A;
+  merge_begin(A);
   for (int s0 = 0; s0 < S; s0 += 4) {
-    float4 e[4];
-    uint4 v[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (s0 + u < S) {
-        e[u] = mlp[s0 + u];
-        v[u][0] = src[(s0 + u) * 64];
-        v[u][1] = src[(s0 + u) * 64 + 1];
-      } else {
-        e[u] = make_float4(-INFINITY, 0.f, __uint_as_float(my_xcc), 0.f);
-        v[u][0] = v[u][1] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    float mg = Mx;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      mg = fmaxf(mg, e[u].x);
-      same_xcd &= __float_as_uint(e[u].z) == my_xcc;
-    }
-    if (mg == -INFINITY) continue;  // nothing visible so far
-    const float rs = Mx == -INFINITY ? 0.0f : __expf(Mx - mg);
-    Lsum *= rs;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] *= rs;
-    Mx = mg;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // a chunk with no visible row has max -inf and a zero partial
-      const float wl = e[u].x == -INFINITY ? 0.0f : __expf(e[u].x - Mx) * e[u].y;
-      Lsum += wl;
-      const float wgt = ldexpf(wl, __float_as_int(e[u].w));  // undo the partial's 2^-e
-      const uint32_t hw[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
-                              v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[2 * j] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] & 0xFFFFu));
-        acc[2 * j + 1] += wgt * (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[j] >> 16));
-      }
+    MergeIn in;
+    merge_load(in, mlp, src, s0, S, my_xcc);
+    merge_fold(A, in, my_xcc);
+  }
+  merge_store<ROPE>(A, bh, d16, out, lse, rope);
+}
+
+// All H heads of sequence b by 512 threads, 16 heads per round, when there
+// are at most four splits: the loads of round r+1 are issued before round r
+// is folded, so the rounds cost one memory round trip between them rather
+// than one each.
+template <bool ROPE>
+__device__ __forceinline__ void merge_all_heads(int b, int H, int S, const float4* __restrict__ ml,
+                                                const uint16_t* __restrict__ part, uint16_t* __restrict__ out,
+                                                float* __restrict__ lse, uint32_t my_xcc, int tid,
+                                                const MergeRope& rope) {
+  const int hh = tid >> 5, d16 = tid & 31;
+  auto load_round = [&](MergeIn& in, int r) {
+    const int64_t bh = (int64_t)b * H + 16 * r + hh;
+    merge_load(in, ml + bh * S, reinterpret_cast<const uint4*>(part + bh * S * 512 + 16 * d16), 0, S, my_xcc);
+  };
+  auto finish_round = [&](const MergeIn& in, int r) {
+    MergeAcc A;
+    merge_begin(A);
+    merge_fold(A, in, my_xcc);
+    merge_store<ROPE>(A, (int64_t)b * H + 16 * r + hh, d16, out, lse, rope);
+  };
+  const int R = H >> 4;
+  MergeIn in0, in1;
+  load_round(in0, 0);
+  for (int r = 0; r < R; r += 2) {
+    if (r + 1 < R) load_round(in1, r + 1);
+    finish_round(in0, r);
+    if (r + 1 < R) {
+      if (r + 2 < R) load_round(in0, r + 2);
+      finish_round(in1, r + 1);
     }
   }
-  float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
-  if (!same_xcd) inv = __uint_as_float(0x7FC00000u);  // never expected: make it loud
-  if (ROPE && d16 >= 28) {
-    // output inverse RoPE: dims 16*d16 .. +15 are pairs 8*(d16-28) .. +7
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rope_pair<true>(acc[2 * i], acc[2 * i + 1], rope.c[i], rope.s[i]);
-  }
-  uint32_t o8[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    o8[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-  uint4* op = reinterpret_cast<uint4*>(out + bh * 512 + 16 * d16);
-  op[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-  op[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-  if (lse && d16 == 0) lse[bh] = !same_xcd ? inv : (Lsum > 0.f ? Mx + logf(Lsum) : -INFINITY);
 }
 
 // One (sequence, 16 heads, chunk of 16*WAVES row slots).  Grid: XCD-aware
@@ -1374,9 +1439,16 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   // 16 heads per round
   if (q_pos) {
     const MergeRope rope = merge_rope(q_pos[b], tid & 31);
-    for (int h0 = 0; h0 < H; h0 += 16) merge_splits<true>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, rope);
+    if (S <= 4)
+      merge_all_heads<true>(b, H, S, ml, part, out, lse, my_xcc, tid, rope);
+    else
+      for (int h0 = 0; h0 < H; h0 += 16) merge_splits<true>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, rope);
   } else {
-    for (int h0 = 0; h0 < H; h0 += 16) merge_splits<false>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, MergeRope{});
+    if (S <= 4)
+      merge_all_heads<false>(b, H, S, ml, part, out, lse, my_xcc, tid, MergeRope{});
+    else
+      for (int h0 = 0; h0 < H; h0 += 16)
+        merge_splits<false>(b, h0, H, S, ml, part, out, lse, my_xcc, tid, MergeRope{});
   }
 }
 
