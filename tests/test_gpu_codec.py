@@ -75,6 +75,36 @@ def test_quantize_random_wide_range_and_edges(fmt, group):
     assert len(bad) == 0, f"rows differ: {bad[:10]}"
 
 
+@pytest.mark.parametrize("fmt,group", [(0, 16), (1, 16), (0, 32)])
+def test_quantize_nonfinite_inputs(fmt, group):
+    """NaN is ignored by the group maximum and encodes as +0; an infinity
+    saturates the scale byte and encodes as the largest magnitude; finite
+    values beside an infinity round to zero.  (The E8M0 path encodes on the
+    gfx950 scaled convert, which saturates NaN and keeps the sign of zero:
+    both are corrected, and these rows pin that.)"""
+    say(f"quantize non-finite fmt={fmt} group={group}")
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    g = np.random.default_rng(5 + fmt + group)
+    X = (g.standard_normal((12, 64)) * 3).astype(np.float32)
+    X[0, 0] = nan                      # one NaN in a finite group
+    X[1, :group] = nan                 # a group of NaNs only
+    X[2, 3] = inf
+    X[3, 5] = -inf
+    X[4, :group] = -nan
+    X[5, 1], X[5, 2] = inf, nan
+    X[6, :group] = -inf
+    X[7, ::3] = nan                    # NaNs scattered over every group
+    X[8, :] = -np.float32(1e-3)        # small negatives beside a large value: zero codes must be +0
+    X[8, 0] = 6.0
+    X[9, :] = -0.0
+    X[10, ::2] = nan
+    X[10, 1::2] = -np.float32(2.0 ** -140)
+    c_ref, s_ref = oracle.quantize(X, group, fmt)
+    c_gpu, s_gpu = _gpu_quant(X, group, fmt)
+    assert np.array_equal(s_gpu, s_ref)
+    assert np.array_equal(c_gpu, c_ref)
+
+
 def test_quantize_rejects_bad_arguments():
     x = torch.zeros(4, 48, device=DEV)
     with pytest.raises(K.Csa2Error):
