@@ -83,6 +83,11 @@ __device__ __forceinline__ uint32_t clear_negative_zeros(uint32_t w) {
   return mag | (w & ((mag + 0x77777777u) & 0x88888888u));  // sign kept where the magnitude is not 0
 }
 
+// one value -> its code (low nibble)
+__device__ __forceinline__ uint32_t e2m1_pow2(float x, float s) {
+  return clear_negative_zeros(__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, nan_to_zero(x), 0.0f, s, 0)) & 15u;
+}
+
 // 8 values -> one code dword (value j in nibble j)
 __device__ __forceinline__ uint32_t e2m1x8_pow2(const float (&v)[8], float s) {
   uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, nan_to_zero(v[0]), nan_to_zero(v[1]), s, 0);
@@ -528,7 +533,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     float amax = fabsf(v);
     amax = group_reduce<32, true>(amax);
     const uint32_t sb = scale_code_e8m0(amax);
-    kc[t] = e2m1_code(v, e8m0_value(sb));
+    kc[t] = e2m1_pow2(v, e8m0_value(sb));
     if (t == 0) idx_scales[row * 4 + ct] = (uint8_t)sb;
   }
   __syncthreads();
