@@ -377,6 +377,45 @@ def _certified_code_mismatch(vals, ref_codes, ref_scales, got_codes, got_scales,
     return n_bad
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cache_write_nonfinite_gates(fmt):
+    """Two-token pooling (m = 2) with infinite and NaN gates, against the
+    oracle's softmax exp(g_t - max) / sum: a +inf gate, a NaN gate or two -inf
+    gates make the channel NaN (exp(inf - inf)), so the whole entry is NaN
+    after RMSNorm and encodes as zero codes and zero scale bytes; a single
+    -inf gate gives the other token the whole weight."""
+    say(f"cache write non-finite gates fmt={fmt}")
+    n = 64
+    wl = syn.small("w", 77, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=2 * n, write_m=2)
+    lat, gate, w = syn.write_inputs(wl, "cpu")
+    g = gate.numpy().view(np.uint16).copy()
+    pinf, ninf, qnan = 0x7F80, 0xFF80, 0x7FC0
+    g[0, 5] = pinf                       # entry 0: +inf beside a finite gate
+    g[3, 100] = ninf                     # entry 1: -inf beside a finite gate
+    g[4, 7] = g[5, 7] = ninf             # entry 2: two -inf gates
+    g[6, 300] = qnan                     # entry 3: NaN gate
+    g[8, 0] = g[9, 0] = pinf             # entry 4: two +inf gates
+    g[10, 511], g[11, 511] = ninf, pinf  # entry 5: -inf and +inf
+    g[12, 20], g[13, 21] = ninf, ninf    # entry 6: one -inf in each of two channels
+    g[15, 64:80] = ninf                  # entry 7: a whole 16-channel group from one token
+    gate = torch.from_numpy(g.view(np.int16))
+    got = K.cache_write(lat.to(DEV), gate.to(DEV), 2, w.to(DEV), fmt)
+    torch.cuda.synchronize()
+    ref = oracle.cache_write(lat.numpy(), gate.numpy(), 2, w.numpy(), fmt)
+    gt = {k_: v.cpu().numpy() for k_, v in got.items()}
+    nan_rows = [0, 2, 3, 4, 5]
+    assert np.isnan(ref["y"][nan_rows]).all() and not np.isnan(ref["y"][[1, 6, 7]]).any()
+    for k_ in ("main_codes", "main_scales", "idx_codes", "idx_scales"):
+        assert (gt[k_][nan_rows] == 0).all() and (ref[k_][nan_rows] == 0).all(), k_
+    fin = [r for r in range(n) if r not in nan_rows]
+    nm = _certified_code_mismatch(ref["y"][fin], ref["main_codes"][fin], ref["main_scales"][fin],
+                                  gt["main_codes"][fin], gt["main_scales"][fin], 16, fmt)
+    nk = _certified_code_mismatch(ref["k"][fin], ref["idx_codes"][fin], ref["idx_scales"][fin],
+                                  gt["idx_codes"][fin], gt["idx_scales"][fin], 32, 0)
+    say(f"  certified mismatches: main {nm}, indexer {nk}")
+    assert nm + nk <= 2
+
+
 def _rope_positions(n, seed):
     """Entry positions for the compressed RoPE: 0, small, 400 (pair 16 turns by
     1 rad), and large values up to 2^31 - 1."""
