@@ -57,8 +57,9 @@ __device__ __forceinline__ float scale_value(uint32_t b) {
   return FMT == 0 ? e8m0_value(b) : e4m3_value(b);
 }
 
-// Nearest E2M1 code of x / s, ties to the even code; all products are exact.
-// (Any scale; E8M0 groups use the converts below, which give the same codes.)
+// Nearest E2M1 code of x / s, ties to the even code; all products are exact
+// while 5 s is finite (every E4M3 scale; E8M0 groups use the converts below,
+// which also cover the scales near 2^127).
 __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   float a = fabsf(x);
   if (!(a > 0.0f)) return 0u;
