@@ -33,18 +33,22 @@ __device__ __forceinline__ uint32_t scale_code_e8m0(float amax) {
   return (uint32_t)b;
 }
 
+// Smallest E4M3 code b (0x7E at most) with 6 * value(b) >= amax, in closed
+// form: t = amax * RN(1/6) taken up to the E4M3 grid -- m * 2^-9 below 2^-6,
+// else the exponent and three fraction bits rounded up -- then one code up if
+// 6 * value(b) < amax (an exact test: 6 * value(b) has at most five
+// significant bits).  t never rounds past a grid value v with 6 v >= amax:
+// 6 RN(1/6) - 1 < 2^-25, so amax RN(1/6) <= v (1 + 2^-25) stays within half
+// an ulp of v (v's significand is at most 1.875).  It can fall below amax / 6
+// by half an ulp, hence the one step up.  Equal to a search over the codes
+// for every non-NaN fp32 amax (checked exhaustively on the host).
 __device__ __forceinline__ uint32_t scale_code_e4m3(float amax) {
   if (!(amax > 0.0f)) return 0u;
-  if (6.0f * e4m3_value(0x7Eu) < amax) return 0x7Eu;  // saturate
-  int lo = 0, hi = 0x7E;                               // smallest b with 6*val(b) >= amax
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (6.0f * e4m3_value((uint32_t)mid) >= amax)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return (uint32_t)lo;
+  const float t = amax * (1.0f / 6.0f);
+  int b = t < 0x1p-6f ? (int)ceilf(t * 512.0f) : (int)((__float_as_uint(t) - (120u << 23) + 0xFFFFFu) >> 20);
+  b = min(b, 0x7E);
+  if (6.0f * e4m3_value((uint32_t)b) < amax) b = min(b + 1, 0x7E);
+  return (uint32_t)b;
 }
 
 template <int FMT>
@@ -57,26 +61,18 @@ __device__ __forceinline__ float scale_value(uint32_t b) {
   return FMT == 0 ? e8m0_value(b) : e4m3_value(b);
 }
 
-// Nearest E2M1 code of x / s, ties to the even code; all products are exact
-// while 5 s is finite (every E4M3 scale; E8M0 groups use the converts below,
-// which also cover the scales near 2^127).
-__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
-  float a = fabsf(x);
-  if (!(a > 0.0f)) return 0u;
-  uint32_t c = (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
-               (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
-               (uint32_t)(a > 5.0f * s);
-  if (c != 0u && (__float_as_uint(x) >> 31)) c |= 8u;
-  return c;
-}
+// The encoding rule: the nearest E2M1 code of x / s, ties to the even code,
+// saturating at 6, a zero magnitude as +0 and NaN as 0.  gfx950's
+// v_cvt_scalef32_pk_fp4_f32 applies it for power-of-two scales, two values
+// per instruction; other scales are divided out first (E4M3 below).
 
 // E2M1 codes of values over a power-of-two scale s (an E8M0 value), two per
 // v_cvt_scalef32_pk_fp4_f32: x / s rounded to nearest, ties to even,
-// saturating at 6 -- measured on gfx950 to agree with e2m1_code for every
+// saturating at 6 -- measured on gfx950 to agree with the rule for every
 // midpoint and its neighbours, every grid point, saturation, subnormal values
-// and subnormal scales, except that it gives a zero magnitude the sign of x
-// and saturates NaN.  So NaN is taken as 0 first and the sign of zero
-// magnitudes is cleared after (+0, as the rule above has it).
+// and subnormal scales (2^-127 .. 2^30), except that it gives a zero
+// magnitude the sign of x and saturates NaN.  So NaN is taken as 0 first and
+// the sign of zero magnitudes is cleared after.
 __device__ __forceinline__ float nan_to_zero(float x) { return x == x ? x : 0.0f; }
 
 __device__ __forceinline__ uint32_t clear_negative_zeros(uint32_t w) {
@@ -98,17 +94,52 @@ __device__ __forceinline__ uint32_t e2m1x8_pow2(const float (&v)[8], float s) {
   return clear_negative_zeros(w);
 }
 
+// E2M1 codes over an E4M3 scale s = 2^E * sig (sig = 1 + j/8; the subnormal
+// codes' m * 2^-9 normalise the same way): the convert takes 2^E, and each
+// value is first divided by sig, correctly rounded -- the product with
+// r = RN(1/sig) and one residual step, q = q0 + (x - q0 sig) r, which gives
+// RN(x / sig) when q0 is within an ulp and r within half an ulp (Markstein's
+// theorem).  The codes follow the rule for x / s: a midpoint M of the grid (at
+// most 3 significant bits) times sig has at most 7, so an fp32 x other than
+// M sig 2^E has x / sig more than half an ulp of M 2^E away from it, and the
+// rounded quotient stays on the same side of every midpoint; x = M sig 2^E
+// gives the midpoint itself, which the convert rounds to the even code.
+// Checked on the host for every fp32 x in [s 2^-7, s 2^5) and every scale
+// code.  NaN is taken as 0 and infinities are clamped to +-2^100 (still
+// saturating) so that the residual stays finite.  Scale code 0 (a group of
+// zeros) converts at 2^0.
+struct E4m3Div {
+  float sig, r, pow2;
+};
+
+__device__ __forceinline__ E4m3Div e4m3_div(float s) {
+  const uint32_t su = __float_as_uint(s);
+  const float sig = __uint_as_float((su & 0x007FFFFFu) | 0x3F800000u);
+  return E4m3Div{sig, 1.0f / sig, s == 0.0f ? 1.0f : __uint_as_float(su & 0x7F800000u)};
+}
+
+__device__ __forceinline__ float e4m3_quot(float x, const E4m3Div& d) {
+  const float xc = fminf(fmaxf(nan_to_zero(x), -0x1p100f), 0x1p100f);
+  const float q0 = xc * d.r;
+  return fmaf(fmaf(-q0, d.sig, xc), d.r, q0);
+}
+
+__device__ __forceinline__ uint32_t e2m1x8_e4m3(const float (&v)[8], float s) {
+  const E4m3Div d = e4m3_div(s);
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, e4m3_quot(v[0], d), e4m3_quot(v[1], d), d.pow2, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e4m3_quot(v[2], d), e4m3_quot(v[3], d), d.pow2, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e4m3_quot(v[4], d), e4m3_quot(v[5], d), d.pow2, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e4m3_quot(v[6], d), e4m3_quot(v[7], d), d.pow2, 3);
+  return clear_negative_zeros(w);
+}
+
 // 8 values -> one code dword with the group's scale s of format FMT
 template <int FMT>
 __device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8], float s) {
-  if constexpr (FMT == 0) {
+  if constexpr (FMT == 0)
     return e2m1x8_pow2(v, s);
-  } else {
-    uint32_t w = 0u;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) w |= e2m1_code(v[c], s) << (4 * c);
-    return w;
-  }
+  else
+    return e2m1x8_e4m3(v, s);
 }
 
 // Softmax pooling of a channel over two tokens (m = 2): the token with the
@@ -147,7 +178,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, nan_to_zero(v.x), nan_to_zero(v.y), s, 0);
     c = clear_negative_zeros(__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, nan_to_zero(v.z), nan_to_zero(v.w), s, 1));
   } else {
-    c = e2m1_code(v.x, s) | (e2m1_code(v.y, s) << 4) | (e2m1_code(v.z, s) << 8) | (e2m1_code(v.w, s) << 12);
+    const E4m3Div d = e4m3_div(s);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, e4m3_quot(v.x, d), e4m3_quot(v.y, d), d.pow2, 0);
+    c = clear_negative_zeros(__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, e4m3_quot(v.z, d), e4m3_quot(v.w, d), d.pow2, 1));
   }
   reinterpret_cast<uint16_t*>(codes)[i4] = (uint16_t)c;
   if ((i4 % LPG) == 0) scales[i4 / LPG] = (uint8_t)b;

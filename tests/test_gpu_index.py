@@ -255,6 +255,44 @@ def test_index_pool_masks_invalid_entries():
     assert np.array_equal(t.cpu().numpy()[0], rt)
 
 
+@pytest.mark.parametrize("pool_cap,misalign", [(16384, False), (16384, True), (12347, False), (4096, True)])
+def test_index_pool_selection_layouts(pool_cap, misalign):
+    """Reindex selection exact on the GPU's own pool scores: pool_cap a
+    multiple of 8 or ragged, scores in a caller buffer 4 bytes past a 16-byte
+    boundary; pool lengths full, ending inside a group, one group and a single
+    entry, and zero; k = 512, 100 and 1; the two-phase call equals the fused
+    one."""
+    B, cap = 4, 40000
+    say(f"index_pool selection pool_cap={pool_cap} misaligned={misalign}")
+    wl = syn.small("pl", 31 + pool_cap, B=B, cap=cap, H_idx=64, k=512, n_blocks=0)
+    cache = build_gpu_cache(wl, 0)
+    lt = torch.full((B,), cap, dtype=torch.int32, device=DEV)
+    rng = np.random.default_rng(pool_cap + misalign)
+    plen = np.array([pool_cap, pool_cap - 5, 9, 0], np.int32)
+    pool = np.full((B, pool_cap), -1, np.int32)
+    for b in range(B):
+        pool[b, :plen[b]] = np.sort(rng.choice(cap, plen[b], replace=False))
+    pool_t = torch.from_numpy(pool).to(DEV)
+    pl_t = torch.from_numpy(plen).to(DEV)
+    q, w = syn.index_query(wl, 0, DEV), syn.index_weights(wl, 0, DEV)
+    pws = torch.empty(K.lib().csa2_index_pool_workspace(B, pool_cap, 512), dtype=torch.uint8, device=DEV)
+    if misalign:
+        ps = torch.empty(B * pool_cap + 1, dtype=torch.float32, device=DEV)[1:].view(B, pool_cap)
+        assert ps.data_ptr() % 16 == 4
+    else:
+        ps = torch.empty(B, pool_cap, dtype=torch.float32, device=DEV)
+    K.index_pool_score(cache["idx_codes"], cache["idx_scales"], lt, pool_t, pl_t, q, w, pws, pool_scores=ps)
+    fused = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool_t, pl_t, q, w, k=512)
+    psn = ps.cpu().numpy()
+    for k in (512, 100, 1):
+        tk = K.index_pool_select(pool_t, pl_t, pws, k=k, pool_scores=ps).cpu().numpy()
+        for b in range(B):
+            n = plen[b]
+            assert np.array_equal(tk[b], brute_topk(psn[b, :n], k, pool[b, :n])), (k, b)
+        if k == 512:
+            assert np.array_equal(tk, fused.cpu().numpy())
+
+
 # ------------------------------------------------------------ FP4 indexer query
 # The query quantised to MX-FP4 (E2M1, E8M0 per 32 dims) by csa2_quantize_fp4;
 # the oracle quantises the same float query itself (bytes must agree), and
