@@ -1309,9 +1309,12 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
         toff[dt] = tr * kTRowB + 256 * wr + (((2 * dt + (ta >> 1)) ^ tswz(tr)) << 4) + 8 * (ta & 1);
     }
     __syncthreads();  // chunk c_begin staged
-    // step s: multiply chunk s-1, stage chunk s+1 (rows in X), then load the
-    // rows of chunk s+4 (index entry in Pn) and the index entries of chunk s+7
+    // step s: stage chunk s+1 (rows in X), multiply chunk s-1, then load the
+    // rows of chunk s+4 (index entry in Pn) and the index entries of chunk s+7.
+    // Staging first puts the value wave's conversions beside the score wave's
+    // products on the same SIMD (R[(s+1)%3] was last read in step s-1).
     auto vstep = [&](int s, TStage& X, int32_t& Pn) {
+      if (s + 1 < nc) stage((s + 1) % 3, X, c_begin + s + 1);
       if (s >= 1 && s <= nc) {
         // ---- O^T(dims of this wave, all heads) += R^T . P^T for chunk s-1
         const uint8_t* Rb = sm.R[(s - 1) % 3];
@@ -1349,7 +1352,6 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
             O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pbv[ht], O[dt][ht], 0, 0, 0);
         }
       }
-      if (s + 1 < nc) stage((s + 1) % 3, X, c_begin + s + 1);
       // issued on every step (past the split they read a dummy row), so that
       // the count of outstanding loads is the same on every path and each
       // wait covers only the loads it needs
