@@ -58,6 +58,40 @@ def test_quantize_exhaustive_codes_and_scales(fmt, group):
 
 
 @pytest.mark.parametrize("fmt,group", [(0, 16), (1, 16), (0, 32)])
+def test_quantize_scale_boundaries(fmt, group):
+    """Group maxima at 6 s for every scale code s and at its fp32 neighbours
+    (one and two ulps either side): the scale byte changes exactly there.
+    The other values sit on E2M1 midpoints of the chosen scale."""
+    say(f"quantize scale boundaries fmt={fmt} group={group}")
+    rows = []
+    for b in _scale_codes(fmt):
+        with np.errstate(over="ignore"):
+            top = np.float32(6.0 * oracle.scale_value(b, fmt))
+        if not np.isfinite(top) or top == 0:
+            continue
+        cands = [top]
+        for d in (1, 2):
+            lo = hi = top
+            for _ in range(d):
+                lo = np.nextafter(lo, np.float32(0))
+                hi = np.nextafter(hi, np.float32(np.inf))
+            cands += [lo, hi]
+        for a in cands:
+            if not np.isfinite(a) or a == 0:
+                continue
+            x = np.zeros(group, np.float32)
+            x[0] = a
+            x[1] = -a
+            x[2:9] = np.float32(a / 6) * np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+            rows.append(x)
+    X = np.stack(rows)
+    c_ref, s_ref = oracle.quantize(X, group, fmt)
+    c_gpu, s_gpu = _gpu_quant(X, group, fmt)
+    assert np.array_equal(s_gpu, s_ref)
+    assert np.array_equal(c_gpu, c_ref)
+
+
+@pytest.mark.parametrize("fmt,group", [(0, 16), (1, 16), (0, 32)])
 def test_quantize_random_wide_range_and_edges(fmt, group):
     say(f"quantize random fmt={fmt} group={group}")
     g = np.random.default_rng(11 + fmt + group)
