@@ -429,7 +429,12 @@ def _rope_positions(n, seed):
                                                 (2, 0, True, 1024, False), (4, 1, True, 1024, False),
                                                 (1, 0, False, 37, False), (2, 1, True, 37, False),
                                                 (1, 0, False, 1024, True), (2, 1, True, 1024, True),
-                                                (1, 1, False, 37, True)])
+                                                (1, 1, False, 37, True),
+                                                # the general pooling loop (odd m, the largest m)
+                                                (3, 0, True, 37, False), (8, 1, False, 300, True),
+                                                # 4 and 8 column tiles per workgroup (from 2,033 and 4,081 entries)
+                                                (1, 1, False, 2100, True), (2, 0, False, 4100, False),
+                                                (2, 1, True, 4100, True)])
 def test_cache_write_parity(m, fmt, gamma, n, rope):
     say(f"cache write m={m} fmt={fmt} gamma={gamma} entries={n} rope={rope}")
     wl = syn.small("w", 31 + m, B=1, cap=1, H_idx=8, k=1, n_blocks=0, write_tokens=n * m, write_m=m)
