@@ -1492,7 +1492,6 @@ static AttnWs attn_ws_layout(int B, int H, int k, int swa_cap) {
 
 size_t attn_ws_bytes(int B, int H, int k, int swa_cap) { return attn_ws_layout(B, H, k, swa_cap).total; }
 
-size_t attn_ws_counter_bytes() { return (size_t)kMaxAttnGroups * sizeof(uint32_t); }
 
 int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const uint8_t* main_scales, int64_t cap, int main_fmt, const int32_t* len,

@@ -64,17 +64,6 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float e8m0_op) {
   return r;
 }
 
-// Eight E2M1 values -> fp32 with unit scale (for E4M3-scaled rows).
-__device__ __forceinline__ void fp4x8_to_f32(uint32_t codes, float out[8]) {
-  const float one = 1.0f;
-  auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0);
-  auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1);
-  auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2);
-  auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3);
-  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
-  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
-}
-
 // ------------------------------------------------------------ compressed RoPE
 // [ggaaooppeenngg.github.io, "DeepSeek-V4.1-Flash 架构解析", 3.2 and 7]: base
 // 160000; 64 of the 512 dims carry position.  These are dims 448..511 as 32
@@ -108,10 +97,6 @@ __device__ __forceinline__ void rope_pair(float& a, float& b, float c, float s) 
 }
 
 // ------------------------------------------------------------ wave helpers
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
-__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {
-  return (uint32_t)__shfl_xor((int)v, mask, kWave);
-}
 
 // Max and sum over lanes l, l^16, l^32, l^48 (one value per 16-lane row)
 // without an LDS round trip: v_permlane16_swap exchanges the odd and even
