@@ -164,8 +164,10 @@ def attn_sweep(batches, fmt_name, steps, window="tail"):
 
 
 def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
-    """Full indexer for Q queries per sequence (a speculative verify block): one
-    csa2_index_full_mq call against Q csa2_index_full calls, same caches and queries."""
+    """A speculative verify block of Q queries per sequence: the Full indexer as one
+    csa2_index_full_mq call against Q csa2_index_full calls, then the block's
+    attention as one csa2_sparse_attn_decode_mq call against Q
+    csa2_sparse_attn_decode calls; same caches, queries and index lists."""
     import torch
     import csa2_synth as syn
     import compressed_kv_cache_mxfp4_amd as K
@@ -222,6 +224,50 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
         res[name] = e0.elapsed_time(e1) * 1e3 / steps
     for i in range(Q):
         assert torch.equal(outs_mq["topk"][:, i], outs_1[i]["topk"]), "multi-query top-k differs"
+    # attention of the verify block: each query over its own top-k (from the
+    # multi-query call) plus the sequence's window, one call for the B x Q
+    # query rows against Q calls of B
+    del ic, isc, ws_mq, ws_1
+    torch.cuda.empty_cache()
+    mc = torch.empty(B, cap, 256, dtype=torch.uint8, device=dev)
+    ms = torch.empty(B, cap, 32, dtype=torch.uint8, device=dev)
+    for b in range(B):
+        K.quantize_fp4(syn.main_values(wl, b, dev), 16, K.E8M0, mc[b], ms[b])
+    W = wl.swa
+    aq = torch.stack([syn.attn_query(wl, i, dev) for i in range(Q)], 1).contiguous()  # [B][Q][64][512]
+    aqs = [aq[:, i].contiguous() for i in range(Q)]
+    tks = [outs_mq["topk"][:, i].contiguous() for i in range(Q)]
+    swa_len = torch.full((B,), W, dtype=torch.int32, device=dev)
+    wkw = dict(swa_codes=mc, swa_scales=ms, swa_len=swa_len, swa_stride=cap, swa_cap=W, swa_row0=cap - W)
+    ws_amq = torch.zeros(L.csa2_attn_workspace(B * Q, 64, wl.k, W), dtype=torch.uint8, device=dev)
+    ws_a1 = torch.zeros(L.csa2_attn_workspace(B, 64, wl.k, W), dtype=torch.uint8, device=dev)
+    out_mq = torch.empty(B, Q, 64, 512, dtype=torch.int16, device=dev)
+    out_1 = [torch.empty(B, 64, 512, dtype=torch.int16, device=dev) for _ in range(Q)]
+
+    def amq():
+        K.sparse_attn_decode_mq(aq, mc, ms, lengths, outs_mq["topk"], K.E8M0, out=dict(out=out_mq), _ws=ws_amq,
+                                **wkw)
+
+    def asep():
+        for i in range(Q):
+            K.sparse_attn_decode(aqs[i], mc, ms, lengths, tks[i], K.E8M0, out=dict(out=out_1[i]), _ws=ws_a1, **wkw)
+
+    for name, fn in (("attn_multi_query", amq), ("attn_separate", asep)):
+        for _ in range(max(warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    attn_bytes = Q * B * (wl.k * 288 + W * 288 + 64 * 512 * 2 * 2 + wl.k * 4 + 8)
     cache_bytes = B * cap * 68
     per_q = B * (wl.H_idx * (68 if index_q == "fp4" else 256) + wl.H_idx * 4 + 4) + B * (wl.k * 4 + wl.n_blocks * 8 * 4 + 4)
     nbytes = cache_bytes + Q * per_q
@@ -233,7 +279,13 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
                           us_multi_query=round(us, 2), us_separate_calls=round(res["separate"], 2),
                           positions_scored_per_s=Q * B * cap / (us * 1e-6),
                           algorithmic_bytes=nbytes, achieved_GBs=round(nbytes / (us * 1e-6) / 1e9, 1),
-                          frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))), flush=True)
+                          frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          attention=dict(query_rows=B * Q, window=W, us_multi_query=round(res["attn_multi_query"], 2),
+                                         us_separate_calls=round(res["attn_separate"], 2),
+                                         algorithmic_bytes=attn_bytes,
+                                         achieved_GBs=round(attn_bytes / (res["attn_multi_query"] * 1e-6) / 1e9, 1),
+                                         frac_hbm=round(attn_bytes / (res["attn_multi_query"] * 1e-6) / 1e9
+                                                        / HBM_PEAK_GBS, 4)))), flush=True)
 
 
 def phase_bytes(wl, B, lengths, pool_len, H_idx, H_attn=64, swa=128):

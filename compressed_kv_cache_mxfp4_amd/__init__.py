@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     lib,
     quantize_fp4,
     sparse_attn_decode,
+    sparse_attn_decode_mq,
     sparse_attn_decode_noalloc,
     sparse_attn_decode_rows,
     window_alloc,

@@ -69,6 +69,8 @@ def lib():
                                           P, i32, f32, P, P, P, P, sz, P]
     L.csa2_sparse_attn_decode_noalloc.argtypes = [P, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
                                                   P, i32, f32, P, P, P, P]
+    L.csa2_sparse_attn_decode_mq.argtypes = [P, i32, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
+                                             P, i32, f32, P, P, P, P, sz, P]
     L.csa2_window_write.argtypes = [P, i32, i32, P, f32, i32, P, i32, P, P, P, P]
     L.csa2_cache_append_paged.argtypes = [P, P, i32, i32, P, f32, P, i32, i32, P, P, P, P, i64, P, i32, i32, P, P, P]
     L.csa2_index_full_paged.argtypes = [P, P, i64, P, i32, i32, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P,
@@ -702,6 +704,56 @@ def sparse_attn_decode(q, main_codes, main_scales, lengths, topk, main_fmt: int,
         swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, int(swa_fmt) if swa_cap else 0,
         float(sm_scale), _ptr(q_pos), _ptr(o),
         _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "csa2_sparse_attn_decode")
+    return (o, lse) if return_lse else o
+
+
+def sparse_attn_decode_mq(q, main_codes, main_scales, lengths, topk, main_fmt: int,
+                          swa_codes=None, swa_scales=None, swa_len=None, swa_stride: int = 0,
+                          swa_cap: int = 0, swa_row0: int = 0, sm_scale: Optional[float] = None,
+                          return_lse: bool = False, out=None, _ws=None, q_pos=None, swa_fmt: int = 0):
+    """Q queries per sequence in one call (csa2_sparse_attn_decode_mq): q bf16/int16
+    [B][Q][H][512], topk int32 [B][Q][k], q_pos int64 [B][Q] or None; the caches,
+    lengths [B] and windows (as in sparse_attn_decode) are per sequence.  Returns
+    out bf16 bits (int16) [B][Q][H][512] (and lse fp32 [B][Q][H])."""
+    q = _bits16(q)
+    _req(q, "q", torch.int16)
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Q][H][512]")
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    _req(q, "q", torch.int16, dev, (B, Q, H, 512))
+    cap = main_codes.shape[1]
+    _req(main_codes, "main_codes", torch.uint8, dev, (B, cap, 256))
+    _req(main_scales, "main_scales", torch.uint8, dev, (B, cap, 32))
+    _req(lengths, "lengths", torch.int32, dev, (B,))
+    k = topk.shape[2]
+    _req(topk, "topk", torch.int32, dev, (B, Q, k))
+    rb, sb = (576, 8) if swa_fmt == SWA_FP8 else (256, 32)
+    if swa_cap > 0:
+        if swa_codes.dtype != torch.uint8 or swa_scales.dtype != torch.uint8:
+            raise TypeError("window planes must be uint8")
+        if not (swa_codes.is_contiguous() and swa_scales.is_contiguous()):
+            raise ValueError("window planes must be contiguous")
+        need = swa_row0 + (B - 1) * swa_stride + swa_cap
+        if swa_row0 < 0 or swa_codes.numel() < need * rb or swa_scales.numel() < need * sb:
+            raise ValueError("window planes smaller than swa_row0 + B rows of swa_stride")
+        _req(swa_len, "swa_len", torch.int32, dev, (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / (512 ** 0.5)
+    if q_pos is not None:
+        _req(q_pos, "q_pos", torch.int64, dev, (B, Q))
+    o = None if out is None else out.get("out")
+    if o is None:
+        o = torch.empty(B, Q, H, 512, dtype=torch.int16, device=dev)
+    lse = torch.empty(B, Q, H, dtype=torch.float32, device=dev) if return_lse else None
+    ws = _ws if _ws is not None else workspace(lib().csa2_attn_workspace(B * Q, H, k, swa_cap), dev, "attn")
+    _check(lib().csa2_sparse_attn_decode_mq(
+        _ptr(q), H, Q, _ptr(main_codes), _ptr(main_scales), cap, main_fmt, _ptr(lengths), _ptr(topk), k, B,
+        ctypes.c_void_p(swa_codes.data_ptr() + rb * swa_row0) if swa_cap else None,
+        ctypes.c_void_p(swa_scales.data_ptr() + sb * swa_row0) if swa_cap else None,
+        swa_stride, swa_cap, _ptr(swa_len) if swa_cap else None, int(swa_fmt) if swa_cap else 0,
+        float(sm_scale), _ptr(q_pos), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)),
+        "csa2_sparse_attn_decode_mq")
     return (o, lse) if return_lse else o
 
 

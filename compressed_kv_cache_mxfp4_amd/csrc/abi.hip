@@ -408,6 +408,23 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                                            as_stream(stream)));
 }
 
+int csa2_sparse_attn_decode_mq(const uint16_t* q, int32_t H, int32_t Q, const uint8_t* main_codes,
+                               const uint8_t* main_scales, int64_t cap, int32_t main_fmt, const int32_t* len,
+                               const int32_t* topk, int32_t k, int32_t B, const uint8_t* swa_codes,
+                               const uint8_t* swa_scales, int64_t swa_stride, int32_t swa_cap,
+                               const int32_t* swa_len, int32_t swa_fmt, float sm_scale, const int64_t* q_pos,
+                               uint16_t* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  if (Q < 1 || Q > CSA2_MAX_QUERIES_PER_SEQ || B < 0 || (int64_t)B * Q > INT32_MAX) return CSA2_ERR_SHAPE;
+  const int32_t R = B * Q;  // query rows
+  const int rc = check_attn(q, H, main_codes, main_scales, cap, CSA2_MAX_CACHE_ROWS, main_fmt, true, len, topk, k,
+                            R, swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale, q_pos, out);
+  if (rc != CSA2_OK || B == 0) return rc;
+  if (!ws || ws_bytes < csa2_attn_workspace(R, H, k, swa_cap)) return CSA2_ERR_WORKSPACE;
+  return launched(csa2::launch_sparse_attn(q, H, main_codes, main_scales, cap, main_fmt, len, topk, k, R,
+                                           swa_codes, swa_scales, swa_stride, swa_cap, swa_len, swa_fmt, sm_scale,
+                                           q_pos, out, lse_opt, ws, as_stream(stream), false, Q));
+}
+
 int csa2_sparse_attn_decode_noalloc(const uint16_t* q, int32_t H, const uint8_t* main_codes,
                                     const uint8_t* main_scales, int64_t cap, int32_t main_fmt,
                                     const int32_t* len, const int32_t* topk, int32_t k, int32_t B,

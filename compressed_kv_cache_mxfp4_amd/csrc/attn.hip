@@ -651,7 +651,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units, int64_t seq_stride) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int seq_units, int64_t seq_stride, int qps) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   using Smem = AttnSmem<WAVES>;
   constexpr int kRows = Smem::kRows, kPP = Smem::kPP, kThreads = 64 * WAVES;
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
                "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
                "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S),
-               "s"(seq_units), "s"(q_pos), "s"(seq_stride));
+               "s"(seq_units), "s"(q_pos), "s"(seq_stride), "s"(qps));
   const int HG = H >> 4;
   // Placement unit: a sequence (all its head groups and chunks) when B >= 8,
   // otherwise one (sequence, head group).  A unit's workgroups get ids
@@ -682,6 +682,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   const int gi = !valid ? 0 : (seq_units ? unit * HG + within / S : unit);  // (sequence, head group)
   const int sidx = within % S;
   const int b = gi / HG, hg = gi - b * HG;
+  // query row b reads cache bc (its rows, length and window); its query,
+  // index list, position, partials and output are its own
+  const int bc = qps == 1 ? b : b / qps;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int kw = WF8 ? (k + 15) & ~15 : k;  // first window slot
   const int nslots = kw + swa_cap;
@@ -701,8 +704,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   const bool wwin = WF8 && kRows * sidx + 16 * w >= kw;
   const int32_t* tp = k > 0 ? topk + (int64_t)b * k + min(slot, k - 1) : reinterpret_cast<const int32_t*>(q);
   const int32_t praw = tp[0];
-  const int32_t Lraw = (len ? len + b : reinterpret_cast<const int32_t*>(q))[vzero];
-  const int32_t SLraw = (swa_len ? swa_len + b : reinterpret_cast<const int32_t*>(q))[vzero];
+  const int32_t Lraw = (len ? len + bc : reinterpret_cast<const int32_t*>(q))[vzero];
+  const int32_t SLraw = (swa_len ? swa_len + bc : reinterpret_cast<const int32_t*>(q))[vzero];
   const uint4* qg = reinterpret_cast<const uint4*>(q + ((int64_t)b * H + 16 * hg) * 512);
   // 16 heads x 64 pieces of 16 B: two pieces per thread
   static_assert(kThreads >= 512 && kThreads < 1024, "two query pieces per thread");
@@ -738,7 +741,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES <= 8 ? 4 : 1) void attn_split_ker
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
   RowFetch row;
   {
-    const RowSrc src = locate_row<WF8>(slot, pidx, nslots, b, k, kw, L, SL, seq_stride, swa_stride, main_codes,
+    const RowSrc src = locate_row<WF8>(slot, pidx, nslots, bc, k, kw, L, SL, seq_stride, swa_stride, main_codes,
                                        main_scales, swa_codes, swa_scales);
     if constexpr (WF8)
       fetch_row_w8(row, src, g);
@@ -1023,17 +1026,20 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     const uint8_t* __restrict__ swa_scales, int64_t swa_stride, int swa_cap,
     const int32_t* __restrict__ swa_len, float sm_scale, const int64_t* __restrict__ q_pos, int B, int S,
     uint16_t* __restrict__ part, float4* __restrict__ ml, uint32_t* __restrict__ cnt,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t seq_stride) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t seq_stride, int qps) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnTSmem& sm = *reinterpret_cast<AttnTSmem*>(smem_raw);
   asm volatile("" ::"s"(q), "s"(main_codes), "s"(main_scales), "s"(len), "s"(topk), "s"(swa_codes),
                "s"(swa_scales), "s"(swa_len), "s"(part), "s"(ml), "s"(cnt), "s"(out), "s"(lse),
-               "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S));
+               "s"(H), "s"(cap), "s"(k), "s"(swa_stride), "s"(swa_cap), "s"(sm_scale), "s"(B), "s"(S), "s"(qps));
   // the S workgroups of a sequence get ids congruent mod 8 (one XCD), so the
   // partials the last one merges are in its L2
   const int id = blockIdx.x, xcd = id & 7, r8 = id >> 3;
   const int b = (r8 / S) * 8 + xcd, sidx = r8 % S;
   if (b >= B) return;  // padding workgroup (uniform, before any barrier)
+  // query row b reads cache bc (its rows, length and window); its query,
+  // index list, position, partials and output are its own
+  const int bc = qps == 1 ? b : b / qps;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const bool scorer = w < 4;  // wave-uniform role
   const int wr = w & 3;       // index within the role
@@ -1051,9 +1057,9 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
   // (the extra steps only synchronise); both roles run exactly this many
   const int nsteps = (nc + 1 + 2) / 3 * 3;
 
-  int64_t L = len ? len[b] : cap;  // no lengths: absolute row ids below cap
+  int64_t L = len ? len[bc] : cap;  // no lengths: absolute row ids below cap
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  int SL = swa_len ? swa_len[b] : 0;
+  int SL = swa_len ? swa_len[bc] : 0;
   SL = SL < 0 ? 0 : (SL > swa_cap ? swa_cap : SL);
 
   // ---- value waves: staging role, row srow of a chunk, dims 64*ssp .. +63;
@@ -1074,7 +1080,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     const int32_t* ip = k > 0 ? tbase + min(slot, k - 1) : reinterpret_cast<const int32_t*>(dummy);
     if (WF8 && c >= kwc) {
       const int rr = (c - kwc) * 16 + wrow;
-      ip = rr < SL ? reinterpret_cast<const int32_t*>(swa_scales + ((int64_t)b * swa_stride + rr) * kWinScaleB +
+      ip = rr < SL ? reinterpret_cast<const int32_t*>(swa_scales + ((int64_t)bc * swa_stride + rr) * kWinScaleB +
                                                       4 * ((wt >> 1) >> 2))
                    : reinterpret_cast<const int32_t*>(dummy);
     }
@@ -1088,13 +1094,13 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
     if (c < c_end) {
       if (slot < k) {
         if (p >= 0 && (int64_t)p < L) {
-          cp = main_codes + ((int64_t)b * seq_stride + p) * 256;
-          scp = main_scales + ((int64_t)b * seq_stride + p) * 32;
+          cp = main_codes + ((int64_t)bc * seq_stride + p) * 256;
+          scp = main_scales + ((int64_t)bc * seq_stride + p) * 32;
           ok = 1u;
         }
       } else if (!WF8 && slot < nslots && slot - k < SL) {
-        cp = swa_codes + ((int64_t)b * swa_stride + (slot - k)) * 256;
-        scp = swa_scales + ((int64_t)b * swa_stride + (slot - k)) * 32;
+        cp = swa_codes + ((int64_t)bc * swa_stride + (slot - k)) * 256;
+        scp = swa_scales + ((int64_t)bc * swa_stride + (slot - k)) * 32;
         ok = 1u;
       }
     }
@@ -1104,7 +1110,7 @@ __global__ __launch_bounds__(512, 1) void attn_seq_kernel(
       // FP8 window record: bit 0 of ok = visible, bits 8..15 = the scale byte
       const int rr = (c - kwc) * 16 + wrow;
       const bool vis = c < c_end && rr < SL;
-      cp = vis ? swa_codes + ((int64_t)b * swa_stride + rr) * kWinDataB : dummy;
+      cp = vis ? swa_codes + ((int64_t)bc * swa_stride + rr) * kWinDataB : dummy;
       a0 = cp + 32 * wt;
       as = cp + 512 + 4 * wt;
       ok = vis ? 1u | ((((uint32_t)p >> (8 * ((wt >> 1) & 3))) & 0xFFu) << 8) : 0u;
@@ -1498,8 +1504,9 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
                        const int32_t* swa_len, int swa_fmt, float sm_scale, const int64_t* q_pos,
-                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st, bool abs_rows) {
+                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st, bool abs_rows, int qps) {
   if (B == 0) return 0;
+  // B counts query rows; with qps > 1 query row b reads cache b / qps
   // abs_rows: the index list holds row ids into one pool of cap rows shared
   // by all sequences (no lengths); otherwise positions into sequence b's cap rows
   const int64_t seq_stride = abs_rows ? 0 : cap;
@@ -1536,7 +1543,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
       if (!lds_ok) return false;
       kern<<<tgrid, 512, sizeof(AttnTSmem), st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                                    swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, Sq,
-                                                   part, ml, cnt, out, lse_opt, seq_stride);
+                                                   part, ml, cnt, out, lse_opt, seq_stride, qps);
       return true;
     };
     bool ok;
@@ -1556,7 +1563,7 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
     if (!lds_ok) return false;
     kern<<<grid, 64 * waves, smem, st>>>(q, H, main_codes, main_scales, cap, len, topk, k, swa_codes,
                                          swa_scales, swa_stride, swa_cap, swa_len, sm_scale, q_pos, B, S,
-                                         part, ml, cnt, out, lse_opt, seq_units, seq_stride);
+                                         part, ml, cnt, out, lse_opt, seq_units, seq_stride, qps);
     return true;
   };
   auto pick = [&](auto fmt_c, auto w8_c) -> bool {

@@ -100,7 +100,8 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
                        const int32_t* topk, int k, int B, const uint8_t* swa_codes,
                        const uint8_t* swa_scales, int64_t swa_stride, int swa_cap,
                        const int32_t* swa_len, int swa_fmt, float sm_scale, const int64_t* q_pos,
-                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st, bool abs_rows = false);
+                       uint16_t* out, float* lse_opt, void* ws, hipStream_t st, bool abs_rows = false,
+                       int qps = 1);
 int launch_window_write(const uint16_t* latent, int B, int n, const float* gamma, float eps, int rope,
                         const int64_t* pos0, int W, uint8_t* data, uint8_t* scales, int32_t* swa_len,
                         hipStream_t st);

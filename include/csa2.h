@@ -81,7 +81,7 @@ extern "C" {
 
 #define CSA2_MAX_TOPK 2048
 #define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
-#define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache in csa2_index_full_mq */
+#define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache (csa2_index_full_mq, csa2_sparse_attn_decode_mq) */
 #define CSA2_MIN_PAGE_SHIFT 6      /* paged cache: pages of 2^6 .. 2^20 entries    */
 #define CSA2_MAX_PAGE_SHIFT 20
 #define CSA2_MAX_POOL_ROWS (1 << 26) /* rows of a paged pool (32-bit byte offsets)  */
@@ -432,6 +432,33 @@ int csa2_sparse_attn_decode(const uint16_t* q, int32_t H, const uint8_t* main_co
                             int64_t swa_stride, int32_t swa_cap, const int32_t* swa_len,
                             int32_t swa_fmt, float sm_scale, const int64_t* q_pos, uint16_t* out,
                             float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_sparse_attn_decode_mq -- csa2_sparse_attn_decode for Q queries per
+ * sequence that arrive together, such as the draft positions of a
+ * speculative verify block [WG 7 (DSpark: 5 parallel draft positions)], each
+ * with its own index list over its sequence's cache, in one call.
+ *   q        : bf16 bits [B][Q][H][512];  topk : int32 [B][Q][k];
+ *   q_pos    : int64 [B][Q] or NULL;  out : bf16 bits [B][Q][H][512];
+ *   lse_opt  : fp32 [B][Q][H] or NULL.
+ *   main planes, len [B], the window planes (sequence b at b*swa_stride) and
+ *   swa_len [B] are per sequence, as in csa2_sparse_attn_decode, and shared
+ *   by the sequence's Q queries.
+ *   Q        : 1..CSA2_MAX_QUERIES_PER_SEQ.
+ *   ws       : at least csa2_attn_workspace(B*Q, H, k, swa_cap) bytes, as above.
+ * Query row (b, i) gives exactly what csa2_sparse_attn_decode gives for a
+ * batch of B*Q queries whose sequence b*Q + i holds sequence b's cache,
+ * length and window; with Q = 1 this is csa2_sparse_attn_decode.  One kernel;
+ * B*Q query rows choose the kernel shape as B*Q sequences would.
+ * Errors: as csa2_sparse_attn_decode; Q outside 1..CSA2_MAX_QUERIES_PER_SEQ
+ * or B*Q beyond int32 is CSA2_ERR_SHAPE.
+ */
+int csa2_sparse_attn_decode_mq(const uint16_t* q, int32_t H, int32_t Q, const uint8_t* main_codes,
+                               const uint8_t* main_scales, int64_t cap, int32_t main_fmt, const int32_t* len,
+                               const int32_t* topk, int32_t k, int32_t B, const uint8_t* swa_codes,
+                               const uint8_t* swa_scales, int64_t swa_stride, int32_t swa_cap,
+                               const int32_t* swa_len, int32_t swa_fmt, float sm_scale, const int64_t* q_pos,
+                               uint16_t* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_sparse_attn_decode_noalloc -- csa2_sparse_attn_decode for callers that

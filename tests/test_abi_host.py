@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
             "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq", "csa2_index_full_mq_fp4q",
             "csa2_cache_append_paged", "csa2_index_full_paged", "csa2_index_pool_rows",
-            "csa2_sparse_attn_decode_rows",
+            "csa2_sparse_attn_decode_rows", "csa2_sparse_attn_decode_mq",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -217,6 +217,35 @@ def test_index_pool_and_attention_validation(lib):
     args = list(base)
     args[15], args[11] = 1, P(0x1004)     # FP8 window records: scale rows need 8-byte alignment
     assert a(*args) == ERR_ALIGN
+
+
+def test_attention_mq_validation(lib):
+    # Q queries per sequence: Q in 1..CSA2_MAX_QUERIES_PER_SEQ, the workspace
+    # sized for B*Q query rows, and every check of the one-query call
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    a = lib.csa2_sparse_attn_decode_mq
+    a.argtypes = [P, i32, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32, P, i32, ctypes.c_float, P, P, P,
+                  P, ctypes.c_size_t, P]
+    base = [FAKE, 64, 5, FAKE, FAKE, 4096, 0, FAKE, FAKE, 512, 16, FAKE, FAKE, 4096, 128, FAKE, 0, 0.04, None,
+            FAKE, None, FAKE, 1 << 40, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return a(*args)
+
+    assert call(2, 0) == ERR_SHAPE        # Q
+    assert call(2, 17) == ERR_SHAPE       # Q beyond CSA2_MAX_QUERIES_PER_SEQ
+    assert call(1, 40) == ERR_UNSUP
+    assert call(14, 129) == ERR_SHAPE     # window > 128
+    assert call(9, 5000) == ERR_SHAPE     # k
+    assert call(0, None) == ERR_NULL
+    assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(10, 0) == CSA2_OK         # empty batch
+    # the workspace must hold B*Q = 80 query rows, not B = 16
+    need = lib.csa2_attn_workspace(80, 64, 512, 128)
+    assert lib.csa2_attn_workspace(16, 64, 512, 128) < need
+    assert call(22, need - 1) == ERR_WS
 
 
 def test_attention_noalloc_validation(lib):

@@ -317,6 +317,62 @@ def test_attention_large_batch(B, k, W, fmt, rope):
     say(f"  {len(picks)} sequences checked, worst relative error {worst:.2e}")
 
 
+@pytest.mark.parametrize("B,Q,k,W,fmt,rope", [(3, 5, 512, 128, 0, False), (16, 5, 512, 128, 1, True),
+                                              (2, 3, 100, 0, 0, False), (1, 1, 64, 16, 1, False),
+                                              (12, 4, 300, 128, 0, True)])
+def test_attention_multi_query(B, Q, k, W, fmt, rope):
+    """Q queries per sequence in one call (csa2_sparse_attn_decode_mq), each
+    with its own index list over its sequence's cache and window: bit for bit
+    what csa2_sparse_attn_decode gives over B*Q sequences holding copies of
+    the caches (the same kernel shape: 15 and 48+ query rows pick the split
+    and the all-heads kernel), and each sampled query row against the oracle."""
+    say(f"attention multi-query B={B} Q={Q} k={k} W={W} fmt={fmt} rope={rope}")
+    cap = 3000
+    g = torch.Generator(device=DEV).manual_seed(900 + B * Q + k)
+    x = torch.randn(B, cap, 512, generator=g, device=DEV)
+    c, s = K.quantize_fp4(x, 16, fmt)
+    rng = np.random.default_rng(900 + B + Q)
+    lens = np.full(B, cap, np.int32)
+    lens[-1] = cap - 777
+    topk = np.stack([np.stack([rng.choice(int(lens[b]), k, replace=False) for _ in range(Q)])
+                     for b in range(B)]).astype(np.int32)
+    topk[0, 0, 3] = -1
+    topk[0, Q - 1, 5] = cap + 9          # out of range: masked
+    swl = np.full(B, W, np.int32)
+    if B > 1 and W:
+        swl[1] = W // 3
+    q = syn.as_bf16_bits(torch.randn(B, Q, 64, 512, generator=torch.Generator().manual_seed(B * 7 + Q)))
+    qpos = torch.from_numpy(rng.integers(0, 1 << 20, (B, Q)).astype(np.int64)) if rope else None
+    lt = torch.from_numpy(lens).to(DEV)
+    kw = dict(swa_codes=c, swa_scales=s, swa_len=torch.from_numpy(swl).to(DEV), swa_stride=cap, swa_cap=W,
+              swa_row0=cap - W) if W else {}
+    out, lse = K.sparse_attn_decode_mq(q.to(DEV), c, s, lt, torch.from_numpy(topk).to(DEV), fmt, return_lse=True,
+                                       q_pos=None if qpos is None else qpos.to(DEV), **kw)
+    # the same B*Q query rows as separate sequences over copies of the caches
+    cr, sr = c.repeat_interleave(Q, 0).contiguous(), s.repeat_interleave(Q, 0).contiguous()
+    kwr = dict(swa_codes=cr, swa_scales=sr, swa_len=torch.from_numpy(np.repeat(swl, Q)).to(DEV), swa_stride=cap,
+               swa_cap=W, swa_row0=cap - W) if W else {}
+    out_r, lse_r = K.sparse_attn_decode(q.view(B * Q, 64, 512).to(DEV), cr, sr, lt.repeat_interleave(Q),
+                                        torch.from_numpy(topk.reshape(B * Q, k)).to(DEV), fmt, return_lse=True,
+                                        q_pos=None if qpos is None else qpos.view(-1).to(DEV), **kwr)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(B * Q, 64, 512), out_r)
+    assert torch.equal(lse.view(B * Q, 64).view(torch.int32), lse_r.view(torch.int32))
+    o, l = out.cpu(), lse.cpu().numpy()
+    cc, scc = c.cpu().numpy(), s.cpu().numpy()
+    for b, i in sorted({(0, 0), (0, Q - 1), (B - 1, Q // 2), (min(1, B - 1), Q - 1)}):
+        rc, rs = cc[b], scc[b]
+        ro, rl = oracle.attention(q[b, i].numpy(), rc, rs, int(lens[b]), fmt, topk[b, i], rc[cap - W:] if W else None,
+                                  rs[cap - W:] if W else None, int(swl[b]), 1 / np.sqrt(512),
+                                  q_pos=None if qpos is None else int(qpos[b, i]))
+        attn_close(o[b, i:i + 1], ro[None])
+        tol = 1e-4
+        if qpos is not None:
+            sel = [int(p) for p in topk[b, i] if 0 <= p < lens[b]] + list(range(cap - W, cap - W + int(swl[b])))
+            tol = _rope_lse_tol(q[b, i].numpy(), oracle.dequantize(rc[sel], rs[sel], 16, fmt), int(qpos[b, i]))
+        np.testing.assert_allclose(l[b, i], rl, atol=tol, rtol=0)
+
+
 def test_attention_window_only_separate_buffer():
     fmt = 1
     B, cap, W = 2, 64, 128
