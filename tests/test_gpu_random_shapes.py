@@ -14,7 +14,10 @@ sequence:
   pool scores;
 - attention over the GPU's top-k plus a separate window buffer, against the
   oracle's attention on the oracle's own quantisation of the same rows
-  (outputs within 1e-2, log-sum-exp within the test's tolerance).
+  (outputs within 1e-2, log-sum-exp within the test's tolerance);
+- the multi-query attention call (Q = 2..5 queries per sequence, each with
+  its own positions) bit for bit against the single-query call over B*Q
+  sequences holding copies of the caches.
 
 The shapes are small enough for the oracle, and span several tiles, ragged
 tails and the degenerate cases (empty sequences, one-entry windows, k larger
@@ -142,4 +145,29 @@ def test_random_shapes_against_oracle(seed):
             tol = _rope_lse_tol(qan[b], np.concatenate(rows) if rows else np.zeros((0, 512)), int(qpos[b]))
         np.testing.assert_allclose(l[b][visible], rl[visible], atol=tol, rtol=0)
         assert np.isneginf(l[b][~visible]).all()
-    say(f"  ok (certified near-tie index differences: {cert})")
+    # ---- the same shapes with Q queries per sequence in one call: bit for bit
+    # the single-query call over B*Q sequences holding copies of the caches
+    Q = int(r.integers(2, 6))
+    kq = max(1, min(k, 600))
+    tq = np.full((B, Q, kq), -1, np.int32)
+    for b in range(B):
+        for i in range(Q):
+            m = min(kq, int(lens[b]))
+            tq[b, i, :m] = r.choice(int(lens[b]), m, replace=False) if m else []
+    qq = syn.as_bf16_bits(torch.from_numpy(r.standard_normal((B, Q, H, 512)).astype(np.float32))).to(DEV)
+    qpq = torch.from_numpy(r.integers(0, 1 << 20, (B, Q)).astype(np.int64)).to(DEV) if c["rope"] else None
+    om, lm = K.sparse_attn_decode_mq(qq, cache["main_codes"], cache["main_scales"], lt, torch.from_numpy(tq).to(DEV),
+                                     fmt, return_lse=True, q_pos=qpq, **kw)
+    kwr = {}
+    if W > 0:
+        kwr = dict(swa_codes=kw["swa_codes"].repeat_interleave(Q, 0).contiguous(),
+                   swa_scales=kw["swa_scales"].repeat_interleave(Q, 0).contiguous(),
+                   swa_len=kw["swa_len"].repeat_interleave(Q), swa_stride=W, swa_cap=W)
+    orr, lrr = K.sparse_attn_decode(qq.view(B * Q, H, 512), cache["main_codes"].repeat_interleave(Q, 0).contiguous(),
+                                    cache["main_scales"].repeat_interleave(Q, 0).contiguous(), lt.repeat_interleave(Q),
+                                    torch.from_numpy(tq.reshape(B * Q, kq)).to(DEV), fmt, return_lse=True,
+                                    q_pos=None if qpq is None else qpq.view(-1), **kwr)
+    torch.cuda.synchronize()
+    assert torch.equal(om.view(B * Q, H, 512), orr), f"multi-query attention (Q={Q}) differs"
+    assert torch.equal(lm.view(B * Q, H).view(torch.int32), lrr.view(torch.int32))
+    say(f"  ok (certified near-tie index differences: {cert}; multi-query Q={Q})")
