@@ -732,8 +732,12 @@ def sparse_attn_decode_mq(q, main_codes, main_scales, lengths, topk, main_fmt: i
     if swa_cap > 0:
         if swa_codes.dtype != torch.uint8 or swa_scales.dtype != torch.uint8:
             raise TypeError("window planes must be uint8")
+        if swa_codes.device != dev or swa_scales.device != dev:
+            raise ValueError("window planes on another device")
         if not (swa_codes.is_contiguous() and swa_scales.is_contiguous()):
             raise ValueError("window planes must be contiguous")
+        if swa_fmt not in (SWA_MAIN, SWA_FP8):
+            raise ValueError("swa_fmt must be 0 (main format) or 1 (FP8 records)")
         need = swa_row0 + (B - 1) * swa_stride + swa_cap
         if swa_row0 < 0 or swa_codes.numel() < need * rb or swa_scales.numel() < need * sb:
             raise ValueError("window planes smaller than swa_row0 + B rows of swa_stride")
