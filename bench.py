@@ -165,9 +165,10 @@ def attn_sweep(batches, fmt_name, steps, window="tail"):
 
 def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
     """A speculative verify block of Q queries per sequence: the Full indexer as one
-    csa2_index_full_mq call against Q csa2_index_full calls, then the block's
-    attention as one csa2_sparse_attn_decode_mq call against Q
-    csa2_sparse_attn_decode calls; same caches, queries and index lists."""
+    csa2_index_full_mq call against Q csa2_index_full calls, a Reindex layer as
+    one csa2_index_pool_mq call against Q csa2_index_pool calls, then the
+    block's attention as one csa2_sparse_attn_decode_mq call against Q
+    csa2_sparse_attn_decode calls; same caches, queries, pools and index lists."""
     import torch
     import csa2_synth as syn
     import compressed_kv_cache_mxfp4_amd as K
@@ -206,8 +207,8 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
         for i in range(Q):
             K.index_full(ic, isc, lengths, qs[i], ws_[i], k=wl.k, n_blocks=wl.n_blocks, out=outs_1[i], _ws=ws_1)
 
-    res = {}
-    for name, fn in (("multi_query", mq), ("separate", sep)):
+    def graph_us(fn):
+        # the call captured once in a HIP graph, replayed `steps` times
         for _ in range(max(warmup, 1)):
             fn()
         torch.cuda.synchronize()
@@ -221,13 +222,45 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    res = {name: graph_us(fn) for name, fn in (("multi_query", mq), ("separate", sep))}
     for i in range(Q):
         assert torch.equal(outs_mq["topk"][:, i], outs_1[i]["topk"]), "multi-query top-k differs"
+    # Reindex of the verify block: each query rescores its own pool (from the
+    # multi-query Full call) with a second layer's bf16 query, one call for
+    # the B x Q query rows against Q calls of B
+    q2 = torch.stack([syn.index_query(wl, Q + i, dev) for i in range(Q)], 1).contiguous()
+    w2 = torch.stack([syn.index_weights(wl, Q + i, dev) for i in range(Q)], 1).contiguous()
+    q2s = [q2[:, i].contiguous() for i in range(Q)]
+    w2s = [w2[:, i].contiguous() for i in range(Q)]
+    pools = [outs_mq["pool"][:, i].contiguous() for i in range(Q)]
+    plens = [outs_mq["pool_len"][:, i].contiguous() for i in range(Q)]
+    pool_cap = wl.n_blocks * 8
+    ws_pmq = torch.empty(L.csa2_index_pool_workspace(B * Q, pool_cap, wl.k), dtype=torch.uint8, device=dev)
+    ws_p1 = torch.empty(L.csa2_index_pool_workspace(B, pool_cap, wl.k), dtype=torch.uint8, device=dev)
+    rt_mq = dict(topk=torch.empty(B, Q, wl.k, dtype=torch.int32, device=dev))
+    rt_1 = [dict(topk=torch.empty(B, wl.k, dtype=torch.int32, device=dev)) for _ in range(Q)]
+
+    def pmq():
+        K.index_pool_mq(ic, isc, lengths, outs_mq["pool"], outs_mq["pool_len"], q2, w2, k=wl.k, out=rt_mq,
+                        _ws=ws_pmq)
+
+    def psep():
+        for i in range(Q):
+            K.index_pool(ic, isc, lengths, pools[i], plens[i], q2s[i], w2s[i], k=wl.k, out=rt_1[i], _ws=ws_p1)
+
+    res["pool_multi_query"], res["pool_separate"] = graph_us(pmq), graph_us(psep)
+    for i in range(Q):
+        assert torch.equal(rt_mq["topk"][:, i], rt_1[i]["topk"]), "multi-query Reindex top-k differs"
+    # every query row gathers its own pool's cache rows (68 B each) and ids,
+    # reads its query and weights, writes its top-k
+    n_pool = int(outs_mq["pool_len"].sum())
+    pool_bytes = n_pool * (68 + 4) + Q * B * (wl.H_idx * 256 + wl.H_idx * 4 + 8 + wl.k * 4)
     # attention of the verify block: each query over its own top-k (from the
     # multi-query call) plus the sequence's window, one call for the B x Q
     # query rows against Q calls of B
-    del ic, isc, ws_mq, ws_1
+    del ic, isc, ws_mq, ws_1, ws_pmq, ws_p1
     torch.cuda.empty_cache()
     mc = torch.empty(B, cap, 256, dtype=torch.uint8, device=dev)
     ms = torch.empty(B, cap, 32, dtype=torch.uint8, device=dev)
@@ -252,21 +285,7 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
         for i in range(Q):
             K.sparse_attn_decode(aqs[i], mc, ms, lengths, tks[i], K.E8M0, out=dict(out=out_1[i]), _ws=ws_a1, **wkw)
 
-    for name, fn in (("attn_multi_query", amq), ("attn_separate", asep)):
-        for _ in range(max(warmup, 1)):
-            fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    res["attn_multi_query"], res["attn_separate"] = graph_us(amq), graph_us(asep)
     attn_bytes = Q * B * (wl.k * 288 + W * 288 + 64 * 512 * 2 * 2 + wl.k * 4 + 8)
     cache_bytes = B * cap * 68
     per_q = B * (wl.H_idx * (68 if index_q == "fp4" else 256) + wl.H_idx * 4 + 4) + B * (wl.k * 4 + wl.n_blocks * 8 * 4 + 4)
@@ -280,6 +299,11 @@ def verify_bench(wl_name, Q, steps, warmup, index_q="bf16"):
                           positions_scored_per_s=Q * B * cap / (us * 1e-6),
                           algorithmic_bytes=nbytes, achieved_GBs=round(nbytes / (us * 1e-6) / 1e9, 1),
                           frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          reindex=dict(query_rows=B * Q, pool_entries=n_pool,
+                                       us_multi_query=round(res["pool_multi_query"], 2),
+                                       us_separate_calls=round(res["pool_separate"], 2),
+                                       algorithmic_bytes=pool_bytes,
+                                       achieved_GBs=round(pool_bytes / (res["pool_multi_query"] * 1e-6) / 1e9, 1)),
                           attention=dict(query_rows=B * Q, window=W, us_multi_query=round(res["attn_multi_query"], 2),
                                          us_separate_calls=round(res["attn_separate"], 2),
                                          algorithmic_bytes=attn_bytes,

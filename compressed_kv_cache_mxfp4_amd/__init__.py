@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     index_pool_rows,
     paged_alloc,
     index_pool,
+    index_pool_mq,
     index_pool_score,
     index_pool_select,
     lib,

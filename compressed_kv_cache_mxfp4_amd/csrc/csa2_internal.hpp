@@ -81,7 +81,7 @@ int launch_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales,
                             const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
                             int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
                             const float* w, int H, float* pool_scores_opt, void* ws, hipStream_t st,
-                            const int32_t* pool_rows = nullptr);
+                            const int32_t* pool_rows = nullptr, int qps = 1);
 int launch_index_pool_select(int B, const int32_t* pool, const int32_t* pool_len, int pool_cap, int k,
                              int32_t* topk, const float* pool_scores_opt, void* ws, hipStream_t st,
                              const int32_t* pool_rows = nullptr, int32_t* topk_rows = nullptr);
@@ -91,7 +91,7 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
                       const float* w, int H, int k,
                       int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st,
-                      const int32_t* pool_rows = nullptr, int32_t* topk_rows = nullptr);
+                      const int32_t* pool_rows = nullptr, int32_t* topk_rows = nullptr, int qps = 1);
 
 size_t attn_ws_bytes(int B, int H, int k, int swa_cap);
 

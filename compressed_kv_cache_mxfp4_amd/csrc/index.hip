@@ -1116,7 +1116,8 @@ int launch_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales,
                             const int32_t* len, int B, const int32_t* pool, const int32_t* pool_len,
                             int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
                             const float* w, int H, float* pool_scores_opt, void* ws, hipStream_t st,
-                            const int32_t* pool_rows) {
+                            const int32_t* pool_rows, int qps) {
+  // B counts query rows; with qps > 1 row b rescores its own pool over cache b / qps
   if (B == 0) return 0;
   const IndexPoolWs l = index_pool_ws_layout(B, pool_cap);
   float* ps = pool_scores_opt ? pool_scores_opt : reinterpret_cast<float*>((char*)ws + l.scores_off);
@@ -1128,7 +1129,7 @@ int launch_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales,
     // with physical pool rows: gather from one pool of cap rows, no lengths
     launch_score<true>(MT, per_seq, B, st, idx_codes, idx_scales, cap, pool_rows ? nullptr : len,
                        pool_rows ? pool_rows : pool, pool_len, pool_cap, q, q4c, q4s, w, H, ps, pool_cap, gmax, ngs,
-                       1, PageMap{nullptr, 0, 0, 0}, pool_rows ? 0 : cap);
+                       qps, PageMap{nullptr, 0, 0, 0}, pool_rows ? 0 : cap);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -1137,10 +1138,10 @@ int launch_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64
                       int pool_cap, const uint16_t* q, const uint8_t* q4c, const uint8_t* q4s,
                       const float* w, int H, int k,
                       int32_t* topk, float* pool_scores_opt, void* ws, hipStream_t st,
-                      const int32_t* pool_rows, int32_t* topk_rows) {
+                      const int32_t* pool_rows, int32_t* topk_rows, int qps) {
   if (B == 0) return 0;
   if (launch_index_pool_score(idx_codes, idx_scales, cap, len, B, pool, pool_len, pool_cap, q, q4c, q4s, w, H,
-                              pool_scores_opt, ws, st, pool_rows) != 0)
+                              pool_scores_opt, ws, st, pool_rows, qps) != 0)
     return -1;
   return launch_index_pool_select(B, pool, pool_len, pool_cap, k, topk, pool_scores_opt, ws, st, pool_rows,
                                   topk_rows);

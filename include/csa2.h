@@ -81,7 +81,7 @@ extern "C" {
 
 #define CSA2_MAX_TOPK 2048
 #define CSA2_MAX_POOL 16384        /* n_blocks * block upper bound                */
-#define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache (csa2_index_full_mq, csa2_sparse_attn_decode_mq) */
+#define CSA2_MAX_QUERIES_PER_SEQ 16 /* queries sharing one cache (the *_mq calls) */
 #define CSA2_MIN_PAGE_SHIFT 6      /* paged cache: pages of 2^6 .. 2^20 entries    */
 #define CSA2_MAX_PAGE_SHIFT 20
 #define CSA2_MAX_POOL_ROWS (1 << 26) /* rows of a paged pool (32-bit byte offsets)  */
@@ -295,6 +295,26 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                     const int32_t* pool_len, int32_t pool_cap, const uint16_t* q,
                     const float* w, int32_t H, int32_t k, int32_t* topk,
                     float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_pool_mq -- csa2_index_pool for Q queries per sequence (the draft
+ * positions of a verify block [WG 7]), each rescoring its own pool (as
+ * csa2_index_full_mq returns them) over its sequence's cache, in one call.
+ *   pool     : int32 [B][Q][pool_cap];  pool_len : int32 [B][Q];
+ *   q        : bf16 bits [B][Q][H][128];  w : fp32 [B][Q][H];
+ *   topk     : out int32 [B][Q][k];  pool_scores_opt : out fp32 [B][Q][pool_cap].
+ *   idx planes and len [B] are per sequence.  Q : 1..CSA2_MAX_QUERIES_PER_SEQ.
+ *   ws       : at least csa2_index_pool_workspace(B*Q, pool_cap, k) bytes.
+ * Query row (b, i) gives exactly what csa2_index_pool gives for row i of the
+ * sequence alone; with Q = 1 this is csa2_index_pool.  The scoring kernel
+ * places a sequence's Q rows side by side (as in csa2_index_full_mq).
+ * Errors: as csa2_index_pool; Q outside 1..CSA2_MAX_QUERIES_PER_SEQ is
+ * CSA2_ERR_SHAPE.
+ */
+int csa2_index_pool_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                       int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                       const uint16_t* q, const float* w, int32_t H, int32_t k, int32_t* topk,
+                       float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_pool_score / csa2_index_pool_select -- the two phases of

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
             "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq", "csa2_index_full_mq_fp4q",
             "csa2_cache_append_paged", "csa2_index_full_paged", "csa2_index_pool_rows",
-            "csa2_sparse_attn_decode_rows", "csa2_sparse_attn_decode_mq",
+            "csa2_sparse_attn_decode_rows", "csa2_sparse_attn_decode_mq", "csa2_index_pool_mq",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -246,6 +246,28 @@ def test_attention_mq_validation(lib):
     need = lib.csa2_attn_workspace(80, 64, 512, 128)
     assert lib.csa2_attn_workspace(16, 64, 512, 128) < need
     assert call(22, need - 1) == ERR_WS
+
+
+def test_index_pool_mq_validation(lib):
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    f = lib.csa2_index_pool_mq
+    f.argtypes = [P, P, i64, P, i32, i32, P, P, i32, P, P, i32, i32, P, P, P, ctypes.c_size_t, P]
+    base = [FAKE, FAKE, 4096, FAKE, 2, 5, FAKE, FAKE, 16384, FAKE, FAKE, 64, 512, FAKE, None, FAKE, 1 << 40, None]
+
+    def call(i, v):
+        args = list(base)
+        args[i] = v
+        return f(*args)
+
+    assert call(5, 0) == ERR_SHAPE        # Q
+    assert call(5, 17) == ERR_SHAPE
+    assert call(8, 20000) == ERR_SHAPE    # pool capacity
+    assert call(11, 12) == ERR_UNSUP      # indexer heads
+    assert call(6, None) == ERR_NULL
+    assert call(0, FAKE_ODD) == ERR_ALIGN
+    assert call(4, 0) == CSA2_OK          # empty batch
+    need = lib.csa2_index_pool_workspace(10, 16384, 512)
+    assert call(16, need - 1) == ERR_WS   # the workspace holds B*Q = 10 rows
 
 
 def test_attention_noalloc_validation(lib):

@@ -420,6 +420,50 @@ def test_index_full_mq_equals_one_query_calls(B, Q, H, k, nb):
 
 
 
+@pytest.mark.parametrize("B,Q,H,k,nb", [(8, 5, 64, 512, 64), (3, 3, 32, 700, 300), (2, 1, 8, 64, 16)])
+def test_index_pool_mq_equals_one_query_calls(B, Q, H, k, nb):
+    # Reindex for several queries per cache: each query row rescores its own
+    # pool (the multi-query Full call's) and must be bit-identical to the
+    # single-query Reindex call on its sequence's cache, and match the oracle
+    say(f"index_pool_mq B={B} Q={Q} H={H} k={k} n_blocks={nb}")
+    cap = 6000
+    wl = syn.small("pmq", 90 + B + Q, B=B, cap=cap, H_idx=H, k=k, n_blocks=nb)
+    cache = build_gpu_cache(wl, 0)
+    lens = [cap, 5999, 1001, 7, 0, 4096, 3000, 65][:B]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q0 = torch.stack([syn.index_query(wl, i, DEV) for i in range(Q)], 1).contiguous()
+    w0 = torch.stack([syn.index_weights(wl, i, DEV) for i in range(Q)], 1).contiguous()
+    _, pool, pool_len = K.index_full_mq(cache["idx_codes"], cache["idx_scales"], lt, q0, w0, k=k, n_blocks=nb)
+    q1 = torch.stack([syn.index_query(wl, Q + i, DEV) for i in range(Q)], 1).contiguous()
+    w1 = torch.stack([syn.index_weights(wl, Q + i, DEV) for i in range(Q)], 1).contiguous()
+    topk, ps = K.index_pool_mq(cache["idx_codes"], cache["idx_scales"], lt, pool, pool_len, q1, w1, k=k,
+                               return_scores=True)
+    torch.cuda.synchronize()
+    pln = pool_len.cpu().numpy()
+    for i in range(Q):
+        t1, s1 = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool[:, i].contiguous(),
+                              pool_len[:, i].contiguous(), q1[:, i].contiguous(), w1[:, i].contiguous(), k=k,
+                              return_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(topk[:, i], t1), f"query {i}: top-k differs from the single-query call"
+        for b in range(B):
+            n = int(pln[b, i])
+            assert torch.equal(ps[b, i, :n].view(torch.int32), s1[b, :n].view(torch.int32))
+    # the oracle on a sample of (sequence, query) rows
+    topk, ps, pooln = topk.cpu().numpy(), ps.cpu().numpy(), pool.cpu().numpy()
+    qn, wn = q1.cpu().numpy(), w1.cpu().numpy()
+    for b, i in sorted({(0, 0), (0, Q - 1), (B - 1, Q // 2), (min(1, B - 1), Q - 1)}):
+        n = int(pln[b, i])
+        if n == 0:
+            assert np.all(topk[b, i] == -1)
+            continue
+        ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
+        _, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], lens[b], pooln[b, i], n, qn[b, i],
+                                   wn[b, i], k)
+        score_close(ps[b, i, :n], rps)
+        assert np.array_equal(topk[b, i], brute_topk(ps[b, i, :n], k, pooln[b, i, :n]))
+
+
 @pytest.mark.parametrize("B,Q,H", [(8, 5, 64), (3, 2, 16)])
 def test_index_full_mq_fp4_query_equals_one_query_calls(B, Q, H):
     # FP4 queries (E2M1 + E8M0 per 32 dims): each query row of the
