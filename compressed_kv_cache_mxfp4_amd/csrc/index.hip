@@ -1024,13 +1024,17 @@ static void launch_score(int MT, int per_seq, int B, hipStream_t st, const uint8
 }
 
 // Workgroups per sequence for `items` scored entries: enough resident waves
-// to cover the chip, never more than one super-tile per wave.
+// to cover the chip, never more than one super-tile per wave.  When the
+// resident target binds, the count rounds down: the waves walk their
+// super-tiles with a grid stride, and a launch even slightly over the target
+// would run its last workgroups as a second, nearly empty round (80 query
+// rows of 16,384 pool entries: 7 workgroups a row is 2,240 waves against
+// 2,048 resident, 6 is 1,920).
 static unsigned score_wgs(int64_t items, int B, int target_waves) {
   const int64_t tiles = (items + kSuperTile - 1) / kSuperTile;
   int64_t waves = target_waves / (B > 0 ? B : 1);
   if (waves < 4) waves = 4;
-  if (waves > tiles) waves = tiles;
-  const int64_t wgs = (waves + 3) / 4;
+  const int64_t wgs = waves >= tiles ? (tiles + 3) / 4 : waves / 4;
   return (unsigned)(wgs > 0 ? wgs : 1);
 }
 
