@@ -1534,9 +1534,14 @@ int launch_sparse_attn(const uint16_t* q, int H, const uint8_t* main_codes,
   float4* ml = reinterpret_cast<float4*>(wsb + l.ml_off);
   if (H == 64 && B >= kSeqMinBatch && nslots >= kTRows) {
     // throughput variant: S splits per sequence, enough to give every CU a
-    // workgroup, at most one per 128 row slots (the workspace's partials)
+    // workgroup, at most one per 128 row slots (the workspace's partials).
+    // The grid holds ceil(B / 8) groups of 8 sequences, so S comes from that
+    // count: 256 / B splits would overfill the chip where B is not a
+    // multiple of 8 (B = 50: 280 workgroups, a second round, 37.9 against
+    // 22.8 us).  At most 4 splits: the merge prefetches its next round of
+    // partials only then (B = 48: 5 splits 26.8 us, 4 splits 23.1 us).
     const int nch = w8 ? (k + 31) / 32 + (swa_cap + 15) / 16 : (nslots + kTRows - 1) / kTRows;
-    int Sq = B >= 256 ? 1 : 256 / (int)B;
+    int Sq = B >= 256 ? 1 : std::min(4, 32 / (((int)B + 7) / 8));
     Sq = std::min(Sq, std::min(nch, attn_splits(k, swa_cap)));
     const unsigned tgrid = (unsigned)(((B + 7) / 8) * Sq * 8);
     auto tgo = [&](auto kern, bool lds_ok) -> bool {

@@ -282,10 +282,12 @@ def _big_batch_case(B, cap, k, W, fmt, seed, sample, rope=False):
                                             (128, 600, 100, 0, False), (256, 77, 0, 1, False),
                                             (256, 512, 128, 0, False), (64, 512, 128, 0, True),
                                             (256, 512, 128, 1, True),
+                                            # 3 splits; 2 splits where 3 would overfill the chip
+                                            (72, 512, 128, 1, False), (84, 600, 128, 0, True),
                                             # 8-wave split kernel (below 48 sequences, past one round of 10-wave)
                                             (40, 512, 128, 0, True), (28, 300, 128, 1, False)])
 def test_attention_large_batch(B, k, W, fmt, rope):
-    """Batches that take the all-heads throughput kernel: 5, 4, 2 and 1 splits
+    """Batches that take the all-heads throughput kernel: 4, 3, 2 and 1 splits
     per sequence (ragged chunk ranges, k not a multiple of the 32-row chunk),
     and, below 48 sequences past one round of 10-wave workgroups, the 8-wave
     split kernel;
