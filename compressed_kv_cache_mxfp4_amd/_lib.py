@@ -72,6 +72,7 @@ def lib():
     L.csa2_sparse_attn_decode_mq.argtypes = [P, i32, i32, P, P, i64, i32, P, P, i32, i32, P, P, i64, i32,
                                              P, i32, f32, P, P, P, P, sz, P]
     L.csa2_index_pool_mq.argtypes = [P, P, i64, P, i32, i32, P, P, i32, P, P, i32, i32, P, P, P, sz, P]
+    L.csa2_index_pool_mq_fp4q.argtypes = [P, P, i64, P, i32, i32, P, P, i32, P, P, P, i32, i32, P, P, P, sz, P]
     L.csa2_window_write.argtypes = [P, i32, i32, P, f32, i32, P, i32, P, P, P, P]
     L.csa2_cache_append_paged.argtypes = [P, P, i32, i32, P, f32, P, i32, i32, P, P, P, P, i64, P, i32, i32, P, P, P]
     L.csa2_index_full_paged.argtypes = [P, P, i64, P, i32, i32, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P,
@@ -519,20 +520,29 @@ def index_full_select(cap: int, lengths, ws, k: int = 512, n_blocks: int = 2048,
 def index_pool_mq(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int = 512,
                   return_scores: bool = False, out=None, _ws=None):
     """Reindex for Q queries per sequence (csa2_index_pool_mq): pool int32
-    [B][Q][pool_cap], pool_len [B][Q], q bf16 [B][Q][H][128], w fp32 [B][Q][H];
-    the indexer cache and lengths [B] are per sequence.  Returns topk int32
-    [B][Q][k] (and the pool scores fp32 [B][Q][pool_cap])."""
+    [B][Q][pool_cap], pool_len [B][Q], q bf16 [B][Q][H][128] -- or FP4 queries
+    (codes u8 [B][Q][H][64], E8M0 scales u8 [B][Q][H][4],
+    csa2_index_pool_mq_fp4q) -- w fp32 [B][Q][H]; the indexer cache and
+    lengths [B] are per sequence.  Returns topk int32 [B][Q][k] (and the pool
+    scores fp32 [B][Q][pool_cap])."""
     _req(idx_codes, "idx_codes", torch.uint8)
     dev = idx_codes.device
     B, cap = idx_codes.shape[0], idx_codes.shape[1]
     _req(idx_codes, "idx_codes", torch.uint8, dev, (B, cap, 64))
     _req(idx_scales, "idx_scales", torch.uint8, dev, (B, cap, 4))
     _req(lengths, "lengths", torch.int32, dev, (B,))
-    q = _bits16(q)
-    if q.dim() != 4:
-        raise ValueError("q must be [B][Q][H][128]")
-    Q, H = q.shape[1], q.shape[2]
-    _req(q, "q", torch.int16, dev, (B, Q, H, 128))
+    if isinstance(q, (tuple, list)):
+        qc, qs = q
+        Q, H = qc.shape[1], qc.shape[2]
+        _req(qc, "q codes", torch.uint8, dev, (B, Q, H, 64))
+        _req(qs, "q scales", torch.uint8, dev, (B, Q, H, 4))
+        q = None
+    else:
+        q = _bits16(q)
+        if q.dim() != 4:
+            raise ValueError("q must be [B][Q][H][128]")
+        Q, H = q.shape[1], q.shape[2]
+        _req(q, "q", torch.int16, dev, (B, Q, H, 128))
     _req(w, "w", torch.float32, dev, (B, Q, H))
     pool_cap = pool.shape[2]
     _req(pool, "pool", torch.int32, dev, (B, Q, pool_cap))
@@ -545,9 +555,15 @@ def index_pool_mq(idx_codes, idx_scales, lengths, pool, pool_len, q, w, k: int =
     if return_scores and ps is None:
         ps = torch.empty(B, Q, pool_cap, dtype=torch.float32, device=dev)
     ws = _ws if _ws is not None else workspace(lib().csa2_index_pool_workspace(B * Q, pool_cap, k), dev, "pool")
-    _check(lib().csa2_index_pool_mq(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q, _ptr(pool),
-                                    _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, k, _ptr(topk), _ptr(ps),
-                                    _ptr(ws), ws.numel(), _stream(dev)), "csa2_index_pool_mq")
+    if q is None:
+        _check(lib().csa2_index_pool_mq_fp4q(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q,
+                                             _ptr(pool), _ptr(pool_len), pool_cap, _ptr(qc), _ptr(qs), _ptr(w), H,
+                                             k, _ptr(topk), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)),
+               "csa2_index_pool_mq_fp4q")
+    else:
+        _check(lib().csa2_index_pool_mq(_ptr(idx_codes), _ptr(idx_scales), cap, _ptr(lengths), B, Q, _ptr(pool),
+                                        _ptr(pool_len), pool_cap, _ptr(q), _ptr(w), H, k, _ptr(topk), _ptr(ps),
+                                        _ptr(ws), ws.numel(), _stream(dev)), "csa2_index_pool_mq")
     return (topk, ps) if return_scores else topk
 
 

@@ -338,23 +338,43 @@ int csa2_index_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t
                                           ws, as_stream(stream)));
 }
 
-int csa2_index_pool_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
-                       int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
-                       const uint16_t* q, const float* w, int32_t H, int32_t k, int32_t* topk,
-                       float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream) {
+static int index_pool_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                         int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                         bool fp4q, const uint16_t* q, const uint8_t* q_codes, const uint8_t* q_scales,
+                         const float* w, int32_t H, int32_t k, int32_t* topk, float* pool_scores_opt, void* ws,
+                         size_t ws_bytes, void* stream) {
   if (Q < 1 || Q > CSA2_MAX_QUERIES_PER_SEQ) return CSA2_ERR_SHAPE;
   if (B < 0 || (int64_t)B * Q > INT32_MAX || cap <= 0 || cap > CSA2_MAX_CACHE_ROWS) return CSA2_ERR_SHAPE;
   if (pool_cap < 0 || pool_cap > CSA2_MAX_POOL) return CSA2_ERR_SHAPE;
   if (k < 1 || k > CSA2_MAX_TOPK) return CSA2_ERR_SHAPE;
   if (!valid_index_heads(H)) return CSA2_ERR_UNSUPPORTED;
   if (B == 0) return CSA2_OK;
-  if (!idx_codes || !idx_scales || !len || !pool || !pool_len || !q || !w || !topk) return CSA2_ERR_NULL;
-  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(q)) return CSA2_ERR_ALIGN;
+  if (!idx_codes || !idx_scales || !len || !pool || !pool_len || !w || !topk) return CSA2_ERR_NULL;
+  if (fp4q ? (!q_codes || !q_scales) : !q) return CSA2_ERR_NULL;
+  if (!aligned16(idx_codes) || !aligned16(idx_scales) || !aligned16(fp4q ? (const void*)q_codes : (const void*)q))
+    return CSA2_ERR_ALIGN;
   const size_t need = csa2_index_pool_workspace(B * Q, pool_cap, k);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
-  return launched(csa2::launch_index_pool(idx_codes, idx_scales, cap, len, B * Q, pool, pool_len, pool_cap, q,
-                                          nullptr, nullptr, w, H, k, topk, pool_scores_opt, ws, as_stream(stream),
-                                          nullptr, nullptr, Q));
+  return launched(csa2::launch_index_pool(idx_codes, idx_scales, cap, len, B * Q, pool, pool_len, pool_cap,
+                                          fp4q ? nullptr : q, fp4q ? q_codes : nullptr, fp4q ? q_scales : nullptr,
+                                          w, H, k, topk,
+                                          pool_scores_opt, ws, as_stream(stream), nullptr, nullptr, Q));
+}
+
+int csa2_index_pool_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                       int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                       const uint16_t* q, const float* w, int32_t H, int32_t k, int32_t* topk,
+                       float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream) {
+  return index_pool_mq(idx_codes, idx_scales, cap, len, B, Q, pool, pool_len, pool_cap, false, q, nullptr, nullptr,
+                       w, H, k, topk, pool_scores_opt, ws, ws_bytes, stream);
+}
+
+int csa2_index_pool_mq_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                            int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                            const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int32_t H, int32_t k,
+                            int32_t* topk, float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream) {
+  return index_pool_mq(idx_codes, idx_scales, cap, len, B, Q, pool, pool_len, pool_cap, true, nullptr, q_codes,
+                       q_scales, w, H, k, topk, pool_scores_opt, ws, ws_bytes, stream);
 }
 
 int csa2_index_pool_score(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,

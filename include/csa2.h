@@ -315,6 +315,19 @@ int csa2_index_pool_mq(const uint8_t* idx_codes, const uint8_t* idx_scales, int6
                        int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
                        const uint16_t* q, const float* w, int32_t H, int32_t k, int32_t* topk,
                        float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
+/*
+ * csa2_index_pool_mq_fp4q -- csa2_index_pool_mq with FP4 indexer queries, as
+ * csa2_index_pool_fp4q takes them [syt-nju.github.io, section FP4 主 KV 缓存]:
+ *   q_codes  : u8 [B][Q][H][64] E2M1 codes, 16-byte aligned;
+ *   q_scales : u8 [B][Q][H][4] E8M0 scale bytes, one per 32 dims.
+ * Every other argument, the outputs and the status codes are those of
+ * csa2_index_pool_mq; query row (b, i) equals csa2_index_pool_fp4q on row i
+ * of the sequence alone.
+ */
+int csa2_index_pool_mq_fp4q(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t cap, const int32_t* len,
+                            int32_t B, int32_t Q, const int32_t* pool, const int32_t* pool_len, int32_t pool_cap,
+                            const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int32_t H, int32_t k,
+                            int32_t* topk, float* pool_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_pool_score / csa2_index_pool_select -- the two phases of

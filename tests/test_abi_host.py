@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"csa2_cache_write", "csa2_cache_append", "csa2_append_state_bytes", "csa2_index_full",
             "csa2_index_pool", "csa2_sparse_attn_decode", "csa2_window_write", "csa2_index_full_mq", "csa2_index_full_mq_fp4q",
             "csa2_cache_append_paged", "csa2_index_full_paged", "csa2_index_pool_rows",
-            "csa2_sparse_attn_decode_rows", "csa2_sparse_attn_decode_mq", "csa2_index_pool_mq",
+            "csa2_sparse_attn_decode_rows", "csa2_sparse_attn_decode_mq", "csa2_index_pool_mq", "csa2_index_pool_mq_fp4q",
             "csa2_quantize_fp4"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
@@ -268,6 +268,17 @@ def test_index_pool_mq_validation(lib):
     assert call(4, 0) == CSA2_OK          # empty batch
     need = lib.csa2_index_pool_workspace(10, 16384, 512)
     assert call(16, need - 1) == ERR_WS   # the workspace holds B*Q = 10 rows
+    g = lib.csa2_index_pool_mq_fp4q
+    g.argtypes = [P, P, i64, P, i32, i32, P, P, i32, P, P, P, i32, i32, P, P, P, ctypes.c_size_t, P]
+    base4 = base[:9] + [FAKE, FAKE] + base[10:]
+    for i, v, want in [(5, 0, ERR_SHAPE), (5, 17, ERR_SHAPE), (9, None, ERR_NULL), (10, None, ERR_NULL),
+                       (9, FAKE_ODD, ERR_ALIGN), (12, 12, ERR_UNSUP), (4, 0, CSA2_OK)]:
+        args = list(base4)
+        args[i] = v
+        assert g(*args) == want, (i, v)
+    args = list(base4)
+    args[17] = need - 1
+    assert g(*args) == ERR_WS
 
 
 def test_attention_noalloc_validation(lib):

@@ -420,12 +420,14 @@ def test_index_full_mq_equals_one_query_calls(B, Q, H, k, nb):
 
 
 
-@pytest.mark.parametrize("B,Q,H,k,nb", [(8, 5, 64, 512, 64), (3, 3, 32, 700, 300), (2, 1, 8, 64, 16)])
-def test_index_pool_mq_equals_one_query_calls(B, Q, H, k, nb):
+@pytest.mark.parametrize("B,Q,H,k,nb,fp4", [(8, 5, 64, 512, 64, False), (3, 3, 32, 700, 300, False),
+                                             (2, 1, 8, 64, 16, False), (8, 5, 64, 512, 64, True),
+                                             (3, 2, 16, 100, 40, True)])
+def test_index_pool_mq_equals_one_query_calls(B, Q, H, k, nb, fp4):
     # Reindex for several queries per cache: each query row rescores its own
     # pool (the multi-query Full call's) and must be bit-identical to the
     # single-query Reindex call on its sequence's cache, and match the oracle
-    say(f"index_pool_mq B={B} Q={Q} H={H} k={k} n_blocks={nb}")
+    say(f"index_pool_mq B={B} Q={Q} H={H} k={k} n_blocks={nb} fp4 query={fp4}")
     cap = 6000
     wl = syn.small("pmq", 90 + B + Q, B=B, cap=cap, H_idx=H, k=k, n_blocks=nb)
     cache = build_gpu_cache(wl, 0)
@@ -436,13 +438,20 @@ def test_index_pool_mq_equals_one_query_calls(B, Q, H, k, nb):
     _, pool, pool_len = K.index_full_mq(cache["idx_codes"], cache["idx_scales"], lt, q0, w0, k=k, n_blocks=nb)
     q1 = torch.stack([syn.index_query(wl, Q + i, DEV) for i in range(Q)], 1).contiguous()
     w1 = torch.stack([syn.index_weights(wl, Q + i, DEV) for i in range(Q)], 1).contiguous()
-    topk, ps = K.index_pool_mq(cache["idx_codes"], cache["idx_scales"], lt, pool, pool_len, q1, w1, k=k,
+    qarg, qrow = q1, lambda i: q1[:, i].contiguous()
+    if fp4:
+        # FP4 queries (E2M1 + E8M0 per 32 dims); the oracle scores their
+        # dequantised values, exact in bf16
+        qc, qs = K.quantize_fp4(q1.view(torch.bfloat16).float().reshape(-1, 128).contiguous(), 32, K.E8M0)
+        qc, qs = qc.view(B, Q, H, 64), qs.view(B, Q, H, 4)
+        qarg, qrow = (qc, qs), lambda i: (qc[:, i].contiguous(), qs[:, i].contiguous())
+    topk, ps = K.index_pool_mq(cache["idx_codes"], cache["idx_scales"], lt, pool, pool_len, qarg, w1, k=k,
                                return_scores=True)
     torch.cuda.synchronize()
     pln = pool_len.cpu().numpy()
     for i in range(Q):
         t1, s1 = K.index_pool(cache["idx_codes"], cache["idx_scales"], lt, pool[:, i].contiguous(),
-                              pool_len[:, i].contiguous(), q1[:, i].contiguous(), w1[:, i].contiguous(), k=k,
+                              pool_len[:, i].contiguous(), qrow(i), w1[:, i].contiguous(), k=k,
                               return_scores=True)
         torch.cuda.synchronize()
         assert torch.equal(topk[:, i], t1), f"query {i}: top-k differs from the single-query call"
@@ -458,8 +467,11 @@ def test_index_pool_mq_equals_one_query_calls(B, Q, H, k, nb):
             assert np.all(topk[b, i] == -1)
             continue
         ref = oracle_cache_seq(wl, b, 0, cache, need_main=False)
-        _, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], lens[b], pooln[b, i], n, qn[b, i],
-                                   wn[b, i], k)
+        qb = qn[b, i]
+        if fp4:
+            qb = _oracle_fp4_query_bits(q1.view(torch.bfloat16).float().cpu().numpy()[b, i],
+                                        qc.cpu().numpy()[b, i], qs.cpu().numpy()[b, i])
+        _, rps = oracle.index_pool(ref["idx_codes"], ref["idx_scales"], lens[b], pooln[b, i], n, qb, wn[b, i], k)
         score_close(ps[b, i, :n], rps)
         assert np.array_equal(topk[b, i], brute_topk(ps[b, i, :n], k, pooln[b, i, :n]))
 
